@@ -1,0 +1,186 @@
+/*
+ * lsa_oracle.c -- plain, slow, double-precision CPU oracle for the LSA decode
+ * hot path.  TEST INFRASTRUCTURE ONLY (see lsa_oracle.h): the product path
+ * never links or calls it.
+ *
+ * Each function follows the definition of its step as the pages state it:
+ *   oracle_score      dual-encoder inner product per chunk (wiki note
+ *                     flowchart + "Key points"; review section 3-2-4; abstract).
+ *   oracle_select     top-k keep set per stream (review section 3-2-3 step 5);
+ *                     ties go to the lower chunk index, NaN ranks last.
+ *   oracle_gather     copy of the kept chunks into a resident pool (wiki note
+ *                     flowchart "Resident KV chunks"; molayo explainer,
+ *                     "selective gather").
+ *   oracle_attention  softmax attention restricted to the kept chunks' tokens
+ *                     (review section 3-2-3 steps 6-7), computed with a full
+ *                     max pass then a weighted-sum pass.
+ */
+#include "lsa_oracle.h"
+
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* Exact widening of one stored element to double. */
+static double elem(const void* base, int64_t i, int32_t dtype) {
+  if (dtype == ORACLE_BF16) {
+    uint16_t h = ((const uint16_t*)base)[i];
+    uint32_t u = ((uint32_t)h) << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+  }
+  return (double)((const float*)base)[i];
+}
+
+int32_t oracle_keep_count(int32_t n_chunks, int32_t num, int32_t den, int32_t round_up) {
+  if (n_chunks <= 0 || num <= 0 || den <= 0) return 0;
+  int64_t p = (int64_t)n_chunks * (int64_t)num;
+  int64_t k = round_up ? (p + den - 1) / den : p / den;
+  if (k < 1) k = 1;
+  if (k > n_chunks) k = n_chunks;
+  return (int32_t)k;
+}
+
+void oracle_score(int32_t B, int32_t D, int32_t dtype, const void* q, const void* emb,
+                  const int32_t* chunk_off, double* scores) {
+  for (int32_t b = 0; b < B; ++b) {
+    for (int64_t row = chunk_off[b]; row < chunk_off[b + 1]; ++row) {
+      double s = 0.0;
+      for (int32_t j = 0; j < D; ++j)
+        s += elem(q, (int64_t)b * D + j, dtype) * elem(emb, row * D + j, dtype);
+      scores[row] = s;
+    }
+  }
+}
+
+typedef struct {
+  double s;
+  int32_t n;
+} ranked;
+
+/* Rank order: higher score first; NaN after every number; equal scores (and
+ * NaN among NaN) by lower chunk index.  -0.0 and +0.0 compare equal. */
+static int rank_cmp(const void* pa, const void* pb) {
+  const ranked* a = (const ranked*)pa;
+  const ranked* b = (const ranked*)pb;
+  int an = isnan(a->s), bn = isnan(b->s);
+  if (an != bn) return an ? 1 : -1;
+  if (!an) {
+    if (a->s > b->s) return -1;
+    if (a->s < b->s) return 1;
+  }
+  return (a->n < b->n) ? -1 : (a->n > b->n);
+}
+
+static int int_cmp(const void* pa, const void* pb) {
+  int32_t a = *(const int32_t*)pa, b = *(const int32_t*)pb;
+  return (a > b) - (a < b);
+}
+
+int32_t oracle_select(int32_t B, const double* scores, const int32_t* chunk_off,
+                      const int32_t* sel_off, int32_t* sel_idx) {
+  for (int32_t b = 0; b < B; ++b) {
+    int32_t n = chunk_off[b + 1] - chunk_off[b];
+    int32_t k = sel_off[b + 1] - sel_off[b];
+    if (k < 0 || k > n) return -1;
+    if (k == 0) continue;
+    ranked* r = (ranked*)malloc(sizeof(ranked) * (size_t)n);
+    for (int32_t i = 0; i < n; ++i) {
+      r[i].s = scores[chunk_off[b] + i];
+      r[i].n = i;
+    }
+    qsort(r, (size_t)n, sizeof(ranked), rank_cmp);
+    int32_t* out = sel_idx + sel_off[b];
+    for (int32_t i = 0; i < k; ++i) out[i] = r[i].n;
+    qsort(out, (size_t)k, sizeof(int32_t), int_cmp);
+    free(r);
+  }
+  return 0;
+}
+
+void oracle_gather(int32_t B, int32_t C, int64_t row_bytes, const void* store,
+                   const int64_t* tok_off, const int32_t* sel_idx, const int32_t* sel_off,
+                   void* pool) {
+  const unsigned char* src = (const unsigned char*)store;
+  unsigned char* dst = (unsigned char*)pool;
+  for (int32_t b = 0; b < B; ++b) {
+    int64_t len = tok_off[b + 1] - tok_off[b];
+    for (int32_t j = sel_off[b]; j < sel_off[b + 1]; ++j) {
+      int64_t first = (int64_t)sel_idx[j] * C;
+      for (int32_t r = 0; r < C; ++r) {
+        unsigned char* d = dst + ((int64_t)j * C + r) * row_bytes;
+        if (first + r < len)
+          memcpy(d, src + (tok_off[b] + first + r) * row_bytes, (size_t)row_bytes);
+        else
+          memset(d, 0, (size_t)row_bytes);
+      }
+    }
+  }
+}
+
+void oracle_attention(int32_t B, int32_t H, int32_t dqk, int32_t dv, int32_t v_aliases_k,
+                      int32_t dtype, int32_t C, double scale, const void* Q, const void* K,
+                      const void* V, const int64_t* tok_off, const int32_t* sel_idx,
+                      const int32_t* sel_off, double* out, double* lse, int32_t nthreads) {
+  const void* vbase = v_aliases_k ? K : V;
+  const int64_t vstride = v_aliases_k ? dqk : dv;
+  const int64_t pairs = (int64_t)B * H;
+  if (nthreads < 1) nthreads = 1;
+#ifdef _OPENMP
+#pragma omp parallel for num_threads(nthreads) schedule(dynamic, 1)
+#endif
+  for (int64_t p = 0; p < pairs; ++p) {
+    const int32_t b = (int32_t)(p / H);
+    const int32_t h = (int32_t)(p % H);
+    const int64_t len = tok_off[b + 1] - tok_off[b];
+    const int64_t max_tok = (int64_t)(sel_off[b + 1] - sel_off[b]) * C;
+    double* x = (double*)malloc(sizeof(double) * (size_t)(max_tok > 0 ? max_tok : 1));
+    int64_t* row = (int64_t*)malloc(sizeof(int64_t) * (size_t)(max_tok > 0 ? max_tok : 1));
+    int64_t nt = 0;
+    /* pass 1: logits of every kept token, and their maximum */
+    double m = -INFINITY;
+    for (int32_t j = sel_off[b]; j < sel_off[b + 1]; ++j) {
+      int64_t first = (int64_t)sel_idx[j] * C;
+      for (int64_t t = first; t < first + C && t < len; ++t) {
+        int64_t r = tok_off[b] + t;
+        double dot = 0.0;
+        for (int32_t i = 0; i < dqk; ++i)
+          dot += elem(Q, ((int64_t)b * H + h) * dqk + i, dtype) * elem(K, r * dqk + i, dtype);
+        x[nt] = scale * dot;
+        row[nt] = r;
+        if (x[nt] > m) m = x[nt];
+        ++nt;
+      }
+    }
+    double* o = out + ((int64_t)b * H + h) * dv;
+    for (int32_t c = 0; c < dv; ++c) o[c] = 0.0;
+    if (nt == 0) {
+      lse[(int64_t)b * H + h] = -INFINITY;
+    } else {
+      /* pass 2: normaliser and weighted sum of value rows */
+      double z = 0.0;
+      for (int64_t i = 0; i < nt; ++i) {
+        double w = exp(x[i] - m);
+        z += w;
+        for (int32_t c = 0; c < dv; ++c) o[c] += w * elem(vbase, row[i] * vstride + c, dtype);
+      }
+      for (int32_t c = 0; c < dv; ++c) o[c] /= z;
+      lse[(int64_t)b * H + h] = m + log(z);
+    }
+    free(x);
+    free(row);
+  }
+}
+
+int32_t oracle_max_threads(void) {
+#ifdef _OPENMP
+  return (int32_t)omp_get_max_threads();
+#else
+  return 1;
+#endif
+}

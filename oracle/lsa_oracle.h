@@ -1,0 +1,89 @@
+/*
+ * lsa_oracle.h -- CPU oracle for the Lookahead Sparse Attention (LSA) decode
+ * hot path.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may include, link or
+ * call this code: only the tests, the smoke check and the benchmark's CPU
+ * baseline leg use it.  It shares no code, header or helper with the HIP
+ * library, and it never reads anything the HIP library wrote except where a
+ * test deliberately hands it the GPU's own fp32 scores to rank.
+ *
+ * Everything is plain C99, accumulates in double precision and follows the
+ * method's definitions directly, with no blocking, splitting or fusion:
+ *
+ *   score      -- dual-encoder relevance: one inner product between a stream's
+ *                 indexer query embedding and each of its chunk embeddings
+ *                 ("FlashMemory-DeepSeek-V4 ... Lookahead Sparse Attention"
+ *                 wiki note, flowchart and "Key points"; dimensionstp review
+ *                 section 3-2-4; arXiv abstract v2).
+ *   select     -- keep the k highest-scoring chunks of each stream (review
+ *                 section 3-2-3, step 5: "top-k ... keep mask").
+ *   gather     -- copy the kept chunks into a resident pool (wiki note
+ *                 flowchart, "Resident KV chunks"; molayo explainer, the
+ *                 "selective gather" paragraph).
+ *   attention  -- softmax attention of each query head restricted to the
+ *                 tokens of the kept chunks (review section 3-2-3, steps 6-7).
+ *
+ * Element encodings: ORACLE_F32 arrays hold IEEE-754 binary32 values;
+ * ORACLE_BF16 arrays hold bfloat16 bit patterns (the upper 16 bits of a
+ * binary32), which are widened exactly.
+ */
+#ifndef LSA_ORACLE_H
+#define LSA_ORACLE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum { ORACLE_F32 = 0, ORACLE_BF16 = 1 };
+
+/* Number of chunks kept out of n_chunks at keep ratio num/den: floor or
+ * ceiling of n_chunks*num/den in exact integer arithmetic, clamped to
+ * [1, n_chunks].  Returns 0 for n_chunks <= 0 or a bad ratio. */
+int32_t oracle_keep_count(int32_t n_chunks, int32_t num, int32_t den, int32_t round_up);
+
+/* scores[chunk_off[b] + n] = sum_j q[b][j] * emb[chunk_off[b] + n][j]
+ * q: [B][D], emb: [chunk_off[B]][D], both of element type dtype. */
+void oracle_score(int32_t B, int32_t D, int32_t dtype, const void* q, const void* emb,
+                  const int32_t* chunk_off, double* scores);
+
+/* For each stream b keep k_b = sel_off[b+1]-sel_off[b] chunks: rank the
+ * stream's chunks by (score descending, chunk index ascending) with NaN
+ * ranked below every number, keep the first k_b and write their indices in
+ * ascending order to sel_idx[sel_off[b] ...].  Returns 0, or -1 when some
+ * k_b is outside [0, N_b]. */
+int32_t oracle_select(int32_t B, const double* scores, const int32_t* chunk_off,
+                      const int32_t* sel_off, int32_t* sel_idx);
+
+/* Byte copy of the kept chunks into a pool: slot sel_off[b]+j receives the
+ * rows of chunk sel_idx[sel_off[b]+j] of stream b (row r of the slot is token
+ * n*C + r); rows at or beyond the stream's length are written as zeros.
+ * row_bytes is the size of one token row of the store. */
+void oracle_gather(int32_t B, int32_t C, int64_t row_bytes, const void* store,
+                   const int64_t* tok_off, const int32_t* sel_idx, const int32_t* sel_off,
+                   void* pool);
+
+/* Sparse decode attention, two passes per (stream, head), no splitting.
+ * Q: [B][H][dqk].  K rows: K[tok_off[b] + t][0..dqk).  V rows: if
+ * v_aliases_k, V[t][c] = K[t][c] for c < dv, else V[tok_off[b]+t][0..dv).
+ * Tokens taken: every t in [n*C, min(n*C+C, L_b)) for each kept chunk n of
+ * stream b, L_b = tok_off[b+1]-tok_off[b].
+ *   x_t = scale * <Q[b][h], K_t>,  m = max x_t,  w_t = exp(x_t - m),
+ *   out[b][h][:] = sum_t w_t V_t / sum_t w_t,  lse[b][h] = m + log(sum_t w_t).
+ * A stream with no token gets out = 0 and lse = -inf.
+ * nthreads > 1 spreads (stream, head) pairs over OpenMP threads; the
+ * arithmetic of each pair does not depend on it. */
+void oracle_attention(int32_t B, int32_t H, int32_t dqk, int32_t dv, int32_t v_aliases_k,
+                      int32_t dtype, int32_t C, double scale, const void* Q, const void* K,
+                      const void* V, const int64_t* tok_off, const int32_t* sel_idx,
+                      const int32_t* sel_off, double* out, double* lse, int32_t nthreads);
+
+/* Threads an OpenMP region may use here (1 when built without OpenMP). */
+int32_t oracle_max_threads(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -1,0 +1,197 @@
+"""Python front end of the CPU oracle for the LSA decode hot path.
+
+TEST INFRASTRUCTURE ONLY: the tests, the smoke check and the benchmark's CPU
+baseline leg may import this module; the product package never does.  It loads
+``liblsa_oracle.so`` (built from ``lsa_oracle.c`` with gcc, no HIP headers)
+and shares nothing with the HIP library.
+
+Step definitions (cited to the pages' sections, see ``lsa_oracle.c``):
+  score      dual-encoder inner product per chunk (wiki note flowchart and
+             "Key points"; review section 3-2-4; arXiv abstract v2)
+  select     top-k keep set per stream (review section 3-2-3 step 5)
+  gather     resident pool of kept chunks (wiki note flowchart; molayo
+             explainer "selective gather")
+  attention  softmax attention over the kept chunks' tokens (review section
+             3-2-3 steps 6-7)
+  decode     the review's decode loop (section 3-2-3 steps 3-7): re-score and
+             re-select every ``reindex_every`` steps, attend every step.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "lsa_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liblsa_oracle.so")
+
+F32 = 0
+BF16 = 1
+
+_lib = None
+
+
+def build(force: bool = False) -> str:
+    """Compile liblsa_oracle.so with the host C compiler (gcc, OpenMP)."""
+    if force or not os.path.exists(_LIB_PATH) or (
+        os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC)
+    ):
+        tmp = _LIB_PATH + f".tmp{os.getpid()}"
+        cmd = ["gcc", "-std=c99", "-O2", "-fopenmp", "-fPIC", "-shared",
+               "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        build()
+        lib = ctypes.CDLL(_LIB_PATH)
+        P = ctypes.c_void_p
+        i32, i64, f64 = ctypes.c_int32, ctypes.c_int64, ctypes.c_double
+        lib.oracle_keep_count.argtypes = [i32, i32, i32, i32]
+        lib.oracle_keep_count.restype = i32
+        lib.oracle_score.argtypes = [i32, i32, i32, P, P, P, P]
+        lib.oracle_score.restype = None
+        lib.oracle_select.argtypes = [i32, P, P, P, P]
+        lib.oracle_select.restype = i32
+        lib.oracle_gather.argtypes = [i32, i32, i64, P, P, P, P, P]
+        lib.oracle_gather.restype = None
+        lib.oracle_attention.argtypes = [i32, i32, i32, i32, i32, i32, i32, f64,
+                                         P, P, P, P, P, P, P, P, i32]
+        lib.oracle_attention.restype = None
+        lib.oracle_max_threads.argtypes = []
+        lib.oracle_max_threads.restype = i32
+        _lib = lib
+    return _lib
+
+
+def _ptr(a: np.ndarray):
+    return ctypes.c_void_p(a.ctypes.data)
+
+
+def _elements(a: np.ndarray) -> tuple[np.ndarray, int]:
+    """Return (contiguous array, dtype code): float32 or bfloat16 bit patterns (uint16)."""
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.float32:
+        return a, F32
+    if a.dtype == np.uint16:
+        return a, BF16
+    raise TypeError(f"oracle inputs are float32 or bf16 bit patterns (uint16), got {a.dtype}")
+
+
+def max_threads() -> int:
+    return int(_load().oracle_max_threads())
+
+
+def keep_count(n_chunks: int, num: int, den: int, round_up: bool) -> int:
+    return int(_load().oracle_keep_count(n_chunks, num, den, int(round_up)))
+
+
+def score(q: np.ndarray, emb: np.ndarray, chunk_off: np.ndarray) -> np.ndarray:
+    """fp64 scores [sum N_b] of each chunk embedding against its stream's query."""
+    q, dt = _elements(q)
+    emb, dt2 = _elements(emb)
+    assert dt == dt2, "q and emb must share an element type"
+    chunk_off = np.ascontiguousarray(chunk_off, dtype=np.int32)
+    B, D = q.shape
+    assert emb.shape[1] == D and emb.shape[0] == chunk_off[-1]
+    out = np.empty(int(chunk_off[-1]), dtype=np.float64)
+    _load().oracle_score(B, D, dt, _ptr(q), _ptr(emb), _ptr(chunk_off), _ptr(out))
+    return out
+
+
+def select(scores: np.ndarray, chunk_off: np.ndarray, sel_off: np.ndarray) -> np.ndarray:
+    """Ascending kept chunk indices per stream (CSR by sel_off)."""
+    s = np.ascontiguousarray(scores, dtype=np.float64)  # float32 -> float64 is exact
+    chunk_off = np.ascontiguousarray(chunk_off, dtype=np.int32)
+    sel_off = np.ascontiguousarray(sel_off, dtype=np.int32)
+    B = len(chunk_off) - 1
+    out = np.empty(int(sel_off[-1]), dtype=np.int32)
+    rc = _load().oracle_select(B, _ptr(s), _ptr(chunk_off), _ptr(sel_off), _ptr(out))
+    if rc != 0:
+        raise ValueError("keep count outside [0, N_b]")
+    return out
+
+
+def gather(store: np.ndarray, C: int, tok_off: np.ndarray, sel_idx: np.ndarray,
+           sel_off: np.ndarray) -> np.ndarray:
+    """Pool [sum k_b, C, row] holding the kept chunks; rows past L_b are zero."""
+    store = np.ascontiguousarray(store)
+    tok_off = np.ascontiguousarray(tok_off, dtype=np.int64)
+    sel_idx = np.ascontiguousarray(sel_idx, dtype=np.int32)
+    sel_off = np.ascontiguousarray(sel_off, dtype=np.int32)
+    B = len(tok_off) - 1
+    row_shape = store.shape[1:]
+    row_bytes = store.itemsize * int(np.prod(row_shape))
+    pool = np.empty((int(sel_off[-1]), C) + tuple(row_shape), dtype=store.dtype)
+    _load().oracle_gather(B, C, row_bytes, _ptr(store), _ptr(tok_off), _ptr(sel_idx),
+                          _ptr(sel_off), _ptr(pool))
+    return pool
+
+
+def attention(Q: np.ndarray, K: np.ndarray, V: np.ndarray | None, tok_off: np.ndarray,
+              sel_idx: np.ndarray, sel_off: np.ndarray, C: int, scale: float,
+              dv: int | None = None, nthreads: int = 1) -> tuple[np.ndarray, np.ndarray]:
+    """Sparse attention (out [B,H,dv] fp64, lse [B,H] fp64).
+
+    V=None means the value rows alias the first dv columns of the key rows.
+    """
+    Q, dt = _elements(Q)
+    K, dtk = _elements(K)
+    assert dt == dtk
+    B, H, dqk = Q.shape
+    assert K.shape[1] == dqk
+    if V is None:
+        alias = 1
+        assert dv is not None and dv <= dqk
+        Vp = K
+    else:
+        alias = 0
+        V, dtv = _elements(V)
+        assert dtv == dt and V.shape[0] == K.shape[0]
+        dv = V.shape[1]
+        Vp = V
+    tok_off = np.ascontiguousarray(tok_off, dtype=np.int64)
+    sel_idx = np.ascontiguousarray(sel_idx, dtype=np.int32)
+    sel_off = np.ascontiguousarray(sel_off, dtype=np.int32)
+    assert len(tok_off) == B + 1 and len(sel_off) == B + 1
+    out = np.empty((B, H, dv), dtype=np.float64)
+    lse = np.empty((B, H), dtype=np.float64)
+    _load().oracle_attention(B, H, dqk, dv, alias, dt, C, float(scale), _ptr(Q), _ptr(K),
+                             _ptr(Vp), _ptr(tok_off), _ptr(sel_idx), _ptr(sel_off),
+                             _ptr(out), _ptr(lse), int(nthreads))
+    return out, lse
+
+
+def all_chunks(tok_off: np.ndarray, C: int) -> tuple[np.ndarray, np.ndarray]:
+    """(sel_idx, sel_off) that keeps every chunk: the dense-attention case."""
+    lens = np.diff(np.asarray(tok_off, dtype=np.int64))
+    n = (lens + C - 1) // C
+    sel_off = np.concatenate([[0], np.cumsum(n)]).astype(np.int32)
+    sel_idx = np.concatenate([np.arange(x, dtype=np.int32) for x in n]) if len(n) else \
+        np.zeros(0, np.int32)
+    return sel_idx.astype(np.int32), sel_off
+
+
+def decode(q_idx: np.ndarray, emb: np.ndarray, chunk_off: np.ndarray, sel_off: np.ndarray,
+           Qs: list, K: np.ndarray, V: np.ndarray | None, tok_off: np.ndarray, C: int,
+           scale: float, reindex_every: int, dv: int | None = None, nthreads: int = 1):
+    """Multi-step decode: per step t, re-score and re-select when t % R == 0,
+    then attend with that step's queries Qs[t].  Returns a list of
+    (sel_idx, out, lse) per step."""
+    results = []
+    sel_idx = None
+    for t, Q in enumerate(Qs):
+        if t % reindex_every == 0:
+            s = score(q_idx, emb, chunk_off)
+            sel_idx = select(s, chunk_off, sel_off)
+        out, lse = attention(Q, K, V, tok_off, sel_idx, sel_off, C, scale, dv=dv,
+                             nthreads=nthreads)
+        results.append((sel_idx, out, lse))
+    return results

@@ -1,0 +1,369 @@
+"""Pins of the CPU oracle to things other than itself.
+
+Every check here fixes the oracle against the pages' definitions through an
+independent route: hand-derived fixtures (tests/golden), closed forms,
+invariants that define the top-k keep set, brute force on tiny inputs, and
+library routines (numpy matmul, torch's scaled_dot_product_attention,
+scipy's logsumexp) for the special cases that reduce to them.  The oracle is
+never compared with itself.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import scipy.special
+import torch
+
+from oracle import oracle
+from learned_kv_chunk_amd import workloads as wl
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _f32(x):
+    return np.asarray(x, dtype=np.float32)
+
+
+# ----------------------------------------------------------------------------- keep count
+def test_keep_count_matches_the_workload_table():
+    # the printed keep counts: 13.5% of 2048 -> 276, 10% of 8192 -> 819, 8% of 8192 -> 655
+    assert oracle.keep_count(2048, 135, 1000, False) == 276
+    assert oracle.keep_count(8192, 10, 100, False) == 819
+    assert oracle.keep_count(8192, 8, 100, False) == 655
+    assert oracle.keep_count(64, 1, 8, False) == 8
+    # rounded-up ratio of the ragged batch, in exact integers
+    for n in [1, 7, 128, 129, 1000, 2000, 4096]:
+        assert oracle.keep_count(n, 135, 1000, True) == -(-n * 135 // 1000) or n * 135 < 1000
+    assert oracle.keep_count(1000, 135, 1000, True) == 135
+    assert oracle.keep_count(1001, 135, 1000, True) == 136
+    assert oracle.keep_count(3, 1, 1000, False) == 1          # clamped to >= 1
+    assert oracle.keep_count(0, 1, 2, False) == 0
+
+
+# ----------------------------------------------------------------------------- score
+def test_score_golden():
+    g = _golden("score_small.json")
+    s = oracle.score(_f32(g["q"]), _f32(g["emb"]), np.array(g["chunk_off"], np.int32))
+    assert s.tolist() == g["expected"]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_score_equals_brute_force_matmul(dtype):
+    rng = np.random.default_rng(7)
+    chunk_off = np.array([0, 5, 5 + 17, 5 + 17 + 3], np.int32)
+    D = 24
+    q = rng.standard_normal((3, D)).astype(np.float32)
+    e = rng.standard_normal((int(chunk_off[-1]), D)).astype(np.float32)
+    if dtype == "bf16":
+        q, e = wl.to_bf16_bits(q), wl.to_bf16_bits(e)
+    s = oracle.score(q, e, chunk_off)
+    q64, e64 = wl.as_f32(q).astype(np.float64), wl.as_f32(e).astype(np.float64)
+    for b in range(3):
+        rows = slice(chunk_off[b], chunk_off[b + 1])
+        np.testing.assert_allclose(s[rows], e64[rows] @ q64[b], rtol=1e-13, atol=1e-13)
+
+
+def test_score_needles_have_cosine_point_nine_and_obey_cauchy_schwarz():
+    w = wl.make_workload(wl.CONFIGS["cfg1"])
+    s = oracle.score(w.q_idx, w.emb, w.chunk_off)
+    q = w.q_idx.astype(np.float64)
+    e = w.emb.astype(np.float64)
+    bound = np.linalg.norm(q[0]) * np.linalg.norm(e, axis=1)
+    assert (np.abs(s) <= bound * (1 + 1e-12)).all()
+    np.testing.assert_allclose(s[w.needles[0]], 0.9, atol=1e-6)
+    others = np.setdiff1d(np.arange(len(s)), w.needles[0])
+    assert s[others].max() < 0.9 - 0.2
+
+
+# ----------------------------------------------------------------------------- select
+def test_select_golden_ties_nan_and_signed_zero():
+    g = _golden("select_ties.json")
+    s = np.array([float(x) for x in g["scores"]], np.float64)
+    n = len(s)
+    for case in g["cases"]:
+        got = oracle.select(s, np.array([0, n], np.int32), np.array([0, case["k"]], np.int32))
+        assert got.tolist() == case["expected"], case
+
+
+def _defining_property_holds(s, k, kept):
+    """kept is the top-k set: every kept chunk outranks every dropped chunk under
+    (score desc, index asc), |kept| = k, strictly ascending."""
+    kept = list(kept)
+    if len(kept) != k or kept != sorted(set(kept)):
+        return False
+    dropped = sorted(set(range(len(s))) - set(kept))
+
+    def outranks(i, j):
+        si, sj = s[i], s[j]
+        if math.isnan(si) != math.isnan(sj):
+            return math.isnan(sj)
+        if not math.isnan(si) and si != sj:
+            return si > sj
+        return i < j
+    return all(outranks(i, j) for i in kept for j in dropped)
+
+
+def test_select_brute_force_defining_property_with_heavy_ties():
+    rng = np.random.default_rng(11)
+    for trial in range(60):
+        n = int(rng.integers(1, 40))
+        vals = rng.choice([-1.0, -0.0, 0.0, 0.25, 0.5, 0.75, np.nan], size=n)
+        k = int(rng.integers(1, n + 1))
+        got = oracle.select(vals, np.array([0, n], np.int32), np.array([0, k], np.int32))
+        assert _defining_property_holds(vals, k, got), (vals, k, got)
+
+
+def test_select_brute_force_over_all_subsets_tiny():
+    # For tiny N, enumerate every k-subset and keep the lexicographically best
+    # (score desc, index asc) ranking of members: it must be the oracle's set.
+    import itertools
+    rng = np.random.default_rng(5)
+    for trial in range(25):
+        n = int(rng.integers(1, 9))
+        s = rng.choice([0.1, 0.2, 0.3, -0.5], size=n)
+        k = int(rng.integers(1, n + 1))
+        best = None
+        for sub in itertools.combinations(range(n), k):
+            key = sorted(((-s[i], i) for i in sub))
+            if best is None or key < best[0]:
+                best = (key, sub)
+        got = oracle.select(s, np.array([0, n], np.int32), np.array([0, k], np.int32))
+        assert tuple(got.tolist()) == best[1]
+
+
+def test_select_special_cases_and_batching():
+    s = np.array([3.0, 3.0, 3.0, 3.0, 1, 2, 5, 4], np.float64)
+    chunk_off = np.array([0, 4, 8], np.int32)
+    # all equal -> lowest indices; k = N -> everything
+    got = oracle.select(s, chunk_off, np.array([0, 2, 6], np.int32))
+    assert got.tolist() == [0, 1, 0, 1, 2, 3]
+    got = oracle.select(s, chunk_off, np.array([0, 4, 5], np.int32))
+    assert got.tolist() == [0, 1, 2, 3, 2]
+    with pytest.raises(ValueError):
+        oracle.select(s, chunk_off, np.array([0, 5, 6], np.int32))
+
+
+def test_select_keeps_every_needle():
+    for name in ["cfg1"]:
+        w = wl.make_workload(wl.CONFIGS[name])
+        sel = oracle.select(oracle.score(w.q_idx, w.emb, w.chunk_off), w.chunk_off, w.sel_off)
+        for b in range(w.B):
+            kept = set(sel[w.sel_off[b]:w.sel_off[b + 1]].tolist())
+            assert set(w.needles[b].tolist()) <= kept
+    cfg = wl.small_variant("cfg2")
+    w = wl.make_workload(cfg)
+    sel = oracle.select(oracle.score(w.q_idx, w.emb, w.chunk_off), w.chunk_off, w.sel_off)
+    for b in range(w.B):
+        assert set(w.needles[b].tolist()) <= set(sel[w.sel_off[b]:w.sel_off[b + 1]].tolist())
+
+
+# ----------------------------------------------------------------------------- gather
+def test_gather_is_a_slice_of_the_store_with_zero_tail():
+    rng = np.random.default_rng(3)
+    C = 4
+    lengths = np.array([10, 4, 7])
+    tok_off = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int64)
+    store = rng.integers(1, 60000, size=(int(tok_off[-1]), 6)).astype(np.uint16)
+    sel_off = np.array([0, 2, 3, 5], np.int32)
+    sel_idx = np.array([0, 2, 0, 0, 1], np.int32)
+    pool = oracle.gather(store, C, tok_off, sel_idx, sel_off)
+    assert pool.shape == (5, C, 6)
+    # stream 0, chunk 2 = tokens 8, 9 then two zero rows
+    np.testing.assert_array_equal(pool[1, :2], store[8:10])
+    assert (pool[1, 2:] == 0).all()
+    np.testing.assert_array_equal(pool[0], store[0:4])
+    np.testing.assert_array_equal(pool[2], store[10:14])
+    np.testing.assert_array_equal(pool[3], store[14:18])
+    np.testing.assert_array_equal(pool[4, :3], store[18:21])
+    assert (pool[4, 3:] == 0).all()
+
+
+# ----------------------------------------------------------------------------- attention
+def _golden_attention(name):
+    g = _golden(name)
+    q = _f32(g["q"])
+    K, V = _f32(g["K"]), _f32(g["V"])
+    tok_off = np.array(g.get("tok_off", [0, len(K)]), np.int64)
+    sel_off = np.array(g.get("sel_off", [0, len(g["sel_idx"])]), np.int32)
+    out, lse = oracle.attention(q, K, V, tok_off, np.array(g["sel_idx"], np.int32), sel_off,
+                                g["chunk_size"], g["scale"])
+    np.testing.assert_allclose(out, np.array(g["expected_out"]), rtol=1e-14, atol=1e-13)
+    np.testing.assert_allclose(lse, np.array(g["expected_lse"]), rtol=1e-14, atol=1e-14)
+
+
+def test_attention_golden_two_tokens():
+    _golden_attention("attention_two_token.json")
+
+
+def test_attention_golden_partial_chunk_and_no_leak():
+    _golden_attention("attention_partial_chunk.json")
+
+
+def _sdpa_reference(Q, K, V, rows, scale):
+    """torch's scaled_dot_product_attention (CPU, float64) over the given key rows."""
+    q = torch.from_numpy(Q.astype(np.float64))[None]               # [1, H, d]
+    q = q[:, :, None, :]                                            # [1, H, 1, d]
+    k = torch.from_numpy(K[rows].astype(np.float64))[None, None].expand(1, Q.shape[0], -1, -1)
+    v = torch.from_numpy(V[rows].astype(np.float64))[None, None].expand(1, Q.shape[0], -1, -1)
+    o = torch.nn.functional.scaled_dot_product_attention(q, k, v, scale=scale)
+    logits = (Q.astype(np.float64) @ K[rows].astype(np.float64).T) * scale
+    return o[0, :, 0, :].numpy(), scipy.special.logsumexp(logits, axis=1)
+
+
+def _ragged_case(dtype, C=8, lengths=(37, 16, 9), H=3, dqk=16, dv=12, seed=1):
+    rng = np.random.default_rng(seed)
+    lengths = np.array(lengths)
+    tok_off = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int64)
+    K = rng.standard_normal((int(tok_off[-1]), dqk)).astype(np.float32)
+    V = rng.standard_normal((int(tok_off[-1]), dv)).astype(np.float32)
+    Q = rng.standard_normal((len(lengths), H, dqk)).astype(np.float32)
+    if dtype == "bf16":
+        K, V, Q = wl.to_bf16_bits(K), wl.to_bf16_bits(V), wl.to_bf16_bits(Q)
+    return tok_off, K, V, Q
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_attention_all_chunks_equals_torch_sdpa(dtype):
+    C = 8
+    tok_off, K, V, Q = _ragged_case(dtype, C=C)
+    scale = 0.37
+    sel_idx, sel_off = oracle.all_chunks(tok_off, C)
+    out, lse = oracle.attention(Q, K, V, tok_off, sel_idx, sel_off, C, scale)
+    Kf, Vf, Qf = wl.as_f32(K), wl.as_f32(V), wl.as_f32(Q)
+    for b in range(len(tok_off) - 1):
+        rows = np.arange(tok_off[b], tok_off[b + 1])
+        o_ref, l_ref = _sdpa_reference(Qf[b], Kf, Vf, rows, scale)
+        np.testing.assert_allclose(out[b], o_ref, rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(lse[b], l_ref, rtol=1e-12, atol=1e-12)
+
+
+def test_attention_sparse_equals_sdpa_over_the_kept_tokens():
+    C = 8
+    tok_off, K, V, Q = _ragged_case("f32", C=C, lengths=(61, 30, 8))
+    sel_off = np.array([0, 3, 5, 6], np.int32)
+    sel_idx = np.array([1, 4, 7, 0, 3, 0], np.int32)   # stream 0 keeps its partial chunk 7
+    scale = 0.25
+    out, lse = oracle.attention(Q, K, V, tok_off, sel_idx, sel_off, C, scale)
+    for b in range(3):
+        rows = []
+        for n in sel_idx[sel_off[b]:sel_off[b + 1]]:
+            rows += [tok_off[b] + t for t in range(n * C, min(n * C + C, tok_off[b + 1] - tok_off[b]))]
+        o_ref, l_ref = _sdpa_reference(Q[b], K, V, np.array(rows), scale)
+        np.testing.assert_allclose(out[b], o_ref, rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(lse[b], l_ref, rtol=1e-12, atol=1e-12)
+
+
+def test_attention_closed_forms():
+    C = 8
+    tok_off, K, V, Q = _ragged_case("f32", C=C, lengths=(29, 40))
+    sel_off = np.array([0, 2, 4], np.int32)
+    sel_idx = np.array([0, 3, 1, 4], np.int32)
+    n_tok = [8 + 5, 8 + 8]
+    # Q = 0: uniform weights -> out = mean of the kept value rows, lse = ln(#tokens)
+    out, lse = oracle.attention(np.zeros_like(Q), K, V, tok_off, sel_idx, sel_off, C, 1.0)
+    mean0 = np.concatenate([V[0:8], V[24:29]]).astype(np.float64).mean(0)
+    mean1 = np.concatenate([V[29 + 8:29 + 16], V[29 + 32:29 + 40]]).astype(np.float64).mean(0)
+    np.testing.assert_allclose(out[0], np.tile(mean0, (Q.shape[1], 1)), rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(out[1], np.tile(mean1, (Q.shape[1], 1)), rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(lse, np.log(np.array(n_tok))[:, None].repeat(Q.shape[1], 1),
+                               rtol=1e-14)
+    # constant value rows -> out = that row
+    Vc = np.tile(np.array([1.5, -2.0, 0.25, 3.0, 0, 0, 0, 0, 1, 1, 1, 1], np.float32),
+                 (V.shape[0], 1))
+    out, _ = oracle.attention(Q, K, Vc, tok_off, sel_idx, sel_off, C, 0.3)
+    np.testing.assert_allclose(out, np.broadcast_to(Vc[0], out.shape), rtol=1e-14, atol=1e-14)
+    # one kept token (C = 1): out = its value row, lse = its logit
+    out, lse = oracle.attention(Q, K, V, tok_off, np.array([6, 30], np.int32),
+                                np.array([0, 1, 2], np.int32), 1, 0.5)
+    np.testing.assert_allclose(out[0], np.tile(V[6], (Q.shape[1], 1)), rtol=1e-14)
+    np.testing.assert_allclose(lse[1], 0.5 * (Q[1].astype(np.float64) @ K[29 + 30].astype(np.float64)),
+                               rtol=1e-13)
+
+
+def test_attention_weights_sum_to_one():
+    # sum_t exp(x_t - lse) = 1 with x_t formed independently of the oracle
+    C = 4
+    tok_off, K, V, Q = _ragged_case("f32", C=C, lengths=(11,), H=2, dqk=6, dv=3)
+    sel_idx = np.array([0, 2], np.int32)
+    sel_off = np.array([0, 2], np.int32)
+    scale = 1.7
+    _, lse = oracle.attention(Q, K, V, tok_off, sel_idx, sel_off, C, scale)
+    rows = [0, 1, 2, 3, 8, 9, 10]
+    for h in range(2):
+        x = [scale * sum(float(Q[0, h, j]) * float(K[r, j]) for j in range(6)) for r in rows]
+        assert abs(sum(math.exp(v - lse[0, h]) for v in x) - 1.0) < 1e-13
+
+
+def test_attention_value_alias_equals_explicit_value_columns():
+    C = 8
+    tok_off, K, _, Q = _ragged_case("bf16", C=C, dqk=20, dv=12)
+    sel_idx, sel_off = oracle.all_chunks(tok_off, C)
+    a = oracle.attention(Q, K, None, tok_off, sel_idx, sel_off, C, 0.2, dv=12)
+    b = oracle.attention(Q, K, np.ascontiguousarray(K[:, :12]), tok_off, sel_idx, sel_off, C, 0.2)
+    np.testing.assert_array_equal(a[0], b[0])
+    np.testing.assert_array_equal(a[1], b[1])
+
+
+def test_attention_reads_bf16_exactly_and_ignores_kept_order():
+    C = 8
+    tok_off, K, V, Q = _ragged_case("bf16", C=C)
+    sel_idx, sel_off = oracle.all_chunks(tok_off, C)
+    a = oracle.attention(Q, K, V, tok_off, sel_idx, sel_off, C, 0.3)
+    b = oracle.attention(wl.as_f32(Q), wl.as_f32(K), wl.as_f32(V), tok_off, sel_idx, sel_off, C, 0.3)
+    np.testing.assert_array_equal(a[0], b[0])
+    rev = np.concatenate([sel_idx[sel_off[i]:sel_off[i + 1]][::-1] for i in range(3)])
+    c = oracle.attention(Q, K, V, tok_off, rev.astype(np.int32), sel_off, C, 0.3)
+    np.testing.assert_allclose(a[0], c[0], rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(a[1], c[1], rtol=1e-13)
+
+
+def test_attention_threads_do_not_change_results():
+    C = 8
+    tok_off, K, V, Q = _ragged_case("f32", C=C, H=5)
+    sel_idx, sel_off = oracle.all_chunks(tok_off, C)
+    a = oracle.attention(Q, K, V, tok_off, sel_idx, sel_off, C, 0.3, nthreads=1)
+    b = oracle.attention(Q, K, V, tok_off, sel_idx, sel_off, C, 0.3, nthreads=4)
+    np.testing.assert_array_equal(a[0], b[0])
+    np.testing.assert_array_equal(a[1], b[1])
+
+
+def test_decode_reindex_schedule():
+    cfg = wl.small_variant("cfg2", lengths=(64 * 20 + 3, 64 * 9), steps=4)
+    w = wl.make_workload(cfg)
+    Qs = [w.queries(t) for t in range(4)]
+    res = oracle.decode(w.q_idx, w.emb, w.chunk_off, w.sel_off, Qs, w.K, w.V, w.tok_off,
+                        cfg.chunk_size, cfg.softmax_scale, reindex_every=2)
+    s = oracle.score(w.q_idx, w.emb, w.chunk_off)
+    sel = oracle.select(s, w.chunk_off, w.sel_off)
+    for t, (sel_t, out_t, lse_t) in enumerate(res):
+        np.testing.assert_array_equal(sel_t, sel)
+        o, l = oracle.attention(Qs[t], w.K, w.V, w.tok_off, sel, w.sel_off, cfg.chunk_size,
+                                cfg.softmax_scale)
+        np.testing.assert_array_equal(out_t, o)
+        np.testing.assert_array_equal(lse_t, l)
+
+
+def test_workload_shapes_of_the_five_configs():
+    # lengths, chunks and keep counts of each workload (no K/V drawn here)
+    for name, (B, N, k) in {"cfg1": (1, 64, 8), "cfg2": (16, 2048, 276), "cfg3": (4, 8192, 819),
+                            "cfg4": (1, 8192, 655)}.items():
+        cfg = wl.CONFIGS[name]
+        L = wl.stream_lengths(cfg)
+        n = (L + cfg.chunk_size - 1) // cfg.chunk_size
+        assert len(L) == B and (n == N).all()
+        assert (wl.keep_counts(cfg, n) == k).all()
+        assert all(oracle.keep_count(int(x), cfg.keep_num, cfg.keep_den, cfg.keep_round_up) == k
+                   for x in n)
+    cfg = wl.CONFIGS["cfg5"]
+    L = wl.stream_lengths(cfg)
+    assert len(L) == 32 and L.min() >= 8192 and L.max() <= 262144
+    n = (L + 63) // 64
+    k = wl.keep_counts(cfg, n)
+    assert all(oracle.keep_count(int(a), 135, 1000, True) == int(b) for a, b in zip(n, k))
