@@ -1,0 +1,310 @@
+#!/usr/bin/env python3
+"""Throughput of the LSA decode hot path on one MI355X.
+
+A step is one call of lsa_decode_step over the whole batch: chunk scoring,
+top-k selection (re-done every `reindex_every` steps), the gather into the
+resident pool when the workload keeps one, split-KV sparse attention and the
+log-sum-exp merge.  Inputs are seeded synthetic data already resident in HBM.
+
+By default each step reads a different copy ("replica") of the workload's
+embeddings and K/V history, cycling through enough copies that the cycle is
+more than twice the 256 MB last-level (Infinity) cache: every step streams its
+bytes from HBM instead of re-reading what the previous step left in cache.
+`--replicas 1` gives the cache-assisted figure.
+
+Prints one JSON line (rank 0, one GPU).  `value` is decode steps per second;
+`roofline` reports the attention kernel's algorithmic bytes per launch over
+its average duration measured with HIP events around that kernel inside the
+timed steps; `cpu_baseline` times the CPU oracle on the host on a bounded
+sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MALL_BYTES = 256 * 2 ** 20     # MI355X Infinity Cache
+DEFAULT_CONFIG = "cfg2"
+
+WORKLOAD_TEXT = {
+    "cfg1": "1 stream x 4096 tokens, chunk 64 (N=64), D=64, k=8, MQA 8 heads x d64, fp32",
+    "cfg2": "16 streams x 131072 tokens, chunk 64 (N=2048), D=128, k=276 (13.5%), "
+            "MQA 16 heads x d128, bf16",
+    "cfg3": "4 streams x 524288 tokens, chunk 64 (N=8192), D=128, k=819 (10%), "
+            "MQA 32 heads x d128, bf16, re-index every 64 steps via a resident pool",
+    "cfg4": "1 stream x 1048576 tokens, chunk 128 (N=8192), D=256, k=655 (8%), "
+            "absorbed MLA 64 heads, d_qk 576 / d_v 512, bf16",
+    "cfg5": "32 streams x U{8192..262144} tokens, chunk 64, D=128, k=ceil(13.5%), "
+            "MQA 16 heads x d128, bf16",
+}
+
+
+def algorithmic_bytes(w):
+    """Bytes the method must move per step, by phase."""
+    import numpy as np
+
+    c = w.cfg
+    es = 2 if c.dtype == "bf16" else 4
+    C = c.chunk_size
+    n_total = int(w.chunk_off[-1])
+    k_total = int(w.sel_off[-1])
+    score = n_total * c.index_dim * es + c.batch * c.index_dim * es + n_total * 4
+    select = n_total * 4 + k_total * 4
+    # kept tokens: full chunks, except a kept partial last chunk (upper bound
+    # computed with the needles' and the last chunk's positions is not known
+    # before selection; the bench adds the exact count from the GPU's selection)
+    row = (c.head_dim_qk + (0 if c.v_aliases_k else c.head_dim_v)) * es
+    q = c.batch * c.num_q_heads * c.head_dim_qk * es
+    o = c.batch * c.num_q_heads * (c.head_dim_v + 1) * 4
+    return dict(score=score, select=select, row=row, q=q, o=o, C=C, k_total=k_total)
+
+
+def kept_tokens(w, sel):
+    """Valid tokens of the kept chunks (a kept partial last chunk counts its
+    valid rows only)."""
+    import numpy as np
+
+    C = w.cfg.chunk_size
+    total = 0
+    for b in range(w.B):
+        n = sel[w.sel_off[b]:w.sel_off[b + 1]].astype(np.int64)
+        total += int(np.minimum(C, w.lengths[b] - n * C).sum())
+    return total
+
+
+def source_hash(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def load_traffic(kernel_file, workload):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
+    taken on the current kernel source; else None."""
+    p = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_sha256_16") != source_hash(kernel_file):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(w, seconds, reindex_every):
+    from oracle import oracle
+
+    threads = max(1, len(os.sched_getaffinity(0)))
+    c = w.cfg
+    steps = 0
+    t0 = time.perf_counter()
+    sel = None
+    while True:
+        if steps % reindex_every == 0:
+            s = oracle.score(w.q_idx, w.emb, w.chunk_off)
+            sel = oracle.select(s, w.chunk_off, w.sel_off)
+        oracle.attention(w.queries(steps % 4), w.K, w.V, w.tok_off, sel, w.sel_off,
+                         c.chunk_size, c.softmax_scale, dv=c.head_dim_v, nthreads=threads)
+        steps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    return {"value": steps / el, "unit": "steps/s", "cores": threads, "kind": "oracle",
+            "sample": f"{steps} full decode step(s) of the same workload (all {c.batch} "
+                      f"streams, score + select + attention, re-index every {reindex_every}) "
+                      f"in {el:.1f} s, fp64 C oracle with OpenMP over (stream, head)"}
+
+
+def run_copy(args):
+    import torch
+
+    from learned_kv_chunk_amd import lsa
+
+    nbytes = args.copy_mib * 2 ** 20
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    lsa.bench_flush(src)
+    for _ in range(3):
+        lsa.bench_copy(dst, src, nbytes)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        lsa.bench_copy(dst, src, nbytes)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / args.steps
+    print(json.dumps({"mode": "copy", "bytes_per_launch": 2 * nbytes, "read_bytes": nbytes,
+                      "write_bytes": nbytes, "us_per_launch": us,
+                      "gbs": 2 * nbytes / us / 1e3}), flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", default=DEFAULT_CONFIG, choices=sorted(WORKLOAD_TEXT))
+    ap.add_argument("--replicas", type=int, default=0,
+                    help="workload copies cycled per step (0: enough to defeat the 256 MB cache)")
+    ap.add_argument("--reindex-every", type=int, default=0, help="0: the workload's schedule")
+    ap.add_argument("--tiles-per-block", type=int, default=0)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--mode", choices=["step", "copy"], default="step")
+    ap.add_argument("--copy-mib", type=int, default=1024)
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this build measures one GPU only (the LSA hot path has no "
+              "multi-GPU component here); run with --gpus 1", file=sys.stderr, flush=True)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from learned_kv_chunk_amd import device as dev
+    from learned_kv_chunk_amd import lsa
+    from learned_kv_chunk_amd import workloads as wl
+
+    lsa.library()  # fail loudly without the HIP library
+    torch.cuda.set_device(0)
+    if args.mode == "copy":
+        run_copy(args)
+        return
+
+    cfg = wl.CONFIGS[args.config]
+    R_idx = args.reindex_every or cfg.reindex_every
+    t0 = time.perf_counter()
+    w = wl.make_workload(cfg)
+    print(f"bench: generated {args.config} in {time.perf_counter() - t0:.1f} s "
+          f"(sum L={int(w.lengths.sum())}, sum N={int(w.chunk_off[-1])}, "
+          f"sum k={int(w.sel_off[-1])})", file=sys.stderr, flush=True)
+    base = dev.upload(w, "cuda", attn_tiles_per_block=args.tiles_per_block)
+    ab = algorithmic_bytes(w)
+
+    # one untimed step to learn the kept set (for the exact kept-token count)
+    base.step(0, reindex=True, materialize_pool=cfg.materialize_pool)
+    torch.cuda.synchronize()
+    sel = dev.to_host(base.sel_idx)
+    ktok = kept_tokens(w, sel)
+    attn_bytes = ktok * ab["row"] + ab["q"]                      # per attention launch
+    gather_bytes = 2 * ktok * ab["row"] if cfg.materialize_pool else 0
+    reidx_bytes = ab["score"] + ab["select"] + gather_bytes
+    step_bytes = attn_bytes + ab["o"] + reidx_bytes / R_idx      # amortised per step
+
+    reps = args.replicas
+    if reps <= 0:
+        reps = max(1, math.ceil(2 * MALL_BYTES / max(1, step_bytes)) + 1)
+    replicas = [base]
+    for _ in range(reps - 1):
+        r = dev.DeviceWorkload(
+            w=w, shape=base.shape, q_idx=base.q_idx.clone(), emb=base.emb.clone(),
+            chunk_off=base.chunk_off, sel_off=base.sel_off, tok_off=base.tok_off,
+            K=base.K.clone(), V=None if base.V is None else base.V.clone(),
+            scores=torch.empty_like(base.scores), sel_idx=base.sel_idx.clone(),
+            out=torch.empty_like(base.out), lse=torch.empty_like(base.lse),
+            workspace=torch.empty_like(base.workspace),
+            k_pool=None if base.k_pool is None else torch.empty_like(base.k_pool),
+            v_pool=None if base.v_pool is None else torch.empty_like(base.v_pool))
+        replicas.append(r)
+    nq = 8
+    qs = [base.queries(t) for t in range(nq)]
+    for r in replicas:  # fill every replica's kept set (and pool) once
+        r.step(0, reindex=True, materialize_pool=cfg.materialize_pool, q=qs[0])
+    torch.cuda.synchronize()
+    print(f"bench: {reps} replica(s), {step_bytes / 1e6:.1f} MB per step", file=sys.stderr,
+          flush=True)
+
+    def run(n, t_begin, evs=None):
+        for i in range(n):
+            t = t_begin + i
+            r = replicas[t % reps]
+            eb, ee = (evs[i] if evs is not None else (None, None))
+            r.step(t, reindex=(t % R_idx == 0), materialize_pool=cfg.materialize_pool,
+                   ev_begin=eb, ev_end=ee, q=qs[t % nq])
+
+    run(args.warmup, 0)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    for a, b in evs:  # create the underlying HIP events before timing
+        a.record()
+        b.record()
+    g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    g0.record()
+    # steps are numbered from a multiple of the re-index interval so that the
+    # timed window holds steps/R_idx re-index steps
+    t_first = ((args.warmup + R_idx - 1) // R_idx) * R_idx
+    run(args.steps, t_first, evs)
+    g1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    ms_per_step = g0.elapsed_time(g1) / args.steps
+    attn_us = float(np.mean([a.elapsed_time(b) for a, b in evs])) * 1e3
+    steps_per_s = 1e3 / ms_per_step
+
+    attn_gbs = attn_bytes / attn_us / 1e3
+    kernel_file = os.path.join(ROOT, "learned_kv_chunk_amd", "csrc",
+                               "attn_mla.hip" if cfg.v_aliases_k else
+                               ("attn_mqa.hip" if cfg.dtype == "bf16" else "attn_portable.hip"))
+    traffic = load_traffic(kernel_file, args.config)
+    line = {
+        "metric": "LSA decode steps/sec at 128K ctx (score+top-k+attn); HBM GB/s vs peak",
+        "value": steps_per_s,
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": f"{args.config}: {WORKLOAD_TEXT[args.config]}",
+            "global_batch": cfg.batch,
+            "seq_len": int(w.lengths.max()),
+            "reindex_every": R_idx,
+            "replicas": reps,
+            "cache": "cold (replicas cycle > 2x Infinity Cache)" if reps * step_bytes >
+                     2 * MALL_BYTES else "warm (cache-assisted)",
+        },
+        "tokens_per_s": steps_per_s * cfg.batch,
+        "step_algorithmic_bytes": int(step_bytes),
+        "step_gbs": step_bytes * steps_per_s / 1e9,
+        "step_hbm_frac": step_bytes * steps_per_s / 1e9 / HBM_PEAK_GBS,
+        "wall_ms_per_step": wall * 1e3 / args.steps,
+        "resident_fraction": w.resident_fraction(),
+        "roofline": {
+            "kernel": os.path.basename(kernel_file).replace(".hip", "") + " (split-KV attention)",
+            "bound": "hbm",
+            "achieved": attn_gbs,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": attn_gbs / HBM_PEAK_GBS,
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": int(attn_bytes),
+            "avg_launch_us": attn_us,
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds, R_idx)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,243 @@
+/*
+ * lsa.h -- C ABI of the Lookahead Sparse Attention (LSA) decode hot path for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The method ("FlashMemory-DeepSeek-V4: Lightning Index Ultra-Long Context via
+ * Lookahead Sparse Attention"): for each decode stream a neural memory indexer
+ * scores every historical KV chunk, only the highest-scoring chunks stay
+ * resident, and attention runs over those chunks alone.  The pages describe
+ * the decode loop in the dimensionstp review, section 3-2-3 ("Lookahead Sparse
+ * Attention", steps 1-7): dense prefill, the K/V history kept as chunks, the
+ * retriever re-scoring all chunks every ~64 decode steps, a top-k or threshold
+ * keep mask, and sparse attention over the kept chunks until the next
+ * re-scoring.  This library implements steps 4-7 on the GPU.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Ownership: the caller owns every buffer.  Pointers named *_dev are device
+ *   (HBM) pointers; the lsa_shape / lsa_step_args structs themselves are read
+ *   on the host during the call and may be freed when it returns.  The library
+ *   keeps no global mutable state, never allocates device or host memory and
+ *   is reentrant; scratch memory is the caller's workspace.
+ * Asynchrony: a call validates its arguments on the host, enqueues kernels on
+ *   `hip_stream` (a hipStream_t; NULL means the legacy null stream) and
+ *   returns.  Results are valid once the stream reaches that point.  No call
+ *   synchronises or copies device data to the host.
+ * Errors: every precondition the host can check is checked before anything
+ *   is enqueued; on failure the call returns a non-zero lsa_status, enqueues
+ *   nothing and leaves every output untouched.  Launch failures are reported
+ *   as LSA_ERR_HIP (the thread's pending HIP error is cleared on entry).
+ *   Device-side preconditions (offset tables monotone and consistent with the
+ *   stated totals, 1 <= k_b <= N_b, kept indices in [0, N_b)) cannot be checked
+ *   without reading device memory; kernels clamp so that a violation never
+ *   writes outside the documented output ranges, but results are then
+ *   unspecified.
+ * Layout: all tensors are dense row-major.  Ragged per-stream data is packed
+ *   back to back and described by CSR offset arrays of B+1 entries whose first
+ *   entry is 0:
+ *     tok_off[B+1]   int64  tokens: stream b owns rows [tok_off[b], tok_off[b+1])
+ *                           of the K/V history; L_b = tok_off[b+1]-tok_off[b].
+ *     chunk_off[B+1] int32  chunks: N_b = chunk_off[b+1]-chunk_off[b] must equal
+ *                           ceil(L_b / C).  Chunk n of stream b covers tokens
+ *                           [n*C, min(n*C+C, L_b)); the last one may be partial.
+ *     sel_off[B+1]   int32  kept chunks: k_b = sel_off[b+1]-sel_off[b].
+ * Element types: LSA_DTYPE_F32 (IEEE binary32) or LSA_DTYPE_BF16 (bfloat16);
+ *   one dtype covers q_idx, chunk embeddings, Q, K and V.  Scores, outputs and
+ *   log-sum-exps are always fp32; arithmetic accumulates in fp32.
+ */
+#ifndef LSA_H
+#define LSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t lsa_status;
+#define LSA_OK 0
+#define LSA_ERR_INVALID_ARGUMENT 1
+#define LSA_ERR_UNSUPPORTED 2
+#define LSA_ERR_WORKSPACE_TOO_SMALL 3
+#define LSA_ERR_HIP 4
+
+enum { LSA_DTYPE_F32 = 0, LSA_DTYPE_BF16 = 1 };
+enum { LSA_KV_STORE = 0, LSA_KV_POOL = 1 };
+
+/* Problem shape.  Every field is read on the host. */
+typedef struct lsa_shape {
+  int32_t batch;          /* B >= 1 decode streams */
+  int32_t chunk_size;     /* C tokens per chunk, 1..1024 */
+  int32_t index_dim;      /* D, indexer embedding width */
+  int32_t num_q_heads;    /* H query heads, all sharing one KV head */
+  int32_t head_dim_qk;    /* key / query width */
+  int32_t head_dim_v;     /* value / output width */
+  int32_t v_aliases_k;    /* 1: V rows are the first head_dim_v columns of the
+                             K rows (absorbed multi-head latent attention);
+                             0: V is its own [sum L, head_dim_v] tensor */
+  int32_t dtype;          /* LSA_DTYPE_* */
+  float softmax_scale;    /* logits = softmax_scale * <q_h, k_t> */
+  int32_t max_chunks;     /* >= max_b N_b */
+  int32_t max_k;          /* >= max_b k_b */
+  int64_t total_chunks;   /* = sum_b N_b = chunk_off[B] */
+  int64_t total_k;        /* = sum_b k_b = sel_off[B] */
+  int32_t attn_tiles_per_block; /* split-KV granularity: 32-token tiles handled
+                             by one attention workgroup; 0 picks a default for
+                             the shape.  Changing it changes results only by
+                             rounding (bf16 inputs: the attention weights are
+                             rounded to bf16 relative to each split's running
+                             maximum, about 2^-9 relative). */
+  int32_t reserved;       /* must be 0 */
+} lsa_shape;
+
+/* Human-readable name of a status code (static storage). */
+const char* lsa_status_string(lsa_status status);
+
+/* Version of this ABI (incremented on incompatible change). */
+int32_t lsa_abi_version(void);
+
+/* Kept chunks out of n_chunks at keep ratio ratio_num/ratio_den: the floor
+ * (round_up = 0) or ceiling (round_up = 1) of n_chunks*ratio_num/ratio_den in
+ * exact integer arithmetic, clamped to [1, n_chunks].  The wiki note and the
+ * abstract quote an average footprint of 13.5% of the full context and more
+ * than 90% reduction at 500K tokens; those are keep ratios of this form.
+ * Returns 0 when n_chunks <= 0 or the ratio is not positive. */
+int32_t lsa_keep_count(int32_t n_chunks, int32_t ratio_num, int32_t ratio_den,
+                       int32_t round_up);
+
+/* Bytes of workspace lsa_sparse_decode_attn / lsa_decode_step need for this
+ * shape (0 if the shape is invalid).  Monotone in batch, total_k, max_k,
+ * num_q_heads and head_dim_v; any buffer at least this large works. */
+size_t lsa_workspace_bytes(const lsa_shape* shape);
+
+/* ---------------------------------------------------------------------------
+ * Chunk scoring (dual-encoder relevance).  Wiki note flowchart and "Key
+ * points"; dimensionstp review sections 2-1 and 3-2-4; abstract v2: the
+ * indexer is a standard dual encoder, so a chunk's relevance is the inner
+ * product of the stream's query embedding with the chunk's embedding.
+ *   scores_dev[chunk_off[b] + n] = sum_j q_idx[b][j] * emb[chunk_off[b] + n][j]
+ * q_idx_dev: [B][D]; emb_dev: [total_chunks][D]; scores_dev: [total_chunks] fp32.
+ * No normalisation and no sigmoid are applied (inputs are expected to be
+ * normalised already; a monotone squashing never changes a top-k).
+ * Requires D*sizeof(elem) to be a multiple of 16 bytes and D <= 1024.
+ * ------------------------------------------------------------------------- */
+lsa_status lsa_score(const lsa_shape* shape, const void* q_idx_dev, const void* emb_dev,
+                     const int32_t* chunk_off_dev, float* scores_dev, void* hip_stream);
+
+/* ---------------------------------------------------------------------------
+ * Top-k keep set.  Dimensionstp review section 3-2-3 step 5 (top-k keep
+ * mask).  For each stream, keeps the k_b chunks ranked first by (score
+ * descending, chunk index ascending); NaN ranks below every number and -0.0
+ * equals +0.0.  Writes their chunk indices (0-based within the stream) in
+ * ascending order to sel_idx_dev[sel_off[b] .. sel_off[b+1]).
+ * scores_dev: [total_chunks] fp32; sel_idx_dev: [total_k] int32.
+ * Requires max_chunks <= 65536.  The result is a deterministic function of the
+ * fp32 scores (bit-identical across runs).
+ * ------------------------------------------------------------------------- */
+lsa_status lsa_select_topk(const lsa_shape* shape, const float* scores_dev,
+                           const int32_t* chunk_off_dev, const int32_t* sel_off_dev,
+                           int32_t* sel_idx_dev, void* hip_stream);
+
+/* ---------------------------------------------------------------------------
+ * Resident chunk pool.  Wiki note flowchart ("Resident KV chunks ~13.5%
+ * footprint"); molayo explainer (a selective gather of the query-critical
+ * chunks instead of a sweep of the whole cache).  Copies each kept chunk into
+ * its pool slot: slot s = sel_off[b] + j receives chunk n = sel_idx[s] of
+ * stream b, row r of the slot being token n*C + r; rows with n*C + r >= L_b
+ * are zero-filled.
+ * k_store_dev: [sum L][head_dim_qk]; k_pool_dev: [total_k][C][head_dim_qk].
+ * v_store_dev / v_pool_dev: [sum L][head_dim_v] / [total_k][C][head_dim_v];
+ * both must be NULL when v_aliases_k (the K pool then carries V too).
+ * A bit-exact copy.
+ * ------------------------------------------------------------------------- */
+lsa_status lsa_gather_chunks(const lsa_shape* shape, const void* k_store_dev,
+                             const void* v_store_dev, const int64_t* tok_off_dev,
+                             const int32_t* sel_idx_dev, const int32_t* sel_off_dev,
+                             void* k_pool_dev, void* v_pool_dev, void* hip_stream);
+
+/* ---------------------------------------------------------------------------
+ * Sparse decode attention over the kept chunks.  Dimensionstp review section
+ * 3-2-3 steps 6-7: unselected chunks are masked out and attention runs over
+ * the kept ones.  For every stream b and head h, over the tokens t of the
+ * kept chunks (t < L_b):
+ *   x_t = softmax_scale * <q[b][h], K_t>
+ *   out[b][h][:] = sum_t exp(x_t) V_t / sum_t exp(x_t)
+ *   lse[b][h]    = log(sum_t exp(x_t))          (natural log)
+ * computed split-KV: workgroups own runs of 32-token tiles, keep an fp32
+ * online softmax, and a merge pass combines their partial (max, sum, output)
+ * by log-sum-exp.
+ * q_dev: [B][H][head_dim_qk].  kv_mode LSA_KV_STORE: k_base/v_base are the
+ * stores ([sum L][d]) and chunk sel_idx[s] of stream b is read in place.
+ * kv_mode LSA_KV_POOL: k_base/v_base are pools written by lsa_gather_chunks
+ * and slot s is read (sel_idx is still needed for the valid-token count of
+ * partial chunks).  v_base must be NULL when v_aliases_k.
+ * out_dev: [B][H][head_dim_v] fp32; lse_dev: [B][H] fp32 (may be NULL).
+ * workspace_dev: >= lsa_workspace_bytes(shape) bytes, 256-byte aligned; its
+ * contents on entry do not matter.
+ * Supported: bf16 with num_q_heads <= 64 and head_dim_qk == head_dim_v in
+ * {64, 128} (multi-query); bf16 with head_dim_qk 576, head_dim_v 512,
+ * v_aliases_k = 1 and num_q_heads a multiple of 16 up to 128 (absorbed
+ * latent attention); fp32 or bf16 with num_q_heads <= 16 and head dims <= 256
+ * (portable kernel).  Anything else returns LSA_ERR_UNSUPPORTED.
+ * ------------------------------------------------------------------------- */
+lsa_status lsa_sparse_decode_attn(const lsa_shape* shape, int32_t kv_mode, const void* q_dev,
+                                  const void* k_base_dev, const void* v_base_dev,
+                                  const int64_t* tok_off_dev, const int32_t* sel_idx_dev,
+                                  const int32_t* sel_off_dev, float* out_dev, float* lse_dev,
+                                  void* workspace_dev, size_t workspace_bytes,
+                                  void* hip_stream);
+
+/* ---------------------------------------------------------------------------
+ * One decode step of the whole path in one call: when `reindex` is non-zero,
+ * score -> select (-> gather into the pool when materialize_pool); then sparse
+ * attention (from the pool when materialize_pool, else in place from the
+ * store).  With reindex == 0 the previous sel_idx (and pool) are reused, which
+ * is the lookahead schedule of the review (section 3-1 table and section 4-3:
+ * re-score about every 64 decode steps).  Every phase is one grid over all
+ * streams; nothing returns to the host between phases.
+ * ev_attn_begin / ev_attn_end: optional hipEvent_t recorded on hip_stream
+ * right before and right after the split-KV attention kernel (the merge pass
+ * runs after ev_attn_end; NULL to skip), so a caller can time that kernel
+ * inside the step.
+ * ------------------------------------------------------------------------- */
+typedef struct lsa_step_args {
+  const void* q_idx_dev;        /* [B][D] indexer query embeddings */
+  const void* emb_dev;          /* [total_chunks][D] chunk embeddings */
+  const int32_t* chunk_off_dev; /* [B+1] */
+  float* scores_dev;            /* [total_chunks] fp32, written when reindex */
+  const int32_t* sel_off_dev;   /* [B+1] */
+  int32_t* sel_idx_dev;         /* [total_k], written when reindex, else read */
+  const void* q_dev;            /* [B][H][head_dim_qk] decode queries */
+  const void* k_store_dev;      /* [sum L][head_dim_qk] */
+  const void* v_store_dev;      /* [sum L][head_dim_v], NULL when v_aliases_k */
+  const int64_t* tok_off_dev;   /* [B+1] */
+  void* k_pool_dev;             /* [total_k][C][head_dim_qk] when materialize_pool */
+  void* v_pool_dev;             /* [total_k][C][head_dim_v] when materialize_pool
+                                   and not v_aliases_k, else NULL */
+  float* out_dev;               /* [B][H][head_dim_v] fp32 */
+  float* lse_dev;               /* [B][H] fp32 or NULL */
+  int32_t reindex;              /* non-zero: re-score and re-select this step */
+  int32_t materialize_pool;     /* non-zero: gather kept chunks into the pool */
+  void* ev_attn_begin;          /* hipEvent_t or NULL */
+  void* ev_attn_end;            /* hipEvent_t or NULL */
+} lsa_step_args;
+
+lsa_status lsa_decode_step(const lsa_shape* shape, const lsa_step_args* args,
+                           void* workspace_dev, size_t workspace_bytes, void* hip_stream);
+
+/* ---------------------------------------------------------------------------
+ * Measurement helpers (not part of the method).
+ * lsa_bench_copy: streaming device copy of `bytes` (a multiple of 16, both
+ *   pointers 16-byte aligned); the reference kernel against which HBM counters
+ *   and achievable bandwidth are calibrated.
+ * lsa_bench_flush: overwrites `bytes` of a caller buffer (multiple of 16) so
+ *   that caches hold none of a workload's data afterwards.
+ * ------------------------------------------------------------------------- */
+lsa_status lsa_bench_copy(void* dst_dev, const void* src_dev, size_t bytes, void* hip_stream);
+lsa_status lsa_bench_flush(void* buf_dev, size_t bytes, void* hip_stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* LSA_H */

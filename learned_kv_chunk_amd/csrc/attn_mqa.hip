@@ -1,0 +1,371 @@
+// attn_mqa.hip -- split-KV sparse decode attention on the matrix cores for
+// multi-query attention (all query heads share one KV head), bf16 inputs,
+// head_dim_qk == head_dim_v == D in {64, 128}.
+//
+// Dimensionstp review, section 3-2-3 steps 6-7: softmax attention restricted
+// to the kept chunks.  Per 32-token tile and group of 16 heads a wave does
+//   S^T[token][head] = K_tile . Q^T        (v_mfma_f32_16x16x32_bf16, K = d)
+//   online softmax in fp32 (exp2 domain), weights rounded to bf16
+//   O^T[col][head]  += V_tile^T . P^T       (v_mfma_f32_16x16x32_bf16, K = tokens)
+// Computing the transposed products makes the softmax state line up with the
+// matrix-core register layouts: in S^T's accumulator a lane holds four tokens
+// of one head (head = lane % 16), which is exactly the lane's slice of the P^T
+// operand of the second product, and the O^T accumulator keeps one head per
+// lane, so rescaling by the running maximum needs no cross-lane traffic.
+// K tiles are loaded straight from HBM into the operand registers (each load
+// instruction covers 16 rows x 64 contiguous bytes); V tiles go through a
+// per-wave LDS buffer because the second product contracts over tokens,
+// which are strided in memory.  Each wave software-pipelines its tiles: the
+// next tile's loads are in flight while the current one is computed.
+// A workgroup's four waves take interleaved tiles of one run, then merge their
+// (max, sum, output) states through LDS into one partial result.
+#include <math.h>
+
+#include "lsa_internal.hpp"
+
+namespace lsa {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kMaxSlots = 264;  // kept chunks one workgroup's tiles can span
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+template <int D>
+struct TileRegs {
+  u32x4 k[2][D / 32];  // K operand: token block (16 rows) x 32-wide d step
+  u32x4 v[D / 16];     // V tile pieces (16 bytes each), written to LDS later
+};
+
+struct TileInfo {
+  int64_t row0;    // element row of the tile's first token in the K/V base
+  int32_t nvalid;  // tokens of the tile inside the stream (0..32)
+};
+
+// Loads are unconditional so that the compiler can count them and keep the
+// next tile in flight: rows past the tile's valid tokens re-read its last
+// valid row (their logits are masked and their weights are zero).
+template <int D>
+__device__ __forceinline__ void issue_tile(const uint16_t* __restrict__ kb,
+                                           const uint16_t* __restrict__ vb, int32_t k_row,
+                                           int32_t v_row, const TileInfo& ti, TileRegs<D>& r,
+                                           int lane) {
+  constexpr int PR = D / 8;  // 16-byte pieces per row
+  const int r16 = lane & 15, g = lane >> 4;
+  const int last = ti.nvalid > 0 ? ti.nvalid - 1 : 0;
+#pragma unroll
+  for (int blk = 0; blk < 2; ++blk) {
+    const int row = min(blk * 16 + r16, last);
+    const u32x4* src = reinterpret_cast<const u32x4*>(kb + (ti.row0 + row) * k_row) + g;
+#pragma unroll
+    for (int s = 0; s < D / 32; ++s) r.k[blk][s] = src[s * 4];
+  }
+#pragma unroll
+  for (int i = 0; i < D / 16; ++i) {
+    const int flat = i * kWave + lane;
+    const int row = min(flat / PR, last), c16 = flat % PR;
+    r.v[i] = reinterpret_cast<const u32x4*>(vb + (ti.row0 + row) * v_row)[c16];
+  }
+}
+
+template <int D, int NHG>
+__device__ __forceinline__ void compute_tile(const TileRegs<D>& r, int32_t nvalid,
+                                             const bf16x8 (&qf)[NHG][D / 32], float (&m)[NHG],
+                                             float (&l)[NHG], f32x4 (&o)[NHG][D / 16],
+                                             unsigned char* __restrict__ sv, float scale_log2,
+                                             int lane) {
+  constexpr int PR = D / 8;
+  constexpr int ROWB = 2 * D + 16;
+  const int r16 = lane & 15, g = lane >> 4;
+
+  // S^T = K Q^T for both 16-token blocks and every head group
+  f32x4 sacc[NHG][2];
+#pragma unroll
+  for (int hg = 0; hg < NHG; ++hg)
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < D / 32; ++s)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(r.k[blk][s]), qf[hg][s], acc, 0,
+                                                      0, 0);
+      sacc[hg][blk] = acc;
+    }
+
+  // V tile -> this wave's LDS buffer (row-major, padded rows)
+#pragma unroll
+  for (int i = 0; i < D / 16; ++i) {
+    const int flat = i * kWave + lane;
+    const int row = flat / PR, c16 = flat % PR;
+    *reinterpret_cast<u32x4*>(sv + row * ROWB + c16 * 16) = r.v[i];
+  }
+
+  // online softmax; the lane's eight weights form its P^T operand directly
+  bf16x8 pf[NHG];
+#pragma unroll
+  for (int hg = 0; hg < NHG; ++hg) {
+    float x[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int tok = 16 * (j >> 2) + 4 * g + (j & 3);
+      x[j] = (tok < nvalid) ? sacc[hg][j >> 2][j & 3] * scale_log2 : -INFINITY;
+    }
+    float mt = x[0];
+#pragma unroll
+    for (int j = 1; j < 8; ++j) mt = fmaxf(mt, x[j]);
+    mt = fmaxf(mt, __shfl_xor(mt, 16, kWave));
+    mt = fmaxf(mt, __shfl_xor(mt, 32, kWave));
+    const float m_new = fmaxf(m[hg], mt);
+    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(m[hg] - m_use);
+    float ps = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float p = __builtin_amdgcn_exp2f(x[j] - m_use);
+      ps += p;
+      pf[hg][j] = static_cast<__bf16>(p);
+    }
+    l[hg] = fmaf(l[hg], alpha, ps);
+    m[hg] = m_new;
+#pragma unroll
+    for (int cg = 0; cg < D / 16; ++cg) o[hg][cg] *= alpha;
+  }
+
+  // O^T += V^T P^T: the V^T operand of a lane is column cg*16 + lane%16 at
+  // the eight tokens that pair with its weights.
+#pragma unroll
+  for (int cg = 0; cg < D / 16; ++cg) {
+    const unsigned char* col = sv + (cg * 16 + r16) * 2;
+    uint16_t e[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int tok = 16 * (j >> 2) + 4 * g + (j & 3);
+      e[j] = *reinterpret_cast<const uint16_t*>(col + tok * ROWB);
+    }
+    u32x4 packed;
+    packed.x = e[0] | (static_cast<uint32_t>(e[1]) << 16);
+    packed.y = e[2] | (static_cast<uint32_t>(e[3]) << 16);
+    packed.z = e[4] | (static_cast<uint32_t>(e[5]) << 16);
+    packed.w = e[6] | (static_cast<uint32_t>(e[7]) << 16);
+    const bf16x8 vt = as_bf16x8(packed);
+#pragma unroll
+    for (int hg = 0; hg < NHG; ++hg)
+      o[hg][cg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt, pf[hg], o[hg][cg], 0, 0, 0);
+  }
+}
+
+template <int D, int NHG>
+struct MqaLds {
+  static constexpr int kRowBytes = 2 * D + 16;
+  static constexpr int kTileBytes = kTileTokens * kRowBytes;              // per wave
+  static constexpr int kStateO = NHG * (D / 16) * kWave * 16;            // lane-major o
+  static constexpr int kStateBytes = kStateO + 2 * NHG * kWave * 4;      // + m, l
+  static constexpr int kBytes = (kAttnWaves * kTileBytes > 2 * kStateBytes)
+                                    ? kAttnWaves * kTileBytes
+                                    : 2 * kStateBytes;
+};
+
+template <int D, int NHG>
+__device__ __forceinline__ void store_state(unsigned char* base, const float (&m)[NHG],
+                                            const float (&l)[NHG], const f32x4 (&o)[NHG][D / 16],
+                                            int lane) {
+  using L = MqaLds<D, NHG>;
+#pragma unroll
+  for (int hg = 0; hg < NHG; ++hg) {
+#pragma unroll
+    for (int cg = 0; cg < D / 16; ++cg)
+      reinterpret_cast<f32x4*>(base)[(hg * (D / 16) + cg) * kWave + lane] = o[hg][cg];
+    reinterpret_cast<float*>(base + L::kStateO)[hg * kWave + lane] = m[hg];
+    reinterpret_cast<float*>(base + L::kStateO)[(NHG + hg) * kWave + lane] = l[hg];
+  }
+}
+
+template <int D, int NHG>
+__device__ __forceinline__ void merge_state(const unsigned char* base, float (&m)[NHG],
+                                            float (&l)[NHG], f32x4 (&o)[NHG][D / 16], int lane) {
+  using L = MqaLds<D, NHG>;
+#pragma unroll
+  for (int hg = 0; hg < NHG; ++hg) {
+    const float mo = reinterpret_cast<const float*>(base + L::kStateO)[hg * kWave + lane];
+    const float lo = reinterpret_cast<const float*>(base + L::kStateO)[(NHG + hg) * kWave + lane];
+    const float mx = fmaxf(m[hg], mo);
+    const float mu = (mx == -INFINITY) ? 0.f : mx;
+    const float fs = __builtin_amdgcn_exp2f(m[hg] - mu);
+    const float fo = __builtin_amdgcn_exp2f(mo - mu);
+    l[hg] = l[hg] * fs + lo * fo;
+    m[hg] = mx;
+#pragma unroll
+    for (int cg = 0; cg < D / 16; ++cg)
+      o[hg][cg] = o[hg][cg] * fs +
+                  reinterpret_cast<const f32x4*>(base)[(hg * (D / 16) + cg) * kWave + lane] * fo;
+  }
+}
+
+template <int D, int NHG>
+__global__ __launch_bounds__(kAttnThreads, NHG == 1 ? 2 : 1) void attn_mqa_kernel(AttnArgs a) {
+  using L = MqaLds<D, NHG>;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[L::kBytes];
+  __shared__ int32_t s_plan[2];
+  __shared__ int32_t s_slot[kMaxSlots];
+
+  const int tid = threadIdx.x;
+  const int wave = tid / kWave;
+  const int lane = tid & (kWave - 1);
+  const int r16 = lane & 15, g = lane >> 4;
+
+  if (wave == 0) {
+    int32_t b, local;
+    find_stream_of_wg(a.sel_off, a.B, a.tiles_per_chunk, a.per, blockIdx.x, &b, &local);
+    if (lane == 0) {
+      s_plan[0] = b;
+      s_plan[1] = local;
+    }
+  }
+  __syncthreads();
+  const int32_t b = s_plan[0];
+  if (b < 0) return;
+  const int32_t tpc = a.tiles_per_chunk, C = a.C, H = a.H;
+  const int32_t sel0 = a.sel_off[b];
+  const int32_t n_tiles = (a.sel_off[b + 1] - sel0) * tpc;
+  const int32_t t_begin = s_plan[1] * a.per;
+  const int32_t t_end = min(n_tiles, t_begin + a.per);
+  const int32_t slot_first = t_begin / tpc;
+  const int32_t nslots = (t_end - 1) / tpc - slot_first + 1;
+  for (int32_t i = tid; i < nslots; i += kAttnThreads) s_slot[i] = a.sel_idx[sel0 + slot_first + i];
+  const int64_t tb = a.tok_off[b];
+  const int64_t len = a.tok_off[b + 1] - tb;
+  const int64_t last_chunk = len > 0 ? (len - 1) / C : 0;
+
+  // Q^T operand: lane holds Q[head hg*16 + lane%16][s*32 + 8*(lane/16) + 0..7]
+  const uint16_t* __restrict__ qb = static_cast<const uint16_t*>(a.q);
+  bf16x8 qf[NHG][D / 32];
+#pragma unroll
+  for (int hg = 0; hg < NHG; ++hg) {
+    const int head = hg * 16 + r16;
+    const u32x4* src =
+        reinterpret_cast<const u32x4*>(qb + (static_cast<int64_t>(b) * H + head) * D) + g;
+#pragma unroll
+    for (int s = 0; s < D / 32; ++s)
+      qf[hg][s] = as_bf16x8(head < H ? src[s * 4] : u32x4{0u, 0u, 0u, 0u});
+  }
+  __syncthreads();
+
+  // Tile i of this wave is t_begin + wave + 4*i.  An empty tile (past the end
+  // of a partial chunk) points at its chunk's first row with nvalid = 0.
+  const int32_t n_mine = (t_end - t_begin - wave + kAttnWaves - 1) / kAttnWaves;
+  auto tile_info = [&](int32_t i) {
+    TileInfo ti;
+    const int32_t t = t_begin + wave + kAttnWaves * i;
+    const int32_t j = t / tpc;
+    const int32_t sub = t - j * tpc;
+    // a kept index outside [0, N_b) (a violated precondition) is clamped so
+    // that no read leaves the stream
+    int64_t n = s_slot[j - slot_first];
+    n = n < 0 ? 0 : (n > last_chunk ? last_chunk : n);
+    int64_t valid = len - n * C;
+    if (valid > C) valid = C;
+    valid -= static_cast<int64_t>(sub) * kTileTokens;
+    const int64_t chunk_row = a.pool ? static_cast<int64_t>(sel0 + j) * C : tb + n * C;
+    if (valid <= 0) {
+      ti.nvalid = 0;
+      ti.row0 = chunk_row;
+    } else {
+      ti.nvalid = valid > kTileTokens ? kTileTokens : static_cast<int32_t>(valid);
+      ti.row0 = chunk_row + sub * kTileTokens;
+    }
+    return ti;
+  };
+
+  const uint16_t* __restrict__ kb = static_cast<const uint16_t*>(a.k);
+  const uint16_t* __restrict__ vb = static_cast<const uint16_t*>(a.v);
+  unsigned char* sv = smem + wave * L::kTileBytes;
+
+  float m[NHG], l[NHG];
+  f32x4 o[NHG][D / 16];
+#pragma unroll
+  for (int hg = 0; hg < NHG; ++hg) {
+    m[hg] = -INFINITY;
+    l[hg] = 0.f;
+#pragma unroll
+    for (int cg = 0; cg < D / 16; ++cg) o[hg][cg] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  // Software pipeline, two register sets: the loads of tile i+1 are in flight
+  // while tile i is computed.  Past the last tile the prefetch repeats the last
+  // tile (an L2 hit) so that every iteration issues the same loads.
+  if (n_mine > 0) {
+    TileRegs<D> ra, rb;
+    TileInfo ia = tile_info(0), ib;
+    issue_tile<D>(kb, vb, a.k_row, a.v_row, ia, ra, lane);
+    for (int32_t i = 0;; i += 2) {
+      ib = tile_info(min(i + 1, n_mine - 1));
+      issue_tile<D>(kb, vb, a.k_row, a.v_row, ib, rb, lane);
+      __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the compute
+      compute_tile<D, NHG>(ra, ia.nvalid, qf, m, l, o, sv, a.scale_log2, lane);
+      if (i + 1 >= n_mine) break;
+      ia = tile_info(min(i + 2, n_mine - 1));
+      issue_tile<D>(kb, vb, a.k_row, a.v_row, ia, ra, lane);
+      __builtin_amdgcn_sched_barrier(0);
+      compute_tile<D, NHG>(rb, ib.nvalid, qf, m, l, o, sv, a.scale_log2, lane);
+      if (i + 2 >= n_mine) break;
+    }
+  }
+
+  // merge the four waves' states: 3,2 -> 1,0 ; 1 -> 0
+  __syncthreads();
+  if (wave >= 2) store_state<D, NHG>(smem + (wave - 2) * L::kStateBytes, m, l, o, lane);
+  __syncthreads();
+  if (wave < 2) merge_state<D, NHG>(smem + wave * L::kStateBytes, m, l, o, lane);
+  __syncthreads();
+  if (wave == 1) store_state<D, NHG>(smem, m, l, o, lane);
+  __syncthreads();
+  if (wave != 0) return;
+  merge_state<D, NHG>(smem, m, l, o, lane);
+
+  const int64_t wg = blockIdx.x;
+#pragma unroll
+  for (int hg = 0; hg < NHG; ++hg) {
+    float lt = l[hg];
+    lt += __shfl_xor(lt, 16, kWave);
+    lt += __shfl_xor(lt, 32, kWave);
+    const int head = hg * 16 + r16;
+    if (head >= H) continue;
+    if (g == 0) {
+      a.ws_m[wg * H + head] = m[hg];
+      a.ws_l[wg * H + head] = lt;
+    }
+#pragma unroll
+    for (int cg = 0; cg < D / 16; ++cg)
+      *reinterpret_cast<f32x4*>(a.ws_o + (wg * H + head) * D + cg * 16 + 4 * g) = o[hg][cg];
+  }
+}
+
+template <int D>
+hipError_t launch_mqa_d(const AttnArgs& a, int64_t grid, hipStream_t st) {
+  const int nhg = (a.H + 15) / 16;
+  dim3 g(static_cast<uint32_t>(grid)), blk(kAttnThreads);
+  if (nhg == 1) hipLaunchKernelGGL((attn_mqa_kernel<D, 1>), g, blk, 0, st, a);
+  else if (nhg == 2) hipLaunchKernelGGL((attn_mqa_kernel<D, 2>), g, blk, 0, st, a);
+  else if (nhg <= 4) hipLaunchKernelGGL((attn_mqa_kernel<D, 4>), g, blk, 0, st, a);
+  else return hipErrorNotSupported;
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool mqa_attn_supported(const lsa_shape& s) {
+  return s.dtype == LSA_DTYPE_BF16 && !s.v_aliases_k && s.head_dim_qk == s.head_dim_v &&
+         (s.head_dim_qk == 64 || s.head_dim_qk == 128) && s.num_q_heads >= 1 &&
+         s.num_q_heads <= 64;
+}
+
+hipError_t launch_attn_mqa(const lsa_shape& s, const AttnArgs& a, int64_t grid, hipStream_t st) {
+  if (s.head_dim_qk == 128) return launch_mqa_d<128>(a, grid, st);
+  if (s.head_dim_qk == 64) return launch_mqa_d<64>(a, grid, st);
+  return hipErrorNotSupported;
+}
+
+}  // namespace lsa

@@ -1,0 +1,288 @@
+// capi.hip -- the extern "C" entry points of lsa.h: host-side validation of
+// every argument, workspace sizing, and kernel enqueueing on the caller's
+// stream.  No entry point allocates, synchronises or reads device memory.
+#include <math.h>
+#include <stdint.h>
+
+#include "lsa_internal.hpp"
+
+namespace lsa {
+namespace {
+
+constexpr int32_t kMaxChunkSize = 1024;
+constexpr int32_t kMaxChunksPerStream = 65536;
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int32_t elem_bytes(const lsa_shape& s) { return s.dtype == LSA_DTYPE_BF16 ? 2 : 4; }
+
+// Checks shared by every entry point: batch, chunking and the CSR totals.
+lsa_status check_common(const lsa_shape* s) {
+  if (s == nullptr) return LSA_ERR_INVALID_ARGUMENT;
+  if (s->batch < 1 || s->chunk_size < 1 || s->chunk_size > kMaxChunkSize) return LSA_ERR_INVALID_ARGUMENT;
+  if (s->dtype != LSA_DTYPE_F32 && s->dtype != LSA_DTYPE_BF16) return LSA_ERR_INVALID_ARGUMENT;
+  if (s->reserved != 0 || s->attn_tiles_per_block < 0) return LSA_ERR_INVALID_ARGUMENT;
+  if (s->max_chunks < 1 || s->max_k < 1 || s->max_k > s->max_chunks) return LSA_ERR_INVALID_ARGUMENT;
+  if (s->total_chunks < s->batch || s->total_chunks > static_cast<int64_t>(s->batch) * s->max_chunks ||
+      s->total_chunks > INT32_MAX)
+    return LSA_ERR_INVALID_ARGUMENT;
+  if (s->total_k < s->batch || s->total_k > static_cast<int64_t>(s->batch) * s->max_k ||
+      s->total_k > s->total_chunks)
+    return LSA_ERR_INVALID_ARGUMENT;
+  return LSA_OK;
+}
+
+lsa_status check_score(const lsa_shape* s) {
+  lsa_status st = check_common(s);
+  if (st != LSA_OK) return st;
+  if (s->index_dim < 1) return LSA_ERR_INVALID_ARGUMENT;
+  if (!score_supported(*s)) return LSA_ERR_UNSUPPORTED;
+  return LSA_OK;
+}
+
+lsa_status check_select(const lsa_shape* s) {
+  lsa_status st = check_common(s);
+  if (st != LSA_OK) return st;
+  if (s->max_chunks > kMaxChunksPerStream) return LSA_ERR_UNSUPPORTED;
+  return LSA_OK;
+}
+
+lsa_status check_attn_shape(const lsa_shape* s) {
+  lsa_status st = check_common(s);
+  if (st != LSA_OK) return st;
+  if (s->num_q_heads < 1 || s->head_dim_qk < 1 || s->head_dim_v < 1) return LSA_ERR_INVALID_ARGUMENT;
+  if (s->v_aliases_k != 0 && s->v_aliases_k != 1) return LSA_ERR_INVALID_ARGUMENT;
+  if (s->v_aliases_k && s->head_dim_v > s->head_dim_qk) return LSA_ERR_INVALID_ARGUMENT;
+  if (!(s->softmax_scale > 0.f) || !isfinite(s->softmax_scale)) return LSA_ERR_INVALID_ARGUMENT;
+  if ((s->head_dim_qk * elem_bytes(*s)) % 16 != 0 || (s->head_dim_v * elem_bytes(*s)) % 16 != 0)
+    return LSA_ERR_UNSUPPORTED;
+  if (!mqa_attn_supported(*s) && !mla_attn_supported(*s) && !portable_attn_supported(*s))
+    return LSA_ERR_UNSUPPORTED;
+  return LSA_OK;
+}
+
+lsa_status hip_status(hipError_t e) { return e == hipSuccess ? LSA_OK : LSA_ERR_HIP; }
+
+// Enqueue the attention partial kernel and the merge; arguments validated.
+// ev_begin / ev_end (may be null) bracket the partial kernel.
+lsa_status enqueue_attention(const lsa_shape& s, int32_t kv_mode, const void* q, const void* kbase,
+                             const void* vbase, const int64_t* tok_off, const int32_t* sel_idx,
+                             const int32_t* sel_off, float* out, float* lse, void* ws,
+                             hipStream_t st, void* ev_begin = nullptr, void* ev_end = nullptr) {
+  const AttnPlan plan = make_attn_plan(s);
+  const PartialLayout pl = partial_layout(s, plan);
+  AttnArgs a;
+  a.q = q;
+  a.k = kbase;
+  a.v = s.v_aliases_k ? kbase : vbase;
+  a.tok_off = tok_off;
+  a.sel_idx = sel_idx;
+  a.sel_off = sel_off;
+  a.out = out;
+  a.lse = lse;
+  a.ws_m = reinterpret_cast<float*>(static_cast<char*>(ws) + pl.m_off);
+  a.ws_l = reinterpret_cast<float*>(static_cast<char*>(ws) + pl.l_off);
+  a.ws_o = reinterpret_cast<float*>(static_cast<char*>(ws) + pl.o_off);
+  a.B = s.batch;
+  a.H = s.num_q_heads;
+  a.dqk = s.head_dim_qk;
+  a.dv = s.head_dim_v;
+  a.C = s.chunk_size;
+  a.k_row = s.head_dim_qk;
+  a.v_row = s.v_aliases_k ? s.head_dim_qk : s.head_dim_v;
+  a.pool = kv_mode == LSA_KV_POOL ? 1 : 0;
+  a.tiles_per_chunk = plan.tiles_per_chunk;
+  a.per = plan.per;
+  a.scale_log2 = s.softmax_scale * 1.4426950408889634f;
+  if (ev_begin && hipEventRecord(static_cast<hipEvent_t>(ev_begin), st) != hipSuccess)
+    return LSA_ERR_HIP;
+  hipError_t e;
+  if (mla_attn_supported(s)) e = launch_attn_mla(s, a, plan.grid, st);
+  else if (mqa_attn_supported(s)) e = launch_attn_mqa(s, a, plan.grid, st);
+  else e = launch_attn_portable(s, a, plan.grid, st);
+  if (e != hipSuccess) return LSA_ERR_HIP;
+  if (ev_end && hipEventRecord(static_cast<hipEvent_t>(ev_end), st) != hipSuccess)
+    return LSA_ERR_HIP;
+  return hip_status(launch_attn_merge(s, a, st));
+}
+
+}  // namespace
+}  // namespace lsa
+
+using namespace lsa;
+
+extern "C" {
+
+const char* lsa_status_string(lsa_status status) {
+  switch (status) {
+    case LSA_OK: return "LSA_OK";
+    case LSA_ERR_INVALID_ARGUMENT: return "LSA_ERR_INVALID_ARGUMENT";
+    case LSA_ERR_UNSUPPORTED: return "LSA_ERR_UNSUPPORTED";
+    case LSA_ERR_WORKSPACE_TOO_SMALL: return "LSA_ERR_WORKSPACE_TOO_SMALL";
+    case LSA_ERR_HIP: return "LSA_ERR_HIP";
+    default: return "LSA_ERR_UNKNOWN";
+  }
+}
+
+int32_t lsa_abi_version(void) { return 1; }
+
+int32_t lsa_keep_count(int32_t n_chunks, int32_t ratio_num, int32_t ratio_den, int32_t round_up) {
+  if (n_chunks <= 0 || ratio_num <= 0 || ratio_den <= 0) return 0;
+  const int64_t prod = static_cast<int64_t>(n_chunks) * ratio_num;
+  int64_t k = round_up ? (prod + ratio_den - 1) / ratio_den : prod / ratio_den;
+  if (k < 1) k = 1;
+  if (k > n_chunks) k = n_chunks;
+  return static_cast<int32_t>(k);
+}
+
+size_t lsa_workspace_bytes(const lsa_shape* shape) {
+  if (check_attn_shape(shape) != LSA_OK) return 0;
+  return partial_layout(*shape, make_attn_plan(*shape)).total;
+}
+
+lsa_status lsa_score(const lsa_shape* shape, const void* q_idx_dev, const void* emb_dev,
+                     const int32_t* chunk_off_dev, float* scores_dev, void* hip_stream) {
+  lsa_status st = check_score(shape);
+  if (st != LSA_OK) return st;
+  if (!q_idx_dev || !emb_dev || !chunk_off_dev || !scores_dev) return LSA_ERR_INVALID_ARGUMENT;
+  if (!aligned(q_idx_dev, 16) || !aligned(emb_dev, 16) || !aligned(chunk_off_dev, 4) ||
+      !aligned(scores_dev, 4))
+    return LSA_ERR_INVALID_ARGUMENT;
+  (void)hipGetLastError();
+  return hip_status(launch_score(*shape, q_idx_dev, emb_dev, chunk_off_dev, scores_dev,
+                                 static_cast<hipStream_t>(hip_stream)));
+}
+
+lsa_status lsa_select_topk(const lsa_shape* shape, const float* scores_dev,
+                           const int32_t* chunk_off_dev, const int32_t* sel_off_dev,
+                           int32_t* sel_idx_dev, void* hip_stream) {
+  lsa_status st = check_select(shape);
+  if (st != LSA_OK) return st;
+  if (!scores_dev || !chunk_off_dev || !sel_off_dev || !sel_idx_dev) return LSA_ERR_INVALID_ARGUMENT;
+  if (!aligned(scores_dev, 4) || !aligned(chunk_off_dev, 4) || !aligned(sel_off_dev, 4) ||
+      !aligned(sel_idx_dev, 4))
+    return LSA_ERR_INVALID_ARGUMENT;
+  (void)hipGetLastError();
+  return hip_status(launch_select(*shape, scores_dev, chunk_off_dev, sel_off_dev, sel_idx_dev,
+                                  static_cast<hipStream_t>(hip_stream)));
+}
+
+lsa_status lsa_gather_chunks(const lsa_shape* shape, const void* k_store_dev,
+                             const void* v_store_dev, const int64_t* tok_off_dev,
+                             const int32_t* sel_idx_dev, const int32_t* sel_off_dev,
+                             void* k_pool_dev, void* v_pool_dev, void* hip_stream) {
+  lsa_status st = check_common(shape);
+  if (st != LSA_OK) return st;
+  const lsa_shape& s = *shape;
+  if (s.head_dim_qk < 1 || (s.v_aliases_k != 0 && s.v_aliases_k != 1)) return LSA_ERR_INVALID_ARGUMENT;
+  if (!s.v_aliases_k && s.head_dim_v < 1) return LSA_ERR_INVALID_ARGUMENT;
+  if (!k_store_dev || !tok_off_dev || !sel_idx_dev || !sel_off_dev || !k_pool_dev)
+    return LSA_ERR_INVALID_ARGUMENT;
+  if (s.v_aliases_k ? (v_store_dev || v_pool_dev) : (!v_store_dev || !v_pool_dev))
+    return LSA_ERR_INVALID_ARGUMENT;
+  const int32_t kb = s.head_dim_qk * elem_bytes(s);
+  const int32_t vb = s.v_aliases_k ? 0 : s.head_dim_v * elem_bytes(s);
+  if (kb % 16 != 0 || vb % 16 != 0) return LSA_ERR_UNSUPPORTED;
+  if (!aligned(k_store_dev, 16) || !aligned(k_pool_dev, 16) ||
+      (v_store_dev && (!aligned(v_store_dev, 16) || !aligned(v_pool_dev, 16))) ||
+      !aligned(tok_off_dev, 8) || !aligned(sel_idx_dev, 4) || !aligned(sel_off_dev, 4))
+    return LSA_ERR_INVALID_ARGUMENT;
+  (void)hipGetLastError();
+  return hip_status(launch_gather(s, k_store_dev, kb, tok_off_dev, sel_idx_dev, sel_off_dev,
+                                  k_pool_dev, v_store_dev, vb, v_pool_dev,
+                                  static_cast<hipStream_t>(hip_stream)));
+}
+
+static lsa_status check_attn_args(const lsa_shape* shape, int32_t kv_mode, const void* q,
+                                  const void* kb, const void* vb, const int64_t* tok_off,
+                                  const int32_t* sel_idx, const int32_t* sel_off, const float* out,
+                                  const float* lse, const void* ws, size_t ws_bytes) {
+  lsa_status st = check_attn_shape(shape);
+  if (st != LSA_OK) return st;
+  if (kv_mode != LSA_KV_STORE && kv_mode != LSA_KV_POOL) return LSA_ERR_INVALID_ARGUMENT;
+  if (!q || !kb || !tok_off || !sel_idx || !sel_off || !out || !ws) return LSA_ERR_INVALID_ARGUMENT;
+  if (shape->v_aliases_k ? (vb != nullptr) : (vb == nullptr)) return LSA_ERR_INVALID_ARGUMENT;
+  if (!aligned(q, 16) || !aligned(kb, 16) || (vb && !aligned(vb, 16)) || !aligned(tok_off, 8) ||
+      !aligned(sel_idx, 4) || !aligned(sel_off, 4) || !aligned(out, 16) ||
+      (lse && !aligned(lse, 4)) || !aligned(ws, 256))
+    return LSA_ERR_INVALID_ARGUMENT;
+  if (ws_bytes < lsa_workspace_bytes(shape)) return LSA_ERR_WORKSPACE_TOO_SMALL;
+  return LSA_OK;
+}
+
+lsa_status lsa_sparse_decode_attn(const lsa_shape* shape, int32_t kv_mode, const void* q_dev,
+                                  const void* k_base_dev, const void* v_base_dev,
+                                  const int64_t* tok_off_dev, const int32_t* sel_idx_dev,
+                                  const int32_t* sel_off_dev, float* out_dev, float* lse_dev,
+                                  void* workspace_dev, size_t workspace_bytes, void* hip_stream) {
+  lsa_status st = check_attn_args(shape, kv_mode, q_dev, k_base_dev, v_base_dev, tok_off_dev,
+                                  sel_idx_dev, sel_off_dev, out_dev, lse_dev, workspace_dev,
+                                  workspace_bytes);
+  if (st != LSA_OK) return st;
+  (void)hipGetLastError();
+  return enqueue_attention(*shape, kv_mode, q_dev, k_base_dev, v_base_dev, tok_off_dev,
+                           sel_idx_dev, sel_off_dev, out_dev, lse_dev, workspace_dev,
+                           static_cast<hipStream_t>(hip_stream));
+}
+
+lsa_status lsa_decode_step(const lsa_shape* shape, const lsa_step_args* args, void* workspace_dev,
+                           size_t workspace_bytes, void* hip_stream) {
+  if (shape == nullptr || args == nullptr) return LSA_ERR_INVALID_ARGUMENT;
+  const lsa_step_args& x = *args;
+  const bool pool = x.materialize_pool != 0;
+  const void* kbase = pool ? x.k_pool_dev : x.k_store_dev;
+  const void* vbase = pool ? x.v_pool_dev : x.v_store_dev;
+  lsa_status st = check_attn_args(shape, pool ? LSA_KV_POOL : LSA_KV_STORE, x.q_dev, kbase, vbase,
+                                  x.tok_off_dev, x.sel_idx_dev, x.sel_off_dev, x.out_dev,
+                                  x.lse_dev, workspace_dev, workspace_bytes);
+  if (st != LSA_OK) return st;
+  if (pool && (!x.k_store_dev || (shape->v_aliases_k ? x.v_store_dev != nullptr : !x.v_store_dev)))
+    return LSA_ERR_INVALID_ARGUMENT;
+  if (pool && (!aligned(x.k_store_dev, 16) || (x.v_store_dev && !aligned(x.v_store_dev, 16))))
+    return LSA_ERR_INVALID_ARGUMENT;
+  if (x.reindex) {
+    st = check_score(shape);
+    if (st != LSA_OK) return st;
+    st = check_select(shape);
+    if (st != LSA_OK) return st;
+    if (!x.q_idx_dev || !x.emb_dev || !x.chunk_off_dev || !x.scores_dev)
+      return LSA_ERR_INVALID_ARGUMENT;
+    if (!aligned(x.q_idx_dev, 16) || !aligned(x.emb_dev, 16) || !aligned(x.chunk_off_dev, 4) ||
+        !aligned(x.scores_dev, 4))
+      return LSA_ERR_INVALID_ARGUMENT;
+  }
+  const hipStream_t hs = static_cast<hipStream_t>(hip_stream);
+  (void)hipGetLastError();
+  if (x.reindex) {
+    if (launch_score(*shape, x.q_idx_dev, x.emb_dev, x.chunk_off_dev, x.scores_dev, hs) != hipSuccess)
+      return LSA_ERR_HIP;
+    if (launch_select(*shape, x.scores_dev, x.chunk_off_dev, x.sel_off_dev, x.sel_idx_dev, hs) !=
+        hipSuccess)
+      return LSA_ERR_HIP;
+    if (pool) {
+      const int32_t kb = shape->head_dim_qk * elem_bytes(*shape);
+      const int32_t vb = shape->v_aliases_k ? 0 : shape->head_dim_v * elem_bytes(*shape);
+      if (launch_gather(*shape, x.k_store_dev, kb, x.tok_off_dev, x.sel_idx_dev, x.sel_off_dev,
+                        x.k_pool_dev, x.v_store_dev, vb, x.v_pool_dev, hs) != hipSuccess)
+        return LSA_ERR_HIP;
+    }
+  }
+  return enqueue_attention(*shape, pool ? LSA_KV_POOL : LSA_KV_STORE, x.q_dev, kbase, vbase,
+                           x.tok_off_dev, x.sel_idx_dev, x.sel_off_dev, x.out_dev, x.lse_dev,
+                           workspace_dev, hs, x.ev_attn_begin, x.ev_attn_end);
+}
+
+lsa_status lsa_bench_copy(void* dst_dev, const void* src_dev, size_t bytes, void* hip_stream) {
+  if (!dst_dev || !src_dev || bytes % 16 != 0 || !aligned(dst_dev, 16) || !aligned(src_dev, 16))
+    return LSA_ERR_INVALID_ARGUMENT;
+  (void)hipGetLastError();
+  return hip_status(launch_bench_copy(dst_dev, src_dev, bytes, static_cast<hipStream_t>(hip_stream)));
+}
+
+lsa_status lsa_bench_flush(void* buf_dev, size_t bytes, void* hip_stream) {
+  if (!buf_dev || bytes % 16 != 0 || !aligned(buf_dev, 16)) return LSA_ERR_INVALID_ARGUMENT;
+  (void)hipGetLastError();
+  return hip_status(launch_bench_flush(buf_dev, bytes, static_cast<hipStream_t>(hip_stream)));
+}
+
+}  // extern "C"

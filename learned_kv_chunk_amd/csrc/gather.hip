@@ -1,0 +1,115 @@
+// gather.hip -- resident chunk pool and measurement helpers.
+//
+// Wiki note flowchart ("Resident KV chunks ~13.5% footprint") and the molayo
+// explainer's selective-gather paragraph: only the kept chunks stay resident.
+// The gather copies each kept chunk of the K (and V) history into its pool
+// slot; rows past the end of the stream are zero-filled.  One workgroup per
+// (kept slot, stream); each thread moves 16-byte vectors with several loads
+// in flight, so a chunk is read and written as whole cache lines.
+#include "lsa_internal.hpp"
+
+namespace lsa {
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kGatherThreads = 256;
+constexpr int kGatherUnroll = 4;
+
+__device__ __forceinline__ void copy_chunk(const char* __restrict__ src, char* __restrict__ dst,
+                                           int64_t valid_bytes, int64_t total_bytes) {
+  const int tid = threadIdx.x;
+  constexpr int64_t kStep = static_cast<int64_t>(kGatherThreads) * 16;
+  for (int64_t off0 = static_cast<int64_t>(tid) * 16; off0 < total_bytes;
+       off0 += kStep * kGatherUnroll) {
+    u32x4 v[kGatherUnroll];
+#pragma unroll
+    for (int u = 0; u < kGatherUnroll; ++u) {
+      const int64_t off = off0 + u * kStep;
+      v[u] = (off < valid_bytes) ? *reinterpret_cast<const u32x4*>(src + off)
+                                 : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int u = 0; u < kGatherUnroll; ++u) {
+      const int64_t off = off0 + u * kStep;
+      if (off < total_bytes) *reinterpret_cast<u32x4*>(dst + off) = v[u];
+    }
+  }
+}
+
+__global__ __launch_bounds__(kGatherThreads) void gather_kernel(
+    const char* __restrict__ store, int32_t row_bytes, const int64_t* __restrict__ tok_off,
+    const int32_t* __restrict__ sel_idx, const int32_t* __restrict__ sel_off,
+    char* __restrict__ pool, const char* __restrict__ store2, int32_t row_bytes2,
+    char* __restrict__ pool2, int32_t C) {
+  const int b = blockIdx.y;
+  const int32_t j = blockIdx.x;
+  const int32_t k = sel_off[b + 1] - sel_off[b];
+  if (j >= k) return;
+  const int64_t slot = static_cast<int64_t>(sel_off[b]) + j;
+  const int64_t len = tok_off[b + 1] - tok_off[b];
+  const int64_t n = sel_idx[slot];
+  int64_t valid = len - n * C;
+  if (n < 0 || valid < 0) valid = 0;
+  if (valid > C) valid = C;
+  const int64_t row0 = tok_off[b] + n * C;
+  copy_chunk(store + row0 * row_bytes, pool + slot * C * row_bytes, valid * row_bytes,
+             static_cast<int64_t>(C) * row_bytes);
+  if (pool2 != nullptr)
+    copy_chunk(store2 + row0 * row_bytes2, pool2 + slot * C * row_bytes2, valid * row_bytes2,
+               static_cast<int64_t>(C) * row_bytes2);
+}
+
+__global__ __launch_bounds__(256) void copy_kernel(const u32x4* __restrict__ src,
+                                                   u32x4* __restrict__ dst, int64_t n) {
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
+       i += stride)
+    dst[i] = src[i];
+}
+
+__global__ __launch_bounds__(256) void flush_kernel(u32x4* __restrict__ buf, int64_t n,
+                                                    uint32_t salt) {
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
+       i += stride)
+    buf[i] = u32x4{salt, static_cast<uint32_t>(i), salt ^ 0x5bd1e995u, 1u};
+}
+
+}  // namespace
+
+hipError_t launch_gather(const lsa_shape& s, const void* store, int32_t row_bytes,
+                         const int64_t* tok_off, const int32_t* sel_idx,
+                         const int32_t* sel_off, void* pool, const void* store2,
+                         int32_t row_bytes2, void* pool2, hipStream_t st) {
+  if (s.max_k <= 0) return hipSuccess;
+  dim3 grid(s.max_k, s.batch);
+  hipLaunchKernelGGL(gather_kernel, grid, dim3(kGatherThreads), 0, st,
+                     static_cast<const char*>(store), row_bytes, tok_off, sel_idx, sel_off,
+                     static_cast<char*>(pool), static_cast<const char*>(store2), row_bytes2,
+                     static_cast<char*>(pool2), s.chunk_size);
+  return hipGetLastError();
+}
+
+hipError_t launch_bench_copy(void* dst, const void* src, size_t bytes, hipStream_t st) {
+  const int64_t n = static_cast<int64_t>(bytes / 16);
+  if (n == 0) return hipSuccess;
+  int64_t blocks = (n + 255) / 256;
+  if (blocks > 256 * 32) blocks = 256 * 32;
+  hipLaunchKernelGGL(copy_kernel, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0, st,
+                     static_cast<const u32x4*>(src), static_cast<u32x4*>(dst), n);
+  return hipGetLastError();
+}
+
+hipError_t launch_bench_flush(void* buf, size_t bytes, hipStream_t st) {
+  const uint32_t salt = 0x9e3779b9u;
+  const int64_t n = static_cast<int64_t>(bytes / 16);
+  if (n == 0) return hipSuccess;
+  int64_t blocks = (n + 255) / 256;
+  if (blocks > 256 * 32) blocks = 256 * 32;
+  hipLaunchKernelGGL(flush_kernel, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0, st,
+                     static_cast<u32x4*>(buf), n, salt);
+  return hipGetLastError();
+}
+
+}  // namespace lsa

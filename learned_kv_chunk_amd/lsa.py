@@ -1,0 +1,335 @@
+"""ctypes binding of liblsa.so (include/lsa.h): argument marshalling only.
+
+Every step of the path runs in the library's HIP kernels; this module checks
+tensor devices, dtypes, shapes and contiguity, fills the lsa_shape struct and
+passes raw device pointers plus torch's current HIP stream.  PyTorch provides
+device memory and streams only.  If the library is missing or fails to load,
+every call raises: there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liblsa.so")
+
+LSA_OK = 0
+LSA_ERR_INVALID_ARGUMENT = 1
+LSA_ERR_UNSUPPORTED = 2
+LSA_ERR_WORKSPACE_TOO_SMALL = 3
+LSA_ERR_HIP = 4
+
+DTYPE_F32 = 0
+DTYPE_BF16 = 1
+KV_STORE = 0
+KV_POOL = 1
+
+
+class LsaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} ({status})")
+
+
+class Shape(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32),
+        ("chunk_size", ctypes.c_int32),
+        ("index_dim", ctypes.c_int32),
+        ("num_q_heads", ctypes.c_int32),
+        ("head_dim_qk", ctypes.c_int32),
+        ("head_dim_v", ctypes.c_int32),
+        ("v_aliases_k", ctypes.c_int32),
+        ("dtype", ctypes.c_int32),
+        ("softmax_scale", ctypes.c_float),
+        ("max_chunks", ctypes.c_int32),
+        ("max_k", ctypes.c_int32),
+        ("total_chunks", ctypes.c_int64),
+        ("total_k", ctypes.c_int64),
+        ("attn_tiles_per_block", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+    ]
+
+
+class StepArgs(ctypes.Structure):
+    _fields_ = [
+        ("q_idx_dev", ctypes.c_void_p),
+        ("emb_dev", ctypes.c_void_p),
+        ("chunk_off_dev", ctypes.c_void_p),
+        ("scores_dev", ctypes.c_void_p),
+        ("sel_off_dev", ctypes.c_void_p),
+        ("sel_idx_dev", ctypes.c_void_p),
+        ("q_dev", ctypes.c_void_p),
+        ("k_store_dev", ctypes.c_void_p),
+        ("v_store_dev", ctypes.c_void_p),
+        ("tok_off_dev", ctypes.c_void_p),
+        ("k_pool_dev", ctypes.c_void_p),
+        ("v_pool_dev", ctypes.c_void_p),
+        ("out_dev", ctypes.c_void_p),
+        ("lse_dev", ctypes.c_void_p),
+        ("reindex", ctypes.c_int32),
+        ("materialize_pool", ctypes.c_int32),
+        ("ev_attn_begin", ctypes.c_void_p),
+        ("ev_attn_end", ctypes.c_void_p),
+    ]
+
+
+# Exported symbols of include/lsa.h with their (argtypes, restype).
+_P = ctypes.c_void_p
+_I32 = ctypes.c_int32
+_SIGNATURES = {
+    "lsa_status_string": ([_I32], ctypes.c_char_p),
+    "lsa_abi_version": ([], _I32),
+    "lsa_keep_count": ([_I32, _I32, _I32, _I32], _I32),
+    "lsa_workspace_bytes": ([ctypes.POINTER(Shape)], ctypes.c_size_t),
+    "lsa_score": ([ctypes.POINTER(Shape), _P, _P, _P, _P, _P], _I32),
+    "lsa_select_topk": ([ctypes.POINTER(Shape), _P, _P, _P, _P, _P], _I32),
+    "lsa_gather_chunks": ([ctypes.POINTER(Shape), _P, _P, _P, _P, _P, _P, _P, _P], _I32),
+    "lsa_sparse_decode_attn": ([ctypes.POINTER(Shape), _I32, _P, _P, _P, _P, _P, _P, _P, _P,
+                                _P, ctypes.c_size_t, _P], _I32),
+    "lsa_decode_step": ([ctypes.POINTER(Shape), ctypes.POINTER(StepArgs), _P, ctypes.c_size_t,
+                         _P], _I32),
+    "lsa_bench_copy": ([_P, _P, ctypes.c_size_t, _P], _I32),
+    "lsa_bench_flush": ([_P, ctypes.c_size_t, _P], _I32),
+}
+
+_lib = None
+
+
+def library() -> ctypes.CDLL:
+    """The loaded liblsa.so; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -c 'import __graft_entry__ as g; g.build()'`")
+        lib = ctypes.CDLL(LIB_PATH)
+        for name, (argtypes, restype) in _SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.argtypes = argtypes
+            fn.restype = restype
+        _lib = lib
+    return _lib
+
+
+def status_string(status: int) -> str:
+    try:
+        return library().lsa_status_string(status).decode()
+    except Exception:  # pragma: no cover - library unavailable while formatting an error
+        return f"status {status}"
+
+
+def _check(status: int, where: str) -> None:
+    if status != LSA_OK:
+        raise LsaError(status, where)
+
+
+# ----------------------------------------------------------------------------- shapes
+@dataclass
+class ProblemShape:
+    batch: int
+    chunk_size: int
+    index_dim: int
+    num_q_heads: int
+    head_dim_qk: int
+    head_dim_v: int
+    v_aliases_k: bool
+    dtype: torch.dtype
+    softmax_scale: float
+    max_chunks: int
+    max_k: int
+    total_chunks: int
+    total_k: int
+    attn_tiles_per_block: int = 0
+
+    def c(self) -> Shape:
+        if self.dtype == torch.bfloat16:
+            dt = DTYPE_BF16
+        elif self.dtype == torch.float32:
+            dt = DTYPE_F32
+        else:
+            raise ValueError(f"unsupported dtype {self.dtype}")
+        return Shape(self.batch, self.chunk_size, self.index_dim, self.num_q_heads,
+                      self.head_dim_qk, self.head_dim_v, int(bool(self.v_aliases_k)), dt,
+                      float(self.softmax_scale), self.max_chunks, self.max_k,
+                      self.total_chunks, self.total_k, self.attn_tiles_per_block, 0)
+
+
+def keep_count(n_chunks: int, ratio_num: int, ratio_den: int, round_up: bool) -> int:
+    return int(library().lsa_keep_count(n_chunks, ratio_num, ratio_den, int(round_up)))
+
+
+def workspace_bytes(shape: ProblemShape) -> int:
+    return int(library().lsa_workspace_bytes(ctypes.byref(shape.c())))
+
+
+def allocate_workspace(shape: ProblemShape, device) -> torch.Tensor:
+    n = workspace_bytes(shape)
+    if n == 0:
+        raise LsaError(LSA_ERR_UNSUPPORTED, "lsa_workspace_bytes")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+# ----------------------------------------------------------------------------- helpers
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None, ndim=None):
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device (HIP) tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must have dtype {dtype}, got {t.dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {t.dim()}")
+    return t
+
+
+# ----------------------------------------------------------------------------- entry points
+def score(shape: ProblemShape, q_idx, emb, chunk_off, scores=None, stream=None) -> torch.Tensor:
+    """lsa_score: fp32 scores [total_chunks]."""
+    _dev(q_idx, "q_idx", shape.dtype, 2)
+    _dev(emb, "emb", shape.dtype, 2)
+    _dev(chunk_off, "chunk_off", torch.int32, 1)
+    if scores is None:
+        scores = torch.empty(shape.total_chunks, dtype=torch.float32, device=emb.device)
+    _dev(scores, "scores", torch.float32, 1)
+    _check(library().lsa_score(ctypes.byref(shape.c()), _ptr(q_idx), _ptr(emb), _ptr(chunk_off),
+                               _ptr(scores), _stream(stream)), "lsa_score")
+    return scores
+
+
+def select_topk(shape: ProblemShape, scores, chunk_off, sel_off, sel_idx=None,
+                stream=None) -> torch.Tensor:
+    """lsa_select_topk: ascending kept chunk indices [total_k] int32."""
+    _dev(scores, "scores", torch.float32, 1)
+    _dev(chunk_off, "chunk_off", torch.int32, 1)
+    _dev(sel_off, "sel_off", torch.int32, 1)
+    if sel_idx is None:
+        sel_idx = torch.empty(shape.total_k, dtype=torch.int32, device=scores.device)
+    _dev(sel_idx, "sel_idx", torch.int32, 1)
+    _check(library().lsa_select_topk(ctypes.byref(shape.c()), _ptr(scores), _ptr(chunk_off),
+                                     _ptr(sel_off), _ptr(sel_idx), _stream(stream)),
+           "lsa_select_topk")
+    return sel_idx
+
+
+def gather_chunks(shape: ProblemShape, k_store, v_store, tok_off, sel_idx, sel_off,
+                  k_pool=None, v_pool=None, stream=None):
+    """lsa_gather_chunks: (k_pool [total_k, C, dqk], v_pool or None)."""
+    _dev(k_store, "k_store", shape.dtype, 2)
+    _dev(tok_off, "tok_off", torch.int64, 1)
+    _dev(sel_idx, "sel_idx", torch.int32, 1)
+    _dev(sel_off, "sel_off", torch.int32, 1)
+    C = shape.chunk_size
+    if k_pool is None:
+        k_pool = torch.empty((shape.total_k, C, shape.head_dim_qk), dtype=shape.dtype,
+                             device=k_store.device)
+    _dev(k_pool, "k_pool", shape.dtype)
+    if shape.v_aliases_k:
+        if v_store is not None or v_pool is not None:
+            raise ValueError("v_store / v_pool must be None when V aliases K")
+    else:
+        _dev(v_store, "v_store", shape.dtype, 2)
+        if v_pool is None:
+            v_pool = torch.empty((shape.total_k, C, shape.head_dim_v), dtype=shape.dtype,
+                                 device=k_store.device)
+        _dev(v_pool, "v_pool", shape.dtype)
+    _check(library().lsa_gather_chunks(ctypes.byref(shape.c()), _ptr(k_store), _ptr(v_store),
+                                       _ptr(tok_off), _ptr(sel_idx), _ptr(sel_off),
+                                       _ptr(k_pool), _ptr(v_pool), _stream(stream)),
+           "lsa_gather_chunks")
+    return k_pool, v_pool
+
+
+def sparse_decode_attn(shape: ProblemShape, q, k_base, v_base, tok_off, sel_idx, sel_off,
+                       kv_mode: int = KV_STORE, out=None, lse=None, workspace=None,
+                       stream=None):
+    """lsa_sparse_decode_attn: (out [B, H, dv] fp32, lse [B, H] fp32)."""
+    _dev(q, "q", shape.dtype, 3)
+    _dev(k_base, "k_base", shape.dtype)
+    if shape.v_aliases_k:
+        if v_base is not None:
+            raise ValueError("v_base must be None when V aliases K")
+    else:
+        _dev(v_base, "v_base", shape.dtype)
+    _dev(tok_off, "tok_off", torch.int64, 1)
+    _dev(sel_idx, "sel_idx", torch.int32, 1)
+    _dev(sel_off, "sel_off", torch.int32, 1)
+    dev = q.device
+    if out is None:
+        out = torch.empty((shape.batch, shape.num_q_heads, shape.head_dim_v),
+                          dtype=torch.float32, device=dev)
+    if lse is None:
+        lse = torch.empty((shape.batch, shape.num_q_heads), dtype=torch.float32, device=dev)
+    _dev(out, "out", torch.float32)
+    _dev(lse, "lse", torch.float32)
+    if workspace is None:
+        workspace = allocate_workspace(shape, dev)
+    _dev(workspace, "workspace", torch.uint8, 1)
+    _check(library().lsa_sparse_decode_attn(
+        ctypes.byref(shape.c()), int(kv_mode), _ptr(q), _ptr(k_base), _ptr(v_base),
+        _ptr(tok_off), _ptr(sel_idx), _ptr(sel_off), _ptr(out), _ptr(lse), _ptr(workspace),
+        workspace.numel(), _stream(stream)), "lsa_sparse_decode_attn")
+    return out, lse
+
+
+def _event_ptr(ev):
+    if ev is None:
+        return None
+    if not ev.cuda_event:  # torch creates the HIP event lazily on first record
+        ev.record()
+    return ctypes.c_void_p(ev.cuda_event)
+
+
+def decode_step(shape: ProblemShape, *, q_idx, emb, chunk_off, scores, sel_off, sel_idx, q,
+                k_store, v_store, tok_off, out, lse, workspace, reindex: bool = True,
+                materialize_pool: bool = False, k_pool=None, v_pool=None,
+                ev_attn_begin=None, ev_attn_end=None, stream=None) -> None:
+    """lsa_decode_step: one whole decode step (score -> select -> [gather] ->
+    attention -> merge) enqueued by one call; outputs written in place."""
+    for name, t, dt in [("q", q, shape.dtype), ("k_store", k_store, shape.dtype),
+                        ("tok_off", tok_off, torch.int64), ("sel_off", sel_off, torch.int32),
+                        ("sel_idx", sel_idx, torch.int32), ("out", out, torch.float32),
+                        ("workspace", workspace, torch.uint8)]:
+        _dev(t, name, dt)
+    if lse is not None:
+        _dev(lse, "lse", torch.float32)
+    if reindex:
+        for name, t, dt in [("q_idx", q_idx, shape.dtype), ("emb", emb, shape.dtype),
+                            ("chunk_off", chunk_off, torch.int32),
+                            ("scores", scores, torch.float32)]:
+            _dev(t, name, dt)
+    args = StepArgs(
+        _ptr(q_idx) if reindex else None, _ptr(emb) if reindex else None,
+        _ptr(chunk_off) if reindex else None, _ptr(scores) if reindex else None,
+        _ptr(sel_off), _ptr(sel_idx), _ptr(q), _ptr(k_store), _ptr(v_store), _ptr(tok_off),
+        _ptr(k_pool), _ptr(v_pool), _ptr(out), _ptr(lse), int(bool(reindex)),
+        int(bool(materialize_pool)), _event_ptr(ev_attn_begin), _event_ptr(ev_attn_end))
+    _check(library().lsa_decode_step(ctypes.byref(shape.c()), ctypes.byref(args),
+                                     _ptr(workspace), workspace.numel(), _stream(stream)),
+           "lsa_decode_step")
+
+
+def bench_copy(dst: torch.Tensor, src: torch.Tensor, nbytes: int, stream=None) -> None:
+    _check(library().lsa_bench_copy(_ptr(dst), _ptr(src), nbytes, _stream(stream)),
+           "lsa_bench_copy")
+
+
+def bench_flush(buf: torch.Tensor, stream=None) -> None:
+    _check(library().lsa_bench_flush(_ptr(buf), buf.numel() * buf.element_size(),
+                                     _stream(stream)), "lsa_bench_flush")

@@ -1,0 +1,168 @@
+"""Host-side checks of the C ABI (include/lsa.h) that need no GPU: the library
+loads and exports every declared entry point, the integer helpers agree with
+the oracle's independent implementation, workspace sizing is monotone, and
+every invalid call is rejected with its documented status before anything is
+enqueued (the dummy pointers below are never dereferenced)."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+from learned_kv_chunk_amd import lsa
+from oracle import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lsa.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(lsa.LIB_PATH),
+                                reason="liblsa.so not built (run __graft_entry__.build())")
+
+
+def declared_entry_points():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(lsa_[a-z_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_entry_points()
+    assert len(names) >= 11, names
+    lib = ctypes.CDLL(lsa.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in lsa.h but not exported"
+    assert set(names) == set(lsa._SIGNATURES), "binding and header disagree"
+
+
+def test_status_strings_and_version():
+    assert lsa.library().lsa_abi_version() == 1
+    for code, name in [(0, "LSA_OK"), (1, "LSA_ERR_INVALID_ARGUMENT"), (2, "LSA_ERR_UNSUPPORTED"),
+                       (3, "LSA_ERR_WORKSPACE_TOO_SMALL"), (4, "LSA_ERR_HIP")]:
+        assert lsa.status_string(code) == name
+    assert lsa.status_string(99) == "LSA_ERR_UNKNOWN"
+
+
+def test_keep_count_agrees_with_oracle():
+    for n in list(range(0, 300)) + [2048, 4096, 8192, 65536]:
+        for num, den in [(135, 1000), (1, 8), (10, 100), (8, 100), (1, 1), (3, 2)]:
+            for up in (False, True):
+                assert lsa.keep_count(n, num, den, up) == oracle.keep_count(n, num, den, up)
+    assert lsa.keep_count(2048, 135, 1000, False) == 276
+    assert lsa.keep_count(5, 0, 1, False) == 0
+
+
+def shape(**kw):
+    base = dict(batch=16, chunk_size=64, index_dim=128, num_q_heads=16, head_dim_qk=128,
+                head_dim_v=128, v_aliases_k=False, dtype=torch.bfloat16,
+                softmax_scale=128 ** -0.5, max_chunks=2048, max_k=276, total_chunks=16 * 2048,
+                total_k=16 * 276)
+    base.update(kw)
+    return lsa.ProblemShape(**base)
+
+
+def test_workspace_sizes_positive_and_monotone():
+    ws = lsa.workspace_bytes
+    assert ws(shape()) > 0
+    assert ws(shape(batch=1, total_chunks=2048, total_k=276)) <= ws(shape())
+    assert ws(shape(num_q_heads=8)) <= ws(shape())
+    assert ws(shape(head_dim_qk=64, head_dim_v=64)) <= ws(shape())
+    prev = 0
+    for k in [1, 8, 64, 276, 1000, 2048]:
+        cur = ws(shape(max_k=k, total_k=16 * k))
+        assert cur >= prev
+        prev = cur
+    # the five workload shapes are all supported
+    assert ws(shape(batch=1, chunk_size=64, index_dim=64, num_q_heads=8, head_dim_qk=64,
+                    head_dim_v=64, dtype=torch.float32, max_chunks=64, max_k=8, total_chunks=64,
+                    total_k=8)) > 0
+    assert ws(shape(batch=4, num_q_heads=32, max_chunks=8192, max_k=819, total_chunks=4 * 8192,
+                    total_k=4 * 819)) > 0
+    # invalid shapes report 0
+    assert ws(shape(batch=0)) == 0
+    assert ws(shape(total_k=10 ** 9)) == 0
+
+
+DUMMY = ctypes.c_void_p(0x100000)  # aligned, never dereferenced
+
+
+def _score(s, q=DUMMY, e=DUMMY, off=DUMMY, out=DUMMY):
+    return lsa.library().lsa_score(ctypes.byref(s.c()), q, e, off, out, None)
+
+
+def _select(s, sc=DUMMY, off=DUMMY, soff=DUMMY, idx=DUMMY):
+    return lsa.library().lsa_select_topk(ctypes.byref(s.c()), sc, off, soff, idx, None)
+
+
+def _attn(s, ws_bytes=None, kv_mode=0, v=DUMMY, ws=DUMMY, q=DUMMY, lse=DUMMY):
+    if ws_bytes is None:
+        ws_bytes = max(lsa.workspace_bytes(s), 1)
+    return lsa.library().lsa_sparse_decode_attn(ctypes.byref(s.c()), kv_mode, q, DUMMY, v, DUMMY,
+                                                DUMMY, DUMMY, DUMMY, lse, ws, ws_bytes, None)
+
+
+def _gather(s, v_store=DUMMY, v_pool=DUMMY):
+    return lsa.library().lsa_gather_chunks(ctypes.byref(s.c()), DUMMY, v_store, DUMMY, DUMMY,
+                                           DUMMY, DUMMY, v_pool, None)
+
+
+@pytest.mark.parametrize("bad", [
+    dict(batch=0), dict(chunk_size=0), dict(chunk_size=2048), dict(max_chunks=0),
+    dict(max_k=0), dict(max_k=3000), dict(total_chunks=15), dict(total_chunks=16 * 2048 + 1),
+    dict(total_k=15), dict(total_k=16 * 276 + 1), dict(attn_tiles_per_block=-1),
+])
+def test_invalid_shapes_rejected_everywhere(bad):
+    s = shape(**bad)
+    assert _score(s) == lsa.LSA_ERR_INVALID_ARGUMENT
+    assert _select(s) == lsa.LSA_ERR_INVALID_ARGUMENT
+    assert _attn(s) == lsa.LSA_ERR_INVALID_ARGUMENT
+    assert _gather(s) == lsa.LSA_ERR_INVALID_ARGUMENT
+
+
+def test_null_and_misaligned_pointers_rejected():
+    s = shape()
+    assert _score(s, q=None) == lsa.LSA_ERR_INVALID_ARGUMENT
+    assert _score(s, out=None) == lsa.LSA_ERR_INVALID_ARGUMENT
+    assert _score(s, e=ctypes.c_void_p(0x100008)) == lsa.LSA_ERR_INVALID_ARGUMENT
+    assert _select(s, idx=None) == lsa.LSA_ERR_INVALID_ARGUMENT
+    assert _select(s, sc=ctypes.c_void_p(0x100002)) == lsa.LSA_ERR_INVALID_ARGUMENT
+    assert _attn(s, q=None) == lsa.LSA_ERR_INVALID_ARGUMENT
+    assert _attn(s, ws=ctypes.c_void_p(0x100010)) == lsa.LSA_ERR_INVALID_ARGUMENT  # not 256-aligned
+    assert _attn(s, v=None) == lsa.LSA_ERR_INVALID_ARGUMENT        # separate V required
+    assert _attn(s, kv_mode=7) == lsa.LSA_ERR_INVALID_ARGUMENT
+    assert _gather(s, v_store=None) == lsa.LSA_ERR_INVALID_ARGUMENT
+    assert lsa.library().lsa_score(None, DUMMY, DUMMY, DUMMY, DUMMY, None) == \
+        lsa.LSA_ERR_INVALID_ARGUMENT
+    assert lsa.library().lsa_decode_step(None, None, DUMMY, 1, None) == lsa.LSA_ERR_INVALID_ARGUMENT
+    assert lsa.library().lsa_bench_copy(DUMMY, DUMMY, 17, None) == lsa.LSA_ERR_INVALID_ARGUMENT
+    assert lsa.library().lsa_bench_flush(None, 16, None) == lsa.LSA_ERR_INVALID_ARGUMENT
+
+
+def test_alias_requires_null_value_pointers():
+    s = shape(v_aliases_k=True, head_dim_qk=576, head_dim_v=512, num_q_heads=64)
+    assert _gather(s) == lsa.LSA_ERR_INVALID_ARGUMENT           # V pointers must be NULL
+    assert _attn(s, v=DUMMY) in (lsa.LSA_ERR_INVALID_ARGUMENT, lsa.LSA_ERR_UNSUPPORTED)
+
+
+def test_unsupported_shapes():
+    assert _score(shape(index_dim=12)) == lsa.LSA_ERR_UNSUPPORTED       # 24 bytes per row
+    assert _score(shape(index_dim=2048)) == lsa.LSA_ERR_UNSUPPORTED
+    assert _select(shape(max_chunks=70000, total_chunks=16 * 70000)) == lsa.LSA_ERR_UNSUPPORTED
+    assert _attn(shape(num_q_heads=100)) == lsa.LSA_ERR_UNSUPPORTED
+    assert _attn(shape(head_dim_qk=96, head_dim_v=80, num_q_heads=32)) == lsa.LSA_ERR_UNSUPPORTED
+    assert _attn(shape(head_dim_qk=12)) == lsa.LSA_ERR_UNSUPPORTED       # 24-byte rows
+    assert lsa.workspace_bytes(shape(num_q_heads=100)) == 0
+
+
+def test_workspace_too_small():
+    s = shape()
+    need = lsa.workspace_bytes(s)
+    assert _attn(s, ws_bytes=need - 1) == lsa.LSA_ERR_WORKSPACE_TOO_SMALL
+
+
+def test_python_layer_rejects_host_tensors():
+    s = shape()
+    with pytest.raises(ValueError):
+        lsa.score(s, torch.zeros(16, 128, dtype=torch.bfloat16),
+                  torch.zeros(16 * 2048, 128, dtype=torch.bfloat16),
+                  torch.zeros(17, dtype=torch.int32))

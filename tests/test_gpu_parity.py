@@ -1,0 +1,268 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle on reduced
+workloads: the same structure, dtypes and head shapes as the five benchmark
+workloads, at lengths the oracle finishes in seconds, spanning many tiles and
+ragged partial last chunks.  Tolerances are those of tests/parity.py."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from learned_kv_chunk_amd import device as dev
+from learned_kv_chunk_amd import lsa
+from learned_kv_chunk_amd import workloads as wl
+from oracle import oracle
+from tests import parity as P
+
+pytestmark = pytest.mark.gpu
+
+SMALL = ["cfg1", "cfg2", "cfg3", "cfg5"]
+
+
+def small_cfg(name):
+    return wl.CONFIGS["cfg1"] if name == "cfg1" else wl.small_variant(name)
+
+
+_cache = {}
+
+
+def small_workload(name):
+    if name not in _cache:
+        w = wl.make_workload(small_cfg(name))
+        _cache[name] = (w, dev.upload(w, "cuda", with_pool=True))
+    return _cache[name]
+
+
+@pytest.mark.parametrize("name", SMALL)
+def test_phases_match_oracle(name):
+    w, d = small_workload(name)
+    s_gpu, sel, out, lse = P.run_phases(d, 0)
+    s_ref = oracle.score(w.q_idx, w.emb, w.chunk_off)
+    P.check_scores(w, s_gpu, s_ref)
+    P.check_selection(w, s_gpu, sel, s_ref)
+    P.check_needles(w, sel)
+    o_ref, l_ref = P.oracle_attention_on(w, 0, sel)
+    print(name, P.check_attention(w.cfg.dtype, out, lse, o_ref, l_ref))
+
+
+@pytest.mark.parametrize("name", SMALL)
+def test_fused_step_equals_phases_and_reuses_selection(name):
+    w, d = small_workload(name)
+    _, sel_a, out_a, lse_a = P.run_phases(d, 0)
+    d.sel_idx.fill_(-1)
+    d.step(0, reindex=True, materialize_pool=w.cfg.materialize_pool)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(dev.to_host(d.sel_idx), sel_a)
+    np.testing.assert_array_equal(dev.to_host(d.out), out_a)
+    np.testing.assert_array_equal(dev.to_host(d.lse), lse_a)
+    # next step: no re-index, fresh queries, same kept set
+    d.scores.fill_(float("nan"))
+    d.step(1, reindex=False, materialize_pool=w.cfg.materialize_pool)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(dev.to_host(d.sel_idx), sel_a)
+    o_ref, l_ref = P.oracle_attention_on(w, 1, sel_a)
+    P.check_attention(w.cfg.dtype, dev.to_host(d.out), dev.to_host(d.lse), o_ref, l_ref)
+
+
+@pytest.mark.parametrize("name", ["cfg2", "cfg3", "cfg1"])
+def test_gather_is_bit_exact_and_pool_attention_matches_store(name):
+    w, d = small_workload(name)
+    _, sel, out_store, lse_store = P.run_phases(d, 0)
+    s = d.shape
+    lsa.gather_chunks(s, d.K, d.V, d.tok_off, d.sel_idx, d.sel_off, d.k_pool, d.v_pool)
+    torch.cuda.synchronize()
+    C = w.cfg.chunk_size
+    np.testing.assert_array_equal(dev.to_host(d.k_pool),
+                                  oracle.gather(w.K, C, w.tok_off, sel, w.sel_off))
+    np.testing.assert_array_equal(dev.to_host(d.v_pool),
+                                  oracle.gather(w.V, C, w.tok_off, sel, w.sel_off))
+    out, lse = lsa.sparse_decode_attn(s, d.queries(0), d.k_pool, d.v_pool, d.tok_off, d.sel_idx,
+                                      d.sel_off, lsa.KV_POOL, workspace=d.workspace)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(dev.to_host(out), out_store)
+    np.testing.assert_array_equal(dev.to_host(lse), lse_store)
+
+
+def test_reindex_schedule_over_several_steps():
+    cfg = wl.small_variant("cfg3", steps=5, reindex_every=2)
+    w = wl.make_workload(cfg)
+    d = dev.upload(w, "cuda")
+    Qs = [w.queries(t) for t in range(cfg.steps)]
+    ref = oracle.decode(w.q_idx, w.emb, w.chunk_off, w.sel_off, Qs, w.K, w.V, w.tok_off,
+                        cfg.chunk_size, cfg.softmax_scale, cfg.reindex_every,
+                        nthreads=oracle.max_threads())
+    for t in range(cfg.steps):
+        d.step(t, reindex=(t % cfg.reindex_every == 0), materialize_pool=True)
+        torch.cuda.synchronize()
+        sel = dev.to_host(d.sel_idx)
+        np.testing.assert_array_equal(sel, ref[t][0])   # no near-ties in this workload
+        P.check_attention("bf16", dev.to_host(d.out), dev.to_host(d.lse), ref[t][1], ref[t][2])
+
+
+def test_keep_all_equals_dense_attention():
+    cfg = wl.small_variant("cfg2", keep_num=1, keep_den=1, n_needles=0)
+    w = wl.make_workload(cfg)
+    d = dev.upload(w, "cuda")
+    _, sel, out, lse = P.run_phases(d, 0)
+    all_idx, all_off = oracle.all_chunks(w.tok_off, cfg.chunk_size)
+    np.testing.assert_array_equal(sel, all_idx)
+    o_ref, l_ref = oracle.attention(w.queries(0), w.K, w.V, w.tok_off, all_idx, all_off,
+                                    cfg.chunk_size, cfg.softmax_scale,
+                                    nthreads=oracle.max_threads())
+    P.check_attention("bf16", out, lse, o_ref, l_ref)
+
+
+def test_split_count_changes_results_only_by_rounding():
+    # Each split rounds its softmax weights to bf16 relative to its own running
+    # maximum, so different splits differ by that rounding (~2^-9 relative per
+    # weight), never by more; every split must also meet the oracle bar.
+    w, d = small_workload("cfg2")
+    _, sel, out_a, lse_a = P.run_phases(d, 0)
+    o_ref, l_ref = P.oracle_attention_on(w, 0, sel)
+    for per in [4, 8, 36, 256]:
+        s = dev.problem_shape(w, attn_tiles_per_block=per)
+        out, lse = lsa.sparse_decode_attn(s, d.queries(0), d.K, d.V, d.tok_off, d.sel_idx,
+                                          d.sel_off)
+        torch.cuda.synchronize()
+        o, l = dev.to_host(out), dev.to_host(lse)
+        P.check_attention("bf16", o, l, o_ref, l_ref)
+        rel = np.linalg.norm(o - out_a, axis=-1) / np.linalg.norm(out_a, axis=-1)
+        assert rel.max() <= 5e-3, (per, rel.max())
+        assert np.abs(l - lse_a).max() <= 1e-5
+
+
+def test_reruns_are_bit_identical():
+    w, d = small_workload("cfg5")
+    a = P.run_phases(d, 0)
+    b = P.run_phases(d, 0)
+    for x, y in zip(a, b):
+        np.testing.assert_array_equal(x, y)
+
+
+def _single_stream(w: wl.Workload, b: int) -> wl.Workload:
+    r0, r1 = int(w.tok_off[b]), int(w.tok_off[b + 1])
+    c0, c1 = int(w.chunk_off[b]), int(w.chunk_off[b + 1])
+    cfg = w.cfg.replace(batch=1, lengths=(r1 - r0,))
+    sub = wl.Workload(cfg=cfg, lengths=w.lengths[b:b + 1], tok_off=np.array([0, r1 - r0]),
+                      chunk_off=np.array([0, c1 - c0], np.int32), keep=w.keep[b:b + 1],
+                      sel_off=np.array([0, w.keep[b]], np.int32), q_idx=w.q_idx[b:b + 1],
+                      emb=w.emb[c0:c1], needles=[w.needles[b]], K=w.K[r0:r1],
+                      V=None if w.V is None else w.V[r0:r1])
+    sub._q_cache = {0: np.ascontiguousarray(w.queries(0)[b:b + 1])}
+    return sub
+
+
+def test_a_stream_alone_equals_the_same_stream_in_a_batch():
+    w, _ = small_workload("cfg5")
+    full = dev.upload(w, "cuda", attn_tiles_per_block=8)
+    _, sel, out, lse = P.run_phases(full, 0)
+    for b in [0, w.B - 1]:
+        one = dev.upload(_single_stream(w, b), "cuda", attn_tiles_per_block=8)
+        _, sel1, out1, lse1 = P.run_phases(one, 0)
+        np.testing.assert_array_equal(sel1, sel[w.sel_off[b]:w.sel_off[b + 1]])
+        np.testing.assert_array_equal(out1[0], out[b])
+        np.testing.assert_array_equal(lse1[0], lse[b])
+
+
+# ----------------------------------------------------------------------------- select edge cases
+def _select_case(scores_per_stream, keep):
+    chunk_off = np.concatenate([[0], np.cumsum([len(s) for s in scores_per_stream])]).astype(np.int32)
+    sel_off = np.concatenate([[0], np.cumsum(keep)]).astype(np.int32)
+    scores = np.concatenate(scores_per_stream).astype(np.float32)
+    shape = lsa.ProblemShape(batch=len(keep), chunk_size=64, index_dim=128, num_q_heads=16,
+                             head_dim_qk=128, head_dim_v=128, v_aliases_k=False,
+                             dtype=torch.bfloat16, softmax_scale=0.1,
+                             max_chunks=int(np.diff(chunk_off).max()), max_k=int(max(keep)),
+                             total_chunks=int(chunk_off[-1]), total_k=int(sel_off[-1]))
+    t = lambda a: torch.from_numpy(a).cuda()
+    sel = lsa.select_topk(shape, t(scores), t(chunk_off), t(sel_off))
+    torch.cuda.synchronize()
+    got = dev.to_host(sel)
+    np.testing.assert_array_equal(got, oracle.select(scores.astype(np.float64), chunk_off, sel_off))
+    return got
+
+
+def test_select_ties_nan_signed_zero_and_extremes():
+    rng = np.random.default_rng(0)
+    golden = np.array([0.5, 0.9, 0.5, 0.9, -0.0, 0.0, 0.1, np.nan], np.float32)
+    for k in range(1, 9):
+        _select_case([golden], [k])
+    streams = [np.full(300, 0.25), rng.choice([-1.0, 0.0, -0.0, 2.0, np.nan], 1000),
+               np.array([3.0]), rng.standard_normal(4097), np.array([np.inf, -np.inf, 1.0, np.nan]),
+               rng.integers(0, 3, 17).astype(np.float64)]
+    keeps = [7, 500, 1, 1000, 3, 17]
+    _select_case(streams, keeps)
+    for k in [1, 2, 999, 2048, 4095, 4096]:
+        _select_case([rng.standard_normal(4096)], [k])
+
+
+def test_select_large_streams():
+    rng = np.random.default_rng(1)
+    s = [rng.standard_normal(65536).astype(np.float32) * 1e-3,
+         np.round(rng.standard_normal(20000), 2), rng.standard_normal(8192)]
+    _select_case(s, [6000, 19999, 655])
+
+
+# ----------------------------------------------------------------------------- shape coverage
+@pytest.mark.parametrize("variant", [
+    dict(num_q_heads=8),                                   # padded head group
+    dict(num_q_heads=24),                                  # two head groups, partially padded
+    dict(num_q_heads=32, head_dim_qk=64, head_dim_v=64),   # d = 64
+    dict(num_q_heads=12, head_dim_qk=96, head_dim_v=80),   # portable kernel, bf16
+    dict(chunk_size=48),                                   # chunk not a multiple of the tile
+    dict(chunk_size=128, index_dim=256),
+    dict(chunk_size=16, index_dim=64),
+])
+def test_attention_shape_variants(variant):
+    cfg = wl.small_variant("cfg2", **variant)
+    w = wl.make_workload(cfg)
+    d = dev.upload(w, "cuda")
+    s_gpu, sel, out, lse = P.run_phases(d, 0)
+    s_ref = oracle.score(w.q_idx, w.emb, w.chunk_off)
+    P.check_scores(w, s_gpu, s_ref)
+    P.check_selection(w, s_gpu, sel, s_ref)
+    o_ref, l_ref = P.oracle_attention_on(w, 0, sel)
+    print(variant, P.check_attention("bf16", out, lse, o_ref, l_ref))
+
+
+def test_fp32_portable_attention_ragged():
+    cfg = wl.small_variant("cfg1", lengths=(4096 + 17, 300, 64 * 40), keep_num=1, keep_den=4)
+    w = wl.make_workload(cfg)
+    d = dev.upload(w, "cuda")
+    s_gpu, sel, out, lse = P.run_phases(d, 0)
+    s_ref = oracle.score(w.q_idx, w.emb, w.chunk_off)
+    P.check_scores(w, s_gpu, s_ref)
+    P.check_selection(w, s_gpu, sel, s_ref)
+    o_ref, l_ref = P.oracle_attention_on(w, 0, sel)
+    P.check_attention("f32", out, lse, o_ref, l_ref)
+
+
+@pytest.mark.parametrize("std", [1.0, 3.0])
+def test_stress_large_logits(std):
+    # unscaled keys and queries: logits of O(10)-O(100), far from uniform weights
+    cfg = wl.small_variant("cfg2", kv_std=std, q_std=std)
+    w = wl.make_workload(cfg)
+    d = dev.upload(w, "cuda")
+    _, sel, out, lse = P.run_phases(d, 0)
+    o_ref, l_ref = P.oracle_attention_on(w, 0, sel)
+    rel = np.linalg.norm(out - o_ref, axis=-1) / np.linalg.norm(o_ref, axis=-1)
+    assert rel.max() <= 1e-2, rel.max()
+    assert (np.abs(lse - l_ref) / np.abs(l_ref)).max() <= 1e-4
+
+
+def test_hot_token_dominates():
+    cfg = wl.small_variant("cfg2", n_needles=8)
+    w = wl.make_workload(cfg)
+    # plant, in stream 1, a key row equal to 40x head 3's query: one token takes ~all weight
+    sel_full = oracle.select(oracle.score(w.q_idx, w.emb, w.chunk_off), w.chunk_off, w.sel_off)
+    b, h = 1, 3
+    n = int(sel_full[w.sel_off[b] + 2])
+    row = int(w.tok_off[b]) + n * cfg.chunk_size + 5
+    q = wl.as_f32(w.queries(0))[b, h]
+    w.K[row] = wl.to_bf16_bits(40.0 * q / np.linalg.norm(q) * math.sqrt(cfg.head_dim_qk))
+    d = dev.upload(w, "cuda")
+    _, sel, out, lse = P.run_phases(d, 0)
+    o_ref, l_ref = P.oracle_attention_on(w, 0, sel)
+    P.check_attention("bf16", out, lse, o_ref, l_ref)
+    v = wl.as_f32(w.V[row])
+    assert np.abs(out[b, h] - v).max() < 0.05 * np.abs(v).max()
