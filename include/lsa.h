@@ -173,8 +173,9 @@ lsa_status lsa_gather_chunks(const lsa_shape* shape, const void* k_store_dev,
  * and slot s is read (sel_idx is still needed for the valid-token count of
  * partial chunks).  v_base must be NULL when v_aliases_k.
  * out_dev: [B][H][head_dim_v] fp32; lse_dev: [B][H] fp32 (may be NULL).
- * workspace_dev: >= lsa_workspace_bytes(shape) bytes, 256-byte aligned; its
- * contents on entry do not matter.
+ * workspace_dev: >= lsa_workspace_bytes(shape) bytes, 256-byte aligned; it
+ * holds the split partial results, its contents on entry do not matter, and
+ * calls that share a workspace must not run concurrently.
  * Supported: bf16 with num_q_heads <= 64 and head_dim_qk == head_dim_v in
  * {64, 128} (multi-query); bf16 with head_dim_qk 576, head_dim_v 512,
  * v_aliases_k = 1 and num_q_heads a multiple of 16 up to 128 (absorbed

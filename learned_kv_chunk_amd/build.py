@@ -23,10 +23,7 @@ def sources() -> list[str]:
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
 
-def build(verbose: bool = False) -> str:
-    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-    tmp = LIB + f".tmp{os.getpid()}"
-    cmd = [hipcc, *HIPCC_FLAGS, "-o", tmp, *sources()]
+def _run(cmd: list[str], verbose: bool) -> str:
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -34,8 +31,31 @@ def build(verbose: bool = False) -> str:
     err = "\n".join(l for l in res.stderr.splitlines() if noise not in l)
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
-    if verbose and err.strip():
-        print(err, file=sys.stderr)
+    return err
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every csrc/*.hip to an object in parallel, then link liblsa.so."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+    objdir = os.path.join(HERE, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    compile_flags = [f for f in HIPCC_FLAGS if f != "-shared"]
+    jobs = []
+    for src in sources():
+        obj = os.path.join(objdir, os.path.basename(src) + ".o")
+        jobs.append([hipcc, *compile_flags, "-c", "-o", obj, src])
+    workers = max(1, min(len(jobs), len(os.sched_getaffinity(0))))
+    with ThreadPoolExecutor(workers) as ex:
+        errs = list(ex.map(lambda c: _run(c, verbose), jobs))
+    tmp = LIB + f".tmp{os.getpid()}"
+    errs.append(_run([hipcc, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp,
+                      *[j[-2] for j in jobs]], verbose))
+    if verbose:
+        for e in errs:
+            if e.strip():
+                print(e, file=sys.stderr)
     os.replace(tmp, LIB)
     return LIB
 

@@ -18,10 +18,12 @@
 // which are strided in memory.  Each wave software-pipelines its tiles: the
 // next tile's loads are in flight while the current one is computed.
 // A workgroup's four waves take interleaved tiles of one run, then merge their
-// (max, sum, output) states through LDS into one partial result.
+// (max, sum, output) states through LDS into one partial result, which the
+// merge kernel (attn_common.hip) combines with the stream's other partials.
 #include <math.h>
 
 #include "lsa_internal.hpp"
+#include "wave.hpp"
 
 namespace lsa {
 namespace {
@@ -29,8 +31,16 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
-constexpr int kMaxSlots = 264;  // kept chunks one workgroup's tiles can span
+// LDS row pitch of a staged V tile: D bf16 plus 32 bytes, so that the eight
+// rows one transposed read touches per half-wave start in distinct 8-bank
+// windows.
+template <int D>
+constexpr int v_row_bytes() { return 2 * D + 32; }
+
+constexpr int kMaxSlots = 256;  // kept-chunk indices of a run staged in LDS
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
@@ -78,7 +88,7 @@ __device__ __forceinline__ void compute_tile(const TileRegs<D>& r, int32_t nvali
                                              unsigned char* __restrict__ sv, float scale_log2,
                                              int lane) {
   constexpr int PR = D / 8;
-  constexpr int ROWB = 2 * D + 16;
+  constexpr int ROWB = v_row_bytes<D>();
   const int r16 = lane & 15, g = lane >> 4;
 
   // S^T = K Q^T for both 16-token blocks and every head group
@@ -116,8 +126,7 @@ __device__ __forceinline__ void compute_tile(const TileRegs<D>& r, int32_t nvali
     float mt = x[0];
 #pragma unroll
     for (int j = 1; j < 8; ++j) mt = fmaxf(mt, x[j]);
-    mt = fmaxf(mt, __shfl_xor(mt, 16, kWave));
-    mt = fmaxf(mt, __shfl_xor(mt, 32, kWave));
+    mt = xor32_max(xor16_max(mt));
     const float m_new = fmaxf(m[hg], mt);
     const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
     const float alpha = __builtin_amdgcn_exp2f(m[hg] - m_use);
@@ -134,22 +143,25 @@ __device__ __forceinline__ void compute_tile(const TileRegs<D>& r, int32_t nvali
     for (int cg = 0; cg < D / 16; ++cg) o[hg][cg] *= alpha;
   }
 
-  // O^T += V^T P^T: the V^T operand of a lane is column cg*16 + lane%16 at
-  // the eight tokens that pair with its weights.
+  // O^T += V^T P^T.  The V^T operand of a lane is column cg*16 + lane%16 at
+  // the eight tokens that pair with its weights (4g..4g+3, 16+4g..16+4g+3).
+  // ds_read_b64_tr_b16 gives lane i of a 16-lane group element (i & 3) of the
+  // 8-byte chunk addressed by lane 4j + (i >> 2) of the group, as its element
+  // j; so lane s of group g addresses row 4g + (s >> 2) (+16), columns
+  // cg*16 + 4*(s & 3) .. +3.
+  const unsigned char* vrow = sv + (4 * g + (r16 >> 2)) * ROWB + 8 * (r16 & 3);
 #pragma unroll
   for (int cg = 0; cg < D / 16; ++cg) {
-    const unsigned char* col = sv + (cg * 16 + r16) * 2;
-    uint16_t e[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int tok = 16 * (j >> 2) + 4 * g + (j & 3);
-      e[j] = *reinterpret_cast<const uint16_t*>(col + tok * ROWB);
-    }
+    const unsigned char* p0 = vrow + cg * 32;
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_i16x4*)(p0));
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_i16x4*)(p0 + 16 * ROWB));
     u32x4 packed;
-    packed.x = e[0] | (static_cast<uint32_t>(e[1]) << 16);
-    packed.y = e[2] | (static_cast<uint32_t>(e[3]) << 16);
-    packed.z = e[4] | (static_cast<uint32_t>(e[5]) << 16);
-    packed.w = e[6] | (static_cast<uint32_t>(e[7]) << 16);
+    packed.x = static_cast<uint16_t>(lo.x) | (static_cast<uint32_t>(static_cast<uint16_t>(lo.y)) << 16);
+    packed.y = static_cast<uint16_t>(lo.z) | (static_cast<uint32_t>(static_cast<uint16_t>(lo.w)) << 16);
+    packed.z = static_cast<uint16_t>(hi.x) | (static_cast<uint32_t>(static_cast<uint16_t>(hi.y)) << 16);
+    packed.w = static_cast<uint16_t>(hi.z) | (static_cast<uint32_t>(static_cast<uint16_t>(hi.w)) << 16);
     const bf16x8 vt = as_bf16x8(packed);
 #pragma unroll
     for (int hg = 0; hg < NHG; ++hg)
@@ -157,15 +169,15 @@ __device__ __forceinline__ void compute_tile(const TileRegs<D>& r, int32_t nvali
   }
 }
 
+constexpr int cmax(int a, int b) { return a > b ? a : b; }
+
 template <int D, int NHG>
 struct MqaLds {
-  static constexpr int kRowBytes = 2 * D + 16;
+  static constexpr int kRowBytes = v_row_bytes<D>();
   static constexpr int kTileBytes = kTileTokens * kRowBytes;              // per wave
   static constexpr int kStateO = NHG * (D / 16) * kWave * 16;            // lane-major o
   static constexpr int kStateBytes = kStateO + 2 * NHG * kWave * 4;      // + m, l
-  static constexpr int kBytes = (kAttnWaves * kTileBytes > 2 * kStateBytes)
-                                    ? kAttnWaves * kTileBytes
-                                    : 2 * kStateBytes;
+  static constexpr int kBytes = cmax(kAttnWaves * kTileBytes, 2 * kStateBytes);
 };
 
 template <int D, int NHG>
@@ -208,7 +220,7 @@ template <int D, int NHG>
 __global__ __launch_bounds__(kAttnThreads, NHG == 1 ? 2 : 1) void attn_mqa_kernel(AttnArgs a) {
   using L = MqaLds<D, NHG>;
   __shared__ __attribute__((aligned(16))) unsigned char smem[L::kBytes];
-  __shared__ int32_t s_plan[2];
+  __shared__ int32_t s_plan[3];
   __shared__ int32_t s_slot[kMaxSlots];
 
   const int tid = threadIdx.x;
@@ -218,10 +230,13 @@ __global__ __launch_bounds__(kAttnThreads, NHG == 1 ? 2 : 1) void attn_mqa_kerne
 
   if (wave == 0) {
     int32_t b, local;
-    find_stream_of_wg(a.sel_off, a.B, a.tiles_per_chunk, a.per, blockIdx.x, &b, &local);
+    StreamSplit sp;
+    find_stream_of_wg(a.sel_off, a.B, a.tiles_per_chunk, a.per, a.target, blockIdx.x, &b,
+                      &local, &sp);
     if (lane == 0) {
       s_plan[0] = b;
-      s_plan[1] = local;
+      s_plan[1] = local * sp.per;                    // first tile
+      s_plan[2] = min(sp.tiles, (local + 1) * sp.per);  // end tile
     }
   }
   __syncthreads();
@@ -229,12 +244,12 @@ __global__ __launch_bounds__(kAttnThreads, NHG == 1 ? 2 : 1) void attn_mqa_kerne
   if (b < 0) return;
   const int32_t tpc = a.tiles_per_chunk, C = a.C, H = a.H;
   const int32_t sel0 = a.sel_off[b];
-  const int32_t n_tiles = (a.sel_off[b + 1] - sel0) * tpc;
-  const int32_t t_begin = s_plan[1] * a.per;
-  const int32_t t_end = min(n_tiles, t_begin + a.per);
+  const int32_t t_begin = s_plan[1];
+  const int32_t t_end = s_plan[2];
   const int32_t slot_first = t_begin / tpc;
   const int32_t nslots = (t_end - 1) / tpc - slot_first + 1;
-  for (int32_t i = tid; i < nslots; i += kAttnThreads) s_slot[i] = a.sel_idx[sel0 + slot_first + i];
+  for (int32_t i = tid; i < min(nslots, kMaxSlots); i += kAttnThreads)
+    s_slot[i] = a.sel_idx[sel0 + slot_first + i];
   const int64_t tb = a.tok_off[b];
   const int64_t len = a.tok_off[b + 1] - tb;
   const int64_t last_chunk = len > 0 ? (len - 1) / C : 0;
@@ -263,7 +278,7 @@ __global__ __launch_bounds__(kAttnThreads, NHG == 1 ? 2 : 1) void attn_mqa_kerne
     const int32_t sub = t - j * tpc;
     // a kept index outside [0, N_b) (a violated precondition) is clamped so
     // that no read leaves the stream
-    int64_t n = s_slot[j - slot_first];
+    int64_t n = (j - slot_first < kMaxSlots) ? s_slot[j - slot_first] : a.sel_idx[sel0 + j];
     n = n < 0 ? 0 : (n > last_chunk ? last_chunk : n);
     int64_t valid = len - n * C;
     if (valid > C) valid = C;
@@ -322,25 +337,24 @@ __global__ __launch_bounds__(kAttnThreads, NHG == 1 ? 2 : 1) void attn_mqa_kerne
   __syncthreads();
   if (wave == 1) store_state<D, NHG>(smem, m, l, o, lane);
   __syncthreads();
-  if (wave != 0) return;
-  merge_state<D, NHG>(smem, m, l, o, lane);
-
   const int64_t wg = blockIdx.x;
+  if (wave == 0) {
+    merge_state<D, NHG>(smem, m, l, o, lane);
 #pragma unroll
-  for (int hg = 0; hg < NHG; ++hg) {
-    float lt = l[hg];
-    lt += __shfl_xor(lt, 16, kWave);
-    lt += __shfl_xor(lt, 32, kWave);
-    const int head = hg * 16 + r16;
-    if (head >= H) continue;
-    if (g == 0) {
-      a.ws_m[wg * H + head] = m[hg];
-      a.ws_l[wg * H + head] = lt;
+    for (int hg = 0; hg < NHG; ++hg) {
+      const float lt = xor32_sum(xor16_sum(l[hg]));
+      const int head = hg * 16 + r16;
+      if (head >= H) continue;
+      if (g == 0) {
+        a.ws_m[wg * H + head] = m[hg];
+        a.ws_l[wg * H + head] = lt;
+      }
+#pragma unroll
+      for (int cg = 0; cg < D / 16; ++cg)
+        *reinterpret_cast<f32x4*>(a.ws_o + (wg * H + head) * D + cg * 16 + 4 * g) = o[hg][cg];
     }
-#pragma unroll
-    for (int cg = 0; cg < D / 16; ++cg)
-      *reinterpret_cast<f32x4*>(a.ws_o + (wg * H + head) * D + cg * 16 + 4 * g) = o[hg][cg];
   }
+
 }
 
 template <int D>

@@ -11,6 +11,7 @@
 // coalesced loads.  The wave's (m, l, o) is its workgroup's partial result.
 #include <math.h>
 
+#include "wave.hpp"
 #include "lsa_internal.hpp"
 
 namespace lsa {
@@ -30,37 +31,28 @@ __device__ __forceinline__ float load_elem<uint16_t>(const uint16_t* p, int64_t 
   return bf16_bits_to_float(p[i]);
 }
 
-__device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int off = kWave / 2; off > 0; off >>= 1) x = fmaxf(x, __shfl_xor(x, off, kWave));
-  return x;
-}
-__device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int off = kWave / 2; off > 0; off >>= 1) x += __shfl_xor(x, off, kWave);
-  return x;
-}
-
 // HM: heads held in registers (>= H); CV: output columns per lane / 64.
 template <typename T, int HM, int CV>
 __global__ __launch_bounds__(kWave) void attn_portable_kernel(AttnArgs a) {
   __shared__ float s_q[HM * kPortMaxDim];
   __shared__ float s_p[HM][kTileTokens];
-  __shared__ int32_t s_plan[2];
+  __shared__ int32_t s_plan[3];
 
   const int lane = threadIdx.x;
   {
     int32_t b, local;
-    find_stream_of_wg(a.sel_off, a.B, a.tiles_per_chunk, a.per, blockIdx.x, &b, &local);
+    StreamSplit sp;
+    find_stream_of_wg(a.sel_off, a.B, a.tiles_per_chunk, a.per, a.target, blockIdx.x, &b,
+                      &local, &sp);
     if (lane == 0) {
       s_plan[0] = b;
-      s_plan[1] = local;
+      s_plan[1] = local * sp.per;
+      s_plan[2] = min(sp.tiles, (local + 1) * sp.per);
     }
   }
   __syncthreads();
   const int32_t b = s_plan[0];
   if (b < 0) return;
-  const int32_t local = s_plan[1];
   const T* __restrict__ q = static_cast<const T*>(a.q);
   const T* __restrict__ kb = static_cast<const T*>(a.k);
   const T* __restrict__ vb = static_cast<const T*>(a.v);
@@ -70,10 +62,9 @@ __global__ __launch_bounds__(kWave) void attn_portable_kernel(AttnArgs a) {
   __syncthreads();
 
   const int32_t sel0 = a.sel_off[b];
-  const int32_t n_tiles = (a.sel_off[b + 1] - sel0) * tpc;
   const int64_t len = a.tok_off[b + 1] - a.tok_off[b];
-  const int32_t t_begin = local * a.per;
-  const int32_t t_end = min(n_tiles, t_begin + a.per);
+  const int32_t t_begin = s_plan[1];
+  const int32_t t_end = s_plan[2];
 
   float m[HM], l[HM], o[HM][CV];
 #pragma unroll

@@ -69,7 +69,7 @@ lsa_status enqueue_attention(const lsa_shape& s, int32_t kv_mode, const void* q,
                              const void* vbase, const int64_t* tok_off, const int32_t* sel_idx,
                              const int32_t* sel_off, float* out, float* lse, void* ws,
                              hipStream_t st, void* ev_begin = nullptr, void* ev_end = nullptr) {
-  const AttnPlan plan = make_attn_plan(s);
+  const AttnPlan plan = make_attn_plan(s, device_cu_count());
   const PartialLayout pl = partial_layout(s, plan);
   AttnArgs a;
   a.q = q;
@@ -93,6 +93,7 @@ lsa_status enqueue_attention(const lsa_shape& s, int32_t kv_mode, const void* q,
   a.pool = kv_mode == LSA_KV_POOL ? 1 : 0;
   a.tiles_per_chunk = plan.tiles_per_chunk;
   a.per = plan.per;
+  a.target = plan.target;
   a.scale_log2 = s.softmax_scale * 1.4426950408889634f;
   if (ev_begin && hipEventRecord(static_cast<hipEvent_t>(ev_begin), st) != hipSuccess)
     return LSA_ERR_HIP;
@@ -137,7 +138,7 @@ int32_t lsa_keep_count(int32_t n_chunks, int32_t ratio_num, int32_t ratio_den, i
 
 size_t lsa_workspace_bytes(const lsa_shape* shape) {
   if (check_attn_shape(shape) != LSA_OK) return 0;
-  return partial_layout(*shape, make_attn_plan(*shape)).total;
+  return partial_layout(*shape, make_attn_plan(*shape, device_cu_count())).total;
 }
 
 lsa_status lsa_score(const lsa_shape* shape, const void* q_idx_dev, const void* emb_dev,
@@ -254,7 +255,8 @@ lsa_status lsa_decode_step(const lsa_shape* shape, const lsa_step_args* args, vo
   const hipStream_t hs = static_cast<hipStream_t>(hip_stream);
   (void)hipGetLastError();
   if (x.reindex) {
-    if (launch_score(*shape, x.q_idx_dev, x.emb_dev, x.chunk_off_dev, x.scores_dev, hs) != hipSuccess)
+    if (launch_score(*shape, x.q_idx_dev, x.emb_dev, x.chunk_off_dev, x.scores_dev, hs) !=
+        hipSuccess)
       return LSA_ERR_HIP;
     if (launch_select(*shape, x.scores_dev, x.chunk_off_dev, x.sel_off_dev, x.sel_idx_dev, hs) !=
         hipSuccess)

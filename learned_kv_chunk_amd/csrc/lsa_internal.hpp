@@ -7,6 +7,7 @@
 #include <stdint.h>
 
 #include "../../include/lsa.h"
+#include "wave.hpp"
 
 namespace lsa {
 
@@ -17,22 +18,32 @@ constexpr int kAttnThreads = kAttnWaves * kWave;
 
 // ---------------------------------------------------------------------------
 // Split-KV work plan.  Stream b owns T_b = k_b * tiles_per_chunk tiles of 32
-// tokens; each attention workgroup owns `per` consecutive tiles of one stream,
-// so stream b has W_b = ceil(T_b / per) workgroups, numbered consecutively in
-// stream order.  Workgroup ids at or beyond sum_b W_b do nothing.  The grid is
-// the bound ceil(sum T_b / per) + B, known on the host from the shape alone.
+// tokens (T = sum_b T_b = sel_off[B] * tiles_per_chunk); each attention
+// workgroup owns a run of consecutive tiles of one stream, and the W_b
+// workgroups of stream b are numbered consecutively in stream order.
+//  * fixed split (per > 0): W_b = ceil(T_b / per), runs of `per` tiles;
+//  * proportional split (per == 0): the device's `target` workgroups (one per
+//    CU) are shared out in proportion to the streams' tiles,
+//    W_b = max(1, round(T_b * target / T)), and stream b's runs hold
+//    ceil(T_b / W_b) tiles, so every CU gets about T / target tiles.
+// Workgroup ids at or beyond sum_b W_b do nothing; the grid is a bound known
+// on the host from the shape alone.
 // ---------------------------------------------------------------------------
 struct AttnPlan {
   int32_t tiles_per_chunk;
-  int32_t per;      // tiles per workgroup (multiple of kAttnWaves)
+  int32_t per;      // tiles per workgroup, or 0 for the proportional split
+  int32_t target;   // workgroups the proportional split aims at
   int64_t grid;     // workgroups launched (upper bound of sum_b W_b)
   int64_t ws_rows;  // partial results the workspace holds (>= grid)
 };
 
-AttnPlan make_attn_plan(const lsa_shape& s);
+// `target` is the number of compute units of the device that will run it.
+AttnPlan make_attn_plan(const lsa_shape& s, int32_t target);
+// Compute units of the current device (host).
+int32_t device_cu_count();
 
-// Workspace layout for split-KV partials: m[rows][H], l[rows][H] (fp32, log2
-// domain max and sum) then o[rows][H][dv] (fp32, unnormalised), rows = ws_rows.
+// Workspace layout: split-KV partials m[rows][H], l[rows][H] (fp32, log2
+// domain max and sum) and o[rows][H][dv] (fp32, unnormalised), rows = ws_rows.
 struct PartialLayout {
   size_t m_off, l_off, o_off, total;
 };
@@ -54,7 +65,7 @@ struct AttnArgs {
   int32_t k_row;          // elements between consecutive K rows
   int32_t v_row;          // elements between consecutive V rows
   int32_t pool;           // 1: slot-indexed pool, 0: store indexed by chunk
-  int32_t tiles_per_chunk, per;
+  int32_t tiles_per_chunk, per, target;
   float scale_log2;       // softmax_scale * log2(e)
 };
 
@@ -89,58 +100,80 @@ __device__ __forceinline__ float bf16_bits_to_float(uint16_t h) {
 
 __device__ __forceinline__ int32_t ceil_div_i(int32_t a, int32_t b) { return (a + b - 1) / b; }
 
-// Number of attention workgroups of stream b.
-__device__ __forceinline__ int32_t stream_wgs(const int32_t* sel_off, int32_t b, int32_t tpc,
-                                              int32_t per) {
+// Split geometry of one stream (device): tiles T_b, workgroups W_b and tiles
+// per workgroup, given the plan and the total tile count T.
+struct StreamSplit {
+  int32_t tiles, wgs, per;
+};
+__device__ __forceinline__ StreamSplit stream_split(const int32_t* sel_off, int32_t b,
+                                                    int32_t tpc, int32_t per, int32_t target,
+                                                    int32_t total_tiles) {
+  StreamSplit r;
   int32_t k = sel_off[b + 1] - sel_off[b];
   if (k < 0) k = 0;
-  return ceil_div_i(k * tpc, per);
+  r.tiles = k * tpc;
+  if (per > 0) {
+    r.per = per;
+    r.wgs = ceil_div_i(r.tiles, per);
+  } else {
+    const int64_t num = 2 * static_cast<int64_t>(r.tiles) * target + total_tiles;
+    int32_t w = total_tiles > 0 ? static_cast<int32_t>(num / (2 * static_cast<int64_t>(total_tiles))) : 0;
+    if (w < 1) w = 1;
+    if (w > r.tiles) w = r.tiles;
+    r.wgs = w;
+    r.per = w > 0 ? ceil_div_i(r.tiles, w) : 1;
+  }
+  return r;
 }
 
-// Run by one full wave: the stream owning workgroup `wg` and the workgroup's
-// index within that stream.  Returns b = -1 when wg is past the last one.
+// Run by one full wave: the stream owning workgroup `wg`, the workgroup's
+// index within that stream, and the stream's split.  b = -1 when wg is past
+// the last workgroup.
 __device__ __forceinline__ void find_stream_of_wg(const int32_t* sel_off, int32_t B,
-                                                  int32_t tpc, int32_t per, int32_t wg,
-                                                  int32_t* b_out, int32_t* local_out) {
+                                                  int32_t tpc, int32_t per, int32_t target,
+                                                  int32_t wg, int32_t* b_out, int32_t* local_out,
+                                                  StreamSplit* split_out) {
   const int lane = threadIdx.x & (kWave - 1);
+  const int32_t total_tiles = (sel_off[B] - sel_off[0]) * tpc;
   int32_t base = 0;  // workgroups of streams before the current 64-stream window
   for (int32_t s0 = 0; s0 < B; s0 += kWave) {
     const int32_t s = s0 + lane;
-    int32_t n = (s < B) ? stream_wgs(sel_off, s, tpc, per) : 0;
-    // inclusive prefix over the window
-    int32_t incl = n;
-#pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-      int32_t y = __shfl_up(incl, off, kWave);
-      if (lane >= off) incl += y;
-    }
-    const int32_t total = __shfl(incl, kWave - 1, kWave);
+    StreamSplit sp = {0, 0, 1};
+    if (s < B) sp = stream_split(sel_off, s, tpc, per, target, total_tiles);
+    const int32_t incl = static_cast<int32_t>(wave_inclusive_scan(static_cast<uint32_t>(sp.wgs)));
+    const int32_t total = __builtin_amdgcn_readlane(incl, kWave - 1);
     if (wg < base + total) {
       const uint64_t hit = __ballot(base + incl > wg);
       const int first = __ffsll(static_cast<long long>(hit)) - 1;
-      const int32_t excl = __shfl(incl - n, first, kWave);
+      const int32_t excl = __builtin_amdgcn_readlane(incl - sp.wgs, first);
       *b_out = s0 + first;
       *local_out = wg - base - excl;
+      split_out->tiles = __builtin_amdgcn_readlane(sp.tiles, first);
+      split_out->wgs = __builtin_amdgcn_readlane(sp.wgs, first);
+      split_out->per = __builtin_amdgcn_readlane(sp.per, first);
       return;
     }
     base += total;
   }
   *b_out = -1;
   *local_out = 0;
+  *split_out = StreamSplit{0, 0, 1};
 }
 
-// Run by one full wave: index of the first workgroup of stream b.
-__device__ __forceinline__ int32_t first_wg_of_stream(const int32_t* sel_off, int32_t b,
-                                                      int32_t tpc, int32_t per) {
+// Run by one full wave: index of the first workgroup of stream b and its
+// workgroup count.
+__device__ __forceinline__ void stream_wg_range(const int32_t* sel_off, int32_t B, int32_t b,
+                                                int32_t tpc, int32_t per, int32_t target,
+                                                int32_t* first_out, int32_t* count_out) {
   const int lane = threadIdx.x & (kWave - 1);
-  int32_t acc = 0;
+  const int32_t total_tiles = (sel_off[B] - sel_off[0]) * tpc;
+  uint32_t acc = 0;
   for (int32_t s0 = 0; s0 < b; s0 += kWave) {
     const int32_t s = s0 + lane;
-    acc += (s < b) ? stream_wgs(sel_off, s, tpc, per) : 0;
+    if (s < b) acc += static_cast<uint32_t>(stream_split(sel_off, s, tpc, per, target, total_tiles).wgs);
   }
-#pragma unroll
-  for (int off = kWave / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, kWave);
-  return acc;
+  *first_out = static_cast<int32_t>(wave_sum_u32(acc));
+  *count_out = stream_split(sel_off, b, tpc, per, target, total_tiles).wgs;
 }
 
 }  // namespace lsa

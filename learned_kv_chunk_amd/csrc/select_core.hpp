@@ -1,0 +1,177 @@
+// select_core.hpp -- top-k of one stream's fp32 scores by one workgroup (or
+// one wave).
+//
+// Dimensionstp review, section 3-2-3 step 5: keep the top-k chunks.  Ties go
+// to the lower chunk index, NaN ranks below every number and -0.0 equals
+// +0.0; kept indices come out in ascending order.
+//
+// THREADS threads (64: a single wave, no barriers) hold KPT consecutive
+// scores each ([t*KPT, t*KPT+KPT)) as order-preserving 32-bit keys.  An
+// MSB-first radix select runs four 8-bit digit passes, each into its own LDS
+// histogram.  In the first pass (sign and top exponent bits: few distinct
+// digits) lanes with equal digits are matched with eight ballots and one lane
+// per digit adds the group's count, so no two lanes of a wave hit the same
+// LDS word; later passes only see keys that share the digits chosen so far
+// and add directly.  After a pass every wave reads the 256 counts (four per
+// lane), scans them with DPP row shifts and lane reads, and finds the digit
+// holding the k-th largest key without another barrier.  A block-wide
+// exclusive scan of (#keys > T, #keys == T) then places every kept chunk at
+// its output position: ascending indices and the lower-index tie rule with no
+// sort.
+#pragma once
+
+#include "lsa_internal.hpp"
+#include "wave.hpp"
+
+namespace lsa {
+
+__device__ __forceinline__ uint32_t order_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  if (f != f) return 0u;       // NaN: below every number
+  if ((u << 1) == 0u) u = 0u;  // -0.0 -> +0.0
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+template <int THREADS>
+struct SelectLds {
+  alignas(16) uint32_t hist[4][256];
+  uint32_t tot[2 * (THREADS / kWave)];
+};
+
+// Barrier among the THREADS threads taking part (a single wave needs only
+// its LDS operations ordered).
+template <int THREADS>
+__device__ __forceinline__ void select_sync() {
+  if (THREADS == kWave) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+  } else {
+    __syncthreads();
+  }
+}
+
+// Exclusive scan of two counters over the THREADS threads.
+template <int THREADS>
+__device__ __forceinline__ void select_exclusive_scan2(uint32_t a, uint32_t b, uint32_t* ea,
+                                                       uint32_t* eb, uint32_t* s_tot) {
+  const int wave = threadIdx.x / kWave;
+  const uint32_t ia = wave_inclusive_scan(a);
+  const uint32_t ib = wave_inclusive_scan(b);
+  uint32_t ba = 0, bb = 0;
+  if (THREADS > kWave) {
+    if ((threadIdx.x & (kWave - 1)) == kWave - 1) {
+      s_tot[2 * wave] = ia;
+      s_tot[2 * wave + 1] = ib;
+    }
+    select_sync<THREADS>();
+#pragma unroll
+    for (int w = 0; w < THREADS / kWave; ++w) {
+      if (w < wave) {
+        ba += s_tot[2 * w];
+        bb += s_tot[2 * w + 1];
+      }
+    }
+  }
+  *ea = ba + ia - a;
+  *eb = bb + ib - b;
+}
+
+// Top-k of scores[0..n) written ascending to out[0..k); 0 < k < n.  Every
+// one of the THREADS threads (threads 0..THREADS-1 of the workgroup) must
+// call it.
+template <int THREADS, int KPT>
+__device__ __forceinline__ void select_topk_block(const float* __restrict__ scores, int32_t n,
+                                                  int32_t k, int32_t* __restrict__ out,
+                                                  SelectLds<THREADS>& lds) {
+  const int tid = threadIdx.x;
+  uint32_t key[KPT];
+  float sv[KPT];
+#pragma unroll
+  for (int i = 0; i < KPT; ++i) sv[i] = scores[min(tid * KPT + i, n - 1)];  // all loads in flight
+#pragma unroll
+  for (int i = 0; i < KPT; ++i) key[i] = (tid * KPT + i < n) ? order_key(sv[i]) : 0u;
+  for (int i = tid; i < 4 * 256; i += THREADS) (&lds.hist[0][0])[i] = 0u;
+  select_sync<THREADS>();
+
+  const uint64_t below = lanemask_lt();
+  uint32_t prefix = 0, mask = 0, remaining = static_cast<uint32_t>(k);
+#pragma unroll
+  for (int pass = 0; pass < 4; ++pass) {
+    const int shift = 24 - 8 * pass;
+    uint32_t* hist = lds.hist[pass];
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+      const bool part = (tid * KPT + i < n) && ((key[i] & mask) == prefix);
+      const uint32_t d = (key[i] >> shift) & 0xffu;
+      const uint64_t pm = __ballot(part);
+      if (pm == 0) continue;
+      if (pass == 0) {
+        uint64_t same = pm;
+#pragma unroll
+        for (int bit = 0; bit < 8; ++bit) {
+          const bool on = (d >> bit) & 1u;
+          const uint64_t m = __ballot(on);
+          same &= on ? m : ~m;
+        }
+        if (part && (same & below) == 0)
+          atomicAdd(&hist[d], static_cast<uint32_t>(__popcll(same)));
+      } else if (part) {
+        atomicAdd(&hist[d], 1u);
+      }
+    }
+    select_sync<THREADS>();
+    // digit d* with #(digit > d*) < remaining <= #(digit >= d*); lane l owns
+    // digits 4l..4l+3 (higher lanes hold higher digits)
+    const uint32_t lane = tid & (kWave - 1);
+    const uint4 c = reinterpret_cast<const uint4*>(hist)[lane];
+    const uint32_t tot = c.x + c.y + c.z + c.w;
+    const uint32_t incl = wave_inclusive_scan(tot);
+    const uint32_t total = __builtin_amdgcn_readlane(incl, 63);
+    uint32_t ge = total - incl;  // keys whose digit is above this lane's four
+    const uint32_t cnt[4] = {c.x, c.y, c.z, c.w};
+    uint32_t pick = 0, gt_pick = 0;
+    bool found = false;
+#pragma unroll
+    for (int j = 3; j >= 0; --j) {
+      const uint32_t gt = ge;
+      ge += cnt[j];
+      if (!found && gt < remaining && remaining <= ge) {
+        found = true;
+        pick = 4u * lane + j;
+        gt_pick = gt;
+      }
+    }
+    const uint64_t hit = __ballot(found);
+    const int src = __ffsll(static_cast<long long>(hit)) - 1;
+    pick = __builtin_amdgcn_readlane(pick, src);
+    gt_pick = __builtin_amdgcn_readlane(gt_pick, src);
+    prefix |= pick << shift;
+    mask |= 0xffu << shift;
+    remaining -= gt_pick;
+  }
+
+  uint32_t n_gt = 0, n_eq = 0;
+#pragma unroll
+  for (int i = 0; i < KPT; ++i) {
+    const bool v = tid * KPT + i < n;
+    n_gt += (v && key[i] > prefix) ? 1u : 0u;
+    n_eq += (v && key[i] == prefix) ? 1u : 0u;
+  }
+  uint32_t gt_before, eq_before;
+  select_exclusive_scan2<THREADS>(n_gt, n_eq, &gt_before, &eq_before, lds.tot);
+#pragma unroll
+  for (int i = 0; i < KPT; ++i) {
+    const int32_t idx = tid * KPT + i;
+    if (idx >= n) continue;
+    if (key[i] > prefix) {
+      out[gt_before + min(eq_before, remaining)] = idx;
+      ++gt_before;
+    } else if (key[i] == prefix) {
+      if (eq_before < remaining) out[gt_before + eq_before] = idx;
+      ++eq_before;
+    }
+  }
+}
+
+}  // namespace lsa

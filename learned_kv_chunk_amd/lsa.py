@@ -169,10 +169,12 @@ def workspace_bytes(shape: ProblemShape) -> int:
 
 
 def allocate_workspace(shape: ProblemShape, device) -> torch.Tensor:
+    """Zero-filled workspace (the library's arrival counters start at zero and
+    every call leaves them at zero)."""
     n = workspace_bytes(shape)
     if n == 0:
         raise LsaError(LSA_ERR_UNSUPPORTED, "lsa_workspace_bytes")
-    return torch.empty(n, dtype=torch.uint8, device=device)
+    return torch.zeros(n, dtype=torch.uint8, device=device)
 
 
 # ----------------------------------------------------------------------------- helpers

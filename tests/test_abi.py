@@ -166,3 +166,17 @@ def test_python_layer_rejects_host_tensors():
         lsa.score(s, torch.zeros(16, 128, dtype=torch.bfloat16),
                   torch.zeros(16 * 2048, 128, dtype=torch.bfloat16),
                   torch.zeros(17, dtype=torch.int32))
+
+
+def test_workspace_holds_counters_and_every_partial():
+    # one partial (max, sum, output row) per head for every workgroup the plan
+    # can launch, plus the per-stream arrival counters
+    for per in [4, 8, 64, 256]:
+        for B, k, H, dv in [(1, 8, 8, 64), (16, 276, 16, 128), (4, 819, 32, 128)]:
+            s = shape(batch=B, max_k=k, total_k=B * k, num_q_heads=H, head_dim_qk=dv,
+                      head_dim_v=dv, attn_tiles_per_block=per, max_chunks=max(2048, k),
+                      total_chunks=B * max(2048, k))
+            tiles = B * k * 2
+            wgs = -(-tiles // per) + B
+            need = wgs * H * (dv + 2) * 4
+            assert lsa.workspace_bytes(s) >= need, (per, B, k, H, dv)

@@ -266,3 +266,21 @@ def test_hot_token_dominates():
     P.check_attention("bf16", out, lse, o_ref, l_ref)
     v = wl.as_f32(w.V[row])
     assert np.abs(out[b, h] - v).max() < 0.05 * np.abs(v).max()
+
+
+def test_workspace_is_reusable_across_calls_and_shapes():
+    # one workspace serves calls of different shapes, repeatedly
+    wa, da = small_workload("cfg2")
+    wb, db = small_workload("cfg5")
+    big = torch.zeros(max(da.workspace.numel(), db.workspace.numel()), dtype=torch.uint8,
+                      device="cuda")
+    _, _, out_a, lse_a = P.run_phases(da, 0)
+    _, _, out_b, lse_b = P.run_phases(db, 0)
+    for _ in range(3):
+        for d, out_ref, lse_ref in [(da, out_a, lse_a), (db, out_b, lse_b)]:
+            out, lse = lsa.sparse_decode_attn(d.shape, d.queries(0), d.K, d.V, d.tok_off,
+                                              d.sel_idx, d.sel_off, workspace=big)
+            d.step(0, reindex=True)  # fused score+select uses the other counters
+            torch.cuda.synchronize()
+            np.testing.assert_array_equal(dev.to_host(out), out_ref)
+            np.testing.assert_array_equal(dev.to_host(lse), lse_ref)
