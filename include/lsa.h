@@ -83,8 +83,10 @@ typedef struct lsa_shape {
   int64_t total_chunks;   /* = sum_b N_b = chunk_off[B] */
   int64_t total_k;        /* = sum_b k_b = sel_off[B] */
   int32_t attn_tiles_per_block; /* split-KV granularity: 32-token tiles handled
-                             by one attention workgroup; 0 picks a default for
-                             the shape.  Changing it changes results only by
+                             by one attention workgroup (values above
+                             1022 * ceil(chunk_size / 32) act as that bound);
+                             0 picks a default for the shape.  Changing it
+                             changes results only by
                              rounding (bf16 inputs: the attention weights are
                              rounded to bf16 relative to each split's running
                              maximum, about 2^-9 relative). */

@@ -16,7 +16,6 @@ namespace lsa {
 
 namespace {
 constexpr int32_t kDefaultTarget = 256;  // compute units of an MI355X
-constexpr int32_t kMaxTilesPerWorkgroup = 1 << 20;
 
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 }  // namespace
@@ -35,17 +34,21 @@ AttnPlan make_attn_plan(const lsa_shape& s, int32_t target) {
   p.tiles_per_chunk = (s.chunk_size + kTileTokens - 1) / kTileTokens;
   const int64_t total_tiles = s.total_k * p.tiles_per_chunk;
   p.target = target > 0 ? target : kDefaultTarget;
+  const int64_t cap = run_tile_cap(p.tiles_per_chunk);
   if (s.attn_tiles_per_block > 0) {
     int64_t per = s.attn_tiles_per_block;
-    if (per > kMaxTilesPerWorkgroup) per = kMaxTilesPerWorkgroup;
+    if (per > cap) per = cap;
     p.per = static_cast<int32_t>(per);
     p.grid = (total_tiles + per - 1) / per + s.batch;
     p.ws_rows = p.grid;
   } else {
-    // sum_b max(1, round(T_b * target / T)) < target + B
+    // sum_b max(1, round(T_b * target / T), ceil(T_b / cap))
+    //   <= sum_b max(1, round(T_b * target / T)) + sum_b ceil(T_b / cap)
+    //   <= (target + B) + (T / cap + B)
     p.per = 0;
-    p.grid = p.target + s.batch;
-    p.ws_rows = (p.target > kDefaultTarget ? p.target : kDefaultTarget) + s.batch;
+    const int64_t extra = 2 * static_cast<int64_t>(s.batch) + total_tiles / cap + 1;
+    p.grid = p.target + extra;
+    p.ws_rows = (p.target > kDefaultTarget ? p.target : kDefaultTarget) + extra;
   }
   return p;
 }

@@ -17,7 +17,8 @@
 // per-wave LDS buffer because the second product contracts over tokens,
 // which are strided in memory.  Each wave software-pipelines its tiles: the
 // next tile's loads are in flight while the current one is computed.
-// A workgroup's four waves take interleaved tiles of one run, then merge their
+// A workgroup's waves (eight, two per SIMD, for up to 16 heads) take
+// interleaved tiles of one run, then merge their
 // (max, sum, output) states through LDS into one partial result, which the
 // merge kernel (attn_common.hip) combines with the stream's other partials.
 #include <math.h>
@@ -40,7 +41,6 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 template <int D>
 constexpr int v_row_bytes() { return 2 * D + 32; }
 
-constexpr int kMaxSlots = 256;  // kept-chunk indices of a run staged in LDS
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
@@ -171,13 +171,19 @@ __device__ __forceinline__ void compute_tile(const TileRegs<D>& r, int32_t nvali
 
 constexpr int cmax(int a, int b) { return a > b ? a : b; }
 
+// Waves per workgroup: 8 (two per SIMD) when one head group leaves room for
+// two waves' registers per SIMD, else 4.
+template <int NHG>
+constexpr int mqa_waves() { return NHG == 1 ? 8 : 4; }
+
 template <int D, int NHG>
 struct MqaLds {
+  static constexpr int kWaves = mqa_waves<NHG>();
   static constexpr int kRowBytes = v_row_bytes<D>();
   static constexpr int kTileBytes = kTileTokens * kRowBytes;              // per wave
   static constexpr int kStateO = NHG * (D / 16) * kWave * 16;            // lane-major o
   static constexpr int kStateBytes = kStateO + 2 * NHG * kWave * 4;      // + m, l
-  static constexpr int kBytes = cmax(kAttnWaves * kTileBytes, 2 * kStateBytes);
+  static constexpr int kBytes = cmax(kWaves * kTileBytes, (kWaves / 2) * kStateBytes);
 };
 
 template <int D, int NHG>
@@ -217,11 +223,14 @@ __device__ __forceinline__ void merge_state(const unsigned char* base, float (&m
 }
 
 template <int D, int NHG>
-__global__ __launch_bounds__(kAttnThreads, NHG == 1 ? 2 : 1) void attn_mqa_kernel(AttnArgs a) {
+__global__ __launch_bounds__(mqa_waves<NHG>() * kWave, NHG == 1 ? 2 : 1) void attn_mqa_kernel(
+    AttnArgs a) {
   using L = MqaLds<D, NHG>;
+  constexpr int NW = L::kWaves;
+  constexpr int kThreads = NW * kWave;
   __shared__ __attribute__((aligned(16))) unsigned char smem[L::kBytes];
   __shared__ int32_t s_plan[3];
-  __shared__ int32_t s_slot[kMaxSlots];
+  __shared__ int32_t s_slot[kMaxRunSlots];  // the run's kept-chunk indices
 
   const int tid = threadIdx.x;
   const int wave = tid / kWave;
@@ -248,7 +257,7 @@ __global__ __launch_bounds__(kAttnThreads, NHG == 1 ? 2 : 1) void attn_mqa_kerne
   const int32_t t_end = s_plan[2];
   const int32_t slot_first = t_begin / tpc;
   const int32_t nslots = (t_end - 1) / tpc - slot_first + 1;
-  for (int32_t i = tid; i < min(nslots, kMaxSlots); i += kAttnThreads)
+  for (int32_t i = tid; i < min(nslots, kMaxRunSlots); i += kThreads)
     s_slot[i] = a.sel_idx[sel0 + slot_first + i];
   const int64_t tb = a.tok_off[b];
   const int64_t len = a.tok_off[b + 1] - tb;
@@ -268,17 +277,17 @@ __global__ __launch_bounds__(kAttnThreads, NHG == 1 ? 2 : 1) void attn_mqa_kerne
   }
   __syncthreads();
 
-  // Tile i of this wave is t_begin + wave + 4*i.  An empty tile (past the end
+  // Tile i of this wave is t_begin + wave + NW*i.  An empty tile (past the end
   // of a partial chunk) points at its chunk's first row with nvalid = 0.
-  const int32_t n_mine = (t_end - t_begin - wave + kAttnWaves - 1) / kAttnWaves;
+  const int32_t n_mine = (t_end - t_begin - wave + NW - 1) / NW;
   auto tile_info = [&](int32_t i) {
     TileInfo ti;
-    const int32_t t = t_begin + wave + kAttnWaves * i;
+    const int32_t t = t_begin + wave + NW * i;
     const int32_t j = t / tpc;
     const int32_t sub = t - j * tpc;
     // a kept index outside [0, N_b) (a violated precondition) is clamped so
     // that no read leaves the stream
-    int64_t n = (j - slot_first < kMaxSlots) ? s_slot[j - slot_first] : a.sel_idx[sel0 + j];
+    int64_t n = s_slot[min(j - slot_first, kMaxRunSlots - 1)];
     n = n < 0 ? 0 : (n > last_chunk ? last_chunk : n);
     int64_t valid = len - n * C;
     if (valid > C) valid = C;
@@ -329,11 +338,15 @@ __global__ __launch_bounds__(kAttnThreads, NHG == 1 ? 2 : 1) void attn_mqa_kerne
     }
   }
 
-  // merge the four waves' states: 3,2 -> 1,0 ; 1 -> 0
-  __syncthreads();
-  if (wave >= 2) store_state<D, NHG>(smem + (wave - 2) * L::kStateBytes, m, l, o, lane);
-  __syncthreads();
-  if (wave < 2) merge_state<D, NHG>(smem + wave * L::kStateBytes, m, l, o, lane);
+  // tree-merge the waves' states into wave 0 (halving the live waves per round)
+#pragma unroll
+  for (int stride = NW / 2; stride >= 2; stride /= 2) {
+    __syncthreads();
+    if (wave >= stride && wave < 2 * stride)
+      store_state<D, NHG>(smem + (wave - stride) * L::kStateBytes, m, l, o, lane);
+    __syncthreads();
+    if (wave < stride) merge_state<D, NHG>(smem + wave * L::kStateBytes, m, l, o, lane);
+  }
   __syncthreads();
   if (wave == 1) store_state<D, NHG>(smem, m, l, o, lane);
   __syncthreads();
@@ -360,10 +373,13 @@ __global__ __launch_bounds__(kAttnThreads, NHG == 1 ? 2 : 1) void attn_mqa_kerne
 template <int D>
 hipError_t launch_mqa_d(const AttnArgs& a, int64_t grid, hipStream_t st) {
   const int nhg = (a.H + 15) / 16;
-  dim3 g(static_cast<uint32_t>(grid)), blk(kAttnThreads);
-  if (nhg == 1) hipLaunchKernelGGL((attn_mqa_kernel<D, 1>), g, blk, 0, st, a);
-  else if (nhg == 2) hipLaunchKernelGGL((attn_mqa_kernel<D, 2>), g, blk, 0, st, a);
-  else if (nhg <= 4) hipLaunchKernelGGL((attn_mqa_kernel<D, 4>), g, blk, 0, st, a);
+  dim3 g(static_cast<uint32_t>(grid));
+  if (nhg == 1)
+    hipLaunchKernelGGL((attn_mqa_kernel<D, 1>), g, dim3(mqa_waves<1>() * kWave), 0, st, a);
+  else if (nhg == 2)
+    hipLaunchKernelGGL((attn_mqa_kernel<D, 2>), g, dim3(mqa_waves<2>() * kWave), 0, st, a);
+  else if (nhg <= 4)
+    hipLaunchKernelGGL((attn_mqa_kernel<D, 4>), g, dim3(mqa_waves<4>() * kWave), 0, st, a);
   else return hipErrorNotSupported;
   return hipGetLastError();
 }

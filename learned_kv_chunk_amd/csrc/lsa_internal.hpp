@@ -13,8 +13,6 @@ namespace lsa {
 
 constexpr int kWave = 64;
 constexpr int kTileTokens = 32;        // tokens per attention tile
-constexpr int kAttnWaves = 4;          // waves per attention workgroup
-constexpr int kAttnThreads = kAttnWaves * kWave;
 
 // ---------------------------------------------------------------------------
 // Split-KV work plan.  Stream b owns T_b = k_b * tiles_per_chunk tiles of 32
@@ -26,9 +24,19 @@ constexpr int kAttnThreads = kAttnWaves * kWave;
 //    CU) are shared out in proportion to the streams' tiles,
 //    W_b = max(1, round(T_b * target / T)), and stream b's runs hold
 //    ceil(T_b / W_b) tiles, so every CU gets about T / target tiles.
-// Workgroup ids at or beyond sum_b W_b do nothing; the grid is a bound known
-// on the host from the shape alone.
+// Either way a run holds at most run_tile_cap(tiles_per_chunk) tiles (W_b is
+// raised where needed), so that the kept-chunk indices of any run fit in
+// kMaxRunSlots LDS words.  Workgroup ids at or beyond sum_b W_b do nothing;
+// the grid is a bound known on the host from the shape alone.
 // ---------------------------------------------------------------------------
+constexpr int32_t kMaxRunSlots = 1024;  // kept chunks one run can span
+
+// Longest run of tiles: a run of n tiles starting anywhere spans at most
+// n / tpc + 2 chunks.
+__host__ __device__ __forceinline__ int32_t run_tile_cap(int32_t tpc) {
+  return (kMaxRunSlots - 2) * tpc;
+}
+
 struct AttnPlan {
   int32_t tiles_per_chunk;
   int32_t per;      // tiles per workgroup, or 0 for the proportional split
@@ -119,6 +127,8 @@ __device__ __forceinline__ StreamSplit stream_split(const int32_t* sel_off, int3
     const int64_t num = 2 * static_cast<int64_t>(r.tiles) * target + total_tiles;
     int32_t w = total_tiles > 0 ? static_cast<int32_t>(num / (2 * static_cast<int64_t>(total_tiles))) : 0;
     if (w < 1) w = 1;
+    const int32_t w_min = ceil_div_i(r.tiles, run_tile_cap(tpc));
+    if (w < w_min) w = w_min;
     if (w > r.tiles) w = r.tiles;
     r.wgs = w;
     r.per = w > 0 ? ceil_div_i(r.tiles, w) : 1;

@@ -16,7 +16,7 @@ from tests import parity as P
 
 pytestmark = pytest.mark.gpu
 
-SMALL = ["cfg1", "cfg2", "cfg3", "cfg5"]
+SMALL = ["cfg1", "cfg2", "cfg3", "cfg4", "cfg5"]
 
 
 def small_cfg(name):
@@ -64,7 +64,7 @@ def test_fused_step_equals_phases_and_reuses_selection(name):
     P.check_attention(w.cfg.dtype, dev.to_host(d.out), dev.to_host(d.lse), o_ref, l_ref)
 
 
-@pytest.mark.parametrize("name", ["cfg2", "cfg3", "cfg1"])
+@pytest.mark.parametrize("name", ["cfg2", "cfg3", "cfg1", "cfg4"])
 def test_gather_is_bit_exact_and_pool_attention_matches_store(name):
     w, d = small_workload(name)
     _, sel, out_store, lse_store = P.run_phases(d, 0)
@@ -74,8 +74,9 @@ def test_gather_is_bit_exact_and_pool_attention_matches_store(name):
     C = w.cfg.chunk_size
     np.testing.assert_array_equal(dev.to_host(d.k_pool),
                                   oracle.gather(w.K, C, w.tok_off, sel, w.sel_off))
-    np.testing.assert_array_equal(dev.to_host(d.v_pool),
-                                  oracle.gather(w.V, C, w.tok_off, sel, w.sel_off))
+    if w.V is not None:  # latent attention: V is part of K, there is no value pool
+        np.testing.assert_array_equal(dev.to_host(d.v_pool),
+                                      oracle.gather(w.V, C, w.tok_off, sel, w.sel_off))
     out, lse = lsa.sparse_decode_attn(s, d.queries(0), d.k_pool, d.v_pool, d.tok_off, d.sel_idx,
                                       d.sel_off, lsa.KV_POOL, workspace=d.workspace)
     torch.cuda.synchronize()
@@ -223,6 +224,38 @@ def test_attention_shape_variants(variant):
     P.check_selection(w, s_gpu, sel, s_ref)
     o_ref, l_ref = P.oracle_attention_on(w, 0, sel)
     print(variant, P.check_attention("bf16", out, lse, o_ref, l_ref))
+
+
+# ----------------------------------------------------------------------------- MLA (absorbed latent)
+def _mla_cfg(**kw):
+    # three ragged streams with partial last chunks, a quarter of the chunks kept,
+    # so that runs of several tiles start and end inside chunks
+    base = dict(lengths=(128 * 61 + 37, 128 * 30, 128 * 47 + 100), keep_num=1, keep_den=4)
+    base.update(kw)
+    return wl.small_variant("cfg4", **base)
+
+
+@pytest.mark.parametrize("per", [0, 1, 2, 3, 7, 40])
+def test_mla_attention_split_variants(per):
+    w = wl.make_workload(_mla_cfg())
+    d = dev.upload(w, "cuda", attn_tiles_per_block=per)
+    s_gpu, sel, out, lse = P.run_phases(d, 0)
+    s_ref = oracle.score(w.q_idx, w.emb, w.chunk_off)
+    P.check_scores(w, s_gpu, s_ref)
+    P.check_selection(w, s_gpu, sel, s_ref)
+    o_ref, l_ref = P.oracle_attention_on(w, 0, sel)
+    print(per, P.check_attention("bf16", out, lse, o_ref, l_ref))
+
+
+@pytest.mark.parametrize("heads", [16, 40, 64])
+def test_mla_attention_head_counts(heads):
+    w = wl.make_workload(_mla_cfg(num_q_heads=heads, kv_std=1.0, q_std=1.0))
+    d = dev.upload(w, "cuda", attn_tiles_per_block=5)
+    _, sel, out, lse = P.run_phases(d, 0)
+    o_ref, l_ref = P.oracle_attention_on(w, 0, sel)
+    rel = np.linalg.norm(out - o_ref, axis=-1) / np.linalg.norm(o_ref, axis=-1)
+    assert rel.max() <= 1e-2, rel.max()
+    assert (np.abs(lse - l_ref) / np.abs(l_ref)).max() <= 1e-4
 
 
 def test_fp32_portable_attention_ragged():
