@@ -65,109 +65,81 @@ PartialLayout partial_layout(const lsa_shape& s, const AttnPlan& p) {
 
 namespace {
 
-constexpr int kMergeThreads = 256;
-constexpr int kMergeBatch = 32;          // partial rows loaded per round trip
-constexpr int kMergeMaxPairs = 4096;     // (partial, head) pairs staged in LDS
-constexpr int kMergeMaxHeads = 33;       // heads one 256-element block can touch (dv >= 8)
+constexpr int kMergeWaves = 8;
+constexpr int kMergeThreads = kMergeWaves * kWave;
+constexpr int kMergeBatch = 16;  // partials whose loads are in flight together
 
-// One workgroup per (stream, 256 output elements): stage the maxima and sums
-// of the stream's partials for the block's heads in LDS, turn them into
-// weights, then every thread sums its element over all partials with
-// kMergeBatch independent loads in flight.
-__global__ __launch_bounds__(kMergeThreads) void merge_kernel(AttnArgs a) {
-  __shared__ float s_m[kMergeMaxPairs];
-  __shared__ float s_l[kMergeMaxPairs];
-  __shared__ float s_mstar[kMergeMaxHeads];
-  __shared__ float s_lstar[kMergeMaxHeads];
-  __shared__ int32_t s_info[2];
-  const int b = blockIdx.x;
-  const int tid = threadIdx.x;
+// One workgroup per (stream, 64 consecutive output elements of the flattened
+// [H][dv] row); lane i owns element i of the block.  The eight waves split
+// the stream's partials into contiguous ranges and fold theirs into a running
+// (max, sum, output) state, kMergeBatch partials per round trip with one
+// rescale per batch; the eight states are then combined through LDS.  The
+// order of the arithmetic depends only on the plan, so reruns are
+// bit-identical.
+__global__ __launch_bounds__(kMergeThreads) void merge_kernel(AttnArgs a, int32_t nblk) {
+  __shared__ float s_state[3][kMergeWaves][kWave];
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
+  const int32_t b = static_cast<int32_t>(blockIdx.x) / nblk;
+  const int32_t blk = static_cast<int32_t>(blockIdx.x) - b * nblk;
   const int32_t H = a.H, dv = a.dv;
   const int32_t elems = H * dv;
-  const int32_t e0 = static_cast<int32_t>(blockIdx.y) * kMergeThreads;
-  if (e0 >= elems) return;
-  if (tid < kWave) {
-    int32_t first, count;
-    stream_wg_range(a.sel_off, a.B, b, a.tiles_per_chunk, a.per, a.target, &first, &count);
-    if (tid == 0) {
-      s_info[0] = first;
-      s_info[1] = count;
-    }
-  }
-  __syncthreads();
-  const int64_t first = s_info[0];
-  const int32_t count = s_info[1];
-  const int32_t h_lo = e0 / dv;
-  const int32_t h_hi = (min(elems, e0 + kMergeThreads) - 1) / dv;
-  const int32_t nh = h_hi - h_lo + 1;
-  const bool staged = count * nh <= kMergeMaxPairs;
-  if (staged) {
-    for (int32_t i = tid; i < count * nh; i += kMergeThreads) {
-      const int32_t p = i / nh, hh = i - p * nh;
-      const int64_t row = (first + p) * H + h_lo + hh;
-      s_m[i] = a.ws_m[row];
-      s_l[i] = a.ws_l[row];
-    }
-  }
-  __syncthreads();
-  // per-head maximum and normaliser: wave w reduces heads w, w+4, ... with its
-  // lanes spread over the partials
-  const int wave = tid / kWave, lane = tid & (kWave - 1);
-  for (int32_t hh = wave; hh < nh; hh += kMergeThreads / kWave) {
-    float mx = -INFINITY;
-    for (int32_t p = lane; p < count; p += kWave)
-      mx = fmaxf(mx, staged ? s_m[p * nh + hh] : a.ws_m[(first + p) * H + h_lo + hh]);
-    mx = wave_max(mx);
-    const float mu = (mx == -INFINITY) ? 0.f : mx;
-    float l = 0.f;
-    for (int32_t p = lane; p < count; p += kWave) {
-      const float mp = staged ? s_m[p * nh + hh] : a.ws_m[(first + p) * H + h_lo + hh];
-      const float lp = staged ? s_l[p * nh + hh] : a.ws_l[(first + p) * H + h_lo + hh];
-      l = fmaf(lp, __builtin_amdgcn_exp2f(mp - mu), l);
-    }
-    l = wave_sum(l);
-    if (lane == 0) {
-      s_mstar[hh] = mx;
-      s_lstar[hh] = l;
-    }
-  }
-  __syncthreads();
-  if (staged) {
-    for (int32_t i = tid; i < count * nh; i += kMergeThreads) {
-      const float mx = s_mstar[i % nh];
-      s_m[i] = (mx == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(s_m[i] - mx);
-    }
-  }
-  __syncthreads();
-  const int32_t e = e0 + tid;
-  if (e >= elems) return;
-  const int32_t h = e / dv;
-  const int32_t hh = h - h_lo;
-  const int32_t c = e - h * dv;
-  const float mx = s_mstar[hh];
-  float acc = 0.f;
-  for (int32_t p0 = 0; p0 < count; p0 += kMergeBatch) {
-    float v[kMergeBatch];
+  const int32_t e = blk * kWave + lane;
+  const int32_t ec = min(e, elems - 1);
+  const int32_t h = ec / dv;
+
+  int32_t first, count;
+  stream_wg_range(a.sel_off, a.B, b, a.tiles_per_chunk, a.per, a.target, &first, &count);
+  const int32_t q = ceil_div_i(count, kMergeWaves);
+  const int32_t p_lo = min(count, wave * q);
+  const int32_t p_hi = min(count, p_lo + q);
+
+  float m_run = -INFINITY, l_run = 0.f, acc = 0.f;
+  for (int32_t p0 = p_lo; p0 < p_hi; p0 += kMergeBatch) {
+    float mv[kMergeBatch], lv[kMergeBatch], ov[kMergeBatch];
 #pragma unroll
     for (int u = 0; u < kMergeBatch; ++u) {
-      const int32_t p = min(p0 + u, count - 1);
-      v[u] = a.ws_o[((first + p) * H + h) * dv + c];
+      const int64_t row = static_cast<int64_t>(first) + min(p0 + u, p_hi - 1);
+      mv[u] = a.ws_m[row * H + h];
+      lv[u] = a.ws_l[row * H + h];
+      ov[u] = a.ws_o[row * elems + ec];
     }
+    float mb = m_run;
+#pragma unroll
+    for (int u = 0; u < kMergeBatch; ++u)
+      if (p0 + u < p_hi) mb = fmaxf(mb, mv[u]);
+    const float mu = (mb == -INFINITY) ? 0.f : mb;
+    const float f = __builtin_amdgcn_exp2f(m_run - mu);
+    acc *= f;
+    l_run *= f;
 #pragma unroll
     for (int u = 0; u < kMergeBatch; ++u) {
-      const int32_t p = p0 + u;
-      if (p < count) {
-        const float w = staged ? s_m[p * nh + hh]
-                               : ((mx == -INFINITY) ? 0.f
-                                                    : __builtin_amdgcn_exp2f(
-                                                          a.ws_m[(first + p) * H + h] - mx));
-        acc = fmaf(v[u], w, acc);
+      if (p0 + u < p_hi) {
+        const float w = __builtin_amdgcn_exp2f(mv[u] - mu);
+        acc = fmaf(ov[u], w, acc);
+        l_run = fmaf(lv[u], w, l_run);
       }
     }
+    m_run = mb;
   }
-  const float l = s_lstar[hh];
+  s_state[0][wave][lane] = m_run;
+  s_state[1][wave][lane] = l_run;
+  s_state[2][wave][lane] = acc;
+  __syncthreads();
+  if (wave != 0 || e >= elems) return;
+  float mx = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < kMergeWaves; ++w) mx = fmaxf(mx, s_state[0][w][lane]);
+  const float mu = (mx == -INFINITY) ? 0.f : mx;
+  float l = 0.f, o = 0.f;
+#pragma unroll
+  for (int w = 0; w < kMergeWaves; ++w) {
+    const float f = __builtin_amdgcn_exp2f(s_state[0][w][lane] - mu);
+    l = fmaf(s_state[1][w][lane], f, l);
+    o = fmaf(s_state[2][w][lane], f, o);
+  }
   const int64_t orow = static_cast<int64_t>(b) * H + h;
-  a.out[orow * dv + c] = (l > 0.f) ? acc / l : 0.f;
+  const int32_t c = e - h * dv;
+  a.out[orow * dv + c] = (l > 0.f) ? o / l : 0.f;
   if (c == 0 && a.lse != nullptr)
     a.lse[orow] = (l > 0.f) ? (mx + log2f(l)) * 0.69314718055994530942f : -INFINITY;
 }
@@ -175,9 +147,10 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(AttnArgs a) {
 }  // namespace
 
 hipError_t launch_attn_merge(const lsa_shape& s, const AttnArgs& a, hipStream_t st) {
-  const int32_t elems = s.num_q_heads * s.head_dim_v;
-  dim3 grid(s.batch, (elems + kMergeThreads - 1) / kMergeThreads);
-  hipLaunchKernelGGL(merge_kernel, grid, dim3(kMergeThreads), 0, st, a);
+  const int32_t nblk = (s.num_q_heads * s.head_dim_v + kWave - 1) / kWave;
+  const int64_t grid = static_cast<int64_t>(nblk) * s.batch;
+  hipLaunchKernelGGL(merge_kernel, dim3(static_cast<uint32_t>(grid)), dim3(kMergeThreads), 0, st,
+                     a, nblk);
   return hipGetLastError();
 }
 

@@ -43,20 +43,30 @@ constexpr int kMlaDqk = 576;
 constexpr int kMlaDv = 512;
 constexpr int kMlaWaves = 8;  // two per SIMD: (head group, half) pairs
 constexpr int kMlaThreads = kMlaWaves * kWave;
-constexpr int kRowVecs = kMlaDqk / 8;                        // 16-byte vectors per row (72)
-constexpr int kPitchVecs = kRowVecs + 1;                     // padded LDS row (73 vectors)
-constexpr int kPitch = kPitchVecs * 16;                      // 1168 bytes
-constexpr int kTileSlots = kTileTokens * kPitchVecs;         // 2336 16-byte slots
-constexpr int kDmaPerWave = (kTileSlots + kMlaThreads - 1) / kMlaThreads;  // 5
-constexpr int kBufBytes = kMlaWaves * kDmaPerWave * kWave * 16;            // 40960
-constexpr int kBufs = 3;
+constexpr int kRowVecs = kMlaDqk / 8;                 // 16-byte vectors per row (72)
+constexpr int kPitch = kRowVecs * 16;                 // 1152-byte LDS rows, no padding
+constexpr int kTileSlots = kTileTokens * kRowVecs;    // 2304 16-byte slots
+constexpr int kTileInsts = kTileSlots / kWave;        // 36 DMA instructions per tile
+constexpr int kDmaMax = (kTileInsts + kMlaWaves - 1) / kMlaWaves;  // 5 (waves 0-3), else 4
+constexpr int kBufBytes = kTileSlots * 16;            // 36864
+constexpr int kBufs = 4;                              // three tiles in flight
+constexpr float kLazyLog2 = 8.f;  // reference-maximum slack of the online softmax (log2)
 
 // s_waitcnt immediate (gfx9 encoding) waiting for every vector-memory
 // operation, leaving the export and LDS/scalar counters unconstrained.
 constexpr int kWaitVmcnt0 = (7 << 4) | (15 << 8);
 
-static_assert(kTileSlots <= kMlaWaves * kDmaPerWave * kWave, "tile does not fit the DMA slots");
-static_assert(kDmaPerWave == 5, "the pipeline waits below count 5 loads per tile");
+static_assert(kTileInsts * kWave == kTileSlots, "DMA instructions must tile the buffer");
+static_assert(kTileInsts == 4 * 5 + 4 * 4, "waves 0-3 issue 5 loads per tile, waves 4-7 issue 4");
+static_assert(kRowVecs % 8 == 0, "the swizzle permutes vectors inside aligned groups of 8");
+
+// LDS layout of a tile: row r (token) at r * kPitch, its 16-byte vector v at
+// slot v ^ swz(r) (swz < 8, so a vector stays in its aligned group of 8).  The
+// pitch is 288 words, so odd rows start half-way round the 64 banks; swz then
+// spreads both read patterns over all banks: the K operand reads (16
+// consecutive rows, one vector each, per 16-lane pass) and the transposed V
+// reads (8 consecutive rows, one aligned vector pair each, per 32-lane pass).
+__device__ __forceinline__ int swz(int r) { return (((r >> 1) & 3) << 1) | ((r >> 3) & 1); }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
@@ -66,18 +76,22 @@ struct TileInfo {
 };
 
 // One 16-byte-per-lane global -> LDS load: lane i's 16 bytes at sbase + voff
-// land at LDS address lds_addr + 16 i.  Written as inline assembly so that the
-// compiler, which does not see the LDS write, adds no wait of its own for it
-// before LDS reads: the pipeline below does its own counting.
+// land at LDS address lds_addr + 16 i (the address is taken from M0, which is
+// restored afterwards).  Written as inline assembly so that the compiler, which
+// does not see the LDS write, adds no wait of its own for it before LDS reads:
+// the pipeline below does its own counting.
 __device__ __forceinline__ void dma16(const unsigned char* sbase, uint32_t voff,
                                       uint32_t lds_addr) {
+  uint32_t saved;
   asm volatile(
-      "s_mov_b32 m0, %0\n\t"
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
       "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %1, %2"
-      :
+      "global_load_lds_dwordx4 %2, %3\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
       : "s"(lds_addr), "v"(voff), "s"(sbase)
-      : "memory", "m0");
+      : "memory");
 }
 
 __device__ __forceinline__ uint32_t lds_address(const unsigned char* p) {
@@ -85,31 +99,53 @@ __device__ __forceinline__ uint32_t lds_address(const unsigned char* p) {
       reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const unsigned char*)p));
 }
 
-// Copy one tile (rows row0 .. row0+31, rows past nvalid repeat the last valid
-// row) into an LDS buffer with padded rows.  Each DMA instruction fills 64
-// consecutive 16-byte slots, lane i writing slot i; slot s of the buffer is
-// row s / 73, vector s % 73 (vector 72 is the pad, and slots past the tile
-// load the tile's first vector).
+// The slots this lane fills: DMA instruction j of wave w is instruction
+// w + 8j of the tile (j < 5 for waves 0-3, j < 4 otherwise) and fills slots
+// (w + 8j) * 64 .. +63, lane i slot (w + 8j) * 64 + i, which holds row
+// slot / 72, vector (slot % 72) ^ swz(row).
+struct DmaLane {
+  uint32_t voff[kDmaMax];  // byte offset in a full tile
+  int32_t rv[kDmaMax];     // row << 8 | vector
+};
+
+__device__ __forceinline__ DmaLane dma_lane(int64_t row_bytes, int wave, int lane) {
+  DmaLane d;
+#pragma unroll
+  for (int j = 0; j < kDmaMax; ++j) {
+    const int slot = min(wave + kMlaWaves * j, kTileInsts - 1) * kWave + lane;
+    const int row = slot / kRowVecs;
+    const int vec = (slot - row * kRowVecs) ^ swz(row);
+    d.voff[j] = static_cast<uint32_t>(row * row_bytes) + vec * 16;
+    d.rv[j] = (row << 8) | vec;
+  }
+  return d;
+}
+
+// Copy one tile (rows row0 .. row0+31; rows past nvalid repeat the last valid
+// row) into an LDS buffer: ND instructions from this wave.
+template <int ND>
 __device__ __forceinline__ void dma_tile(const unsigned char* __restrict__ kbytes,
                                          int64_t row_bytes, const TileInfo& ti,
-                                         const unsigned char* buf, int wave, int lane) {
-  const int last = ti.nvalid > 0 ? ti.nvalid - 1 : 0;
+                                         const DmaLane& dl, const unsigned char* buf,
+                                         int wave) {
   const uint64_t addr = reinterpret_cast<uint64_t>(kbytes) + static_cast<uint64_t>(ti.row0 * row_bytes);
   const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(addr));
   const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(addr >> 32));
   const unsigned char* sbase =
       reinterpret_cast<const unsigned char*>((static_cast<uint64_t>(hi) << 32) | lo);
-  const uint32_t lds0 = lds_address(buf);
+  const uint32_t lds0 = lds_address(buf) + wave * kWave * 16;
+  if (ti.nvalid == kTileTokens) {
 #pragma unroll
-  for (int j = 0; j < kDmaPerWave; ++j) {
-    const int inst = wave * kDmaPerWave + j;
-    const int slot = inst * kWave + lane;
-    const int row = slot / kPitchVecs;
-    const int vec = slot - row * kPitchVecs;
-    const bool real = row < kTileTokens && vec < kRowVecs;
-    const uint32_t voff =
-        real ? static_cast<uint32_t>(min(row, last) * row_bytes) + vec * 16 : 0u;
-    dma16(sbase, voff, __builtin_amdgcn_readfirstlane(lds0 + inst * kWave * 16));
+    for (int j = 0; j < ND; ++j)
+      dma16(sbase, dl.voff[j], __builtin_amdgcn_readfirstlane(lds0 + j * kMlaWaves * kWave * 16));
+  } else {
+    const int last = ti.nvalid > 0 ? ti.nvalid - 1 : 0;
+#pragma unroll
+    for (int j = 0; j < ND; ++j) {
+      const int row = dl.rv[j] >> 8, vec = dl.rv[j] & 255;
+      const uint32_t voff = static_cast<uint32_t>(min(row, last) * row_bytes) + vec * 16;
+      dma16(sbase, voff, __builtin_amdgcn_readfirstlane(lds0 + j * kMlaWaves * kWave * 16));
+    }
   }
 }
 
@@ -119,48 +155,90 @@ __device__ __forceinline__ void dma_tile(const unsigned char* __restrict__ kbyte
 // Barrier after this wave's LDS writes have completed.
 #define LSA_MLA_BARRIER() asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory")
 
-// S^T for one 16-token half of a tile and the 16 heads of this wave:
-// S^T[token][head] = K . Q^T over the 576 key dims.  The K operand of a lane is
-// token (half*16 + lane%16), dims s*32 + 8g .. +7; all 18 operands are read
-// before the products so the LDS latency is paid once.
-__device__ __forceinline__ f32x4 qk_half(const unsigned char* __restrict__ kt, int half,
-                                         const bf16x8 (&qf)[kMlaDqk / 32], int lane) {
+// Per-lane LDS read addresses (byte offsets inside a tile buffer).
+struct ReadLane {
+  uint32_t k[2];  // K operand, steps s = 2q + r: k[r] + 128 q (+ 16 rows for half 1)
+  uint32_t v[4];  // V^T operand, column groups cg = 4q + r: v[r] + 128 q (+ 16 rows)
+};
+
+// K operand of lane (r16, g): row r16, vector 4s + g.  V^T operand of lane
+// (r16, g): rows 4g + (r16 >> 2) (and +16), the 8-byte piece 8 * (r16 & 3) of
+// the 32-byte span of column group cg (vectors 2cg, 2cg + 1), in this wave's
+// column half.  swz(r) depends on r & 15 only, so rows r and r + 16 share it.
+__device__ __forceinline__ ReadLane read_lane(int col_half, int lane) {
+  ReadLane rl;
   const int r16 = lane & 15, g = lane >> 4;
-  const unsigned char* ka = kt + (half * 16 + r16) * kPitch + g * 16;
-  u32x4 av[kMlaDqk / 32];
+  const int fk = swz(r16);
 #pragma unroll
-  for (int s = 0; s < kMlaDqk / 32; ++s) av[s] = *reinterpret_cast<const u32x4*>(ka + s * 64);
-  __builtin_amdgcn_sched_barrier(0);  // keep every read ahead of the products
+  for (int r = 0; r < 2; ++r) rl.k[r] = r16 * kPitch + 16 * (g ^ (fk & 3)) + 64 * (r ^ (fk >> 2));
+  const int row = 4 * g + (r16 >> 2);
+  const int fv = swz(row);
+  const int t = (r16 >> 1) & 1;
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+    rl.v[r] = row * kPitch + 512 * col_half + 32 * (r ^ (fv >> 1)) + 16 * (t ^ (fv & 1)) +
+              8 * (r16 & 1);
+  return rl;
+}
+
+// S^T for one 16-token half of a tile and the 16 heads of this wave:
+// S^T[token][head] = K . Q^T over the 576 key dims (token = half*16 + lane%16,
+// dims s*32 + 8g .. +7 in lane (r16, g)).  Operands are read nine at a time
+// ahead of their products.
+__device__ __forceinline__ f32x4 qk_half(const unsigned char* __restrict__ kt, int half,
+                                         const ReadLane& rl, const bf16x8 (&qf)[kMlaDqk / 32]) {
+  const unsigned char* kh = kt + half * 16 * kPitch;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int s = 0; s < kMlaDqk / 32; ++s)
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av[s]), qf[s], acc, 0, 0, 0);
+  for (int s0 = 0; s0 < kMlaDqk / 32; s0 += 9) {
+    u32x4 av[9];
+#pragma unroll
+    for (int u = 0; u < 9; ++u) {
+      const int s = s0 + u;
+      av[u] = *reinterpret_cast<const u32x4*>(kh + rl.k[s & 1] + 128 * (s >> 1));
+    }
+#pragma unroll
+    for (int u = 0; u < 9; ++u)
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av[u]), qf[s0 + u], acc, 0, 0, 0);
+  }
   return acc;
 }
 
 // Online softmax of one tile for this wave's 16 heads, given S^T of both
 // halves, then O^T += V^T P^T over this wave's 256 latent columns.
 // Lane (r16, g) holds tokens 4g..4g+3 (first half) and 16+4g..16+4g+3 (second
-// half) of head r16, which is exactly its slice of the P^T operand.
-__device__ __forceinline__ void softmax_pv(const unsigned char* __restrict__ kt, int col_half,
-                                           f32x4 s0, f32x4 s1, int32_t nvalid, float& m,
-                                           float& l, f32x4 (&o)[kMlaDv / 32], float scale_log2,
-                                           int lane) {
-  const int r16 = lane & 15, g = lane >> 4;
+// half) of head r16, which is exactly its slice of the P^T operand.  The
+// weights are taken against a reference maximum m that is raised only when a
+// tile's maximum exceeds it by more than kLazyLog2, so weights stay below
+// 2^kLazyLog2 and the accumulators are rescaled only on those tiles.
+__device__ __forceinline__ void softmax_pv(const unsigned char* __restrict__ kt,
+                                           const ReadLane& rl, f32x4 s0, f32x4 s1,
+                                           int32_t nvalid, float& m, float& l,
+                                           f32x4 (&o)[kMlaDv / 32], float scale_log2, int lane) {
+  const int g = lane >> 4;
   float x[8];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int tok = 16 * (j >> 2) + 4 * g + (j & 3);
-    const float sv = (j < 4) ? s0[j & 3] : s1[j & 3];
-    x[j] = (tok < nvalid) ? sv * scale_log2 : -INFINITY;
+  for (int j = 0; j < 8; ++j) x[j] = ((j < 4) ? s0[j & 3] : s1[j & 3]) * scale_log2;
+  if (nvalid < kTileTokens) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int tok = 16 * (j >> 2) + 4 * g + (j & 3);
+      if (tok >= nvalid) x[j] = -INFINITY;
+    }
   }
   float mt = x[0];
 #pragma unroll
   for (int j = 1; j < 8; ++j) mt = fmaxf(mt, x[j]);
   mt = xor32_max(xor16_max(mt));
-  const float m_new = fmaxf(m, mt);
-  const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-  const float alpha = __builtin_amdgcn_exp2f(m - m_use);
+  if (__ballot(mt > m + kLazyLog2) != 0) {
+    const float m_new = (mt > m + kLazyLog2) ? mt : m;
+    const float alpha = (m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m - m_new);
+    l *= alpha;
+#pragma unroll
+    for (int c = 0; c < kMlaDv / 32; ++c) o[c] *= alpha;
+    m = m_new;
+  }
+  const float m_use = (m == -INFINITY) ? 0.f : m;
   bf16x8 pf;
   float ps = 0.f;
 #pragma unroll
@@ -169,32 +247,25 @@ __device__ __forceinline__ void softmax_pv(const unsigned char* __restrict__ kt,
     ps += p;
     pf[j] = static_cast<__bf16>(p);
   }
-  l = fmaf(l, alpha, ps);
-  m = m_new;
+  l += ps;
 
-  // ds_read_b64_tr_b16 gives lane i of a 16-lane group element (i & 3) of the
-  // 8-byte chunk addressed by lane 4j + (i >> 2) of the group, as its element
-  // j: lane s of group g addresses row 4g + (s >> 2) (and +16), columns
-  // c0 + 4*(s & 3) .. +3 of the 16-column group starting at c0.
-  const unsigned char* vrow =
-      kt + (4 * g + (r16 >> 2)) * kPitch + 8 * (r16 & 3) + col_half * (kMlaDv / 2) * 2;
   constexpr int kBatch = 8;  // column groups whose operands are read together
 #pragma unroll
-  for (int c0 = 0; c0 < kMlaDv / 32; c0 += kBatch) {
+  for (int q = 0; q < kMlaDv / 32 / kBatch; ++q) {
     u32x4 vt[kBatch];
 #pragma unroll
-    for (int c = 0; c < kBatch; ++c) {
-      const unsigned char* p0 = vrow + (c0 + c) * 32;
+    for (int r = 0; r < kBatch; ++r) {
+      const unsigned char* p0 = kt + rl.v[r & 3] + 128 * (q * (kBatch / 4) + (r >> 2));
       const u32x2 lo =
           __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p0)));
       const u32x2 hi = __builtin_bit_cast(
           u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p0 + 16 * kPitch)));
-      vt[c] = u32x4{lo.x, lo.y, hi.x, hi.y};
+      vt[r] = u32x4{lo.x, lo.y, hi.x, hi.y};
     }
 #pragma unroll
-    for (int c = 0; c < kBatch; ++c)
-      o[c0 + c] =
-          __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vt[c]), pf, o[c0 + c] * alpha, 0, 0, 0);
+    for (int r = 0; r < kBatch; ++r)
+      o[q * kBatch + r] =
+          __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vt[r]), pf, o[q * kBatch + r], 0, 0, 0);
   }
 }
 
@@ -271,30 +342,31 @@ __global__ __launch_bounds__(kMlaThreads, 1) void attn_mla_kernel(AttnArgs a) {
 #pragma unroll
   for (int c = 0; c < kMlaDv / 32; ++c) o[c] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // Three-buffer pipeline: tiles i+1 and i+2 are in flight while tile i is
-  // computed.  Each wave issues exactly kDmaPerWave loads per tile and no
-  // other vector-memory operation inside the loop, so "tile i has landed" is
-  // "at most kDmaPerWave of this wave's loads outstanding" (the loads of tile
-  // i+1), and the first barrier makes every wave's part of tile i visible.
-  // The buffer refilled with tile i+2 held tile i-1, which every wave finished
-  // before that barrier.  The second barrier publishes the S^T halves; a half
-  // is rewritten only after the next first barrier, which its reader reaches
-  // after reading it.
+  // Four-buffer pipeline: tiles i+1 .. i+3 are in flight while tile i is
+  // computed.  Each wave issues a fixed number nd of loads per tile (5 for
+  // waves 0-3, 4 for waves 4-7) and no other vector-memory operation inside
+  // the loop, so "tile i has landed" is "at most nd times the number of later
+  // tiles issued of this wave's loads outstanding", and the first barrier
+  // makes every wave's part of tile i visible.  The buffer refilled with tile
+  // i+3 held tile i-1, which every wave finished before that barrier.  The
+  // second barrier publishes the S^T halves; a half is rewritten only after
+  // the next first barrier, which its reader reaches after reading it.
+  const DmaLane dl = dma_lane(row_bytes, wave, lane);
+  const ReadLane rl = read_lane(half, lane);
+  const bool five = wave < 4;  // wave-uniform: 5 loads per tile, else 4
+  auto issue = [&](int32_t t, int slot) {
+    const TileInfo ti = tile_info(t_begin + t);
+    if (five) dma_tile<5>(kbytes, row_bytes, ti, dl, smem + slot * kBufBytes, wave);
+    else dma_tile<4>(kbytes, row_bytes, ti, dl, smem + slot * kBufBytes, wave);
+    return ti.nvalid;
+  };
   const int32_t n = t_end - t_begin;
-  int32_t nv0 = 0, nv1 = 0, nv2 = 0;  // valid tokens of tiles i, i+1, i+2
-  if (n > 0) {
-    const TileInfo t0 = tile_info(t_begin);
-    nv0 = t0.nvalid;
-    dma_tile(kbytes, row_bytes, t0, smem, wave, lane);
-  }
-  if (n > 1) {
-    const TileInfo t1 = tile_info(t_begin + 1);
-    nv1 = t1.nvalid;
-    dma_tile(kbytes, row_bytes, t1, smem + kBufBytes, wave, lane);
-  }
+  int32_t nv[kBufs] = {0, 0, 0, 0};  // valid tokens of the tile in each buffer
+  for (int32_t t = 0; t < kBufs - 1; ++t)
+    if (t < n) nv[t] = issue(t, t);
 
   // Q^T operand of this wave's heads: lane holds Q[head][s*32 + 8g .. +7].
-  // Loaded after the first two tiles' copies are under way and waited for
+  // Loaded after the first tiles' copies are under way and waited for
   // together with them, so the loop holds no compiler-tracked load.
   bf16x8 qf[kMlaDqk / 32];
   {
@@ -307,31 +379,34 @@ __global__ __launch_bounds__(kMlaThreads, 1) void attn_mla_kernel(AttnArgs a) {
   }
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
 
-  int buf = 0;
   for (int32_t i = 0; i < n; ++i) {
-    if (i + 1 < n) LSA_MLA_WAIT_BARRIER(5);
-    else LSA_MLA_WAIT_BARRIER(0);
-    if (i + 2 < n) {
-      const int nb = buf >= 1 ? buf - 1 : kBufs - 1;  // (i + 2) % 3
-      const TileInfo t2 = tile_info(t_begin + i + 2);
-      nv2 = t2.nvalid;
-      dma_tile(kbytes, row_bytes, t2, smem + nb * kBufBytes, wave, lane);
+    const int32_t later = min(n - 1 - i, kBufs - 2);  // tiles issued after tile i
+    if (later == 2) {
+      if (five) LSA_MLA_WAIT_BARRIER(10);
+      else LSA_MLA_WAIT_BARRIER(8);
+    } else if (later == 1) {
+      if (five) LSA_MLA_WAIT_BARRIER(5);
+      else LSA_MLA_WAIT_BARRIER(4);
+    } else {
+      LSA_MLA_WAIT_BARRIER(0);
+    }
+    const int buf = i & (kBufs - 1);
+    if (i + kBufs - 1 < n) {
+      const int nb = (i + kBufs - 1) & (kBufs - 1);
+      nv[nb] = issue(i + kBufs - 1, nb);
     }
     const unsigned char* kt = smem + buf * kBufBytes;
     f32x4 s_mine = {0.f, 0.f, 0.f, 0.f};
     if (active) {
-      s_mine = qk_half(kt, half, qf, lane);
+      s_mine = qk_half(kt, half, rl, qf);
       s_xch[wave][lane] = s_mine;
     }
     LSA_MLA_BARRIER();
     if (active) {
       const f32x4 s_other = s_xch[wave ^ 1][lane];
-      softmax_pv(kt, half, half ? s_other : s_mine, half ? s_mine : s_other, nv0, m, l, o,
+      softmax_pv(kt, rl, half ? s_other : s_mine, half ? s_mine : s_other, nv[buf], m, l, o,
                  a.scale_log2, lane);
     }
-    nv0 = nv1;
-    nv1 = nv2;
-    buf = buf + 1 == kBufs ? 0 : buf + 1;
   }
 
   if (!active || head >= H) return;
