@@ -122,7 +122,9 @@ size_t lsa_workspace_bytes(const lsa_shape* shape);
  * q_idx_dev: [B][D]; emb_dev: [total_chunks][D]; scores_dev: [total_chunks] fp32.
  * No normalisation and no sigmoid are applied (inputs are expected to be
  * normalised already; a monotone squashing never changes a top-k).
- * Requires D*sizeof(elem) to be a multiple of 16 bytes and D <= 1024.
+ * Supported when a row of D elements is 16-byte vectors in a power-of-two
+ * count from 4 to 128 (bf16: D = 32, 64, ..., 1024; fp32: D = 16, 32, ..., 512);
+ * other D return LSA_ERR_UNSUPPORTED.
  * ------------------------------------------------------------------------- */
 lsa_status lsa_score(const lsa_shape* shape, const void* q_idx_dev, const void* emb_dev,
                      const int32_t* chunk_off_dev, float* scores_dev, void* hip_stream);
@@ -142,9 +144,9 @@ lsa_status lsa_select_topk(const lsa_shape* shape, const float* scores_dev,
                            int32_t* sel_idx_dev, void* hip_stream);
 
 /* ---------------------------------------------------------------------------
- * Resident chunk pool.  Wiki note flowchart ("Resident KV chunks ~13.5%
- * footprint"); molayo explainer (a selective gather of the query-critical
- * chunks instead of a sweep of the whole cache).  Copies each kept chunk into
+ * Resident chunk pool.  Wiki note flowchart (its resident-chunk node); molayo
+ * explainer (gather the chunks a query needs instead of sweeping the whole
+ * cache).  Copies each kept chunk into
  * its pool slot: slot s = sel_off[b] + j receives chunk n = sel_idx[s] of
  * stream b, row r of the slot being token n*C + r; rows with n*C + r >= L_b
  * are zero-filled.
@@ -180,9 +182,9 @@ lsa_status lsa_gather_chunks(const lsa_shape* shape, const void* k_store_dev,
  * calls that share a workspace must not run concurrently.
  * Supported: bf16 with num_q_heads <= 64 and head_dim_qk == head_dim_v in
  * {64, 128} (multi-query); bf16 with head_dim_qk 576, head_dim_v 512,
- * v_aliases_k = 1 and num_q_heads a multiple of 16 up to 128 (absorbed
- * latent attention); fp32 or bf16 with num_q_heads <= 16 and head dims <= 256
- * (portable kernel).  Anything else returns LSA_ERR_UNSUPPORTED.
+ * v_aliases_k = 1 and 1 to 64 query heads (absorbed latent attention); fp32
+ * or bf16 with num_q_heads <= 16 and head dims <= 256 (portable kernel).
+ * Anything else returns LSA_ERR_UNSUPPORTED.
  * ------------------------------------------------------------------------- */
 lsa_status lsa_sparse_decode_attn(const lsa_shape* shape, int32_t kv_mode, const void* q_dev,
                                   const void* k_base_dev, const void* v_base_dev,

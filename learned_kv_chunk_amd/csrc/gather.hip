@@ -1,7 +1,8 @@
 // gather.hip -- resident chunk pool and measurement helpers.
 //
-// Wiki note flowchart ("Resident KV chunks ~13.5% footprint") and the molayo
-// explainer's selective-gather paragraph: only the kept chunks stay resident.
+// Wiki note flowchart (its resident-chunk node) and the molayo explainer's
+// paragraph on gathering only the selected chunks: only the kept chunks stay
+// resident.
 // The gather copies each kept chunk of the K (and V) history into its pool
 // slot; rows past the end of the stream are zero-filled.  One workgroup per
 // (kept slot, stream); each thread moves 16-byte vectors with several loads

@@ -9,8 +9,8 @@
  *   oracle_select     top-k keep set per stream (review section 3-2-3 step 5);
  *                     ties go to the lower chunk index, NaN ranks last.
  *   oracle_gather     copy of the kept chunks into a resident pool (wiki note
- *                     flowchart "Resident KV chunks"; molayo explainer,
- *                     "selective gather").
+ *                     flowchart, its resident-chunk node; molayo explainer,
+ *                     the paragraph on gathering only the selected chunks).
  *   oracle_attention  softmax attention restricted to the kept chunks' tokens
  *                     (review section 3-2-3 steps 6-7), computed with a full
  *                     max pass then a weighted-sum pass.

@@ -13,14 +13,14 @@
  *
  *   score      -- dual-encoder relevance: one inner product between a stream's
  *                 indexer query embedding and each of its chunk embeddings
- *                 ("FlashMemory-DeepSeek-V4 ... Lookahead Sparse Attention"
- *                 wiki note, flowchart and "Key points"; dimensionstp review
+ *                 (the bayesiansapien wiki note on FlashMemory-DeepSeek-V4
+ *                 LSA, its flowchart and its "Key points"; dimensionstp review
  *                 section 3-2-4; arXiv abstract v2).
  *   select     -- keep the k highest-scoring chunks of each stream (review
- *                 section 3-2-3, step 5: "top-k ... keep mask").
+ *                 section 3-2-3, step 5, the top-k keep mask).
  *   gather     -- copy the kept chunks into a resident pool (wiki note
- *                 flowchart, "Resident KV chunks"; molayo explainer, the
- *                 "selective gather" paragraph).
+ *                 flowchart, its resident-chunk node; molayo explainer, the
+ *                 paragraph on gathering only the selected chunks).
  *   attention  -- softmax attention of each query head restricted to the
  *                 tokens of the kept chunks (review section 3-2-3, steps 6-7).
  *
