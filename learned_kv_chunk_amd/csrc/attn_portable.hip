@@ -8,7 +8,8 @@
 // (queries staged in LDS as fp32), the wave keeps an fp32 online softmax per
 // head (wave-wide max / sum reductions), the tile's weights go through LDS,
 // and lanes accumulate output columns c, c+64, ... reading value rows with
-// coalesced loads.  The wave's (m, l, o) is its workgroup's partial result.
+// coalesced loads.  Key and value reads are issued kPortBatch at a time so
+// that their memory latency overlaps.  The wave's (m, l, o) is its workgroup's partial result.
 #include <math.h>
 
 #include "wave.hpp"
@@ -19,6 +20,7 @@ namespace {
 
 constexpr int kPortHeads = 16;
 constexpr int kPortMaxDim = 256;
+constexpr int kPortBatch = 16;  // independent loads in flight per lane
 
 template <typename T>
 __device__ __forceinline__ float load_elem(const T* p, int64_t i);
@@ -92,12 +94,20 @@ __global__ __launch_bounds__(kWave) void attn_portable_kernel(AttnArgs a) {
 #pragma unroll
     for (int h = 0; h < HM; ++h) x[h] = 0.f;
     if (lane < nv) {
+      // the token's key row, kPortBatch elements per round trip
       const int64_t kr = (row0 + lane) * a.k_row;
-      for (int32_t j = 0; j < dqk; ++j) {
-        const float kj = load_elem(kb, kr + j);
+      for (int32_t j0 = 0; j0 < dqk; j0 += kPortBatch) {
+        float kv[kPortBatch];
 #pragma unroll
-        for (int h = 0; h < HM; ++h)
-          if (h < H) x[h] = fmaf(s_q[h * dqk + j], kj, x[h]);
+        for (int u = 0; u < kPortBatch; ++u) kv[u] = load_elem(kb, kr + min(j0 + u, dqk - 1));
+#pragma unroll
+        for (int u = 0; u < kPortBatch; ++u) {
+          if (j0 + u < dqk) {
+#pragma unroll
+            for (int h = 0; h < HM; ++h)
+              if (h < H) x[h] = fmaf(s_q[h * dqk + j0 + u], kv[u], x[h]);
+          }
+        }
       }
     }
     float alpha[HM];
@@ -124,11 +134,19 @@ __global__ __launch_bounds__(kWave) void attn_portable_kernel(AttnArgs a) {
       float acc[HM];
 #pragma unroll
       for (int h = 0; h < HM; ++h) acc[h] = o[h][i] * alpha[h];
-      for (int32_t tok = 0; tok < nv; ++tok) {
-        const float vt = load_elem(vb, (row0 + tok) * a.v_row + c);
+      for (int32_t t0 = 0; t0 < nv; t0 += kPortBatch) {
+        float vv[kPortBatch];
 #pragma unroll
-        for (int h = 0; h < HM; ++h)
-          if (h < H) acc[h] = fmaf(s_p[h][tok], vt, acc[h]);
+        for (int u = 0; u < kPortBatch; ++u)
+          vv[u] = load_elem(vb, (row0 + min(t0 + u, nv - 1)) * a.v_row + c);
+#pragma unroll
+        for (int u = 0; u < kPortBatch; ++u) {
+          if (t0 + u < nv) {
+#pragma unroll
+            for (int h = 0; h < HM; ++h)
+              if (h < H) acc[h] = fmaf(s_p[h][t0 + u], vv[u], acc[h]);
+          }
+        }
       }
 #pragma unroll
       for (int h = 0; h < HM; ++h) o[h][i] = acc[h];

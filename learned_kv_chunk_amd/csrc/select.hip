@@ -39,15 +39,16 @@ hipError_t launch_select_t(const lsa_shape& s, const float* scores, const int32_
 
 }  // namespace
 
-// 1024 threads with at most 8 keys each up to 8192 chunks (compact code, one
-// barrier per radix pass), more keys per thread beyond.
+// Four keys per thread (one 16-byte load) and as few waves as that allows up
+// to 4096 chunks, then 1024 threads with more keys each (measured fastest for
+// 2048 and 8192 chunks).
 hipError_t launch_select(const lsa_shape& s, const float* scores, const int32_t* chunk_off,
                          const int32_t* sel_off, int32_t* sel_idx, hipStream_t st) {
   const int32_t n = s.max_chunks;
 #define LSA_SEL(T_, K_) \
   if (n <= (T_) * (K_)) return launch_select_t<T_, K_>(s, scores, chunk_off, sel_off, sel_idx, st);
-  LSA_SEL(256, 1) LSA_SEL(512, 1) LSA_SEL(1024, 1) LSA_SEL(1024, 2) LSA_SEL(1024, 4)
-  LSA_SEL(1024, 8) LSA_SEL(1024, 16) LSA_SEL(1024, 32) LSA_SEL(1024, 64)
+  LSA_SEL(256, 1) LSA_SEL(256, 4) LSA_SEL(512, 4) LSA_SEL(1024, 4) LSA_SEL(1024, 8)
+  LSA_SEL(1024, 16) LSA_SEL(1024, 32) LSA_SEL(1024, 64)
 #undef LSA_SEL
   return hipErrorNotSupported;
 }

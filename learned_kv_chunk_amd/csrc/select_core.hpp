@@ -9,10 +9,10 @@
 // scores each ([t*KPT, t*KPT+KPT)) as order-preserving 32-bit keys.  An
 // MSB-first radix select runs four 8-bit digit passes, each into its own LDS
 // histogram.  In the first pass (sign and top exponent bits: few distinct
-// digits) lanes with equal digits are matched with eight ballots and one lane
-// per digit adds the group's count, so no two lanes of a wave hit the same
-// LDS word; later passes only see keys that share the digits chosen so far
-// and add directly.  After a pass every wave reads the 256 counts (four per
+// digits) the lanes holding the first participating lane's digit (usually the
+// wave's most common one) add their count once, so few lanes of a wave hit the
+// same LDS word; later passes only see keys that share the digits chosen so
+// far and add directly.  After a pass every wave reads the 256 counts (four per
 // lane), scans them with DPP row shifts and lane reads, and finds the digit
 // holding the k-th largest key without another barrier.  A block-wide
 // exclusive scan of (#keys > T, #keys == T) then places every kept chunk at
@@ -87,8 +87,21 @@ __device__ __forceinline__ void select_topk_block(const float* __restrict__ scor
   const int tid = threadIdx.x;
   uint32_t key[KPT];
   float sv[KPT];
+  // all loads in flight; 16-byte loads where the stream's scores are aligned
+  if (KPT % 4 == 0 && (reinterpret_cast<uintptr_t>(scores) & 15u) == 0 && (tid + 1) * KPT <= n) {
+    const float4* v = reinterpret_cast<const float4*>(scores + tid * KPT);
 #pragma unroll
-  for (int i = 0; i < KPT; ++i) sv[i] = scores[min(tid * KPT + i, n - 1)];  // all loads in flight
+    for (int i = 0; i < KPT / 4; ++i) {
+      const float4 f = v[i];
+      sv[4 * i] = f.x;
+      sv[4 * i + 1] = f.y;
+      sv[4 * i + 2] = f.z;
+      sv[4 * i + 3] = f.w;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) sv[i] = scores[min(tid * KPT + i, n - 1)];
+  }
 #pragma unroll
   for (int i = 0; i < KPT; ++i) key[i] = (tid * KPT + i < n) ? order_key(sv[i]) : 0u;
   for (int i = tid; i < 4 * 256; i += THREADS) (&lds.hist[0][0])[i] = 0u;
@@ -107,15 +120,15 @@ __device__ __forceinline__ void select_topk_block(const float* __restrict__ scor
       const uint64_t pm = __ballot(part);
       if (pm == 0) continue;
       if (pass == 0) {
-        uint64_t same = pm;
-#pragma unroll
-        for (int bit = 0; bit < 8; ++bit) {
-          const bool on = (d >> bit) & 1u;
-          const uint64_t m = __ballot(on);
-          same &= on ? m : ~m;
+        // the leading digit is shared by most lanes: the lanes holding the
+        // first participating lane's digit add as one, the others directly
+        const uint32_t lead = __builtin_amdgcn_readlane(d, __ffsll(static_cast<long long>(pm)) - 1);
+        const uint64_t same = __ballot(part && d == lead);
+        if (part && d == lead) {
+          if ((same & below) == 0) atomicAdd(&hist[d], static_cast<uint32_t>(__popcll(same)));
+        } else if (part) {
+          atomicAdd(&hist[d], 1u);
         }
-        if (part && (same & below) == 0)
-          atomicAdd(&hist[d], static_cast<uint32_t>(__popcll(same)));
       } else if (part) {
         atomicAdd(&hist[d], 1u);
       }
