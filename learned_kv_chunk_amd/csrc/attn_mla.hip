@@ -272,8 +272,8 @@ __device__ __forceinline__ void softmax_pv(const unsigned char* __restrict__ kt,
 __global__ __launch_bounds__(kMlaThreads, 1) void attn_mla_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned char smem[kBufs * kBufBytes];
   __shared__ __attribute__((aligned(16))) f32x4 s_xch[kMlaWaves][kWave];  // S^T halves
-  __shared__ int32_t s_plan[3];
   __shared__ int32_t s_slot[kMaxRunSlots];  // the run's kept-chunk indices
+  __shared__ AttnRun s_run;
 
   const int tid = threadIdx.x;
   const int wave = tid / kWave;
@@ -282,34 +282,19 @@ __global__ __launch_bounds__(kMlaThreads, 1) void attn_mla_kernel(AttnArgs a) {
   const int hg = wave >> 1;    // head group: heads 16 hg .. 16 hg + 15
   const int half = wave & 1;   // token half of S^T and column half of O^T
 
-  if (wave == 0) {
-    int32_t b, local;
-    StreamSplit sp;
-    find_stream_of_wg(a.sel_off, a.B, a.tiles_per_chunk, a.per, a.target, blockIdx.x, &b,
-                      &local, &sp);
-    if (lane == 0) {
-      s_plan[0] = b;
-      s_plan[1] = local * sp.per;                       // first tile
-      s_plan[2] = min(sp.tiles, (local + 1) * sp.per);  // end tile
-    }
-  }
-  __syncthreads();
-  const int32_t b = s_plan[0];
-  if (b < 0) return;
+  const AttnRun run = attn_prologue(a, s_slot, &s_run);
+  if (run.b < 0) return;
+  const int32_t b = run.b;
   const int32_t tpc = a.tiles_per_chunk, C = a.C, H = a.H;
-  const int32_t sel0 = a.sel_off[b];
-  const int32_t t_begin = s_plan[1];
-  const int32_t t_end = s_plan[2];
-  const int32_t slot_first = t_begin / tpc;
-  const int32_t nslots = (t_end - 1) / tpc - slot_first + 1;
-  for (int32_t i = tid; i < min(nslots, kMaxRunSlots); i += kMlaThreads)
-    s_slot[i] = a.sel_idx[sel0 + slot_first + i];
-  const int64_t tb = a.tok_off[b];
-  const int64_t len = a.tok_off[b + 1] - tb;
+  const int32_t sel0 = run.sel0;
+  const int32_t t_begin = run.t_begin;
+  const int32_t t_end = run.t_end;
+  const int32_t slot_first = run.slot_first;
+  const int64_t tb = run.tb;
+  const int64_t len = run.len;
   const int64_t last_chunk = len > 0 ? (len - 1) / C : 0;
   const int head = hg * 16 + r16;
   const bool active = hg * 16 < H;  // wave-uniform
-  __syncthreads();
 
   // tile t of the run: an empty tile (past the end of a partial chunk) points
   // at its chunk's first row with nvalid = 0; a kept index outside [0, N_b)

@@ -17,10 +17,13 @@
 // per-wave LDS buffer because the second product contracts over tokens,
 // which are strided in memory.  Each wave software-pipelines its tiles: the
 // next tile's loads are in flight while the current one is computed.
-// A workgroup's waves (eight, two per SIMD, for up to 16 heads) take
-// interleaved tiles of one run, then merge their
-// (max, sum, output) states through LDS into one partial result, which the
-// merge kernel (attn_common.hip) combines with the stream's other partials.
+// For up to 16 heads a workgroup has eight waves (two per SIMD, so one wave's
+// loads are in flight while the other computes); a wave serving two head
+// groups needs the registers of a whole SIMD, so up to 32 heads use four
+// waves, and up to 64 heads two teams of two such waves.  The waves of a team
+// take interleaved tiles of the workgroup's run, then merge their (max, sum,
+// output) states through LDS into one partial result, which the merge kernel
+// (attn_common.hip) combines with the stream's other partials.
 #include <math.h>
 
 #include "lsa_internal.hpp"
@@ -171,8 +174,8 @@ __device__ __forceinline__ void compute_tile(const TileRegs<D>& r, int32_t nvali
 
 constexpr int cmax(int a, int b) { return a > b ? a : b; }
 
-// Waves per workgroup: 8 (two per SIMD) when one head group leaves room for
-// two waves' registers per SIMD, else 4.
+// Waves per workgroup: eight (two per SIMD) when a wave serves one head group,
+// four when it serves two (their registers allow one wave per SIMD).
 template <int NHG>
 constexpr int mqa_waves() { return NHG == 1 ? 8 : 4; }
 
@@ -222,67 +225,62 @@ __device__ __forceinline__ void merge_state(const unsigned char* base, float (&m
   }
 }
 
-template <int D, int NHG>
+// Each wave serves NHG groups of 16 heads.  The workgroup's waves form HS
+// teams; team t serves head groups t*NHG .. t*NHG + NHG - 1 and its waves
+// interleave the run's tiles among themselves, so a tile is read once per team
+// (HS = 1 except for more than 32 heads).
+template <int D, int NHG, int HS>
 __global__ __launch_bounds__(mqa_waves<NHG>() * kWave, NHG == 1 ? 2 : 1) void attn_mqa_kernel(
     AttnArgs a) {
   using L = MqaLds<D, NHG>;
   constexpr int NW = L::kWaves;
+  constexpr int WPG = NW / HS;  // waves per team
   constexpr int kThreads = NW * kWave;
   __shared__ __attribute__((aligned(16))) unsigned char smem[L::kBytes];
-  __shared__ int32_t s_plan[3];
   __shared__ int32_t s_slot[kMaxRunSlots];  // the run's kept-chunk indices
+  __shared__ AttnRun s_run;
 
   const int tid = threadIdx.x;
   const int wave = tid / kWave;
   const int lane = tid & (kWave - 1);
   const int r16 = lane & 15, g = lane >> 4;
+  const int grp = wave / WPG;  // team of this wave
+  const int wl = wave % WPG;   // index among the team's waves
 
-  if (wave == 0) {
-    int32_t b, local;
-    StreamSplit sp;
-    find_stream_of_wg(a.sel_off, a.B, a.tiles_per_chunk, a.per, a.target, blockIdx.x, &b,
-                      &local, &sp);
-    if (lane == 0) {
-      s_plan[0] = b;
-      s_plan[1] = local * sp.per;                    // first tile
-      s_plan[2] = min(sp.tiles, (local + 1) * sp.per);  // end tile
-    }
-  }
-  __syncthreads();
-  const int32_t b = s_plan[0];
-  if (b < 0) return;
+  const AttnRun run = attn_prologue(a, s_slot, &s_run);
+  if (run.b < 0) return;
+  const int32_t b = run.b;
   const int32_t tpc = a.tiles_per_chunk, C = a.C, H = a.H;
-  const int32_t sel0 = a.sel_off[b];
-  const int32_t t_begin = s_plan[1];
-  const int32_t t_end = s_plan[2];
-  const int32_t slot_first = t_begin / tpc;
-  const int32_t nslots = (t_end - 1) / tpc - slot_first + 1;
-  for (int32_t i = tid; i < min(nslots, kMaxRunSlots); i += kThreads)
-    s_slot[i] = a.sel_idx[sel0 + slot_first + i];
-  const int64_t tb = a.tok_off[b];
-  const int64_t len = a.tok_off[b + 1] - tb;
+  const int32_t sel0 = run.sel0;
+  const int32_t t_begin = run.t_begin;
+  const int32_t t_end = run.t_end;
+  const int32_t slot_first = run.slot_first;
+  const int64_t tb = run.tb;
+  const int64_t len = run.len;
   const int64_t last_chunk = len > 0 ? (len - 1) / C : 0;
 
-  // Q^T operand: lane holds Q[head hg*16 + lane%16][s*32 + 8*(lane/16) + 0..7]
+  // Q^T operand: lane holds Q[head][s*32 + 8*(lane/16) + 0..7] for the heads
+  // (grp*NHG + hg)*16 + lane%16 of its team
+  const int head0 = grp * NHG * 16 + r16;
   const uint16_t* __restrict__ qb = static_cast<const uint16_t*>(a.q);
   bf16x8 qf[NHG][D / 32];
 #pragma unroll
   for (int hg = 0; hg < NHG; ++hg) {
-    const int head = hg * 16 + r16;
-    const u32x4* src =
-        reinterpret_cast<const u32x4*>(qb + (static_cast<int64_t>(b) * H + head) * D) + g;
+    const int head = head0 + hg * 16;
+    const u32x4* src = reinterpret_cast<const u32x4*>(
+                           qb + (static_cast<int64_t>(b) * H + min(head, H - 1)) * D) + g;
 #pragma unroll
     for (int s = 0; s < D / 32; ++s)
       qf[hg][s] = as_bf16x8(head < H ? src[s * 4] : u32x4{0u, 0u, 0u, 0u});
   }
-  __syncthreads();
 
-  // Tile i of this wave is t_begin + wave + NW*i.  An empty tile (past the end
+  // Tile i of this wave is t_begin + wl + WPG*i.  An empty tile (past the end
   // of a partial chunk) points at its chunk's first row with nvalid = 0.
-  const int32_t n_mine = (t_end - t_begin - wave + NW - 1) / NW;
+  // A team whose heads all lie past H (only with HS > 1) skips the work.
+  const int32_t n_mine = grp * NHG * 16 < H ? (t_end - t_begin - wl + WPG - 1) / WPG : 0;
   auto tile_info = [&](int32_t i) {
     TileInfo ti;
-    const int32_t t = t_begin + wave + NW * i;
+    const int32_t t = t_begin + wl + WPG * i;
     const int32_t j = t / tpc;
     const int32_t sub = t - j * tpc;
     // a kept index outside [0, N_b) (a violated precondition) is clamped so
@@ -319,45 +317,44 @@ __global__ __launch_bounds__(mqa_waves<NHG>() * kWave, NHG == 1 ? 2 : 1) void at
 
   // Software pipeline, two register sets: the loads of tile i+1 are in flight
   // while tile i is computed.  Past the last tile the prefetch repeats the last
-  // tile (an L2 hit) so that every iteration issues the same loads.
+  // tile (a cache hit) so that every step issues the same loads.
   if (n_mine > 0) {
+    auto step = [&](TileRegs<D>& rc, const TileInfo& ic, TileRegs<D>& rn, TileInfo& in,
+                    int32_t next) {
+      in = tile_info(min(next, n_mine - 1));
+      issue_tile<D>(kb, vb, a.k_row, a.v_row, in, rn, lane);
+      __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the compute
+      compute_tile<D, NHG>(rc, ic.nvalid, qf, m, l, o, sv, a.scale_log2, lane);
+    };
     TileRegs<D> ra, rb;
     TileInfo ia = tile_info(0), ib;
     issue_tile<D>(kb, vb, a.k_row, a.v_row, ia, ra, lane);
     for (int32_t i = 0;; i += 2) {
-      ib = tile_info(min(i + 1, n_mine - 1));
-      issue_tile<D>(kb, vb, a.k_row, a.v_row, ib, rb, lane);
-      __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the compute
-      compute_tile<D, NHG>(ra, ia.nvalid, qf, m, l, o, sv, a.scale_log2, lane);
+      step(ra, ia, rb, ib, i + 1);
       if (i + 1 >= n_mine) break;
-      ia = tile_info(min(i + 2, n_mine - 1));
-      issue_tile<D>(kb, vb, a.k_row, a.v_row, ia, ra, lane);
-      __builtin_amdgcn_sched_barrier(0);
-      compute_tile<D, NHG>(rb, ib.nvalid, qf, m, l, o, sv, a.scale_log2, lane);
+      step(rb, ib, ra, ia, i + 2);
       if (i + 2 >= n_mine) break;
     }
   }
 
-  // tree-merge the waves' states into wave 0 (halving the live waves per round)
+  // tree-merge the states of each head group's waves into its first wave
+  // (halving the live waves per round; a group's slots follow its index)
 #pragma unroll
-  for (int stride = NW / 2; stride >= 2; stride /= 2) {
+  for (int stride = WPG / 2; stride >= 1; stride /= 2) {
     __syncthreads();
-    if (wave >= stride && wave < 2 * stride)
-      store_state<D, NHG>(smem + (wave - stride) * L::kStateBytes, m, l, o, lane);
+    if (wl >= stride && wl < 2 * stride)
+      store_state<D, NHG>(smem + (grp * (WPG / 2) + wl - stride) * L::kStateBytes, m, l, o, lane);
     __syncthreads();
-    if (wave < stride) merge_state<D, NHG>(smem + wave * L::kStateBytes, m, l, o, lane);
+    if (wl < stride)
+      merge_state<D, NHG>(smem + (grp * (WPG / 2) + wl) * L::kStateBytes, m, l, o, lane);
   }
-  __syncthreads();
-  if (wave == 1) store_state<D, NHG>(smem, m, l, o, lane);
-  __syncthreads();
   const int64_t wg = blockIdx.x;
-  if (wave == 0) {
-    merge_state<D, NHG>(smem, m, l, o, lane);
+  if (wl == 0) {
 #pragma unroll
     for (int hg = 0; hg < NHG; ++hg) {
-      const float lt = xor32_sum(xor16_sum(l[hg]));
-      const int head = hg * 16 + r16;
+      const int head = head0 + hg * 16;
       if (head >= H) continue;
+      const float lt = xor32_sum(xor16_sum(l[hg]));
       if (g == 0) {
         a.ws_m[wg * H + head] = m[hg];
         a.ws_l[wg * H + head] = lt;
@@ -367,7 +364,6 @@ __global__ __launch_bounds__(mqa_waves<NHG>() * kWave, NHG == 1 ? 2 : 1) void at
         *reinterpret_cast<f32x4*>(a.ws_o + (wg * H + head) * D + cg * 16 + 4 * g) = o[hg][cg];
     }
   }
-
 }
 
 template <int D>
@@ -375,11 +371,11 @@ hipError_t launch_mqa_d(const AttnArgs& a, int64_t grid, hipStream_t st) {
   const int nhg = (a.H + 15) / 16;
   dim3 g(static_cast<uint32_t>(grid));
   if (nhg == 1)
-    hipLaunchKernelGGL((attn_mqa_kernel<D, 1>), g, dim3(mqa_waves<1>() * kWave), 0, st, a);
+    hipLaunchKernelGGL((attn_mqa_kernel<D, 1, 1>), g, dim3(mqa_waves<1>() * kWave), 0, st, a);
   else if (nhg == 2)
-    hipLaunchKernelGGL((attn_mqa_kernel<D, 2>), g, dim3(mqa_waves<2>() * kWave), 0, st, a);
+    hipLaunchKernelGGL((attn_mqa_kernel<D, 2, 1>), g, dim3(mqa_waves<2>() * kWave), 0, st, a);
   else if (nhg <= 4)
-    hipLaunchKernelGGL((attn_mqa_kernel<D, 4>), g, dim3(mqa_waves<4>() * kWave), 0, st, a);
+    hipLaunchKernelGGL((attn_mqa_kernel<D, 2, 2>), g, dim3(mqa_waves<2>() * kWave), 0, st, a);
   else return hipErrorNotSupported;
   return hipGetLastError();
 }

@@ -142,14 +142,19 @@ __device__ __forceinline__ StreamSplit stream_split(const int32_t* sel_off, int3
 __device__ __forceinline__ void find_stream_of_wg(const int32_t* sel_off, int32_t B,
                                                   int32_t tpc, int32_t per, int32_t target,
                                                   int32_t wg, int32_t* b_out, int32_t* local_out,
-                                                  StreamSplit* split_out) {
+                                                  StreamSplit* split_out,
+                                                  int32_t* sel0_out = nullptr) {
   const int lane = threadIdx.x & (kWave - 1);
   const int32_t total_tiles = (sel_off[B] - sel_off[0]) * tpc;
   int32_t base = 0;  // workgroups of streams before the current 64-stream window
   for (int32_t s0 = 0; s0 < B; s0 += kWave) {
     const int32_t s = s0 + lane;
     StreamSplit sp = {0, 0, 1};
-    if (s < B) sp = stream_split(sel_off, s, tpc, per, target, total_tiles);
+    int32_t so = 0;
+    if (s < B) {
+      sp = stream_split(sel_off, s, tpc, per, target, total_tiles);
+      so = sel_off[s];
+    }
     const int32_t incl = static_cast<int32_t>(wave_inclusive_scan(static_cast<uint32_t>(sp.wgs)));
     const int32_t total = __builtin_amdgcn_readlane(incl, kWave - 1);
     if (wg < base + total) {
@@ -161,6 +166,7 @@ __device__ __forceinline__ void find_stream_of_wg(const int32_t* sel_off, int32_
       split_out->tiles = __builtin_amdgcn_readlane(sp.tiles, first);
       split_out->wgs = __builtin_amdgcn_readlane(sp.wgs, first);
       split_out->per = __builtin_amdgcn_readlane(sp.per, first);
+      if (sel0_out) *sel0_out = __builtin_amdgcn_readlane(so, first);
       return;
     }
     base += total;
@@ -168,6 +174,49 @@ __device__ __forceinline__ void find_stream_of_wg(const int32_t* sel_off, int32_
   *b_out = -1;
   *local_out = 0;
   *split_out = StreamSplit{0, 0, 1};
+  if (sel0_out) *sel0_out = 0;
+}
+
+// The run of tiles one attention workgroup owns.
+struct AttnRun {
+  int32_t b;           // stream, or -1 when the workgroup has no work
+  int32_t t_begin;     // tiles [t_begin, t_end) of the stream's kept tokens
+  int32_t t_end;
+  int32_t sel0;        // sel_off[b]
+  int32_t slot_first;  // the run's first kept chunk, counted within the stream
+  int64_t tb;          // tok_off[b]
+  int64_t len;         // L_b
+};
+
+// Workgroup prologue of the attention kernels, called by every thread; ends
+// with a barrier.  Wave 0 finds the workgroup's stream and run (one round trip
+// over sel_off), then loads the stream's token range and the run's kept-chunk
+// indices together (a second round trip) into `s_slot` (kMaxRunSlots words)
+// and `s_run`, which every thread then reads.
+__device__ __forceinline__ AttnRun attn_prologue(const AttnArgs& a, int32_t* s_slot,
+                                                 AttnRun* s_run) {
+  if (threadIdx.x < kWave) {
+    const int lane = threadIdx.x;
+    const int32_t tpc = a.tiles_per_chunk;
+    int32_t b, local, sel0;
+    StreamSplit sp;
+    find_stream_of_wg(a.sel_off, a.B, tpc, a.per, a.target, blockIdx.x, &b, &local, &sp, &sel0);
+    AttnRun r = {b, 0, 0, 0, 0, 0, 0};
+    if (b >= 0) {
+      r.t_begin = local * sp.per;
+      r.t_end = min(sp.tiles, (local + 1) * sp.per);
+      r.sel0 = sel0;
+      r.slot_first = r.t_begin / tpc;
+      const int32_t nslots = min((r.t_end - 1) / tpc - r.slot_first + 1, kMaxRunSlots);
+      const int64_t t0 = a.tok_off[b], t1 = a.tok_off[b + 1];
+      for (int32_t i = lane; i < nslots; i += kWave) s_slot[i] = a.sel_idx[sel0 + r.slot_first + i];
+      r.tb = t0;
+      r.len = t1 - t0;
+    }
+    if (lane == 0) *s_run = r;
+  }
+  __syncthreads();
+  return *s_run;
 }
 
 // Run by one full wave: index of the first workgroup of stream b and its
