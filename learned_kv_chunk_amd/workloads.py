@@ -22,6 +22,15 @@ does not depend on the block size used to draw its neighbours or on threads):
   standard deviation (1/sqrt(d));
 * bf16 configurations: values are drawn in fp32 and rounded to bf16 with
   round-to-nearest-even; both the oracle and the GPU read those bit patterns.
+
+Inputs of the multi-head compressed-key scorer (``make_mh_inputs``): per
+stream, Hs head queries of dimension D (Gaussian, std 1/sqrt(D), bf16) and Hs
+non-negative head weights (|Gaussian| / Hs, fp32); per chunk a record of D
+float8 e4m3 key values and a float32 scale: the key is Gaussian (std 1),
+the scale is max|key| / 448 and the values are key / scale rounded to the
+nearest e4m3 value (ties to the even code).  Needle chunks (the same positions
+as the embedding needles) get the key 3 sqrt(D) u, with u the unit vector of
+the weighted head-query sum sum_h w_h q_h.
 """
 from __future__ import annotations
 
@@ -36,7 +45,8 @@ import numpy as np
 DTYPES = ("f32", "bf16")
 
 # purpose tags of the random streams
-_P_LENGTHS, _P_QIDX, _P_EMB, _P_NEEDLE_POS, _P_NEEDLE_DIR, _P_K, _P_V, _P_Q = range(8)
+(_P_LENGTHS, _P_QIDX, _P_EMB, _P_NEEDLE_POS, _P_NEEDLE_DIR, _P_K, _P_V, _P_Q,
+ _P_MH_Q, _P_MH_W, _P_MH_KEY) = range(11)
 
 _ROWS_PER_BLOCK = 1 << 14
 
@@ -274,3 +284,61 @@ def small_variant(name: str, **overrides) -> Config:
     if "lengths" in overrides and "batch" not in overrides:
         kw["batch"] = len(overrides["lengths"])
     return base.replace(**kw)
+
+
+# ----------------------------------------------------------------------------- float8 inputs
+def _e4m3_nonneg_values() -> np.ndarray:
+    """Values of the non-negative finite float8 e4m3 codes 0x00..0x7e, in code
+    order (which is increasing value order)."""
+    codes = np.arange(0x7F)
+    e = codes >> 3
+    m = codes & 7
+    return np.where(e == 0, m * 2.0 ** -9, (8 + m) * 2.0 ** (e.astype(np.float64) - 10))
+
+
+_E4M3 = _e4m3_nonneg_values()
+
+
+def to_e4m3_codes(x: np.ndarray) -> np.ndarray:
+    """Round values with |x| <= 448 to the nearest float8 e4m3 code (ties to
+    the even code); returns uint8 codes."""
+    x = np.asarray(x, dtype=np.float64)
+    a = np.abs(x)
+    if (a > 448.0).any() or np.isnan(a).any():
+        raise ValueError("float8 e4m3 encoding needs finite |x| <= 448")
+    hi = np.clip(np.searchsorted(_E4M3, a), 1, len(_E4M3) - 1)
+    lo = hi - 1
+    dlo = a - _E4M3[lo]
+    dhi = _E4M3[hi] - a
+    take_hi = (dhi < dlo) | ((dhi == dlo) & (hi % 2 == 0))
+    code = np.where(take_hi, hi, lo).astype(np.uint8)
+    return np.where(x < 0, code | 0x80, code).astype(np.uint8)  # sign kept, also on -0
+
+
+def make_mh_inputs(w: Workload, heads: int = 128, head_dim: int = 128):
+    """Head queries [B][heads][head_dim] (bf16 bit patterns), head weights
+    [B][heads] (fp32) and compressed-key records [sum N][head_dim + 4] (uint8)
+    for the multi-head scorer, aligned with the workload's chunks."""
+    cfg = w.cfg
+    B = cfg.batch
+    n_total = int(w.chunk_off[-1])
+    q = np.stack([_rng(cfg, _P_MH_Q, b).standard_normal((heads, head_dim), dtype=np.float32)
+                  / np.float32(math.sqrt(head_dim)) for b in range(B)])
+    wt = np.stack([np.abs(_rng(cfg, _P_MH_W, b).standard_normal(heads, dtype=np.float32))
+                   / np.float32(heads) for b in range(B)])
+    q_bits = to_bf16_bits(q)
+    rec = np.empty((n_total, head_dim + 4), dtype=np.uint8)
+    for b in range(B):
+        r0, r1 = int(w.chunk_off[b]), int(w.chunk_off[b + 1])
+        keys = _rng(cfg, _P_MH_KEY, b).standard_normal((r1 - r0, head_dim))
+        pos = w.needles[b]
+        if len(pos):
+            dvec = (wt[b][:, None].astype(np.float64) * bf16_bits_to_f32(q_bits[b])).sum(0)
+            keys[pos] = 3.0 * math.sqrt(head_dim) * dvec / np.linalg.norm(dvec)
+        scale = (np.abs(keys).max(axis=1) / 448.0).astype(np.float32)
+        scale = np.where(scale > 0, scale, np.float32(1.0))
+        # |key / scale| <= 448 up to the rounding of the scale to fp32
+        vals = np.clip(keys / scale.astype(np.float64)[:, None], -448.0, 448.0)
+        rec[r0:r1, :head_dim] = to_e4m3_codes(vals)
+        rec[r0:r1, head_dim:] = scale.astype("<f4").view(np.uint8).reshape(-1, 4)
+    return q_bits, wt.astype(np.float32), rec

@@ -14,6 +14,10 @@
  *   oracle_attention  softmax attention restricted to the kept chunks' tokens
  *                     (review section 3-2-3 steps 6-7), computed with a full
  *                     max pass then a weighted-sum pass.
+ *   oracle_score_fp8mh  the multi-head scorer of float8 compressed-key chunk
+ *                     records (review sections 3-2-1, 3-2-2, 4-3): decode
+ *                     each key value, dot with every head's query, scale,
+ *                     ReLU, weighted sum over heads.
  */
 #include "lsa_oracle.h"
 
@@ -175,6 +179,45 @@ void oracle_attention(int32_t B, int32_t H, int32_t dqk, int32_t dv, int32_t v_a
     free(x);
     free(row);
   }
+}
+
+double oracle_fp8_e4m3(uint8_t code) {
+  const int sign = code >> 7;
+  const int e = (code >> 3) & 15;
+  const int m = code & 7;
+  double v;
+  if (e == 15 && m == 7) return NAN;
+  if (e == 0)
+    v = ldexp((double)m, -9);             /* subnormal: m / 8 * 2^(1 - 7) */
+  else
+    v = ldexp((double)(8 + m), e - 10);   /* (1 + m / 8) * 2^(e - 7) */
+  return sign ? -v : v;
+}
+
+void oracle_score_fp8mh(int32_t B, int32_t Hs, int32_t D, int32_t dtype, const void* q,
+                        const float* w, const uint8_t* rec, const int32_t* chunk_off,
+                        double* scores) {
+  const int64_t rec_bytes = (int64_t)D + 4;
+  double* k = (double*)malloc(sizeof(double) * (size_t)D);
+  for (int32_t b = 0; b < B; ++b) {
+    for (int64_t n = chunk_off[b]; n < chunk_off[b + 1]; ++n) {
+      const uint8_t* r = rec + n * rec_bytes;
+      float cf;
+      memcpy(&cf, r + D, sizeof cf);
+      for (int32_t d = 0; d < D; ++d) k[d] = oracle_fp8_e4m3(r[d]);
+      double x = 0.0;
+      for (int32_t h = 0; h < Hs; ++h) {
+        double dot = 0.0;
+        for (int32_t d = 0; d < D; ++d)
+          dot += elem(q, ((int64_t)b * Hs + h) * D + d, dtype) * k[d];
+        double a = (double)cf * dot;
+        if (a < 0.0) a = 0.0;
+        x += (double)w[(int64_t)b * Hs + h] * a;
+      }
+      scores[n] = x;
+    }
+  }
+  free(k);
 }
 
 int32_t oracle_max_threads(void) {

@@ -23,6 +23,9 @@
  *                 paragraph on gathering only the selected chunks).
  *   attention  -- softmax attention of each query head restricted to the
  *                 tokens of the kept chunks (review section 3-2-3, steps 6-7).
+ *   score_fp8mh -- the released retriever's multi-head scorer over float8
+ *                 compressed-key chunk records (review sections 3-2-1, 3-2-2
+ *                 and 4-3).
  *
  * Element encodings: ORACLE_F32 arrays hold IEEE-754 binary32 values;
  * ORACLE_BF16 arrays hold bfloat16 bit patterns (the upper 16 bits of a
@@ -79,6 +82,23 @@ void oracle_attention(int32_t B, int32_t H, int32_t dqk, int32_t dv, int32_t v_a
                       int32_t dtype, int32_t C, double scale, const void* Q, const void* K,
                       const void* V, const int64_t* tok_off, const int32_t* sel_idx,
                       const int32_t* sel_off, double* out, double* lse, int32_t nthreads);
+
+/* Value of one float8 e4m3 code (the OCP E4M3 encoding with no infinities:
+ * sign, 4 exponent bits with bias 7, 3 mantissa bits; exponent 0 encodes
+ * m * 2^-9; the all-ones exponent and mantissa encode NaN), exactly. */
+double oracle_fp8_e4m3(uint8_t code);
+
+/* Multi-head relevance of compressed-key chunk records (dimensionstp review,
+ * section 3-2-1 record table and section 3-2-2 scorer; section 4-3 shapes).
+ * Record n of the table, rec_bytes = D + 4 bytes: D float8 e4m3 key values
+ * k[0..D) followed by a little-endian float32 dequantisation scale c.  For
+ * stream b and each of its chunks:
+ *   x = sum_h w[b][h] * max(0, c * sum_d q[b][h][d] * k[d])
+ * q: [B][Hs][D] of element type dtype; w: [B][Hs] float32.  The sigmoid of
+ * the pages' formula is monotone and is not applied: x is the ranking score. */
+void oracle_score_fp8mh(int32_t B, int32_t Hs, int32_t D, int32_t dtype, const void* q,
+                        const float* w, const uint8_t* rec, const int32_t* chunk_off,
+                        double* scores);
 
 /* Threads an OpenMP region may use here (1 when built without OpenMP). */
 int32_t oracle_max_threads(void);

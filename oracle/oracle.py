@@ -10,9 +10,11 @@ Step definitions (cited to the pages' sections, see ``lsa_oracle.c``):
              "Key points"; review section 3-2-4; arXiv abstract v2)
   select     top-k keep set per stream (review section 3-2-3 step 5)
   gather     resident pool of kept chunks (wiki note flowchart; molayo
-             explainer "selective gather")
+             explainer, gathering only the selected chunks)
   attention  softmax attention over the kept chunks' tokens (review section
              3-2-3 steps 6-7)
+  score_fp8mh  multi-head relevance of float8 compressed-key chunk records
+             (review sections 3-2-1, 3-2-2 and 4-3)
   decode     the review's decode loop (section 3-2-3 steps 3-7): re-score and
              re-select every ``reindex_every`` steps, attend every step.
 """
@@ -65,6 +67,10 @@ def _load():
         lib.oracle_attention.argtypes = [i32, i32, i32, i32, i32, i32, i32, f64,
                                          P, P, P, P, P, P, P, P, i32]
         lib.oracle_attention.restype = None
+        lib.oracle_fp8_e4m3.argtypes = [ctypes.c_uint8]
+        lib.oracle_fp8_e4m3.restype = f64
+        lib.oracle_score_fp8mh.argtypes = [i32, i32, i32, i32, P, P, P, P, P]
+        lib.oracle_score_fp8mh.restype = None
         lib.oracle_max_threads.argtypes = []
         lib.oracle_max_threads.restype = i32
         _lib = lib
@@ -103,6 +109,28 @@ def score(q: np.ndarray, emb: np.ndarray, chunk_off: np.ndarray) -> np.ndarray:
     assert emb.shape[1] == D and emb.shape[0] == chunk_off[-1]
     out = np.empty(int(chunk_off[-1]), dtype=np.float64)
     _load().oracle_score(B, D, dt, _ptr(q), _ptr(emb), _ptr(chunk_off), _ptr(out))
+    return out
+
+
+def fp8_e4m3(code: int) -> float:
+    """Exact value of one float8 e4m3 code."""
+    return float(_load().oracle_fp8_e4m3(int(code) & 0xFF))
+
+
+def score_fp8mh(q_heads: np.ndarray, head_w: np.ndarray, rec: np.ndarray,
+                chunk_off: np.ndarray) -> np.ndarray:
+    """fp64 multi-head scores [sum N_b] of compressed-key chunk records.
+    q_heads: [B][Hs][D] float32 or bf16 patterns; head_w: [B][Hs] float32;
+    rec: [sum N_b][D + 4] uint8 (D float8 e4m3 values, then a float32 scale)."""
+    q, dt = _elements(q_heads)
+    w = np.ascontiguousarray(head_w, dtype=np.float32)
+    rec = np.ascontiguousarray(rec, dtype=np.uint8)
+    chunk_off = np.ascontiguousarray(chunk_off, dtype=np.int32)
+    B, Hs, D = q.shape
+    assert w.shape == (B, Hs) and rec.shape == (int(chunk_off[-1]), D + 4)
+    out = np.empty(int(chunk_off[-1]), dtype=np.float64)
+    _load().oracle_score_fp8mh(B, Hs, D, dt, _ptr(q), _ptr(w), _ptr(rec), _ptr(chunk_off),
+                               _ptr(out))
     return out
 
 

@@ -367,3 +367,100 @@ def test_workload_shapes_of_the_five_configs():
     n = (L + 63) // 64
     k = wl.keep_counts(cfg, n)
     assert all(oracle.keep_count(int(a), 135, 1000, True) == int(b) for a, b in zip(n, k))
+
+
+# ----------------------------------------------------------------------------- multi-head fp8 scorer
+def test_fp8_e4m3_decoding_matches_torch_and_the_format_anchors():
+    # every code against torch's float8_e4m3fn, plus values fixed by the format
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).float().numpy().astype(np.float64)
+    mine = np.array([oracle.fp8_e4m3(c) for c in codes])
+    nan = np.isnan(ref)
+    assert (np.isnan(mine) == nan).all() and nan.sum() == 2  # 0x7f and 0xff
+    np.testing.assert_array_equal(mine[~nan], ref[~nan])
+    anchors = {0x00: 0.0, 0x01: 2.0 ** -9, 0x07: 7 * 2.0 ** -9, 0x08: 2.0 ** -6, 0x38: 1.0,
+               0x3C: 1.5, 0x40: 2.0, 0x7E: 448.0, 0xB8: -1.0, 0xFE: -448.0}
+    for c, v in anchors.items():
+        assert oracle.fp8_e4m3(c) == v, hex(c)
+
+
+def _mh_brute_force(q_bits, w, rec, chunk_off):
+    # independent route: torch's fp8 decode, float64 matrix products
+    B, Hs, D = q_bits.shape
+    q = wl.bf16_bits_to_f32(q_bits).astype(np.float64)
+    k = torch.from_numpy(np.ascontiguousarray(rec[:, :D])).view(torch.float8_e4m3fn).double().numpy()
+    c = np.ascontiguousarray(rec[:, D:]).view("<f4").reshape(-1).astype(np.float64)
+    out = np.empty(len(rec))
+    for b in range(B):
+        r0, r1 = chunk_off[b], chunk_off[b + 1]
+        dots = k[r0:r1] @ q[b].T                       # [n, Hs]
+        out[r0:r1] = np.maximum(c[r0:r1, None] * dots, 0.0) @ w[b].astype(np.float64)
+    return out
+
+
+def _mh_case(B=2, Hs=16, D=32, n=(9, 5), seed=3):
+    g = np.random.default_rng(seed)
+    q = wl.to_bf16_bits(g.standard_normal((B, Hs, D)).astype(np.float32))
+    w = np.abs(g.standard_normal((B, Hs))).astype(np.float32)
+    chunk_off = np.concatenate([[0], np.cumsum(n)]).astype(np.int32)
+    keys = g.standard_normal((int(chunk_off[-1]), D))
+    scale = (np.abs(keys).max(1) / 448).astype(np.float32)
+    rec = np.empty((len(keys), D + 4), np.uint8)
+    rec[:, :D] = wl.to_e4m3_codes(np.clip(keys / scale[:, None].astype(np.float64), -448, 448))
+    rec[:, D:] = scale.astype("<f4").view(np.uint8).reshape(-1, 4)
+    return q, w, rec, chunk_off
+
+
+def test_fp8_multihead_score_equals_brute_force():
+    q, w, rec, co = _mh_case()
+    np.testing.assert_allclose(oracle.score_fp8mh(q, w, rec, co), _mh_brute_force(q, w, rec, co),
+                               rtol=1e-12, atol=1e-12)
+    # fp32 head queries and a negative scale take the same definition
+    g = np.random.default_rng(9)
+    q32 = g.standard_normal((1, 4, 16)).astype(np.float32)
+    rec = np.zeros((3, 20), np.uint8)
+    rec[:, :16] = g.integers(0, 256, size=(3, 16)).astype(np.uint8) & 0x77  # finite codes
+    rec[:, 16:] = np.array([0.5, -2.0, 3.0], "<f4").view(np.uint8).reshape(-1, 4)
+    w = np.array([[1.0, 0.25, 2.0, 0.0]], np.float32)
+    co = np.array([0, 3], np.int32)
+    k = torch.from_numpy(rec[:, :16].copy()).view(torch.float8_e4m3fn).double().numpy()
+    c = np.array([0.5, -2.0, 3.0])
+    ref = np.maximum(c[:, None] * (k @ q32[0].astype(np.float64).T), 0) @ w[0].astype(np.float64)
+    np.testing.assert_allclose(oracle.score_fp8mh(q32, w, rec, co), ref, rtol=1e-12, atol=1e-12)
+
+
+def test_fp8_multihead_score_relu_weights_and_scale():
+    q, w, rec, co = _mh_case(B=1, Hs=8, D=32, n=(6,))
+    base = oracle.score_fp8mh(q, w, rec, co)
+    # positive homogeneity in the per-chunk scale
+    rec2 = rec.copy()
+    c = rec[:, 32:].copy().view("<f4").reshape(-1)
+    rec2[:, 32:] = (2 * c).astype("<f4").view(np.uint8).reshape(-1, 4)
+    np.testing.assert_allclose(oracle.score_fp8mh(q, w, rec2, co), 2 * base, rtol=1e-12)
+    # flipping every key flips every head's dot: the score becomes the weighted
+    # sum of the heads the ReLU dropped before
+    rec3 = rec.copy()
+    rec3[:, :32] ^= 0x80
+    kq = _mh_brute_force(q, np.ones_like(w), rec, co)  # sum of positive parts, unit weights
+    k = torch.from_numpy(rec[:, :32].copy()).view(torch.float8_e4m3fn).double().numpy()
+    dots = c[:, None].astype(np.float64) * (k @ wl.bf16_bits_to_f32(q[0]).astype(np.float64).T)
+    np.testing.assert_allclose(oracle.score_fp8mh(q, np.ones_like(w), rec3, co),
+                               np.maximum(-dots, 0).sum(1), rtol=1e-12, atol=1e-15)
+    np.testing.assert_allclose(kq, np.maximum(dots, 0).sum(1), rtol=1e-12, atol=1e-15)
+    # a one-hot weight picks a single head's positive part
+    oh = np.zeros_like(w)
+    oh[0, 5] = 1.0
+    np.testing.assert_allclose(oracle.score_fp8mh(q, oh, rec, co), np.maximum(dots[:, 5], 0),
+                               rtol=1e-12, atol=1e-15)
+    # zero weights give zero scores
+    assert (oracle.score_fp8mh(q, np.zeros_like(w), rec, co) == 0).all()
+
+
+def test_fp8_multihead_needles_are_kept():
+    w = wl.make_workload(wl.small_variant("cfg2"))
+    q, hw, rec = wl.make_mh_inputs(w)
+    s = oracle.score_fp8mh(q, hw, rec, w.chunk_off)
+    sel = oracle.select(s, w.chunk_off, w.sel_off)
+    for b in range(w.B):
+        kept = set(sel[w.sel_off[b]:w.sel_off[b + 1]].tolist())
+        assert set(w.needles[b].tolist()) <= kept
