@@ -147,6 +147,84 @@ def run_copy(args):
                       "gbs": 2 * nbytes / us / 1e3}), flush=True)
 
 
+def run_scorer(args):
+    """Times lsa_score_fp8_multihead (the released retriever's multi-head scorer
+    over float8 compressed-key records) on the chunks of a workload, cold: each
+    launch reads a different copy of the records."""
+    import numpy as np
+    import torch
+
+    from learned_kv_chunk_amd import device as dev
+    from learned_kv_chunk_amd import lsa
+    from learned_kv_chunk_amd import workloads as wl
+    from oracle import oracle
+
+    cfg = wl.CONFIGS[args.config]
+    w = wl.make_workload(cfg)
+    heads, head_dim = 128, 128
+    q_bits, hw, rec = wl.make_mh_inputs(w, heads=heads, head_dim=head_dim)
+    shape = dev.problem_shape(w)
+    qd = torch.from_numpy(q_bits.view(np.int16)).view(torch.bfloat16).cuda()
+    wd = torch.from_numpy(hw).cuda()
+    co = torch.from_numpy(w.chunk_off).cuda()
+    scores = torch.empty(shape.total_chunks, dtype=torch.float32, device="cuda")
+    n_total = int(w.chunk_off[-1])
+    launch_bytes = rec.nbytes + q_bits.nbytes + hw.nbytes + 4 * n_total
+    reps = args.replicas or max(1, math.ceil(2 * MALL_BYTES / launch_bytes) + 1)
+    recs = [torch.from_numpy(rec).cuda() for _ in range(min(reps, 256))]
+    reps = len(recs)
+    for r in recs[:3]:
+        lsa.score_fp8_multihead(shape, qd, wd, r, co, scores)
+    torch.cuda.synchronize()
+    # a launch takes a few microseconds of device time, less than the host
+    # needs to issue it through the binding: the K timed launches are captured
+    # once in a HIP graph (the scorer allocates and clears nothing) and the
+    # graph is replayed, so that the events see device time only
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for i in range(args.steps):
+            lsa.score_fp8_multihead(shape, qd, wd, recs[i % reps], co, scores)
+    graph.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / args.steps
+    flops = 2.0 * n_total * heads * head_dim
+    line = {
+        "metric": "fp8 multi-head chunk scoring: records scored per second",
+        "value": n_total / us * 1e6, "unit": "records/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": 3, "ms_per_step": us / 1e3, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "fp8 keys, bf16 queries, fp32 accumulate",
+        "data": "synthetic",
+        "config": {"workload": f"{args.config} chunks: {n_total} records of {head_dim + 4} B, "
+                               f"{heads} heads x {head_dim}", "replicas": reps,
+                   "timing": "HIP graph of the timed launches, replayed once"},
+        "roofline": {"kernel": "score_mh_kernel", "bound": "hbm",
+                     "achieved": launch_bytes / us / 1e3, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": launch_bytes / us / 1e3 / HBM_PEAK_GBS, "traffic": None,
+                     "algorithmic_bytes_per_launch": launch_bytes, "avg_launch_us": us,
+                     "mfma_tflops": flops / us / 1e6},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        threads = max(1, len(os.sched_getaffinity(0)))
+        t0 = time.perf_counter()
+        calls = 0
+        while time.perf_counter() - t0 < args.cpu_seconds:
+            oracle.score_fp8mh(q_bits, hw, rec, w.chunk_off)
+            calls += 1
+        el = time.perf_counter() - t0
+        line["cpu_baseline"] = {"value": calls * n_total / el, "unit": "records/s", "cores": 1,
+                                "kind": "oracle",
+                                "sample": f"{calls} full scoring pass(es) of all {n_total} records "
+                                          f"in {el:.1f} s, single-threaded fp64 C oracle "
+                                          f"({threads} cores available)"}
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -159,7 +237,7 @@ def main():
     ap.add_argument("--tiles-per-block", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--mode", choices=["step", "copy"], default="step")
+    ap.add_argument("--mode", choices=["step", "copy", "scorer"], default="step")
     ap.add_argument("--copy-mib", type=int, default=1024)
     args = ap.parse_args()
 
@@ -180,6 +258,9 @@ def main():
     torch.cuda.set_device(0)
     if args.mode == "copy":
         run_copy(args)
+        return
+    if args.mode == "scorer":
+        run_scorer(args)
         return
 
     cfg = wl.CONFIGS[args.config]

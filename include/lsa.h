@@ -130,6 +130,30 @@ lsa_status lsa_score(const lsa_shape* shape, const void* q_idx_dev, const void* 
                      const int32_t* chunk_off_dev, float* scores_dev, void* hip_stream);
 
 /* ---------------------------------------------------------------------------
+ * Multi-head relevance of float8 compressed-key chunk records.  Dimensionstp
+ * review, section 3-2-1 (the compressed-key record: head_dim float8 e4m3 key
+ * values followed by a float32 per-chunk dequantisation scale, 132 bytes for
+ * head_dim 128), section 3-2-2 (the released retriever's scorer) and section
+ * 4-3 (128 heads of dimension 128).  For stream b and each of its chunks:
+ *   scores_dev[chunk_off[b] + n] =
+ *       sum_h head_w[b][h] * max(0, scale_n * sum_d q_heads[b][h][d] * k_n[d])
+ * where k_n[d] is the d-th float8 e4m3 value of record chunk_off[b] + n (the
+ * OCP E4M3 encoding: no infinities, 0x7f / 0xff are NaN) and scale_n its
+ * float32 scale (little-endian).  The sigmoid of the pages' formula is
+ * monotone and is not applied; the result ranks chunks for lsa_select_topk.
+ * q_heads_dev: [B][num_heads][head_dim] bf16 (shape->dtype must be bf16),
+ * 16-byte aligned; head_w_dev: [B][num_heads] fp32; records_dev:
+ * [total_chunks][head_dim + 4] bytes, 4-byte aligned; scores_dev:
+ * [total_chunks] fp32.  Only batch, chunk_size, max_chunks and the totals of
+ * the shape are used.  Supported: head_dim 64 or 128 and num_heads 16, 32, 64
+ * or 128 (LSA_ERR_UNSUPPORTED otherwise).
+ * ------------------------------------------------------------------------- */
+lsa_status lsa_score_fp8_multihead(const lsa_shape* shape, int32_t num_heads, int32_t head_dim,
+                                   const void* q_heads_dev, const float* head_w_dev,
+                                   const void* records_dev, const int32_t* chunk_off_dev,
+                                   float* scores_dev, void* hip_stream);
+
+/* ---------------------------------------------------------------------------
  * Top-k keep set.  Dimensionstp review section 3-2-3 step 5 (top-k keep
  * mask).  For each stream, keeps the k_b chunks ranked first by (score
  * descending, chunk index ascending); NaN ranks below every number and -0.0

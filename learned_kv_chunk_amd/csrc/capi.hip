@@ -154,6 +154,26 @@ lsa_status lsa_score(const lsa_shape* shape, const void* q_idx_dev, const void* 
                                  static_cast<hipStream_t>(hip_stream)));
 }
 
+lsa_status lsa_score_fp8_multihead(const lsa_shape* shape, int32_t num_heads, int32_t head_dim,
+                                   const void* q_heads_dev, const float* head_w_dev,
+                                   const void* records_dev, const int32_t* chunk_off_dev,
+                                   float* scores_dev, void* hip_stream) {
+  lsa_status st = check_common(shape);
+  if (st != LSA_OK) return st;
+  if (num_heads < 1 || head_dim < 1) return LSA_ERR_INVALID_ARGUMENT;
+  if (shape->dtype != LSA_DTYPE_BF16 || !score_mh_supported(num_heads, head_dim))
+    return LSA_ERR_UNSUPPORTED;
+  if (!q_heads_dev || !head_w_dev || !records_dev || !chunk_off_dev || !scores_dev)
+    return LSA_ERR_INVALID_ARGUMENT;
+  if (!aligned(q_heads_dev, 16) || !aligned(head_w_dev, 4) || !aligned(records_dev, 4) ||
+      !aligned(chunk_off_dev, 4) || !aligned(scores_dev, 4))
+    return LSA_ERR_INVALID_ARGUMENT;
+  (void)hipGetLastError();
+  return hip_status(launch_score_mh(*shape, num_heads, head_dim, q_heads_dev, head_w_dev,
+                                    records_dev, chunk_off_dev, scores_dev,
+                                    static_cast<hipStream_t>(hip_stream)));
+}
+
 lsa_status lsa_select_topk(const lsa_shape* shape, const float* scores_dev,
                            const int32_t* chunk_off_dev, const int32_t* sel_off_dev,
                            int32_t* sel_idx_dev, void* hip_stream) {

@@ -88,6 +88,8 @@ _SIGNATURES = {
     "lsa_keep_count": ([_I32, _I32, _I32, _I32], _I32),
     "lsa_workspace_bytes": ([ctypes.POINTER(Shape)], ctypes.c_size_t),
     "lsa_score": ([ctypes.POINTER(Shape), _P, _P, _P, _P, _P], _I32),
+    "lsa_score_fp8_multihead": ([ctypes.POINTER(Shape), _I32, _I32, _P, _P, _P, _P, _P, _P],
+                                _I32),
     "lsa_select_topk": ([ctypes.POINTER(Shape), _P, _P, _P, _P, _P], _I32),
     "lsa_gather_chunks": ([ctypes.POINTER(Shape), _P, _P, _P, _P, _P, _P, _P, _P], _I32),
     "lsa_sparse_decode_attn": ([ctypes.POINTER(Shape), _I32, _P, _P, _P, _P, _P, _P, _P, _P,
@@ -212,6 +214,28 @@ def score(shape: ProblemShape, q_idx, emb, chunk_off, scores=None, stream=None) 
     _dev(scores, "scores", torch.float32, 1)
     _check(library().lsa_score(ctypes.byref(shape.c()), _ptr(q_idx), _ptr(emb), _ptr(chunk_off),
                                _ptr(scores), _stream(stream)), "lsa_score")
+    return scores
+
+
+def score_fp8_multihead(shape: ProblemShape, q_heads, head_w, records, chunk_off, scores=None,
+                        stream=None) -> torch.Tensor:
+    """lsa_score_fp8_multihead: fp32 multi-head scores [total_chunks] of
+    compressed-key records.  q_heads [B][heads][head_dim] bf16, head_w
+    [B][heads] fp32, records [total_chunks][head_dim + 4] uint8."""
+    _dev(q_heads, "q_heads", torch.bfloat16, 3)
+    _dev(head_w, "head_w", torch.float32, 2)
+    _dev(records, "records", torch.uint8, 2)
+    _dev(chunk_off, "chunk_off", torch.int32, 1)
+    B, heads, head_dim = q_heads.shape
+    if head_w.shape != (B, heads) or records.shape != (shape.total_chunks, head_dim + 4):
+        raise ValueError("q_heads / head_w / records shapes do not agree")
+    if scores is None:
+        scores = torch.empty(shape.total_chunks, dtype=torch.float32, device=records.device)
+    _dev(scores, "scores", torch.float32, 1)
+    _check(library().lsa_score_fp8_multihead(ctypes.byref(shape.c()), heads, head_dim,
+                                             _ptr(q_heads), _ptr(head_w), _ptr(records),
+                                             _ptr(chunk_off), _ptr(scores), _stream(stream)),
+           "lsa_score_fp8_multihead")
     return scores
 
 

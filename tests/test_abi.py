@@ -23,7 +23,7 @@ pytestmark = pytest.mark.skipif(not os.path.exists(lsa.LIB_PATH),
 def declared_entry_points():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(lsa_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(lsa_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_every_declared_symbol_is_exported():
@@ -180,3 +180,21 @@ def test_workspace_holds_counters_and_every_partial():
             wgs = -(-tiles // per) + B
             need = wgs * H * (dv + 2) * 4
             assert lsa.workspace_bytes(s) >= need, (per, B, k, H, dv)
+
+
+def _mh(s, heads=128, dim=128, q=DUMMY, w=DUMMY, rec=DUMMY, co=DUMMY, out=DUMMY):
+    return lsa.library().lsa_score_fp8_multihead(ctypes.byref(s.c()), heads, dim, q, w, rec, co,
+                                                 out, None)
+
+
+def test_multihead_scorer_validation():
+    s = shape()
+    assert _mh(s, q=None) == lsa.LSA_ERR_INVALID_ARGUMENT
+    assert _mh(s, out=None) == lsa.LSA_ERR_INVALID_ARGUMENT
+    assert _mh(s, q=ctypes.c_void_p(0x100008)) == lsa.LSA_ERR_INVALID_ARGUMENT   # 16-byte aligned
+    assert _mh(s, rec=ctypes.c_void_p(0x100002)) == lsa.LSA_ERR_INVALID_ARGUMENT  # 4-byte aligned
+    assert _mh(s, heads=0) == lsa.LSA_ERR_INVALID_ARGUMENT
+    assert _mh(shape(batch=0)) == lsa.LSA_ERR_INVALID_ARGUMENT
+    assert _mh(s, heads=48) == lsa.LSA_ERR_UNSUPPORTED
+    assert _mh(s, dim=96) == lsa.LSA_ERR_UNSUPPORTED
+    assert _mh(shape(dtype=torch.float32)) == lsa.LSA_ERR_UNSUPPORTED
