@@ -315,22 +315,25 @@ def to_e4m3_codes(x: np.ndarray) -> np.ndarray:
     return np.where(x < 0, code | 0x80, code).astype(np.uint8)  # sign kept, also on -0
 
 
-def make_mh_inputs(w: Workload, heads: int = 128, head_dim: int = 128):
+def make_mh_inputs(w: Workload, heads: int = 128, head_dim: int = 128, layer: int = 0):
     """Head queries [B][heads][head_dim] (bf16 bit patterns), head weights
     [B][heads] (fp32) and compressed-key records [sum N][head_dim + 4] (uint8)
-    for the multi-head scorer, aligned with the workload's chunks."""
+    for the multi-head scorer, aligned with the workload's chunks.  `layer`
+    selects independent draws for one layer of an ensemble; the needles sit
+    at the same chunks in every layer."""
     cfg = w.cfg
     B = cfg.batch
     n_total = int(w.chunk_off[-1])
-    q = np.stack([_rng(cfg, _P_MH_Q, b).standard_normal((heads, head_dim), dtype=np.float32)
+    q = np.stack([_rng(cfg, _P_MH_Q, b, layer).standard_normal((heads, head_dim),
+                                                                 dtype=np.float32)
                   / np.float32(math.sqrt(head_dim)) for b in range(B)])
-    wt = np.stack([np.abs(_rng(cfg, _P_MH_W, b).standard_normal(heads, dtype=np.float32))
+    wt = np.stack([np.abs(_rng(cfg, _P_MH_W, b, layer).standard_normal(heads, dtype=np.float32))
                    / np.float32(heads) for b in range(B)])
     q_bits = to_bf16_bits(q)
     rec = np.empty((n_total, head_dim + 4), dtype=np.uint8)
     for b in range(B):
         r0, r1 = int(w.chunk_off[b]), int(w.chunk_off[b + 1])
-        keys = _rng(cfg, _P_MH_KEY, b).standard_normal((r1 - r0, head_dim))
+        keys = _rng(cfg, _P_MH_KEY, b, layer).standard_normal((r1 - r0, head_dim))
         pos = w.needles[b]
         if len(pos):
             dvec = (wt[b][:, None].astype(np.float64) * bf16_bits_to_f32(q_bits[b])).sum(0)
@@ -342,3 +345,10 @@ def make_mh_inputs(w: Workload, heads: int = 128, head_dim: int = 128):
         rec[r0:r1, :head_dim] = to_e4m3_codes(vals)
         rec[r0:r1, head_dim:] = scale.astype("<f4").view(np.uint8).reshape(-1, 4)
     return q_bits, wt.astype(np.float32), rec
+
+
+def make_mh_layer_inputs(w: Workload, layers: int = 3, heads: int = 128, head_dim: int = 128):
+    """make_mh_inputs for `layers` layers, stacked layer-major: queries
+    [L][B][heads][head_dim], weights [L][B][heads], records [L][sum N][head_dim + 4]."""
+    parts = [make_mh_inputs(w, heads, head_dim, layer=l) for l in range(layers)]
+    return tuple(np.ascontiguousarray(np.stack([p[i] for p in parts])) for i in range(3))

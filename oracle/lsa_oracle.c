@@ -18,6 +18,11 @@
  *                     records (review sections 3-2-1, 3-2-2, 4-3): decode
  *                     each key value, dot with every head's query, scale,
  *                     ReLU, weighted sum over heads.
+ *   oracle_score_fp8mh_layers  the same per layer, combined by max or mean
+ *                     (review section 3-2-2, the layer ensemble).
+ *   oracle_select_threshold  threshold keep mask, capped by a top-k, with a
+ *                     dense fallback for a stream where no chunk passes
+ *                     (review section 3-2-3 step 5, sections 4-3 and 5-1).
  */
 #include "lsa_oracle.h"
 
@@ -226,4 +231,57 @@ int32_t oracle_max_threads(void) {
 #else
   return 1;
 #endif
+}
+
+void oracle_score_fp8mh_layers(int32_t L, int32_t combine, int32_t B, int32_t Hs, int32_t D,
+                               int32_t dtype, const void* q, const float* w, const uint8_t* rec,
+                               const int32_t* chunk_off, double* scores) {
+  const int64_t total = chunk_off[B];
+  const size_t esize = dtype == ORACLE_BF16 ? 2 : 4;
+  double* x = (double*)malloc(sizeof(double) * (size_t)(total > 0 ? total : 1));
+  for (int32_t l = 0; l < L; ++l) {
+    const char* ql = (const char*)q + (size_t)l * (size_t)B * (size_t)Hs * (size_t)D * esize;
+    const float* wl = w + (int64_t)l * B * Hs;
+    const uint8_t* rl = rec + (int64_t)l * total * ((int64_t)D + 4);
+    oracle_score_fp8mh(B, Hs, D, dtype, ql, wl, rl, chunk_off, x);
+    for (int64_t n = 0; n < total; ++n) {
+      if (l == 0) scores[n] = x[n];
+      else if (combine == ORACLE_COMBINE_MAX) scores[n] = x[n] > scores[n] ? x[n] : scores[n];
+      else scores[n] += x[n];
+    }
+  }
+  if (combine == ORACLE_COMBINE_MEAN)
+    for (int64_t n = 0; n < total; ++n) scores[n] /= (double)L;
+  free(x);
+}
+
+void oracle_select_threshold(int32_t B, const double* scores, const int32_t* chunk_off,
+                             double tau, int32_t max_keep, int32_t* sel_off, int32_t* sel_idx,
+                             int32_t* fallback) {
+  sel_off[0] = 0;
+  for (int32_t b = 0; b < B; ++b) {
+    const int32_t n = chunk_off[b + 1] - chunk_off[b];
+    const double* s = scores + chunk_off[b];
+    int32_t* out = sel_idx + sel_off[b];
+    int32_t kept = 0;
+    for (int32_t i = 0; i < n; ++i)
+      if (s[i] >= tau) out[kept++] = i;
+    fallback[b] = (kept == 0 && n > 0) ? 1 : 0;
+    if (fallback[b]) {
+      for (int32_t i = 0; i < n; ++i) out[i] = i;
+      kept = n;
+    } else if (max_keep > 0 && kept > max_keep) {
+      ranked* r = (ranked*)malloc(sizeof(ranked) * (size_t)kept);
+      for (int32_t i = 0; i < kept; ++i) {
+        r[i].s = s[out[i]];
+        r[i].n = out[i];
+      }
+      qsort(r, (size_t)kept, sizeof(ranked), rank_cmp);
+      for (int32_t i = 0; i < max_keep; ++i) out[i] = r[i].n;
+      qsort(out, (size_t)max_keep, sizeof(int32_t), int_cmp);
+      free(r);
+      kept = max_keep;
+    }
+    sel_off[b + 1] = sel_off[b] + kept;
+  }
 }

@@ -100,6 +100,34 @@ void oracle_score_fp8mh(int32_t B, int32_t Hs, int32_t D, int32_t dtype, const v
                         const float* w, const uint8_t* rec, const int32_t* chunk_off,
                         double* scores);
 
+/* Multi-layer ensemble of the multi-head scorer (dimensionstp review,
+ * section 3-2-2: the released retriever scores chunks in several CSA layers,
+ * each with its own weights, and combines the per-layer scores by max or
+ * mean).  Layer l has its own q [B][Hs][D], w [B][Hs] and record table
+ * [total][D + 4], stored layer after layer (q, w and rec point at layer 0).
+ * combine ORACLE_COMBINE_MAX: x = max_l x_l; ORACLE_COMBINE_MEAN: x = (sum_l
+ * x_l) / L, each x_l as oracle_score_fp8mh computes it. */
+#define ORACLE_COMBINE_MAX 0
+#define ORACLE_COMBINE_MEAN 1
+void oracle_score_fp8mh_layers(int32_t L, int32_t combine, int32_t B, int32_t Hs, int32_t D,
+                               int32_t dtype, const void* q, const float* w, const uint8_t* rec,
+                               const int32_t* chunk_off, double* scores);
+
+/* Threshold keep mask with a dense fallback (dimensionstp review, section
+ * 3-2-3 step 5: the keep mask comes from a top-k or a threshold; sections 4-3
+ * and 5-1: exact-retrieval tasks need a threshold fallback).  Per stream b:
+ *   pass_b = { n : scores[n] >= tau }            (NaN never passes)
+ *   if pass_b is empty: keep every chunk of the stream, fallback[b] = 1
+ *   else if max_keep > 0 and |pass_b| > max_keep: keep the max_keep chunks of
+ *        pass_b ranked first by (score descending, index ascending)
+ *   else keep pass_b; fallback[b] = 0.
+ * Kept indices are written ascending to sel_idx[sel_off[b] ..), with sel_off
+ * [B+1] the running totals of the kept counts (sel_off[0] = 0); sel_idx needs
+ * room for chunk_off[B] entries. */
+void oracle_select_threshold(int32_t B, const double* scores, const int32_t* chunk_off,
+                             double tau, int32_t max_keep, int32_t* sel_off, int32_t* sel_idx,
+                             int32_t* fallback);
+
 /* Threads an OpenMP region may use here (1 when built without OpenMP). */
 int32_t oracle_max_threads(void);
 

@@ -15,6 +15,11 @@ Step definitions (cited to the pages' sections, see ``lsa_oracle.c``):
              3-2-3 steps 6-7)
   score_fp8mh  multi-head relevance of float8 compressed-key chunk records
              (review sections 3-2-1, 3-2-2 and 4-3)
+  score_fp8mh_layers  the same over several layers, combined by max or
+             mean (review section 3-2-2, the layer ensemble)
+  select_threshold  threshold keep mask capped by a top-k, with a dense
+             fallback where no chunk passes (review section 3-2-3 step 5,
+             sections 4-3 and 5-1)
   decode     the review's decode loop (section 3-2-3 steps 3-7): re-score and
              re-select every ``reindex_every`` steps, attend every step.
 """
@@ -71,6 +76,10 @@ def _load():
         lib.oracle_fp8_e4m3.restype = f64
         lib.oracle_score_fp8mh.argtypes = [i32, i32, i32, i32, P, P, P, P, P]
         lib.oracle_score_fp8mh.restype = None
+        lib.oracle_score_fp8mh_layers.argtypes = [i32, i32, i32, i32, i32, i32, P, P, P, P, P]
+        lib.oracle_score_fp8mh_layers.restype = None
+        lib.oracle_select_threshold.argtypes = [i32, P, P, f64, i32, P, P, P]
+        lib.oracle_select_threshold.restype = None
         lib.oracle_max_threads.argtypes = []
         lib.oracle_max_threads.restype = i32
         _lib = lib
@@ -132,6 +141,43 @@ def score_fp8mh(q_heads: np.ndarray, head_w: np.ndarray, rec: np.ndarray,
     _load().oracle_score_fp8mh(B, Hs, D, dt, _ptr(q), _ptr(w), _ptr(rec), _ptr(chunk_off),
                                _ptr(out))
     return out
+
+
+COMBINE_MAX = 0
+COMBINE_MEAN = 1
+
+
+def score_fp8mh_layers(q_heads: np.ndarray, head_w: np.ndarray, rec: np.ndarray,
+                       chunk_off: np.ndarray, combine: int) -> np.ndarray:
+    """fp64 ensemble scores [sum N_b] over L layers: q_heads [L][B][Hs][D],
+    head_w [L][B][Hs], rec [L][sum N_b][D + 4]; combine COMBINE_MAX or
+    COMBINE_MEAN."""
+    q, dt = _elements(q_heads)
+    w = np.ascontiguousarray(head_w, dtype=np.float32)
+    rec = np.ascontiguousarray(rec, dtype=np.uint8)
+    chunk_off = np.ascontiguousarray(chunk_off, dtype=np.int32)
+    L, B, Hs, D = q.shape
+    assert w.shape == (L, B, Hs) and rec.shape == (L, int(chunk_off[-1]), D + 4)
+    assert combine in (COMBINE_MAX, COMBINE_MEAN)
+    out = np.empty(int(chunk_off[-1]), dtype=np.float64)
+    _load().oracle_score_fp8mh_layers(L, combine, B, Hs, D, dt, _ptr(q), _ptr(w), _ptr(rec),
+                                      _ptr(chunk_off), _ptr(out))
+    return out
+
+
+def select_threshold(scores: np.ndarray, chunk_off: np.ndarray, tau: float,
+                     max_keep: int = 0) -> tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """Threshold keep mask: (sel_off [B+1], ascending kept indices, fallback
+    flags [B]); see oracle_select_threshold."""
+    s = np.ascontiguousarray(scores, dtype=np.float64)
+    chunk_off = np.ascontiguousarray(chunk_off, dtype=np.int32)
+    B = len(chunk_off) - 1
+    sel_off = np.empty(B + 1, dtype=np.int32)
+    sel_idx = np.empty(max(1, int(chunk_off[-1])), dtype=np.int32)
+    fb = np.empty(B, dtype=np.int32)
+    _load().oracle_select_threshold(B, _ptr(s), _ptr(chunk_off), float(tau), int(max_keep),
+                                    _ptr(sel_off), _ptr(sel_idx), _ptr(fb))
+    return sel_off, sel_idx[:int(sel_off[-1])].copy(), fb
 
 
 def select(scores: np.ndarray, chunk_off: np.ndarray, sel_off: np.ndarray) -> np.ndarray:

@@ -464,3 +464,110 @@ def test_fp8_multihead_needles_are_kept():
     for b in range(w.B):
         kept = set(sel[w.sel_off[b]:w.sel_off[b + 1]].tolist())
         assert set(w.needles[b].tolist()) <= kept
+
+
+# --- threshold keep mask with dense fallback, and the layer ensemble ----------
+
+def _golden_threshold_case():
+    g = _golden("select_threshold.json")
+    streams = [[float(x) for x in s] for s in g["streams"]]
+    co = np.concatenate([[0], np.cumsum([len(s) for s in streams])]).astype(np.int32)
+    return g, np.array(sum(streams, []), np.float64), co
+
+
+def test_threshold_select_golden():
+    g, s, co = _golden_threshold_case()
+    for case in g["cases"]:
+        off, idx, fb = oracle.select_threshold(s, co, float(case["tau"]), case["max_keep"])
+        assert off.tolist() == case["sel_off"], case
+        assert idx.tolist() == case["sel_idx"], case
+        assert fb.tolist() == case["fallback"], case
+
+
+def test_threshold_select_properties_and_top_k_equivalence():
+    g = np.random.default_rng(21)
+    n = np.array([1, 7, 40, 64, 3, 100])
+    co = np.concatenate([[0], np.cumsum(n)]).astype(np.int32)
+    # few distinct values: heavy ties at and around the threshold
+    s = g.integers(0, 6, size=int(co[-1])).astype(np.float64) / 4
+    for tau in (-np.inf, 0.0, 0.5, 1.0, 1.25, 2.0):
+        for cap in (0, 1, 5, 1000):
+            off, idx, fb = oracle.select_threshold(s, co, tau, cap)
+            for b in range(len(n)):
+                sb = s[co[b]:co[b + 1]]
+                kept = idx[off[b]:off[b + 1]].tolist()
+                passing = [i for i in range(n[b]) if sb[i] >= tau]
+                assert fb[b] == (not passing)
+                if not passing:
+                    assert kept == list(range(n[b]))
+                elif cap and len(passing) > cap:
+                    # capped: exactly the top-cap set of the whole stream
+                    assert kept == oracle.select(sb, np.array([0, n[b]], np.int32),
+                                                 np.array([0, cap], np.int32)).tolist()
+                    assert _defining_property_holds(sb, cap, kept)
+                else:
+                    assert kept == passing
+
+
+def test_threshold_select_equals_top_k_at_the_kth_score():
+    # a threshold at the k-th largest of distinct scores keeps the top-k set
+    g = np.random.default_rng(5)
+    s = g.standard_normal(500)
+    co = np.array([0, 500], np.int32)
+    for k in (1, 17, 250, 500):
+        tau = np.sort(s)[::-1][k - 1]
+        _, idx, fb = oracle.select_threshold(s, co, tau)
+        assert fb.tolist() == [0]
+        assert idx.tolist() == oracle.select(s, co, np.array([0, k], np.int32)).tolist()
+
+
+def _mh_layers_case(L=3, **kw):
+    cases = [_mh_case(seed=40 + l, **kw) for l in range(L)]
+    q = np.stack([c[0] for c in cases])
+    w = np.stack([c[1] for c in cases])
+    rec = np.stack([c[2] for c in cases])
+    return q, w, rec, cases[0][3]
+
+
+def test_layer_ensemble_equals_brute_force_per_layer():
+    q, w, rec, co = _mh_layers_case()
+    per = np.stack([_mh_brute_force(q[l], w[l], rec[l], co) for l in range(3)])
+    np.testing.assert_allclose(oracle.score_fp8mh_layers(q, w, rec, co, oracle.COMBINE_MAX),
+                               per.max(0), rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(oracle.score_fp8mh_layers(q, w, rec, co, oracle.COMBINE_MEAN),
+                               per.mean(0), rtol=1e-12, atol=1e-12)
+
+
+def test_layer_ensemble_special_cases():
+    q, w, rec, co = _mh_layers_case(L=2)
+    one = oracle.score_fp8mh(q[0], w[0], rec[0], co)
+    for comb in (oracle.COMBINE_MAX, oracle.COMBINE_MEAN):
+        np.testing.assert_array_equal(oracle.score_fp8mh_layers(q[:1], w[:1], rec[:1], co, comb),
+                                      one)
+    # a layer with zero weights scores 0 <= every score: the max is the other layer
+    wz = w.copy()
+    wz[1] = 0
+    np.testing.assert_allclose(oracle.score_fp8mh_layers(q, wz, rec, co, oracle.COMBINE_MAX), one,
+                               rtol=1e-15)
+    # the mean of a layer and of its copy with weights doubled (exact in fp32)
+    # is 1.5 times the layer
+    q2, w2, r2 = np.stack([q[0], q[0]]), np.stack([w[0], 2 * w[0]]), np.stack([rec[0], rec[0]])
+    np.testing.assert_allclose(oracle.score_fp8mh_layers(q2, w2, r2, co, oracle.COMBINE_MEAN),
+                               1.5 * one, rtol=1e-12)
+
+
+def test_layer_ensemble_needles_pass_a_threshold():
+    # every planted needle scores above every other chunk in each layer, so a
+    # threshold between the two keeps the needles, and max and mean agree
+    w = wl.make_workload(wl.small_variant("cfg2"))
+    q, hw, rec = wl.make_mh_layer_inputs(w, layers=3)
+    for comb in (oracle.COMBINE_MAX, oracle.COMBINE_MEAN):
+        s = oracle.score_fp8mh_layers(q, hw, rec, w.chunk_off, comb)
+        for b in range(w.B):
+            sb = s[w.chunk_off[b]:w.chunk_off[b + 1]]
+            nd = w.needles[b]
+            rest = np.delete(sb, nd)
+            assert sb[nd].min() > rest.max()
+            tau = (sb[nd].min() + rest.max()) / 2
+            _, idx, fb = oracle.select_threshold(sb, np.array([0, len(sb)], np.int32), tau)
+            assert fb.tolist() == [0] and sorted(idx.tolist()) == sorted(nd.tolist())
