@@ -177,21 +177,10 @@ def run_scorer(args):
         lsa.score_fp8_multihead(shape, qd, wd, r, co, scores)
     torch.cuda.synchronize()
     # a launch takes a few microseconds of device time, less than the host
-    # needs to issue it through the binding: the K timed launches are captured
-    # once in a HIP graph (the scorer allocates and clears nothing) and the
-    # graph is replayed, so that the events see device time only
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
-        for i in range(args.steps):
-            lsa.score_fp8_multihead(shape, qd, wd, recs[i % reps], co, scores)
-    graph.replay()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    graph.replay()
-    e1.record()
-    torch.cuda.synchronize()
-    us = e0.elapsed_time(e1) * 1e3 / args.steps
+    # needs to issue it through the binding: the K timed launches are replayed
+    # from a HIP graph, so that the events see device time only
+    us = _graph_us(lambda i: lsa.score_fp8_multihead(shape, qd, wd, recs[i % reps], co, scores),
+                   args.steps)
     flops = 2.0 * n_total * heads * head_dim
     line = {
         "metric": "fp8 multi-head chunk scoring: records scored per second",
@@ -225,6 +214,163 @@ def run_scorer(args):
     print(json.dumps(line), flush=True)
 
 
+def _graph_us(fn, n):
+    """Average device time of fn(i), i = 0..n-1, captured once in a HIP graph
+    and replayed (the captured calls allocate and clear nothing)."""
+    import torch
+
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for i in range(n):
+            fn(i)
+    graph.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / n
+
+
+def run_retriever(args):
+    """Times the retriever-side decode step: the three-layer ensemble of the
+    float8 multi-head scorer (max), the threshold keep set with its dense
+    fallback, and sparse attention over the kept set the device produced.
+    Cold: each step reads a different copy of the records and of the K/V
+    history.  The steps are captured once in a HIP graph and replayed, so the
+    host's issue rate (four binding calls per step) is not measured."""
+    import numpy as np
+    import torch
+
+    from learned_kv_chunk_amd import device as dev
+    from learned_kv_chunk_amd import lsa
+    from learned_kv_chunk_amd import workloads as wl
+
+    cfg = wl.CONFIGS[args.config]
+    layers, heads, head_dim, keep = 3, 128, 128, 0.135
+    w = wl.make_workload(cfg)
+    q, hw, rec = wl.make_mh_layer_inputs(w, layers=layers, heads=heads, head_dim=head_dim)
+    base = dev.upload(w, "cuda")
+    shape = dev.problem_shape(w)
+    shape.max_k = shape.max_chunks        # the kept counts are known on the device only
+    shape.total_k = shape.total_chunks
+    B, n_total = w.B, int(w.chunk_off[-1])
+    qd = torch.from_numpy(q.view(np.int16)).view(torch.bfloat16).cuda()
+    wd = torch.from_numpy(hw).cuda()
+    co = base.chunk_off
+    scores = torch.empty(n_total, dtype=torch.float32, device="cuda")
+    sel_off = torch.empty(B + 1, dtype=torch.int32, device="cuda")
+    sel_idx = torch.empty(n_total, dtype=torch.int32, device="cuda")
+    fb = torch.empty(B, dtype=torch.int32, device="cuda")
+    tws = torch.empty(lsa.select_threshold_workspace_bytes(shape), dtype=torch.uint8,
+                      device="cuda")
+    out = torch.empty_like(base.out)
+    lse = torch.empty_like(base.lse)
+    aws = lsa.allocate_workspace(shape, "cuda")
+    rec0 = torch.from_numpy(rec).cuda()
+
+    # the threshold: the fp32 score at the (1 - keep) quantile of an untimed
+    # scoring pass, so that about `keep` of all chunks pass
+    lsa.score_fp8_multihead_layers(shape, qd, wd, rec0, co, lsa.COMBINE_MAX, scores)
+    torch.cuda.synchronize()
+    s_host = dev.to_host(scores)
+    tau = float(np.float32(np.quantile(s_host, 1.0 - keep)))
+    lsa.select_threshold(shape, scores, co, tau, 0, sel_off, sel_idx, fb, tws)
+    torch.cuda.synchronize()
+    off_h = dev.to_host(sel_off)
+    idx_h = dev.to_host(sel_idx)[:int(off_h[-1])]
+    C = cfg.chunk_size
+    ktok = 0
+    for b in range(B):
+        n = idx_h[off_h[b]:off_h[b + 1]].astype(np.int64)
+        ktok += int(np.minimum(C, w.lengths[b] - n * C).sum())
+    ab = algorithmic_bytes(w)
+    score_bytes = rec.nbytes + q.nbytes + hw.nbytes + 4 * n_total
+    thr_bytes = 2 * 4 * n_total + 4 * int(off_h[-1]) + 4 * (2 * B + 1)
+    attn_bytes = ktok * ab["row"] + ab["q"]
+    step_bytes = score_bytes + thr_bytes + attn_bytes + ab["o"]
+
+    reps = args.replicas or max(1, math.ceil(2 * MALL_BYTES / step_bytes) + 1)
+    recs = [rec0] + [rec0.clone() for _ in range(reps - 1)]
+    Ks = [base.K] + [base.K.clone() for _ in range(reps - 1)]
+    Vs = [base.V] + [None if base.V is None else base.V.clone() for _ in range(reps - 1)]
+    nq = 8
+    qs = [base.queries(t) for t in range(nq)]
+    torch.cuda.synchronize()
+
+    def score(i):
+        lsa.score_fp8_multihead_layers(shape, qd, wd, recs[i % reps], co, lsa.COMBINE_MAX, scores)
+
+    def select(i):
+        lsa.select_threshold(shape, scores, co, tau, 0, sel_off, sel_idx, fb, tws)
+
+    def attend(i):
+        lsa.sparse_decode_attn(shape, qs[i % nq], Ks[i % reps], Vs[i % reps], base.tok_off,
+                               sel_idx, sel_off, lsa.KV_STORE, out, lse, aws)
+
+    def step(i):
+        score(i)
+        select(i)
+        attend(i)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    us_step = _graph_us(step, args.steps)
+    us_score = _graph_us(score, args.steps)
+    us_select = _graph_us(select, args.steps)
+    us_attend = _graph_us(attend, args.steps)
+    score_gbs = score_bytes / us_score / 1e3
+    line = {
+        "metric": "retriever decode steps/sec at 128K ctx (3-layer fp8 multi-head score + "
+                  "threshold keep + sparse attn)",
+        "value": 1e6 / us_step, "unit": "steps/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": us_step / 1e3, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "fp8 keys + bf16 KV, fp32 accumulate",
+        "data": "synthetic",
+        "config": {"workload": f"{args.config}: {WORKLOAD_TEXT[args.config]}; {layers} layers of "
+                               f"{n_total} compressed-key records ({heads} heads x {head_dim}), "
+                               f"max ensemble, threshold at the {1 - keep:.3f} score quantile",
+                   "threshold": tau, "kept_chunks": int(off_h[-1]),
+                   "kept_fraction": int(off_h[-1]) / n_total,
+                   "fallback_streams": int(dev.to_host(fb).sum()), "replicas": reps,
+                   "timing": "HIP graph of the timed steps, replayed once"},
+        "phase_us": {"ensemble_score": us_score, "threshold_select": us_select,
+                     "attention_and_merge": us_attend},
+        "step_algorithmic_bytes": int(step_bytes),
+        "roofline": {"kernel": "score_mh_kernel (3-layer ensemble)", "bound": "hbm",
+                     "achieved": score_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": score_gbs / HBM_PEAK_GBS, "traffic": None,
+                     "algorithmic_bytes_per_launch": int(score_bytes),
+                     "avg_launch_us": us_score,
+                     "attention_gbs": attn_bytes / us_attend / 1e3},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        from oracle import oracle
+
+        threads = max(1, len(os.sched_getaffinity(0)))
+        t0 = time.perf_counter()
+        steps = 0
+        while True:
+            s = oracle.score_fp8mh_layers(q, hw, rec, w.chunk_off, oracle.COMBINE_MAX)
+            o_off, o_idx, _ = oracle.select_threshold(s, w.chunk_off, tau)
+            oracle.attention(w.queries(steps % 4), w.K, w.V, w.tok_off, o_idx, o_off,
+                             cfg.chunk_size, cfg.softmax_scale, dv=cfg.head_dim_v,
+                             nthreads=threads)
+            steps += 1
+            el = time.perf_counter() - t0
+            if el >= args.cpu_seconds:
+                break
+        line["cpu_baseline"] = {
+            "value": steps / el, "unit": "steps/s", "cores": threads, "kind": "oracle",
+            "sample": f"{steps} full retriever step(s) (all {B} streams) in {el:.1f} s: "
+                      f"single-threaded fp64 C ensemble scoring and threshold, attention "
+                      f"with OpenMP over (stream, head)"}
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -237,7 +383,7 @@ def main():
     ap.add_argument("--tiles-per-block", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--mode", choices=["step", "copy", "scorer"], default="step")
+    ap.add_argument("--mode", choices=["step", "copy", "scorer", "retriever"], default="step")
     ap.add_argument("--copy-mib", type=int, default=1024)
     args = ap.parse_args()
 
@@ -261,6 +407,9 @@ def main():
         return
     if args.mode == "scorer":
         run_scorer(args)
+        return
+    if args.mode == "retriever":
+        run_retriever(args)
         return
 
     cfg = wl.CONFIGS[args.config]

@@ -154,6 +154,32 @@ lsa_status lsa_score_fp8_multihead(const lsa_shape* shape, int32_t num_heads, in
                                    float* scores_dev, void* hip_stream);
 
 /* ---------------------------------------------------------------------------
+ * Layer ensemble of the multi-head scorer.  Dimensionstp review, section
+ * 3-2-2: the released retriever scores chunks in several CSA layers, each
+ * with its own weights and compressed keys, and combines the per-layer scores
+ * by max (close to a union of the layers' choices) or by mean.  Layer l's
+ * score x_l is what lsa_score_fp8_multihead computes from layer l's inputs:
+ *   combine LSA_COMBINE_MAX:  scores_dev[i] = max_l x_l[i]
+ *   combine LSA_COMBINE_MEAN: scores_dev[i] = (x_0[i] + ... + x_{L-1}[i]) / L
+ *                             (fp32 sum in layer order, then one division)
+ * The inputs are stored layer after layer: q_heads_dev
+ * [num_layers][B][num_heads][head_dim] bf16, head_w_dev
+ * [num_layers][B][num_heads] fp32, records_dev
+ * [num_layers][total_chunks][head_dim + 4] bytes; alignment, shapes and
+ * support as for lsa_score_fp8_multihead.  1 <= num_layers <= 16, else
+ * LSA_ERR_INVALID_ARGUMENT; a combine other than the two above is
+ * LSA_ERR_INVALID_ARGUMENT.  With num_layers = 1 the result equals
+ * lsa_score_fp8_multihead's bit for bit.  All layers are read in one pass.
+ * ------------------------------------------------------------------------- */
+enum { LSA_COMBINE_MAX = 0, LSA_COMBINE_MEAN = 1 };
+
+lsa_status lsa_score_fp8_multihead_layers(const lsa_shape* shape, int32_t num_layers,
+                                          int32_t combine, int32_t num_heads, int32_t head_dim,
+                                          const void* q_heads_dev, const float* head_w_dev,
+                                          const void* records_dev, const int32_t* chunk_off_dev,
+                                          float* scores_dev, void* hip_stream);
+
+/* ---------------------------------------------------------------------------
  * Top-k keep set.  Dimensionstp review section 3-2-3 step 5 (top-k keep
  * mask).  For each stream, keeps the k_b chunks ranked first by (score
  * descending, chunk index ascending); NaN ranks below every number and -0.0
@@ -166,6 +192,39 @@ lsa_status lsa_score_fp8_multihead(const lsa_shape* shape, int32_t num_heads, in
 lsa_status lsa_select_topk(const lsa_shape* shape, const float* scores_dev,
                            const int32_t* chunk_off_dev, const int32_t* sel_off_dev,
                            int32_t* sel_idx_dev, void* hip_stream);
+
+/* ---------------------------------------------------------------------------
+ * Threshold keep set with a dense fallback.  Dimensionstp review section
+ * 3-2-3 step 5 (the keep mask comes from a top-k or from a threshold);
+ * sections 4-3 and 5-1 (exact-retrieval tasks need a threshold fallback).
+ * For each stream b:
+ *   pass_b = { n : scores[chunk_off[b] + n] >= threshold }  (fp32 compare;
+ *            NaN never passes, -0.0 == +0.0)
+ *   pass_b empty (and N_b > 0): keep all N_b chunks -- dense attention for
+ *            that stream -- and set fallback_dev[b] = 1;
+ *   otherwise, when max_keep > 0 and |pass_b| > max_keep: keep the max_keep
+ *            chunks of pass_b ranked first by (score descending, index
+ *            ascending), as lsa_select_topk would; else keep pass_b;
+ *            fallback_dev[b] = 0.
+ * Writes the kept counts' running totals to sel_off_dev[0 .. B] (sel_off[0]
+ * = 0; a CSR table lsa_sparse_decode_attn and lsa_gather_chunks accept) and
+ * the kept indices, ascending within each stream, to sel_idx_dev
+ * [sel_off[b] .. sel_off[b+1]).  sel_idx_dev must hold total_chunks int32
+ * (every chunk may be kept); fallback_dev [B] int32 may be NULL.  Calls that
+ * consume this keep set take a shape whose total_k / max_k are the bounds
+ * total_chunks / max_chunks, since the counts are known on the device only.
+ * workspace_dev: at least lsa_select_threshold_workspace_bytes(shape) bytes,
+ * 256-byte aligned (else LSA_ERR_WORKSPACE_TOO_SMALL / INVALID_ARGUMENT);
+ * threshold must not be NaN and max_keep must be >= 0 (else
+ * LSA_ERR_INVALID_ARGUMENT).  Requires max_chunks <= 65536.  Two kernels:
+ * the per-stream counts, then the offsets and the indices.
+ * ------------------------------------------------------------------------- */
+size_t lsa_select_threshold_workspace_bytes(const lsa_shape* shape);
+
+lsa_status lsa_select_threshold(const lsa_shape* shape, const float* scores_dev,
+                                const int32_t* chunk_off_dev, float threshold, int32_t max_keep,
+                                int32_t* sel_off_dev, int32_t* sel_idx_dev, int32_t* fallback_dev,
+                                void* workspace_dev, size_t workspace_bytes, void* hip_stream);
 
 /* ---------------------------------------------------------------------------
  * Resident chunk pool.  Wiki note flowchart (its resident-chunk node); molayo

@@ -11,6 +11,9 @@ namespace {
 
 constexpr int32_t kMaxChunkSize = 1024;
 constexpr int32_t kMaxChunksPerStream = 65536;
+constexpr int32_t kMaxScoreLayers = 16;
+
+size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -154,12 +157,15 @@ lsa_status lsa_score(const lsa_shape* shape, const void* q_idx_dev, const void* 
                                  static_cast<hipStream_t>(hip_stream)));
 }
 
-lsa_status lsa_score_fp8_multihead(const lsa_shape* shape, int32_t num_heads, int32_t head_dim,
-                                   const void* q_heads_dev, const float* head_w_dev,
-                                   const void* records_dev, const int32_t* chunk_off_dev,
-                                   float* scores_dev, void* hip_stream) {
+lsa_status lsa_score_fp8_multihead_layers(const lsa_shape* shape, int32_t num_layers,
+                                          int32_t combine, int32_t num_heads, int32_t head_dim,
+                                          const void* q_heads_dev, const float* head_w_dev,
+                                          const void* records_dev, const int32_t* chunk_off_dev,
+                                          float* scores_dev, void* hip_stream) {
   lsa_status st = check_common(shape);
   if (st != LSA_OK) return st;
+  if (num_layers < 1 || num_layers > kMaxScoreLayers) return LSA_ERR_INVALID_ARGUMENT;
+  if (combine != LSA_COMBINE_MAX && combine != LSA_COMBINE_MEAN) return LSA_ERR_INVALID_ARGUMENT;
   if (num_heads < 1 || head_dim < 1) return LSA_ERR_INVALID_ARGUMENT;
   if (shape->dtype != LSA_DTYPE_BF16 || !score_mh_supported(num_heads, head_dim))
     return LSA_ERR_UNSUPPORTED;
@@ -169,9 +175,45 @@ lsa_status lsa_score_fp8_multihead(const lsa_shape* shape, int32_t num_heads, in
       !aligned(chunk_off_dev, 4) || !aligned(scores_dev, 4))
     return LSA_ERR_INVALID_ARGUMENT;
   (void)hipGetLastError();
-  return hip_status(launch_score_mh(*shape, num_heads, head_dim, q_heads_dev, head_w_dev,
-                                    records_dev, chunk_off_dev, scores_dev,
+  return hip_status(launch_score_mh(*shape, num_layers, combine, num_heads, head_dim, q_heads_dev,
+                                    head_w_dev, records_dev, chunk_off_dev, scores_dev,
                                     static_cast<hipStream_t>(hip_stream)));
+}
+
+lsa_status lsa_score_fp8_multihead(const lsa_shape* shape, int32_t num_heads, int32_t head_dim,
+                                   const void* q_heads_dev, const float* head_w_dev,
+                                   const void* records_dev, const int32_t* chunk_off_dev,
+                                   float* scores_dev, void* hip_stream) {
+  return lsa_score_fp8_multihead_layers(shape, 1, LSA_COMBINE_MAX, num_heads, head_dim,
+                                        q_heads_dev, head_w_dev, records_dev, chunk_off_dev,
+                                        scores_dev, hip_stream);
+}
+
+size_t lsa_select_threshold_workspace_bytes(const lsa_shape* shape) {
+  if (check_select(shape) != LSA_OK) return 0;
+  return align256(static_cast<size_t>(shape->batch) * sizeof(int32_t));
+}
+
+lsa_status lsa_select_threshold(const lsa_shape* shape, const float* scores_dev,
+                                const int32_t* chunk_off_dev, float threshold, int32_t max_keep,
+                                int32_t* sel_off_dev, int32_t* sel_idx_dev, int32_t* fallback_dev,
+                                void* workspace_dev, size_t workspace_bytes, void* hip_stream) {
+  lsa_status st = check_select(shape);
+  if (st != LSA_OK) return st;
+  if (isnan(threshold) || max_keep < 0) return LSA_ERR_INVALID_ARGUMENT;
+  if (!scores_dev || !chunk_off_dev || !sel_off_dev || !sel_idx_dev || !workspace_dev)
+    return LSA_ERR_INVALID_ARGUMENT;
+  if (!aligned(scores_dev, 4) || !aligned(chunk_off_dev, 4) || !aligned(sel_off_dev, 4) ||
+      !aligned(sel_idx_dev, 4) || (fallback_dev && !aligned(fallback_dev, 4)) ||
+      !aligned(workspace_dev, 256))
+    return LSA_ERR_INVALID_ARGUMENT;
+  if (workspace_bytes < lsa_select_threshold_workspace_bytes(shape))
+    return LSA_ERR_WORKSPACE_TOO_SMALL;
+  (void)hipGetLastError();
+  return hip_status(launch_select_threshold(*shape, scores_dev, chunk_off_dev, threshold, max_keep,
+                                            sel_off_dev, sel_idx_dev, fallback_dev,
+                                            static_cast<int32_t*>(workspace_dev),
+                                            static_cast<hipStream_t>(hip_stream)));
 }
 
 lsa_status lsa_select_topk(const lsa_shape* shape, const float* scores_dev,

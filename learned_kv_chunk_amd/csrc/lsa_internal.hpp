@@ -88,9 +88,13 @@ hipError_t launch_gather(const lsa_shape& s, const void* store, int32_t row_byte
                          int32_t row_bytes2, void* pool2, hipStream_t st);
 bool score_supported(const lsa_shape& s);
 bool score_mh_supported(int32_t heads, int32_t head_dim);
-hipError_t launch_score_mh(const lsa_shape& s, int32_t heads, int32_t head_dim, const void* q,
-                           const float* w, const void* rec, const int32_t* chunk_off,
-                           float* scores, hipStream_t st);
+hipError_t launch_score_mh(const lsa_shape& s, int32_t layers, int32_t combine, int32_t heads,
+                           int32_t head_dim, const void* q, const float* w, const void* rec,
+                           const int32_t* chunk_off, float* scores, hipStream_t st);
+hipError_t launch_select_threshold(const lsa_shape& s, const float* scores,
+                                   const int32_t* chunk_off, float threshold, int32_t max_keep,
+                                   int32_t* sel_off, int32_t* sel_idx, int32_t* fallback,
+                                   int32_t* counts, hipStream_t st);
 // Attention partial kernels (one per kernel family) and the merge.
 bool mqa_attn_supported(const lsa_shape& s);
 hipError_t launch_attn_mqa(const lsa_shape& s, const AttnArgs& a, int64_t grid, hipStream_t st);

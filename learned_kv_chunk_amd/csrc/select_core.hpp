@@ -77,15 +77,12 @@ __device__ __forceinline__ void select_exclusive_scan2(uint32_t a, uint32_t b, u
   *eb = bb + ib - b;
 }
 
-// Top-k of scores[0..n) written ascending to out[0..k); 0 < k < n.  Every
-// one of the THREADS threads (threads 0..THREADS-1 of the workgroup) must
-// call it.
+// Loads scores[0..n) as order keys, KPT consecutive ones per thread (keys
+// past n are 0 and never counted).
 template <int THREADS, int KPT>
-__device__ __forceinline__ void select_topk_block(const float* __restrict__ scores, int32_t n,
-                                                  int32_t k, int32_t* __restrict__ out,
-                                                  SelectLds<THREADS>& lds) {
+__device__ __forceinline__ void select_load_keys(const float* __restrict__ scores, int32_t n,
+                                                 uint32_t (&key)[KPT]) {
   const int tid = threadIdx.x;
-  uint32_t key[KPT];
   float sv[KPT];
   // all loads in flight; 16-byte loads where the stream's scores are aligned
   if (KPT % 4 == 0 && (reinterpret_cast<uintptr_t>(scores) & 15u) == 0 && (tid + 1) * KPT <= n) {
@@ -104,6 +101,16 @@ __device__ __forceinline__ void select_topk_block(const float* __restrict__ scor
   }
 #pragma unroll
   for (int i = 0; i < KPT; ++i) key[i] = (tid * KPT + i < n) ? order_key(sv[i]) : 0u;
+}
+
+// Top-k of the n keys held as select_load_keys leaves them, written ascending
+// to out[0..k); 0 < k < n.  Every one of the THREADS threads (threads
+// 0..THREADS-1 of the workgroup) must call it.
+template <int THREADS, int KPT>
+__device__ __forceinline__ void select_topk_keys(const uint32_t (&key)[KPT], int32_t n,
+                                                 int32_t k, int32_t* __restrict__ out,
+                                                 SelectLds<THREADS>& lds) {
+  const int tid = threadIdx.x;
   for (int i = tid; i < 4 * 256; i += THREADS) (&lds.hist[0][0])[i] = 0u;
   select_sync<THREADS>();
 
@@ -185,6 +192,16 @@ __device__ __forceinline__ void select_topk_block(const float* __restrict__ scor
       ++eq_before;
     }
   }
+}
+
+// Top-k of scores[0..n) written ascending to out[0..k); 0 < k < n.
+template <int THREADS, int KPT>
+__device__ __forceinline__ void select_topk_block(const float* __restrict__ scores, int32_t n,
+                                                  int32_t k, int32_t* __restrict__ out,
+                                                  SelectLds<THREADS>& lds) {
+  uint32_t key[KPT];
+  select_load_keys<THREADS, KPT>(scores, n, key);
+  select_topk_keys<THREADS, KPT>(key, n, k, out, lds);
 }
 
 }  // namespace lsa

@@ -24,6 +24,9 @@ LSA_ERR_UNSUPPORTED = 2
 LSA_ERR_WORKSPACE_TOO_SMALL = 3
 LSA_ERR_HIP = 4
 
+COMBINE_MAX = 0
+COMBINE_MEAN = 1
+
 DTYPE_F32 = 0
 DTYPE_BF16 = 1
 KV_STORE = 0
@@ -90,7 +93,12 @@ _SIGNATURES = {
     "lsa_score": ([ctypes.POINTER(Shape), _P, _P, _P, _P, _P], _I32),
     "lsa_score_fp8_multihead": ([ctypes.POINTER(Shape), _I32, _I32, _P, _P, _P, _P, _P, _P],
                                 _I32),
+    "lsa_score_fp8_multihead_layers": ([ctypes.POINTER(Shape), _I32, _I32, _I32, _I32, _P, _P,
+                                        _P, _P, _P, _P], _I32),
     "lsa_select_topk": ([ctypes.POINTER(Shape), _P, _P, _P, _P, _P], _I32),
+    "lsa_select_threshold_workspace_bytes": ([ctypes.POINTER(Shape)], ctypes.c_size_t),
+    "lsa_select_threshold": ([ctypes.POINTER(Shape), _P, _P, ctypes.c_float, _I32, _P, _P, _P,
+                              _P, ctypes.c_size_t, _P], _I32),
     "lsa_gather_chunks": ([ctypes.POINTER(Shape), _P, _P, _P, _P, _P, _P, _P, _P], _I32),
     "lsa_sparse_decode_attn": ([ctypes.POINTER(Shape), _I32, _P, _P, _P, _P, _P, _P, _P, _P,
                                 _P, ctypes.c_size_t, _P], _I32),
@@ -171,12 +179,16 @@ def workspace_bytes(shape: ProblemShape) -> int:
 
 
 def allocate_workspace(shape: ProblemShape, device) -> torch.Tensor:
-    """Zero-filled workspace (the library's arrival counters start at zero and
-    every call leaves them at zero)."""
+    """Workspace for lsa_sparse_decode_attn / lsa_decode_step (its contents
+    need no initialisation; zero-filled for reproducible debugging)."""
     n = workspace_bytes(shape)
     if n == 0:
         raise LsaError(LSA_ERR_UNSUPPORTED, "lsa_workspace_bytes")
     return torch.zeros(n, dtype=torch.uint8, device=device)
+
+
+def select_threshold_workspace_bytes(shape: ProblemShape) -> int:
+    return int(library().lsa_select_threshold_workspace_bytes(ctypes.byref(shape.c())))
 
 
 # ----------------------------------------------------------------------------- helpers
@@ -237,6 +249,61 @@ def score_fp8_multihead(shape: ProblemShape, q_heads, head_w, records, chunk_off
                                              _ptr(chunk_off), _ptr(scores), _stream(stream)),
            "lsa_score_fp8_multihead")
     return scores
+
+
+def score_fp8_multihead_layers(shape: ProblemShape, q_heads, head_w, records, chunk_off,
+                               combine: int = COMBINE_MAX, scores=None,
+                               stream=None) -> torch.Tensor:
+    """lsa_score_fp8_multihead_layers: fp32 ensemble scores [total_chunks] over
+    L layers.  q_heads [L][B][heads][head_dim] bf16, head_w [L][B][heads]
+    fp32, records [L][total_chunks][head_dim + 4] uint8."""
+    _dev(q_heads, "q_heads", torch.bfloat16, 4)
+    _dev(head_w, "head_w", torch.float32, 3)
+    _dev(records, "records", torch.uint8, 3)
+    _dev(chunk_off, "chunk_off", torch.int32, 1)
+    L, B, heads, head_dim = q_heads.shape
+    if head_w.shape != (L, B, heads) or records.shape != (L, shape.total_chunks, head_dim + 4):
+        raise ValueError("q_heads / head_w / records shapes do not agree")
+    if scores is None:
+        scores = torch.empty(shape.total_chunks, dtype=torch.float32, device=records.device)
+    _dev(scores, "scores", torch.float32, 1)
+    _check(library().lsa_score_fp8_multihead_layers(
+        ctypes.byref(shape.c()), L, int(combine), heads, head_dim, _ptr(q_heads), _ptr(head_w),
+        _ptr(records), _ptr(chunk_off), _ptr(scores), _stream(stream)),
+        "lsa_score_fp8_multihead_layers")
+    return scores
+
+
+def select_threshold(shape: ProblemShape, scores, chunk_off, threshold: float, max_keep: int = 0,
+                     sel_off=None, sel_idx=None, fallback=None, workspace=None, stream=None):
+    """lsa_select_threshold: (sel_off [B+1], sel_idx [total_chunks] of which
+    the first sel_off[B] are meaningful, fallback [B]) int32 tensors."""
+    _dev(scores, "scores", torch.float32, 1)
+    _dev(chunk_off, "chunk_off", torch.int32, 1)
+    dev = scores.device
+    if sel_off is None:
+        sel_off = torch.empty(shape.batch + 1, dtype=torch.int32, device=dev)
+    if sel_idx is None:
+        sel_idx = torch.empty(shape.total_chunks, dtype=torch.int32, device=dev)
+    if fallback is None:
+        fallback = torch.empty(shape.batch, dtype=torch.int32, device=dev)
+    if workspace is None:
+        n = select_threshold_workspace_bytes(shape)
+        if n == 0:
+            raise LsaError(LSA_ERR_UNSUPPORTED, "lsa_select_threshold_workspace_bytes")
+        workspace = torch.empty(n, dtype=torch.uint8, device=dev)
+    _dev(sel_off, "sel_off", torch.int32, 1)
+    _dev(sel_idx, "sel_idx", torch.int32, 1)
+    _dev(fallback, "fallback", torch.int32, 1)
+    _dev(workspace, "workspace", torch.uint8, 1)
+    if sel_off.numel() != shape.batch + 1 or sel_idx.numel() < shape.total_chunks or \
+            fallback.numel() != shape.batch:
+        raise ValueError("sel_off / sel_idx / fallback sizes do not match the shape")
+    _check(library().lsa_select_threshold(
+        ctypes.byref(shape.c()), _ptr(scores), _ptr(chunk_off), float(threshold), int(max_keep),
+        _ptr(sel_off), _ptr(sel_idx), _ptr(fallback), _ptr(workspace), workspace.numel(),
+        _stream(stream)), "lsa_select_threshold")
+    return sel_off, sel_idx, fallback
 
 
 def select_topk(shape: ProblemShape, scores, chunk_off, sel_off, sel_idx=None,

@@ -198,3 +198,46 @@ def test_multihead_scorer_validation():
     assert _mh(s, heads=48) == lsa.LSA_ERR_UNSUPPORTED
     assert _mh(s, dim=96) == lsa.LSA_ERR_UNSUPPORTED
     assert _mh(shape(dtype=torch.float32)) == lsa.LSA_ERR_UNSUPPORTED
+
+
+def _mhl(s, layers=3, combine=lsa.COMBINE_MAX, heads=128, dim=128, q=DUMMY, w=DUMMY, rec=DUMMY,
+         co=DUMMY, out=DUMMY):
+    return lsa.library().lsa_score_fp8_multihead_layers(ctypes.byref(s.c()), layers, combine,
+                                                        heads, dim, q, w, rec, co, out, None)
+
+
+def test_layer_ensemble_scorer_validation():
+    s = shape()
+    assert _mhl(s, layers=0) == lsa.LSA_ERR_INVALID_ARGUMENT
+    assert _mhl(s, layers=17) == lsa.LSA_ERR_INVALID_ARGUMENT
+    assert _mhl(s, combine=2) == lsa.LSA_ERR_INVALID_ARGUMENT
+    assert _mhl(s, combine=-1) == lsa.LSA_ERR_INVALID_ARGUMENT
+    assert _mhl(s, w=None) == lsa.LSA_ERR_INVALID_ARGUMENT
+    assert _mhl(s, q=ctypes.c_void_p(0x100004)) == lsa.LSA_ERR_INVALID_ARGUMENT
+    assert _mhl(s, heads=8) == lsa.LSA_ERR_UNSUPPORTED
+    assert _mhl(shape(dtype=torch.float32)) == lsa.LSA_ERR_UNSUPPORTED
+
+
+def _thr(s, tau=0.5, cap=0, scores=DUMMY, co=DUMMY, off=DUMMY, idx=DUMMY, fb=DUMMY, ws=DUMMY,
+         ws_bytes=None):
+    if ws_bytes is None:
+        ws_bytes = lsa.select_threshold_workspace_bytes(s)
+    return lsa.library().lsa_select_threshold(ctypes.byref(s.c()), scores, co, tau, cap, off, idx,
+                                              fb, ws, ws_bytes, None)
+
+
+def test_threshold_select_validation():
+    s = shape()
+    need = lsa.select_threshold_workspace_bytes(s)
+    assert need >= 4 * s.batch and need % 256 == 0
+    assert lsa.select_threshold_workspace_bytes(shape(batch=0)) == 0
+    assert _thr(s, tau=float("nan")) == lsa.LSA_ERR_INVALID_ARGUMENT
+    assert _thr(s, cap=-1) == lsa.LSA_ERR_INVALID_ARGUMENT
+    assert _thr(s, scores=None) == lsa.LSA_ERR_INVALID_ARGUMENT
+    assert _thr(s, off=None) == lsa.LSA_ERR_INVALID_ARGUMENT
+    assert _thr(s, idx=None) == lsa.LSA_ERR_INVALID_ARGUMENT
+    assert _thr(s, ws=None) == lsa.LSA_ERR_INVALID_ARGUMENT
+    assert _thr(s, ws=ctypes.c_void_p(0x100080)) == lsa.LSA_ERR_INVALID_ARGUMENT  # 256-byte aligned
+    assert _thr(s, fb=ctypes.c_void_p(0x100002)) == lsa.LSA_ERR_INVALID_ARGUMENT
+    assert _thr(s, ws_bytes=need - 1) == lsa.LSA_ERR_WORKSPACE_TOO_SMALL
+    assert _thr(shape(max_chunks=65537, total_chunks=16 * 65537)) == lsa.LSA_ERR_UNSUPPORTED
