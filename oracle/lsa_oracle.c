@@ -23,6 +23,9 @@
  *   oracle_select_threshold  threshold keep mask, capped by a top-k, with a
  *                     dense fallback for a stream where no chunk passes
  *                     (review section 3-2-3 step 5, sections 4-3 and 5-1).
+ *   oracle_pool_delta  the pool's slot table after a re-index when only the
+ *                     newly kept chunks are copied in (wiki note flowchart,
+ *                     the swap between GPU and host memory).
  */
 #include "lsa_oracle.h"
 
@@ -283,5 +286,44 @@ void oracle_select_threshold(int32_t B, const double* scores, const int32_t* chu
       kept = max_keep;
     }
     sel_off[b + 1] = sel_off[b] + kept;
+  }
+}
+
+void oracle_pool_delta(int32_t B, const int32_t* chunk_off, const int32_t* sel_idx,
+                       const int32_t* sel_off, const int32_t* table_in, int32_t* table_out,
+                       int32_t* loads, int32_t* load_count) {
+  for (int32_t b = 0; b < B; ++b) {
+    const int32_t n = chunk_off[b + 1] - chunk_off[b];
+    const int32_t s0 = sel_off[b], k = sel_off[b + 1] - sel_off[b];
+    unsigned char* wanted = (unsigned char*)calloc((size_t)(n > 0 ? n : 1), 1);
+    unsigned char* held = (unsigned char*)calloc((size_t)(n > 0 ? n : 1), 1);
+    for (int32_t j = 0; j < k; ++j) wanted[sel_idx[s0 + j]] = 1;
+    /* slots keeping a still-wanted chunk; every other slot is free */
+    int32_t n_free = 0;
+    int32_t* free_slots = (int32_t*)malloc(sizeof(int32_t) * (size_t)(k > 0 ? k : 1));
+    for (int32_t p = 0; p < k; ++p) {
+      const int32_t c = table_in[s0 + p];
+      if (c >= 0 && c < n && wanted[c] && !held[c]) {
+        held[c] = 1;
+        table_out[s0 + p] = c;
+      } else {
+        free_slots[n_free++] = s0 + p;
+      }
+    }
+    /* newly kept chunks, ascending, into the free slots, ascending */
+    int32_t n_load = 0;
+    for (int32_t j = 0; j < k; ++j) {
+      const int32_t c = sel_idx[s0 + j];
+      if (held[c]) continue;
+      const int32_t slot = free_slots[n_load];
+      table_out[slot] = c;
+      loads[s0 + n_load] = slot;
+      ++n_load;
+    }
+    for (int32_t i = n_load; i < n_free; ++i) table_out[free_slots[i]] = -1;
+    load_count[b] = n_load;
+    free(free_slots);
+    free(held);
+    free(wanted);
   }
 }

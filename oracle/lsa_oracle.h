@@ -128,6 +128,23 @@ void oracle_select_threshold(int32_t B, const double* scores, const int32_t* chu
                              double tau, int32_t max_keep, int32_t* sel_off, int32_t* sel_idx,
                              int32_t* fallback);
 
+/* Delta residency of the chunk pool (wiki note flowchart: only the selected
+ * chunks stay on the GPU, the rest live in host memory and are swapped in
+ * when needed; dimensionstp review section 3-2-5: that offload engine is
+ * unreleased, so the rule below is this build's plain reading).  Stream b
+ * owns the k_b pool slots sel_off[b] .. sel_off[b+1]-1; table[slot] is the
+ * chunk a slot holds (-1: none).  Given the new kept set sel_idx (ascending,
+ * k_b chunks per stream) and the old table:
+ *   a slot whose chunk is still kept keeps it (no copy);
+ *   the other slots are free; the new chunks not held by any slot are loaded,
+ *   the i-th of them (ascending chunk index) into the i-th free slot
+ *   (ascending slot index); free slots left over hold -1.
+ * Writes the new table to table_out, the slots loaded to loads[sel_off[b] ..
+ * sel_off[b] + load_count[b]) in load order, and their number to load_count. */
+void oracle_pool_delta(int32_t B, const int32_t* chunk_off, const int32_t* sel_idx,
+                       const int32_t* sel_off, const int32_t* table_in, int32_t* table_out,
+                       int32_t* loads, int32_t* load_count);
+
 /* Threads an OpenMP region may use here (1 when built without OpenMP). */
 int32_t oracle_max_threads(void);
 

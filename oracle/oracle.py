@@ -20,6 +20,8 @@ Step definitions (cited to the pages' sections, see ``lsa_oracle.c``):
   select_threshold  threshold keep mask capped by a top-k, with a dense
              fallback where no chunk passes (review section 3-2-3 step 5,
              sections 4-3 and 5-1)
+  pool_delta the pool's slot table after a re-index when only newly kept
+             chunks are copied in from host memory (wiki note flowchart)
   decode     the review's decode loop (section 3-2-3 steps 3-7): re-score and
              re-select every ``reindex_every`` steps, attend every step.
 """
@@ -80,6 +82,8 @@ def _load():
         lib.oracle_score_fp8mh_layers.restype = None
         lib.oracle_select_threshold.argtypes = [i32, P, P, f64, i32, P, P, P]
         lib.oracle_select_threshold.restype = None
+        lib.oracle_pool_delta.argtypes = [i32, P, P, P, P, P, P, P]
+        lib.oracle_pool_delta.restype = None
         lib.oracle_max_threads.argtypes = []
         lib.oracle_max_threads.restype = i32
         _lib = lib
@@ -207,6 +211,24 @@ def gather(store: np.ndarray, C: int, tok_off: np.ndarray, sel_idx: np.ndarray,
     _load().oracle_gather(B, C, row_bytes, _ptr(store), _ptr(tok_off), _ptr(sel_idx),
                           _ptr(sel_off), _ptr(pool))
     return pool
+
+
+def pool_delta(chunk_off: np.ndarray, sel_idx: np.ndarray, sel_off: np.ndarray,
+               table: np.ndarray) -> tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """(new slot table [sum k_b], loaded slots [sum k_b] of which the first
+    load_count[b] after sel_off[b] are meaningful, load_count [B])."""
+    chunk_off = np.ascontiguousarray(chunk_off, dtype=np.int32)
+    sel_idx = np.ascontiguousarray(sel_idx, dtype=np.int32)
+    sel_off = np.ascontiguousarray(sel_off, dtype=np.int32)
+    table = np.ascontiguousarray(table, dtype=np.int32)
+    B = len(chunk_off) - 1
+    assert len(table) == len(sel_idx) == int(sel_off[-1])
+    out = np.empty_like(table)
+    loads = np.full(max(1, len(table)), -1, dtype=np.int32)
+    count = np.empty(B, dtype=np.int32)
+    _load().oracle_pool_delta(B, _ptr(chunk_off), _ptr(sel_idx), _ptr(sel_off), _ptr(table),
+                              _ptr(out), _ptr(loads), _ptr(count))
+    return out, loads[:len(table)], count
 
 
 def attention(Q: np.ndarray, K: np.ndarray, V: np.ndarray | None, tok_off: np.ndarray,

@@ -571,3 +571,70 @@ def test_layer_ensemble_needles_pass_a_threshold():
             tau = (sb[nd].min() + rest.max()) / 2
             _, idx, fb = oracle.select_threshold(sb, np.array([0, len(sb)], np.int32), tau)
             assert fb.tolist() == [0] and sorted(idx.tolist()) == sorted(nd.tolist())
+
+
+# --- delta residency of the pool -----------------------------------------------
+
+def test_pool_delta_golden():
+    g = _golden("pool_delta.json")
+    co, so = np.array(g["chunk_off"], np.int32), np.array(g["sel_off"], np.int32)
+    for st in g["steps"]:
+        table, loads, count = oracle.pool_delta(co, np.array(st["sel_idx"], np.int32), so,
+                                                np.array(st["table_in"], np.int32))
+        assert table.tolist() == st["table_out"], st
+        for b in range(len(so) - 1):
+            assert loads[so[b]:so[b] + count[b]].tolist() == st["loads"][b], (st, b)
+
+
+def _random_keep_sets(rng, n, k, steps, churn):
+    cur = np.sort(rng.choice(n, size=k, replace=False))
+    out = [cur]
+    for _ in range(steps - 1):
+        keep = rng.choice(cur, size=k - churn, replace=False)
+        rest = np.setdiff1d(np.arange(n), keep)
+        cur = np.sort(np.concatenate([keep, rng.choice(rest, size=churn, replace=False)]))
+        out.append(cur)
+    return out
+
+
+def test_pool_delta_invariants_and_pool_contents():
+    rng = np.random.default_rng(11)
+    n_list, k_list = [50, 7, 300], [9, 7, 40]
+    co = np.concatenate([[0], np.cumsum(n_list)]).astype(np.int32)
+    so = np.concatenate([[0], np.cumsum(k_list)]).astype(np.int32)
+    C, L = 4, np.array(n_list) * 4 - np.array([1, 0, 3])      # partial last chunks
+    tok_off = np.concatenate([[0], np.cumsum(L)]).astype(np.int64)
+    store = rng.integers(0, 2 ** 16, size=(int(tok_off[-1]), 3), dtype=np.uint16)
+    seqs = [_random_keep_sets(rng, n, k, 6, churn) for n, k, churn in
+            zip(n_list, k_list, [3, 0, 11])]
+    table = np.full(int(so[-1]), -1, np.int32)
+    pool = np.zeros((int(so[-1]), C, 3), np.uint16)
+    for t in range(6):
+        sel = np.concatenate([s[t] for s in seqs]).astype(np.int32)
+        new, loads, count = oracle.pool_delta(co, sel, so, table)
+        for b in range(3):
+            s0, s1 = so[b], so[b + 1]
+            old_b, new_b, want = table[s0:s1], new[s0:s1], set(sel[s0:s1].tolist())
+            assert sorted(new_b.tolist()) == sorted(want)                 # holds the kept set
+            held = set(old_b.tolist()) & want
+            for p in range(s1 - s0):                                      # kept chunks stay put
+                if old_b[p] in held:
+                    assert new_b[p] == old_b[p]
+            assert count[b] == len(want - set(old_b.tolist()))            # minimal copies
+            ld = loads[s0:s0 + count[b]]
+            assert sorted(ld.tolist()) == ld.tolist() and len(set(ld.tolist())) == count[b]
+            assert {int(new[p]) for p in ld} == want - set(old_b.tolist())
+            if t == 0:
+                assert new_b.tolist() == sorted(want)                     # empty start: in order
+        # applying only the loads to the previous pool gives the gather of the new table
+        for b in range(3):
+            for p in loads[so[b]:so[b] + count[b]]:
+                one = oracle.gather(store[tok_off[b]:tok_off[b + 1]], C,
+                                    np.array([0, L[b]], np.int64), np.array([new[p]], np.int32),
+                                    np.array([0, 1], np.int32))
+                pool[p] = one[0]
+        np.testing.assert_array_equal(pool, oracle.gather(store, C, tok_off, new, so))
+        again, _, count2 = oracle.pool_delta(co, sel, so, new)            # idempotent
+        np.testing.assert_array_equal(again, new)
+        assert (count2 == 0).all()
+        table = new
