@@ -244,6 +244,41 @@ lsa_status lsa_gather_chunks(const lsa_shape* shape, const void* k_store_dev,
                              void* k_pool_dev, void* v_pool_dev, void* hip_stream);
 
 /* ---------------------------------------------------------------------------
+ * Delta residency of the chunk pool over a host-memory backing store.  Wiki
+ * note flowchart: only the selected chunks stay resident on the GPU, the rest
+ * of the cache lives in host memory and chunks are swapped in as the
+ * selection changes (dimensionstp review section 3-2-5: that engine is
+ * unreleased; the slot rule below is this library's).  Stream b owns pool
+ * slots sel_off[b] .. sel_off[b+1]-1 and table_dev[slot] names the chunk a
+ * slot holds (-1: none; start from all -1).  Given the new kept set
+ * sel_idx_dev (ascending, k_b chunks per stream, as lsa_select_topk writes):
+ *   a slot whose chunk is still kept keeps it and is not copied;
+ *   the other slots are freed; the newly kept chunks, in ascending order, are
+ *   copied from the host store into the freed slots, in ascending slot order
+ *   (rows past the end of the stream zero-filled); freed slots left over
+ *   hold -1.
+ * Outputs: table_dev [total_k] (updated in place), loads_dev [total_k] (the
+ * slots written, stream b's in loads[sel_off[b] .. sel_off[b] +
+ * load_count[b])), load_count_dev [B].  k_pool_dev / v_pool_dev as for
+ * lsa_gather_chunks, except that slot s holds chunk table[s]: attention then
+ * reads the pool with kv_mode LSA_KV_POOL and sel_idx = table (any order of a
+ * stream's chunks gives the same result up to rounding).
+ * k_host / v_host: the K and V history [sum L][head_dim] in page-locked host
+ * memory (hipHostMalloc or a pinned torch tensor), 16-byte aligned; v_host
+ * NULL when v_aliases_k.  Memory that is not page-locked host memory is
+ * LSA_ERR_INVALID_ARGUMENT (checked with hipPointerGetAttributes).  Rows must
+ * be multiples of 16 bytes and max_chunks <= 65536 (else LSA_ERR_UNSUPPORTED).
+ * Preconditions on the device: k_b is the same as when the table was written,
+ * and a stream's table entries are distinct.  Two kernels; only the loaded
+ * chunks cross the host link.
+ * ------------------------------------------------------------------------- */
+lsa_status lsa_pool_delta_update(const lsa_shape* shape, const void* k_host, const void* v_host,
+                                 const int64_t* tok_off_dev, const int32_t* chunk_off_dev,
+                                 const int32_t* sel_idx_dev, const int32_t* sel_off_dev,
+                                 int32_t* table_dev, int32_t* loads_dev, int32_t* load_count_dev,
+                                 void* k_pool_dev, void* v_pool_dev, void* hip_stream);
+
+/* ---------------------------------------------------------------------------
  * Sparse decode attention over the kept chunks.  Dimensionstp review section
  * 3-2-3 steps 6-7: unselected chunks are masked out and attention runs over
  * the kept ones.  For every stream b and head h, over the tokens t of the

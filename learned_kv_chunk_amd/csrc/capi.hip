@@ -273,6 +273,52 @@ static lsa_status check_attn_args(const lsa_shape* shape, int32_t kv_mode, const
   return LSA_OK;
 }
 
+// Device address of page-locked host memory, or null when `p` is not such memory.
+static const void* pinned_device_pointer(const void* p) {
+  hipPointerAttribute_t attr;
+  if (hipPointerGetAttributes(&attr, p) != hipSuccess) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  if (attr.type != hipMemoryTypeHost) return nullptr;
+  return attr.devicePointer;
+}
+
+lsa_status lsa_pool_delta_update(const lsa_shape* shape, const void* k_host, const void* v_host,
+                                 const int64_t* tok_off_dev, const int32_t* chunk_off_dev,
+                                 const int32_t* sel_idx_dev, const int32_t* sel_off_dev,
+                                 int32_t* table_dev, int32_t* loads_dev, int32_t* load_count_dev,
+                                 void* k_pool_dev, void* v_pool_dev, void* hip_stream) {
+  lsa_status st = check_common(shape);
+  if (st != LSA_OK) return st;
+  const lsa_shape& s = *shape;
+  if (s.head_dim_qk < 1 || s.head_dim_v < 1 || (s.v_aliases_k != 0 && s.v_aliases_k != 1))
+    return LSA_ERR_INVALID_ARGUMENT;
+  if (s.max_chunks > pool_delta_max_stream_chunks()) return LSA_ERR_UNSUPPORTED;
+  const int32_t kb = s.head_dim_qk * elem_bytes(s);
+  const int32_t vb = s.v_aliases_k ? 0 : s.head_dim_v * elem_bytes(s);
+  if (kb % 16 != 0 || vb % 16 != 0) return LSA_ERR_UNSUPPORTED;
+  if (!k_host || !tok_off_dev || !chunk_off_dev || !sel_idx_dev || !sel_off_dev || !table_dev ||
+      !loads_dev || !load_count_dev || !k_pool_dev)
+    return LSA_ERR_INVALID_ARGUMENT;
+  if (s.v_aliases_k ? (v_host != nullptr || v_pool_dev != nullptr)
+                    : (v_host == nullptr || v_pool_dev == nullptr))
+    return LSA_ERR_INVALID_ARGUMENT;
+  if (!aligned(k_host, 16) || (v_host && !aligned(v_host, 16)) || !aligned(k_pool_dev, 16) ||
+      (v_pool_dev && !aligned(v_pool_dev, 16)) || !aligned(tok_off_dev, 8) ||
+      !aligned(chunk_off_dev, 4) || !aligned(sel_idx_dev, 4) || !aligned(sel_off_dev, 4) ||
+      !aligned(table_dev, 4) || !aligned(loads_dev, 4) || !aligned(load_count_dev, 4))
+    return LSA_ERR_INVALID_ARGUMENT;
+  const void* k_dev = pinned_device_pointer(k_host);
+  const void* v_dev = v_host ? pinned_device_pointer(v_host) : nullptr;
+  if (!k_dev || (v_host && !v_dev)) return LSA_ERR_INVALID_ARGUMENT;
+  (void)hipGetLastError();
+  return hip_status(launch_pool_delta(s, k_dev, kb, v_dev, vb, tok_off_dev, chunk_off_dev,
+                                      sel_idx_dev, sel_off_dev, table_dev, loads_dev,
+                                      load_count_dev, k_pool_dev, v_pool_dev,
+                                      static_cast<hipStream_t>(hip_stream)));
+}
+
 lsa_status lsa_sparse_decode_attn(const lsa_shape* shape, int32_t kv_mode, const void* q_dev,
                                   const void* k_base_dev, const void* v_base_dev,
                                   const int64_t* tok_off_dev, const int32_t* sel_idx_dev,

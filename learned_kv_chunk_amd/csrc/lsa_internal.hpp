@@ -95,6 +95,13 @@ hipError_t launch_select_threshold(const lsa_shape& s, const float* scores,
                                    const int32_t* chunk_off, float threshold, int32_t max_keep,
                                    int32_t* sel_off, int32_t* sel_idx, int32_t* fallback,
                                    int32_t* counts, hipStream_t st);
+int32_t pool_delta_max_stream_chunks();
+hipError_t launch_pool_delta(const lsa_shape& s, const void* k_host_dev, int32_t k_row_bytes,
+                             const void* v_host_dev, int32_t v_row_bytes,
+                             const int64_t* tok_off, const int32_t* chunk_off,
+                             const int32_t* sel_idx, const int32_t* sel_off, int32_t* table,
+                             int32_t* loads, int32_t* load_count, void* k_pool, void* v_pool,
+                             hipStream_t st);
 // Attention partial kernels (one per kernel family) and the merge.
 bool mqa_attn_supported(const lsa_shape& s);
 hipError_t launch_attn_mqa(const lsa_shape& s, const AttnArgs& a, int64_t grid, hipStream_t st);

@@ -100,6 +100,8 @@ _SIGNATURES = {
     "lsa_select_threshold": ([ctypes.POINTER(Shape), _P, _P, ctypes.c_float, _I32, _P, _P, _P,
                               _P, ctypes.c_size_t, _P], _I32),
     "lsa_gather_chunks": ([ctypes.POINTER(Shape), _P, _P, _P, _P, _P, _P, _P, _P], _I32),
+    "lsa_pool_delta_update": ([ctypes.POINTER(Shape), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                               _P], _I32),
     "lsa_sparse_decode_attn": ([ctypes.POINTER(Shape), _I32, _P, _P, _P, _P, _P, _P, _P, _P,
                                 _P, ctypes.c_size_t, _P], _I32),
     "lsa_decode_step": ([ctypes.POINTER(Shape), ctypes.POINTER(StepArgs), _P, ctypes.c_size_t,
@@ -347,6 +349,49 @@ def gather_chunks(shape: ProblemShape, k_store, v_store, tok_off, sel_idx, sel_o
                                        _ptr(k_pool), _ptr(v_pool), _stream(stream)),
            "lsa_gather_chunks")
     return k_pool, v_pool
+
+
+def _pinned(t, name: str, dtype):
+    if not isinstance(t, torch.Tensor) or t.is_cuda or not t.is_pinned():
+        raise ValueError(f"{name} must be a page-locked (pinned) host tensor")
+    if not t.is_contiguous() or t.dtype != dtype or t.dim() != 2:
+        raise ValueError(f"{name} must be a contiguous 2-D {dtype} tensor")
+    return t
+
+
+def pool_delta_update(shape: ProblemShape, k_host, v_host, tok_off, chunk_off, sel_idx, sel_off,
+                      table, k_pool, v_pool=None, loads=None, load_count=None, stream=None):
+    """lsa_pool_delta_update: copies the newly kept chunks from the pinned host
+    stores into the pool and rewrites the slot table in place; returns
+    (loads [total_k], load_count [B]) int32 device tensors."""
+    _pinned(k_host, "k_host", shape.dtype)
+    if shape.v_aliases_k:
+        if v_host is not None or v_pool is not None:
+            raise ValueError("v_host / v_pool must be None when V aliases K")
+    else:
+        _pinned(v_host, "v_host", shape.dtype)
+        _dev(v_pool, "v_pool", shape.dtype)
+    _dev(k_pool, "k_pool", shape.dtype)
+    for t, n in ((tok_off, "tok_off"),):
+        _dev(t, n, torch.int64, 1)
+    for t, n in ((chunk_off, "chunk_off"), (sel_idx, "sel_idx"), (sel_off, "sel_off"),
+                 (table, "table")):
+        _dev(t, n, torch.int32, 1)
+    dev = table.device
+    if loads is None:
+        loads = torch.empty(shape.total_k, dtype=torch.int32, device=dev)
+    if load_count is None:
+        load_count = torch.empty(shape.batch, dtype=torch.int32, device=dev)
+    _dev(loads, "loads", torch.int32, 1)
+    _dev(load_count, "load_count", torch.int32, 1)
+    if table.numel() != shape.total_k or loads.numel() != shape.total_k or \
+            load_count.numel() != shape.batch:
+        raise ValueError("table / loads / load_count sizes do not match the shape")
+    _check(library().lsa_pool_delta_update(
+        ctypes.byref(shape.c()), _ptr(k_host), _ptr(v_host), _ptr(tok_off), _ptr(chunk_off),
+        _ptr(sel_idx), _ptr(sel_off), _ptr(table), _ptr(loads), _ptr(load_count), _ptr(k_pool),
+        _ptr(v_pool), _stream(stream)), "lsa_pool_delta_update")
+    return loads, load_count
 
 
 def sparse_decode_attn(shape: ProblemShape, q, k_base, v_base, tok_off, sel_idx, sel_off,

@@ -46,7 +46,7 @@ DTYPES = ("f32", "bf16")
 
 # purpose tags of the random streams
 (_P_LENGTHS, _P_QIDX, _P_EMB, _P_NEEDLE_POS, _P_NEEDLE_DIR, _P_K, _P_V, _P_Q,
- _P_MH_Q, _P_MH_W, _P_MH_KEY) = range(11)
+ _P_MH_Q, _P_MH_W, _P_MH_KEY, _P_DRIFT) = range(12)
 
 _ROWS_PER_BLOCK = 1 << 14
 
@@ -264,6 +264,22 @@ def make_workload(cfg: Config) -> Workload:
                                                     cfg.head_dim_v, cfg.kv_std)
     return Workload(cfg=cfg, lengths=lengths, tok_off=tok_off, chunk_off=chunk_off, keep=keep,
                     sel_off=sel_off, q_idx=q_idx, emb=emb, needles=needles, K=K, V=V)
+
+
+def drift_query(w: Workload, epoch: int, eps: float = 0.5) -> np.ndarray:
+    """Indexer queries of re-index epoch `epoch` under drift: per stream
+    normalize(q + eps * g) with q the workload's query (as drawn, before
+    rounding) and g a unit Gaussian direction of its own per (stream, epoch);
+    epoch 0 returns the workload's own queries.  Encoded like q_idx."""
+    if epoch == 0:
+        return w.q_idx.copy()
+    cfg = w.cfg
+    rows = []
+    for b in range(cfg.batch):
+        q = _unit_rows(_rng(cfg, _P_QIDX, b).standard_normal(cfg.index_dim))
+        g = _unit_rows(_rng(cfg, _P_DRIFT, b, epoch).standard_normal(cfg.index_dim))
+        rows.append(_unit_rows(q + eps * g))
+    return _encode(np.stack(rows).astype(np.float32), cfg.dtype)
 
 
 def small_variant(name: str, **overrides) -> Config:

@@ -241,3 +241,37 @@ def test_threshold_select_validation():
     assert _thr(s, fb=ctypes.c_void_p(0x100002)) == lsa.LSA_ERR_INVALID_ARGUMENT
     assert _thr(s, ws_bytes=need - 1) == lsa.LSA_ERR_WORKSPACE_TOO_SMALL
     assert _thr(shape(max_chunks=65537, total_chunks=16 * 65537)) == lsa.LSA_ERR_UNSUPPORTED
+
+
+def _delta(s, k_host, v_host=DUMMY, pool_v=DUMMY, **kw):
+    args = dict(tok=DUMMY, co=DUMMY, sel=DUMMY, so=DUMMY, table=DUMMY, loads=DUMMY, cnt=DUMMY,
+                pool_k=DUMMY)
+    args.update(kw)
+    return lsa.library().lsa_pool_delta_update(
+        ctypes.byref(s.c()), k_host, v_host, args["tok"], args["co"], args["sel"], args["so"],
+        args["table"], args["loads"], args["cnt"], args["pool_k"], pool_v, None)
+
+
+def test_pool_delta_validation():
+    import numpy as np
+    s = shape()
+    plain = np.zeros(4096, np.uint8)            # ordinary (not page-locked) host memory
+    p = ctypes.c_void_p(plain.ctypes.data)
+    assert _delta(s, None) == lsa.LSA_ERR_INVALID_ARGUMENT
+    assert _delta(s, DUMMY, table=None) == lsa.LSA_ERR_INVALID_ARGUMENT
+    assert _delta(s, DUMMY, v_host=None) == lsa.LSA_ERR_INVALID_ARGUMENT   # V needed
+    assert _delta(shape(v_aliases_k=True, head_dim_v=64), DUMMY) == lsa.LSA_ERR_INVALID_ARGUMENT
+    assert _delta(s, DUMMY, loads=ctypes.c_void_p(0x100002)) == lsa.LSA_ERR_INVALID_ARGUMENT
+    assert _delta(shape(max_chunks=65537, total_chunks=16 * 65537), DUMMY) == \
+        lsa.LSA_ERR_UNSUPPORTED
+    assert _delta(shape(head_dim_qk=6, head_dim_v=6, dtype=torch.float32), DUMMY) == \
+        lsa.LSA_ERR_UNSUPPORTED                                             # 16-byte rows
+    # pointers that are not page-locked host memory are refused before any launch
+    assert _delta(s, p, v_host=p) == lsa.LSA_ERR_INVALID_ARGUMENT
+    with pytest.raises(ValueError):
+        lsa.pool_delta_update(lsa.ProblemShape(**{**dict(
+            batch=1, chunk_size=64, index_dim=128, num_q_heads=16, head_dim_qk=128,
+            head_dim_v=128, v_aliases_k=False, dtype=torch.bfloat16, softmax_scale=0.1,
+            max_chunks=4, max_k=2, total_chunks=4, total_k=2)}),
+            torch.zeros(256, 128, dtype=torch.bfloat16), None, None, None, None, None, None,
+            None)
