@@ -371,6 +371,202 @@ def run_retriever(args):
     print(json.dumps(line), flush=True)
 
 
+LINK_PEAK_GBS = 64.0   # MI355X host interface, PCIe 5.0 x16, one direction (published)
+
+
+def run_residency(args):
+    """Times decode with delta residency on a pool workload: every
+    `reindex_every` steps the drifting indexer query is re-scored and
+    re-selected and only the newly kept chunks are copied from the pinned host
+    store into the pool (lsa_pool_delta_update); every step attends from the
+    pool through the slot table.  Attention steps are replayed from a HIP
+    graph; the re-index phase runs eagerly (its host-link copy dominates)."""
+    import numpy as np
+    import torch
+
+    from learned_kv_chunk_amd import device as dev
+    from learned_kv_chunk_amd import lsa
+    from learned_kv_chunk_amd import workloads as wl
+
+    name = args.config if args.config != DEFAULT_CONFIG else "cfg3"
+    cfg = wl.CONFIGS[name]
+    R = args.reindex_every or max(cfg.reindex_every, 1)
+    eps = args.drift
+    w = wl.make_workload(cfg)
+    d = dev.upload(w, "cuda")
+    shape = d.shape
+    c = cfg
+    dt = shape.dtype
+
+    def pinned(a):
+        t = torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16) \
+            if a.dtype == np.uint16 else torch.from_numpy(np.ascontiguousarray(a))
+        return t.pin_memory()
+
+    kh = pinned(w.K)
+    vh = None if w.V is None else pinned(w.V)
+    k_pool = torch.empty((shape.total_k, c.chunk_size, c.head_dim_qk), dtype=dt, device="cuda")
+    v_pool = None if w.V is None else torch.empty((shape.total_k, c.chunk_size, c.head_dim_v),
+                                                  dtype=dt, device="cuda")
+    table = torch.full((shape.total_k,), -1, dtype=torch.int32, device="cuda")
+    loads = torch.empty(shape.total_k, dtype=torch.int32, device="cuda")
+    cnt = torch.empty(shape.batch, dtype=torch.int32, device="cuda")
+    out = torch.empty_like(d.out)
+    lse = torch.empty_like(d.lse)
+    aws = lsa.allocate_workspace(shape, "cuda")
+    n_epochs = max(2, args.epochs)
+    qs_idx = []
+    for e in range(n_epochs + 1):
+        q = wl.drift_query(w, e, eps)
+        qs_idx.append(torch.from_numpy(q.view(np.int16)).view(torch.bfloat16).cuda()
+                      if q.dtype == np.uint16 else torch.from_numpy(q).cuda())
+    nq = 8
+    qs = [d.queries(t) for t in range(nq)]
+    row = (c.head_dim_qk + (0 if c.v_aliases_k else c.head_dim_v)) * (2 if c.dtype == "bf16" else 4)
+    chunk_bytes = c.chunk_size * row
+
+    def reindex(e):
+        lsa.score(shape, qs_idx[e], d.emb, d.chunk_off, d.scores)
+        lsa.select_topk(shape, d.scores, d.chunk_off, d.sel_off, d.sel_idx)
+        lsa.pool_delta_update(shape, kh, vh, d.tok_off, d.chunk_off, d.sel_idx, d.sel_off, table,
+                              k_pool, v_pool, loads, cnt)
+
+    def attend(i):
+        lsa.sparse_decode_attn(shape, qs[i % nq], k_pool, v_pool, d.tok_off, table, d.sel_off,
+                               lsa.KV_POOL, out, lse, aws)
+
+    # epoch 0 fills the pool from empty (every kept chunk crosses the link)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    reindex(0)
+    e1.record()
+    torch.cuda.synchronize()
+    fill_us = e0.elapsed_time(e1) * 1e3
+    fill_loads = int(dev.to_host(cnt).sum())
+
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for i in range(R):
+            attend(i)
+    graph.replay()
+    torch.cuda.synchronize()
+
+    # timed: epochs 1..n, each a re-index with the drifted query and R steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(n_epochs)]
+    churn = []
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    for e in range(n_epochs):
+        a, b, cc = ev[e]
+        a.record()
+        reindex(e + 1)
+        b.record()
+        graph.replay()
+        cc.record()
+        churn.append(cnt.clone())
+    t1.record()
+    torch.cuda.synchronize()
+    total_us = t0.elapsed_time(t1) * 1e3
+    reidx_us = [a.elapsed_time(b) * 1e3 for a, b, _ in ev]
+    attn_us = [b.elapsed_time(cc) * 1e3 / R for _, b, cc in ev]
+    loads_per = [int(dev.to_host(x).sum()) for x in churn]
+    steps = n_epochs * R
+    link_bytes = [n * chunk_bytes for n in loads_per]
+
+    # the delta copy kernel alone: HIP events around one update of a fresh epoch
+    # whose kept set differs from the pool's
+    reindex_parts = []
+    for e in range(2):
+        lsa.score(shape, qs_idx[(n_epochs + e) % (n_epochs + 1)], d.emb, d.chunk_off, d.scores)
+        lsa.select_topk(shape, d.scores, d.chunk_off, d.sel_off, d.sel_idx)
+        x0, x1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        x0.record()
+        lsa.pool_delta_update(shape, kh, vh, d.tok_off, d.chunk_off, d.sel_idx, d.sel_off, table,
+                              k_pool, v_pool, loads, cnt)
+        x1.record()
+        torch.cuda.synchronize()
+        reindex_parts.append((x0.elapsed_time(x1) * 1e3, int(dev.to_host(cnt).sum()) * chunk_bytes))
+    delta_us, delta_bytes = reindex_parts[-1]
+
+    # the link's achievable rate: one pinned host-to-device copy of the same size
+    nb = max(delta_bytes, 1 << 20)
+    src = torch.empty(nb, dtype=torch.uint8).pin_memory()
+    dst = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    dst.copy_(src, non_blocking=True)
+    torch.cuda.synchronize()
+    y0, y1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    y0.record()
+    for _ in range(5):
+        dst.copy_(src, non_blocking=True)
+    y1.record()
+    torch.cuda.synchronize()
+    memcpy_gbs = 5 * nb / (y0.elapsed_time(y1) * 1e3) / 1e3
+
+    delta_gbs = delta_bytes / delta_us / 1e3
+    line = {
+        "metric": "decode steps/sec with delta residency over a pinned host store "
+                  f"(re-index every {R} steps, drifting query)",
+        "value": steps / total_us * 1e6, "unit": "steps/s", "n_gpus": 1, "steps": steps,
+        "warmup": 1, "ms_per_step": total_us / steps / 1e3, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": c.dtype, "data": "synthetic",
+        "config": {"workload": f"{name}: {WORKLOAD_TEXT[name]}; host-resident K/V, pool of the "
+                               f"kept chunks", "reindex_every": R, "drift_eps": eps,
+                   "epochs": n_epochs,
+                   "timing": "attention steps replayed from a HIP graph, re-index eager"},
+        "fill_from_empty": {"chunks": fill_loads, "bytes": fill_loads * chunk_bytes,
+                            "us": fill_us},
+        "chunks_loaded_per_reindex": loads_per,
+        "link_bytes_per_reindex": link_bytes,
+        "reindex_us": reidx_us,
+        "attention_us_per_step": attn_us,
+        "resident_bytes": int(shape.total_k) * chunk_bytes,
+        "history_bytes": int(w.tok_off[-1]) * row,
+        "roofline": {"kernel": "pool_delta_kernel + pool_load_kernel (host link)",
+                     "bound": "link", "achieved": delta_gbs, "peak": LINK_PEAK_GBS,
+                     "unit": "GB/s", "frac": delta_gbs / LINK_PEAK_GBS, "traffic": None,
+                     "algorithmic_bytes_per_launch": int(delta_bytes), "avg_launch_us": delta_us,
+                     "pinned_memcpy_gbs": memcpy_gbs},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        from oracle import oracle
+
+        threads = max(1, len(os.sched_getaffinity(0)))
+        tab = np.full(int(shape.total_k), -1, np.int32)
+        pool_k = np.zeros((int(shape.total_k), c.chunk_size) + w.K.shape[1:], w.K.dtype)
+        t_start = time.perf_counter()
+        steps_done = reidx_done = 0
+        e = 0
+        while True:
+            if steps_done % R == 0:
+                q = wl.drift_query(w, e, eps)
+                sc = oracle.score(q, w.emb, w.chunk_off)
+                sel = oracle.select(sc, w.chunk_off, w.sel_off)
+                tab, ld, n = oracle.pool_delta(w.chunk_off, sel, w.sel_off, tab)
+                for b in range(w.B):       # copy only the loaded slots
+                    for p in ld[w.sel_off[b]:w.sel_off[b] + n[b]]:
+                        pool_k[p] = oracle.gather(w.K[w.tok_off[b]:w.tok_off[b + 1]], c.chunk_size,
+                                                  np.array([0, w.lengths[b]], np.int64),
+                                                  np.array([tab[p]], np.int32),
+                                                  np.array([0, 1], np.int32))[0]
+                reidx_done += 1
+                e += 1
+            oracle.attention(w.queries(steps_done % 4), w.K, w.V, w.tok_off, sel, w.sel_off,
+                             c.chunk_size, c.softmax_scale, dv=c.head_dim_v, nthreads=threads)
+            steps_done += 1
+            el = time.perf_counter() - t_start
+            if el >= args.cpu_seconds:
+                break
+        line["cpu_baseline"] = {
+            "value": steps_done / el, "unit": "steps/s", "cores": threads, "kind": "oracle",
+            "sample": f"{steps_done} decode step(s) with {reidx_done} re-index(es) in {el:.1f} s "
+                      f"(scoring, select, slot table and K chunk copies single-threaded; "
+                      f"attention with OpenMP over (stream, head))"}
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -383,7 +579,11 @@ def main():
     ap.add_argument("--tiles-per-block", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--mode", choices=["step", "copy", "scorer", "retriever"], default="step")
+    ap.add_argument("--mode", choices=["step", "copy", "scorer", "retriever", "residency"],
+                    default="step")
+    ap.add_argument("--drift", type=float, default=0.5,
+                    help="residency mode: indexer query drift per re-index epoch")
+    ap.add_argument("--epochs", type=int, default=4, help="residency mode: timed re-index epochs")
     ap.add_argument("--copy-mib", type=int, default=1024)
     args = ap.parse_args()
 
@@ -410,6 +610,9 @@ def main():
         return
     if args.mode == "retriever":
         run_retriever(args)
+        return
+    if args.mode == "residency":
+        run_residency(args)
         return
 
     cfg = wl.CONFIGS[args.config]
