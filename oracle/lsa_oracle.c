@@ -26,6 +26,9 @@
  *   oracle_pool_delta  the pool's slot table after a re-index when only the
  *                     newly kept chunks are copied in (wiki note flowchart,
  *                     the swap between GPU and host memory).
+ *   oracle_keep_recent  the attention keep set of a context that grew since
+ *                     the last re-index: kept chunks, the last scored chunk
+ *                     and the chunks not yet scored.
  */
 #include "lsa_oracle.h"
 
@@ -325,5 +328,34 @@ void oracle_pool_delta(int32_t B, const int32_t* chunk_off, const int32_t* sel_i
     free(free_slots);
     free(held);
     free(wanted);
+  }
+}
+
+void oracle_keep_recent(int32_t B, int32_t C, const int64_t* seq_len, const int32_t* chunk_off,
+                        const int32_t* sel_idx, const int32_t* sel_off, int32_t max_recent,
+                        int32_t* out_idx, int32_t* out_off) {
+  out_off[0] = 0;
+  for (int32_t b = 0; b < B; ++b) {
+    const int32_t m = chunk_off[b + 1] - chunk_off[b];
+    const int32_t k = sel_off[b + 1] - sel_off[b];
+    const int64_t len = seq_len[b];
+    const int32_t total = (int32_t)((len + C - 1) / C);
+    int32_t* out = out_idx + out_off[b];
+    int32_t n = 0;
+    int32_t last_kept = 0;
+    for (int32_t i = 0; i < k; ++i) {
+      out[n++] = sel_idx[sel_off[b] + i];
+      if (sel_idx[sel_off[b] + i] == m - 1) last_kept = 1;
+    }
+    int32_t extra = 0;
+    if (m > 0 && !last_kept && extra < max_recent) {
+      out[n++] = m - 1;
+      ++extra;
+    }
+    for (int32_t c = m; c < total && extra < max_recent; ++c) {
+      out[n++] = c;
+      ++extra;
+    }
+    out_off[b + 1] = out_off[b] + n;
   }
 }

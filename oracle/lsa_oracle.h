@@ -145,6 +145,21 @@ void oracle_pool_delta(int32_t B, const int32_t* chunk_off, const int32_t* sel_i
                        const int32_t* sel_off, const int32_t* table_in, int32_t* table_out,
                        int32_t* loads, int32_t* load_count);
 
+/* Attention keep set of a growing context (dimensionstp review section
+ * 3-2-3 steps 2 and 7: history goes to the cache and decode attends to the
+ * kept chunks; the pages say nothing of tokens added after the last
+ * re-index, so this is this build's reading): the chunks of the last
+ * selection (ascending, all below M_b = chunk_off[b+1]-chunk_off[b], the
+ * chunks the indexer has scored), plus the last scored chunk M_b-1 when it
+ * was not kept (it was the partial tail when scored and may have grown
+ * since), plus every chunk from M_b to ceil(seq_len[b]/C)-1 (not yet
+ * scored): at most max_recent chunks beyond the kept ones per stream, in
+ * that order.  Writes the ascending union to out_idx[out_off[b] ..] with
+ * out_off[B+1] its running totals. */
+void oracle_keep_recent(int32_t B, int32_t C, const int64_t* seq_len, const int32_t* chunk_off,
+                        const int32_t* sel_idx, const int32_t* sel_off, int32_t max_recent,
+                        int32_t* out_idx, int32_t* out_off);
+
 /* Threads an OpenMP region may use here (1 when built without OpenMP). */
 int32_t oracle_max_threads(void);
 

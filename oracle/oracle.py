@@ -22,6 +22,8 @@ Step definitions (cited to the pages' sections, see ``lsa_oracle.c``):
              sections 4-3 and 5-1)
   pool_delta the pool's slot table after a re-index when only newly kept
              chunks are copied in from host memory (wiki note flowchart)
+  keep_recent the attention keep set of a context grown since the last
+             re-index: kept chunks, the last scored chunk, unscored chunks
   decode     the review's decode loop (section 3-2-3 steps 3-7): re-score and
              re-select every ``reindex_every`` steps, attend every step.
 """
@@ -84,6 +86,8 @@ def _load():
         lib.oracle_select_threshold.restype = None
         lib.oracle_pool_delta.argtypes = [i32, P, P, P, P, P, P, P]
         lib.oracle_pool_delta.restype = None
+        lib.oracle_keep_recent.argtypes = [i32, i32, P, P, P, P, i32, P, P]
+        lib.oracle_keep_recent.restype = None
         lib.oracle_max_threads.argtypes = []
         lib.oracle_max_threads.restype = i32
         _lib = lib
@@ -229,6 +233,21 @@ def pool_delta(chunk_off: np.ndarray, sel_idx: np.ndarray, sel_off: np.ndarray,
     _load().oracle_pool_delta(B, _ptr(chunk_off), _ptr(sel_idx), _ptr(sel_off), _ptr(table),
                               _ptr(out), _ptr(loads), _ptr(count))
     return out, loads[:len(table)], count
+
+
+def keep_recent(C: int, seq_len: np.ndarray, chunk_off: np.ndarray, sel_idx: np.ndarray,
+                sel_off: np.ndarray, max_recent: int) -> tuple[np.ndarray, np.ndarray]:
+    """(out_off [B+1], ascending attention keep set) of a grown context."""
+    seq_len = np.ascontiguousarray(seq_len, dtype=np.int64)
+    chunk_off = np.ascontiguousarray(chunk_off, dtype=np.int32)
+    sel_idx = np.ascontiguousarray(sel_idx, dtype=np.int32)
+    sel_off = np.ascontiguousarray(sel_off, dtype=np.int32)
+    B = len(seq_len)
+    out = np.empty(int(sel_off[-1]) + B * max(0, max_recent) + 1, dtype=np.int32)
+    off = np.empty(B + 1, dtype=np.int32)
+    _load().oracle_keep_recent(B, C, _ptr(seq_len), _ptr(chunk_off), _ptr(sel_idx),
+                               _ptr(sel_off), int(max_recent), _ptr(out), _ptr(off))
+    return off, out[:int(off[-1])].copy()
 
 
 def attention(Q: np.ndarray, K: np.ndarray, V: np.ndarray | None, tok_off: np.ndarray,

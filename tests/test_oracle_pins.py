@@ -638,3 +638,50 @@ def test_pool_delta_invariants_and_pool_contents():
         np.testing.assert_array_equal(again, new)
         assert (count2 == 0).all()
         table = new
+
+
+# --- attention keep set of a growing context -------------------------------------
+
+def test_keep_recent_golden():
+    g = _golden("keep_recent.json")
+    for case in g["cases"]:
+        off, idx = oracle.keep_recent(g["C"], np.array(g["seq_len"]), np.array(g["chunk_off"]),
+                                      np.array(g["sel_idx"]), np.array(g["sel_off"]),
+                                      case["max_recent"])
+        assert off.tolist() == case["out_off"] and idx.tolist() == case["out_idx"], case
+
+
+def test_keep_recent_properties_and_grown_attention():
+    rng = np.random.default_rng(17)
+    C = 8
+    L0 = np.array([40, 33, 8, 100])
+    M = (L0 + C - 1) // C
+    grow = np.array([0, 7, 30, 12])   # stream 3 fills its partial chunk and starts two more
+    L = L0 + grow
+    co = np.concatenate([[0], np.cumsum(M)]).astype(np.int32)
+    k = np.array([2, 1, 1, 5])
+    so = np.concatenate([[0], np.cumsum(k)]).astype(np.int32)
+    sel = np.concatenate([np.sort(rng.choice(m, size=kk, replace=False)) for m, kk in zip(M, k)])
+    off, idx = oracle.keep_recent(C, L, co, sel, so, 64)
+    for b in range(4):
+        got = idx[off[b]:off[b + 1]].tolist()
+        want = set(sel[so[b]:so[b + 1]].tolist()) | {int(M[b]) - 1} | \
+            set(range(int(M[b]), int((L[b] + C - 1) // C)))
+        assert got == sorted(want)
+    # attention over the keep set of the grown context equals attention over
+    # the kept chunks' tokens plus every token appended since (all of them lie
+    # in the last scored chunk or in unscored chunks)
+    D = 16
+    K = rng.standard_normal((int(L.sum()), D)).astype(np.float32)
+    V = rng.standard_normal((int(L.sum()), D)).astype(np.float32)
+    Q = rng.standard_normal((4, 2, D)).astype(np.float32)
+    tok = np.concatenate([[0], np.cumsum(L)]).astype(np.int64)
+    o1, l1 = oracle.attention(Q, K, V, tok, idx, off, C, 0.25)
+    for b in range(4):
+        rows = [t for c in sel[so[b]:so[b + 1]] for t in range(c * C, min(c * C + C, L[b]))]
+        rows = sorted(set(rows) | set(range(int(L0[b]), int(L[b]))) |
+                      set(range((int(M[b]) - 1) * C, min(int(M[b]) * C, int(L[b])))))
+        x = K[tok[b] + np.array(rows)].astype(np.float64) @ Q[b].T.astype(np.float64) * 0.25
+        wgt = scipy.special.softmax(x, axis=0)
+        np.testing.assert_allclose(o1[b], wgt.T @ V[tok[b] + np.array(rows)].astype(np.float64),
+                                   rtol=1e-10, atol=1e-12)
