@@ -244,6 +244,50 @@ lsa_status lsa_gather_chunks(const lsa_shape* shape, const void* k_store_dev,
                              void* k_pool_dev, void* v_pool_dev, void* hip_stream);
 
 /* ---------------------------------------------------------------------------
+ * Decode-time growth of the context.  Dimensionstp review section 3-2-3,
+ * steps 2 and 7: new history goes to the cache and decode attends to the
+ * kept chunks.  The stores use a capacity layout: stream b owns rows
+ * base_off[b] .. base_off[b+1]-1 (int64 [B+1], base_off[0] = 0) of which the
+ * first seq_len[b] (int64 [B], device) hold tokens.
+ * lsa_append_kv: writes k_new[b] ([B][head_dim_qk]) and v_new[b]
+ *   ([B][head_dim_v]; NULL when v_aliases_k) as row seq_len[b] of stream b
+ *   and increments seq_len[b]; a stream whose rows are all used is left
+ *   unchanged.  Rows must be multiples of 16 bytes (else UNSUPPORTED); all
+ *   pointers 16-byte aligned (offsets 8).
+ * lsa_keep_recent: the keep set attention needs once the context grew after
+ *   the last re-index (the pages are silent on those tokens; this library's
+ *   reading): per stream, the kept chunks sel_idx (ascending, all below M_b =
+ *   chunk_off[b+1]-chunk_off[b], the chunks the indexer scored), then the
+ *   last scored chunk M_b-1 unless kept (it was the partial tail when scored
+ *   and may have grown since), then every chunk from M_b to
+ *   ceil(seq_len[b]/C)-1; at most max_recent chunks beyond the kept ones.
+ *   Writes the ascending union to out_sel_idx_dev (room for total_k +
+ *   B*max_recent) and its CSR offsets to out_sel_off_dev [B+1], computed on
+ *   the device.  Attention over it takes a shape whose total_k / max_k are
+ *   the bounds total_k + B*max_recent / max_k + max_recent and whose chunk
+ *   bounds cover the capacity.
+ * lsa_sparse_decode_attn_varlen: lsa_sparse_decode_attn over the capacity
+ *   layout: rows of stream b start at base_off[b] and L_b = seq_len[b]
+ *   (clamped to the capacity).  Same kernels, same workspace.
+ * ------------------------------------------------------------------------- */
+lsa_status lsa_append_kv(const lsa_shape* shape, const void* k_new_dev, const void* v_new_dev,
+                         const int64_t* base_off_dev, int64_t* seq_len_dev, void* k_store_dev,
+                         void* v_store_dev, void* hip_stream);
+
+lsa_status lsa_keep_recent(const lsa_shape* shape, const int64_t* seq_len_dev,
+                           const int32_t* chunk_off_dev, const int32_t* sel_idx_dev,
+                           const int32_t* sel_off_dev, int32_t max_recent,
+                           int32_t* out_sel_idx_dev, int32_t* out_sel_off_dev, void* hip_stream);
+
+lsa_status lsa_sparse_decode_attn_varlen(const lsa_shape* shape, int32_t kv_mode,
+                                         const void* q_dev, const void* k_base_dev,
+                                         const void* v_base_dev, const int64_t* base_off_dev,
+                                         const int64_t* seq_len_dev, const int32_t* sel_idx_dev,
+                                         const int32_t* sel_off_dev, float* out_dev,
+                                         float* lse_dev, void* workspace_dev,
+                                         size_t workspace_bytes, void* hip_stream);
+
+/* ---------------------------------------------------------------------------
  * Delta residency of the chunk pool over a host-memory backing store.  Wiki
  * note flowchart: only the selected chunks stay resident on the GPU, the rest
  * of the cache lives in host memory and chunks are swapped in as the

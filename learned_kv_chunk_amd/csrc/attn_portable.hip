@@ -64,7 +64,9 @@ __global__ __launch_bounds__(kWave) void attn_portable_kernel(AttnArgs a) {
   __syncthreads();
 
   const int32_t sel0 = a.sel_off[b];
-  const int64_t len = a.tok_off[b + 1] - a.tok_off[b];
+  const int64_t cap = a.tok_off[b + 1] - a.tok_off[b];
+  const int64_t sl = a.seq_len ? a.seq_len[b] : cap;
+  const int64_t len = sl < 0 ? 0 : (sl < cap ? sl : cap);
   const int32_t t_begin = s_plan[1];
   const int32_t t_end = s_plan[2];
 

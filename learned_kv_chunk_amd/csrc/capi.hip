@@ -71,7 +71,8 @@ lsa_status hip_status(hipError_t e) { return e == hipSuccess ? LSA_OK : LSA_ERR_
 lsa_status enqueue_attention(const lsa_shape& s, int32_t kv_mode, const void* q, const void* kbase,
                              const void* vbase, const int64_t* tok_off, const int32_t* sel_idx,
                              const int32_t* sel_off, float* out, float* lse, void* ws,
-                             hipStream_t st, void* ev_begin = nullptr, void* ev_end = nullptr) {
+                             hipStream_t st, void* ev_begin = nullptr, void* ev_end = nullptr,
+                             const int64_t* seq_len = nullptr) {
   const AttnPlan plan = make_attn_plan(s, device_cu_count());
   const PartialLayout pl = partial_layout(s, plan);
   AttnArgs a;
@@ -79,6 +80,7 @@ lsa_status enqueue_attention(const lsa_shape& s, int32_t kv_mode, const void* q,
   a.k = kbase;
   a.v = s.v_aliases_k ? kbase : vbase;
   a.tok_off = tok_off;
+  a.seq_len = seq_len;
   a.sel_idx = sel_idx;
   a.sel_off = sel_off;
   a.out = out;
@@ -332,6 +334,68 @@ lsa_status lsa_sparse_decode_attn(const lsa_shape* shape, int32_t kv_mode, const
   return enqueue_attention(*shape, kv_mode, q_dev, k_base_dev, v_base_dev, tok_off_dev,
                            sel_idx_dev, sel_off_dev, out_dev, lse_dev, workspace_dev,
                            static_cast<hipStream_t>(hip_stream));
+}
+
+lsa_status lsa_sparse_decode_attn_varlen(const lsa_shape* shape, int32_t kv_mode,
+                                         const void* q_dev, const void* k_base_dev,
+                                         const void* v_base_dev, const int64_t* base_off_dev,
+                                         const int64_t* seq_len_dev, const int32_t* sel_idx_dev,
+                                         const int32_t* sel_off_dev, float* out_dev,
+                                         float* lse_dev, void* workspace_dev,
+                                         size_t workspace_bytes, void* hip_stream) {
+  lsa_status st = check_attn_args(shape, kv_mode, q_dev, k_base_dev, v_base_dev, base_off_dev,
+                                  sel_idx_dev, sel_off_dev, out_dev, lse_dev, workspace_dev,
+                                  workspace_bytes);
+  if (st != LSA_OK) return st;
+  if (!seq_len_dev || !aligned(seq_len_dev, 8)) return LSA_ERR_INVALID_ARGUMENT;
+  (void)hipGetLastError();
+  return enqueue_attention(*shape, kv_mode, q_dev, k_base_dev, v_base_dev, base_off_dev,
+                           sel_idx_dev, sel_off_dev, out_dev, lse_dev, workspace_dev,
+                           static_cast<hipStream_t>(hip_stream), nullptr, nullptr, seq_len_dev);
+}
+
+lsa_status lsa_append_kv(const lsa_shape* shape, const void* k_new_dev, const void* v_new_dev,
+                         const int64_t* base_off_dev, int64_t* seq_len_dev, void* k_store_dev,
+                         void* v_store_dev, void* hip_stream) {
+  lsa_status st = check_common(shape);
+  if (st != LSA_OK) return st;
+  const lsa_shape& s = *shape;
+  if (s.head_dim_qk < 1 || s.head_dim_v < 1 || (s.v_aliases_k != 0 && s.v_aliases_k != 1))
+    return LSA_ERR_INVALID_ARGUMENT;
+  const int32_t kb = s.head_dim_qk * elem_bytes(s);
+  const int32_t vb = s.v_aliases_k ? 0 : s.head_dim_v * elem_bytes(s);
+  if (kb % 16 != 0 || vb % 16 != 0) return LSA_ERR_UNSUPPORTED;
+  if (!k_new_dev || !base_off_dev || !seq_len_dev || !k_store_dev) return LSA_ERR_INVALID_ARGUMENT;
+  if (s.v_aliases_k ? (v_new_dev != nullptr || v_store_dev != nullptr)
+                    : (v_new_dev == nullptr || v_store_dev == nullptr))
+    return LSA_ERR_INVALID_ARGUMENT;
+  if (!aligned(k_new_dev, 16) || (v_new_dev && !aligned(v_new_dev, 16)) ||
+      !aligned(k_store_dev, 16) || (v_store_dev && !aligned(v_store_dev, 16)) ||
+      !aligned(base_off_dev, 8) || !aligned(seq_len_dev, 8))
+    return LSA_ERR_INVALID_ARGUMENT;
+  (void)hipGetLastError();
+  return hip_status(launch_append_kv(s, k_new_dev, v_new_dev, kb, vb, base_off_dev, seq_len_dev,
+                                     k_store_dev, v_store_dev,
+                                     static_cast<hipStream_t>(hip_stream)));
+}
+
+lsa_status lsa_keep_recent(const lsa_shape* shape, const int64_t* seq_len_dev,
+                           const int32_t* chunk_off_dev, const int32_t* sel_idx_dev,
+                           const int32_t* sel_off_dev, int32_t max_recent,
+                           int32_t* out_sel_idx_dev, int32_t* out_sel_off_dev, void* hip_stream) {
+  lsa_status st = check_common(shape);
+  if (st != LSA_OK) return st;
+  if (max_recent < 0) return LSA_ERR_INVALID_ARGUMENT;
+  if (!seq_len_dev || !chunk_off_dev || !sel_idx_dev || !sel_off_dev || !out_sel_idx_dev ||
+      !out_sel_off_dev)
+    return LSA_ERR_INVALID_ARGUMENT;
+  if (!aligned(seq_len_dev, 8) || !aligned(chunk_off_dev, 4) || !aligned(sel_idx_dev, 4) ||
+      !aligned(sel_off_dev, 4) || !aligned(out_sel_idx_dev, 4) || !aligned(out_sel_off_dev, 4))
+    return LSA_ERR_INVALID_ARGUMENT;
+  (void)hipGetLastError();
+  return hip_status(launch_keep_recent(*shape, seq_len_dev, chunk_off_dev, sel_idx_dev,
+                                       sel_off_dev, max_recent, out_sel_idx_dev, out_sel_off_dev,
+                                       static_cast<hipStream_t>(hip_stream)));
 }
 
 lsa_status lsa_decode_step(const lsa_shape* shape, const lsa_step_args* args, void* workspace_dev,

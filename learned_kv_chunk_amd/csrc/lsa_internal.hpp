@@ -61,7 +61,8 @@ struct AttnArgs {
   const void* q;          // [B][H][dqk]
   const void* k;          // store or pool
   const void* v;          // store or pool (== k when aliased)
-  const int64_t* tok_off;
+  const int64_t* tok_off;  // rows of stream b start at tok_off[b]
+  const int64_t* seq_len;  // L_b, or null: L_b = tok_off[b+1] - tok_off[b]
   const int32_t* sel_idx;
   const int32_t* sel_off;
   float* out;
@@ -96,6 +97,13 @@ hipError_t launch_select_threshold(const lsa_shape& s, const float* scores,
                                    int32_t* sel_off, int32_t* sel_idx, int32_t* fallback,
                                    int32_t* counts, hipStream_t st);
 int32_t pool_delta_max_stream_chunks();
+hipError_t launch_append_kv(const lsa_shape& s, const void* k_new, const void* v_new,
+                           int32_t k_row_bytes, int32_t v_row_bytes, const int64_t* base_off,
+                           int64_t* seq_len, void* k_store, void* v_store, hipStream_t st);
+hipError_t launch_keep_recent(const lsa_shape& s, const int64_t* seq_len,
+                              const int32_t* chunk_off, const int32_t* sel_idx,
+                              const int32_t* sel_off, int32_t max_recent, int32_t* out_idx,
+                              int32_t* out_off, hipStream_t st);
 hipError_t launch_pool_delta(const lsa_shape& s, const void* k_host_dev, int32_t k_row_bytes,
                              const void* v_host_dev, int32_t v_row_bytes,
                              const int64_t* tok_off, const int32_t* chunk_off,
@@ -224,9 +232,10 @@ __device__ __forceinline__ AttnRun attn_prologue(const AttnArgs& a, int32_t* s_s
       r.slot_first = r.t_begin / tpc;
       const int32_t nslots = min((r.t_end - 1) / tpc - r.slot_first + 1, kMaxRunSlots);
       const int64_t t0 = a.tok_off[b], t1 = a.tok_off[b + 1];
+      const int64_t sl = a.seq_len ? a.seq_len[b] : t1 - t0;
       for (int32_t i = lane; i < nslots; i += kWave) s_slot[i] = a.sel_idx[sel0 + r.slot_first + i];
       r.tb = t0;
-      r.len = t1 - t0;
+      r.len = sl < 0 ? 0 : (sl < t1 - t0 ? sl : t1 - t0);
     }
     if (lane == 0) *s_run = r;
   }

@@ -100,6 +100,10 @@ _SIGNATURES = {
     "lsa_select_threshold": ([ctypes.POINTER(Shape), _P, _P, ctypes.c_float, _I32, _P, _P, _P,
                               _P, ctypes.c_size_t, _P], _I32),
     "lsa_gather_chunks": ([ctypes.POINTER(Shape), _P, _P, _P, _P, _P, _P, _P, _P], _I32),
+    "lsa_append_kv": ([ctypes.POINTER(Shape), _P, _P, _P, _P, _P, _P, _P], _I32),
+    "lsa_keep_recent": ([ctypes.POINTER(Shape), _P, _P, _P, _P, _I32, _P, _P, _P], _I32),
+    "lsa_sparse_decode_attn_varlen": ([ctypes.POINTER(Shape), _I32, _P, _P, _P, _P, _P, _P, _P,
+                                       _P, _P, _P, ctypes.c_size_t, _P], _I32),
     "lsa_pool_delta_update": ([ctypes.POINTER(Shape), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                _P], _I32),
     "lsa_sparse_decode_attn": ([ctypes.POINTER(Shape), _I32, _P, _P, _P, _P, _P, _P, _P, _P,
@@ -349,6 +353,84 @@ def gather_chunks(shape: ProblemShape, k_store, v_store, tok_off, sel_idx, sel_o
                                        _ptr(k_pool), _ptr(v_pool), _stream(stream)),
            "lsa_gather_chunks")
     return k_pool, v_pool
+
+
+def append_kv(shape: ProblemShape, k_new, v_new, base_off, seq_len, k_store, v_store=None,
+              stream=None) -> None:
+    """lsa_append_kv: row seq_len[b] of each stream receives k_new[b] (and
+    v_new[b]); seq_len advances in place."""
+    _dev(k_new, "k_new", shape.dtype, 2)
+    _dev(k_store, "k_store", shape.dtype, 2)
+    if shape.v_aliases_k:
+        if v_new is not None or v_store is not None:
+            raise ValueError("v_new / v_store must be None when V aliases K")
+    else:
+        _dev(v_new, "v_new", shape.dtype, 2)
+        _dev(v_store, "v_store", shape.dtype, 2)
+    _dev(base_off, "base_off", torch.int64, 1)
+    _dev(seq_len, "seq_len", torch.int64, 1)
+    if k_new.shape[0] != shape.batch or seq_len.numel() != shape.batch or \
+            base_off.numel() != shape.batch + 1:
+        raise ValueError("k_new / seq_len / base_off sizes do not match the batch")
+    _check(library().lsa_append_kv(ctypes.byref(shape.c()), _ptr(k_new), _ptr(v_new),
+                                   _ptr(base_off), _ptr(seq_len), _ptr(k_store), _ptr(v_store),
+                                   _stream(stream)), "lsa_append_kv")
+
+
+def keep_recent(shape: ProblemShape, seq_len, chunk_off, sel_idx, sel_off, max_recent: int,
+                out_idx=None, out_off=None, stream=None):
+    """lsa_keep_recent: (out_off [B+1], out_idx [total_k + B*max_recent]) of
+    which the first out_off[B] indices are meaningful."""
+    _dev(seq_len, "seq_len", torch.int64, 1)
+    for t, n in ((chunk_off, "chunk_off"), (sel_idx, "sel_idx"), (sel_off, "sel_off")):
+        _dev(t, n, torch.int32, 1)
+    dev = sel_idx.device
+    cap = shape.total_k + shape.batch * max(0, int(max_recent))
+    if out_idx is None:
+        out_idx = torch.empty(max(cap, 1), dtype=torch.int32, device=dev)
+    if out_off is None:
+        out_off = torch.empty(shape.batch + 1, dtype=torch.int32, device=dev)
+    _dev(out_idx, "out_idx", torch.int32, 1)
+    _dev(out_off, "out_off", torch.int32, 1)
+    if out_idx.numel() < cap or out_off.numel() != shape.batch + 1:
+        raise ValueError("out_idx / out_off too small for the shape")
+    _check(library().lsa_keep_recent(ctypes.byref(shape.c()), _ptr(seq_len), _ptr(chunk_off),
+                                     _ptr(sel_idx), _ptr(sel_off), int(max_recent),
+                                     _ptr(out_idx), _ptr(out_off), _stream(stream)),
+           "lsa_keep_recent")
+    return out_off, out_idx
+
+
+def sparse_decode_attn_varlen(shape: ProblemShape, q, k_base, v_base, base_off, seq_len, sel_idx,
+                              sel_off, kv_mode: int = KV_STORE, out=None, lse=None,
+                              workspace=None, stream=None):
+    """lsa_sparse_decode_attn_varlen: (out [B, H, dv], lse [B, H]) over a
+    capacity layout (rows of stream b from base_off[b], L_b = seq_len[b])."""
+    _dev(q, "q", shape.dtype, 3)
+    _dev(k_base, "k_base", shape.dtype)
+    if shape.v_aliases_k:
+        if v_base is not None:
+            raise ValueError("v_base must be None when V aliases K")
+    else:
+        _dev(v_base, "v_base", shape.dtype)
+    _dev(base_off, "base_off", torch.int64, 1)
+    _dev(seq_len, "seq_len", torch.int64, 1)
+    _dev(sel_idx, "sel_idx", torch.int32, 1)
+    _dev(sel_off, "sel_off", torch.int32, 1)
+    dev = q.device
+    if out is None:
+        out = torch.empty((shape.batch, shape.num_q_heads, shape.head_dim_v),
+                          dtype=torch.float32, device=dev)
+    if lse is None:
+        lse = torch.empty((shape.batch, shape.num_q_heads), dtype=torch.float32, device=dev)
+    if workspace is None:
+        workspace = allocate_workspace(shape, dev)
+    _dev(workspace, "workspace", torch.uint8, 1)
+    _check(library().lsa_sparse_decode_attn_varlen(
+        ctypes.byref(shape.c()), int(kv_mode), _ptr(q), _ptr(k_base), _ptr(v_base),
+        _ptr(base_off), _ptr(seq_len), _ptr(sel_idx), _ptr(sel_off), _ptr(out), _ptr(lse),
+        _ptr(workspace), workspace.numel(), _stream(stream)), "lsa_sparse_decode_attn_varlen")
+    return out, lse
 
 
 def _pinned(t, name: str, dtype):

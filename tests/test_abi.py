@@ -275,3 +275,27 @@ def test_pool_delta_validation():
             max_chunks=4, max_k=2, total_chunks=4, total_k=2)}),
             torch.zeros(256, 128, dtype=torch.bfloat16), None, None, None, None, None, None,
             None)
+
+
+def test_append_and_keep_recent_validation():
+    s = shape()
+    lib = lsa.library()
+    ap = lambda sh, kn=DUMMY, vn=DUMMY, bo=DUMMY, sl=DUMMY, ks=DUMMY, vs=DUMMY: \
+        lib.lsa_append_kv(ctypes.byref(sh.c()), kn, vn, bo, sl, ks, vs, None)
+    assert ap(s, kn=None) == lsa.LSA_ERR_INVALID_ARGUMENT
+    assert ap(s, vn=None) == lsa.LSA_ERR_INVALID_ARGUMENT
+    assert ap(shape(v_aliases_k=True, head_dim_v=64)) == lsa.LSA_ERR_INVALID_ARGUMENT
+    assert ap(s, sl=ctypes.c_void_p(0x100004)) == lsa.LSA_ERR_INVALID_ARGUMENT
+    assert ap(shape(head_dim_qk=6, head_dim_v=6, dtype=torch.float32)) == lsa.LSA_ERR_UNSUPPORTED
+    kr = lambda sh, mr=4, sl=DUMMY, oi=DUMMY: lib.lsa_keep_recent(
+        ctypes.byref(sh.c()), sl, DUMMY, DUMMY, DUMMY, mr, oi, DUMMY, None)
+    assert kr(s, mr=-1) == lsa.LSA_ERR_INVALID_ARGUMENT
+    assert kr(s, sl=None) == lsa.LSA_ERR_INVALID_ARGUMENT
+    assert kr(s, oi=ctypes.c_void_p(0x100002)) == lsa.LSA_ERR_INVALID_ARGUMENT
+    assert kr(shape(batch=0)) == lsa.LSA_ERR_INVALID_ARGUMENT
+    need = lsa.workspace_bytes(s)
+    av = lambda sh, sl=DUMMY: lib.lsa_sparse_decode_attn_varlen(
+        ctypes.byref(sh.c()), lsa.KV_STORE, DUMMY, DUMMY, DUMMY, DUMMY, sl, DUMMY, DUMMY, DUMMY,
+        DUMMY, DUMMY, need, None)
+    assert av(s, sl=None) == lsa.LSA_ERR_INVALID_ARGUMENT
+    assert av(s, sl=ctypes.c_void_p(0x100004)) == lsa.LSA_ERR_INVALID_ARGUMENT
