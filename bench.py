@@ -514,7 +514,9 @@ def run_residency(args):
         "config": {"workload": f"{name}: {WORKLOAD_TEXT[name]}; host-resident K/V, pool of the "
                                f"kept chunks", "reindex_every": R, "drift_eps": eps,
                    "epochs": n_epochs,
-                   "timing": "attention steps replayed from a HIP graph, re-index eager"},
+                   "timing": "attention steps replayed from a HIP graph, re-index eager",
+                   "cache": "warm: the pool (107 MB) fits the 256 MB Infinity Cache and is "
+                            "re-read every step"},
         "fill_from_empty": {"chunks": fill_loads, "bytes": fill_loads * chunk_bytes,
                             "us": fill_us},
         "chunks_loaded_per_reindex": loads_per,
@@ -567,6 +569,166 @@ def run_residency(args):
     print(json.dumps(line), flush=True)
 
 
+def run_append(args):
+    """Times decode over a growing context: every step appends one K/V row per
+    stream (lsa_append_kv), builds the keep set of the grown context
+    (lsa_keep_recent: kept chunks, the last scored chunk, unscored chunks) and
+    attends over the capacity layout (lsa_sparse_decode_attn_varlen); every
+    `reindex_every` steps the scored chunks are re-scored and re-selected.
+    Everything runs on the device, so the timed steps are replayed from one
+    HIP graph; each replay starts from the same lengths."""
+    import dataclasses
+
+    import numpy as np
+    import torch
+
+    from learned_kv_chunk_amd import device as dev
+    from learned_kv_chunk_amd import lsa
+    from learned_kv_chunk_amd import workloads as wl
+
+    cfg = wl.CONFIGS[args.config]
+    C = cfg.chunk_size
+    R = args.reindex_every or 64
+    steps = args.steps
+    max_recent = 2 + (steps + C - 1) // C
+    w = wl.make_workload(cfg)
+    d = dev.upload(w, "cuda")
+    shape = d.shape
+    es = 2 if cfg.dtype == "bf16" else 4
+    L0 = w.lengths.astype(np.int64)
+    cap = L0 + steps + C
+    base = np.concatenate([[0], np.cumsum(cap)]).astype(np.int64)
+    dt = shape.dtype
+    kd = torch.empty((int(base[-1]), cfg.head_dim_qk), dtype=dt, device="cuda")
+    vd = None if w.V is None else torch.empty((int(base[-1]), cfg.head_dim_v), dtype=dt,
+                                                 device="cuda")
+    for b in range(w.B):
+        kd[base[b]:base[b] + L0[b]] = d.K[w.tok_off[b]:w.tok_off[b + 1]]
+        if vd is not None:
+            vd[base[b]:base[b] + L0[b]] = d.V[w.tok_off[b]:w.tok_off[b + 1]]
+    base_d = torch.from_numpy(base).cuda()
+    seq0 = torch.from_numpy(L0.copy()).cuda()
+    seq_d = seq0.clone()
+    g = torch.Generator(device="cuda")
+    g.manual_seed(0)
+    k_new = (torch.randn((steps, w.B, cfg.head_dim_qk), generator=g, device="cuda")
+             * cfg.kv_std).to(dt)
+    v_new = None if vd is None else (torch.randn((steps, w.B, cfg.head_dim_v), generator=g,
+                                                 device="cuda") * cfg.kv_std).to(dt)
+    n_cap = (cap + C - 1) // C
+    attn_shape = dataclasses.replace(
+        shape, max_chunks=int(n_cap.max()), total_chunks=int(n_cap.sum()),
+        max_k=shape.max_k + max_recent, total_k=shape.total_k + w.B * max_recent)
+    ws = lsa.allocate_workspace(attn_shape, "cuda")
+    out_idx = torch.empty(attn_shape.total_k, dtype=torch.int32, device="cuda")
+    out_off = torch.empty(w.B + 1, dtype=torch.int32, device="cuda")
+    out = torch.empty_like(d.out)
+    lse = torch.empty_like(d.lse)
+    nq = 8
+    qs = [d.queries(t) for t in range(nq)]
+
+    def step(t):
+        if t % R == 0:
+            lsa.score(shape, d.q_idx, d.emb, d.chunk_off, d.scores)
+            lsa.select_topk(shape, d.scores, d.chunk_off, d.sel_off, d.sel_idx)
+        lsa.append_kv(shape, k_new[t], None if v_new is None else v_new[t], base_d, seq_d, kd, vd)
+        lsa.keep_recent(shape, seq_d, d.chunk_off, d.sel_idx, d.sel_off, max_recent, out_idx,
+                        out_off)
+        lsa.sparse_decode_attn_varlen(attn_shape, qs[t % nq], kd, vd, base_d, seq_d, out_idx,
+                                      out_off, lsa.KV_STORE, out, lse, ws)
+
+    for t in range(min(args.warmup, steps)):
+        step(t)
+    torch.cuda.synchronize()
+    seq_d.copy_(seq0)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for t in range(steps):
+            step(t)
+    seq_d.copy_(seq0)
+    graph.replay()
+    torch.cuda.synchronize()
+    grown = dev.to_host(seq_d)
+    assert (grown == L0 + steps).all(), "every step appended one row per stream"
+    seq_d.copy_(seq0)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / steps
+    kept = dev.to_host(out_off)
+    idx = dev.to_host(out_idx)[:int(kept[-1])]
+    grown = L0 + steps
+    ktok = 0
+    for b in range(w.B):
+        n = idx[kept[b]:kept[b + 1]].astype(np.int64)
+        ktok += int(np.minimum(C, grown[b] - n * C).sum())
+    ab = algorithmic_bytes(w)
+    attn_bytes = ktok * ab["row"] + ab["q"]
+    # the attention launch alone at the grown length (partial kernel and merge)
+    attn_us = _graph_us(lambda i: lsa.sparse_decode_attn_varlen(
+        attn_shape, qs[i % nq], kd, vd, base_d, seq_d, out_idx, out_off, lsa.KV_STORE, out, lse,
+        ws), steps)
+    attn_gbs = attn_bytes / attn_us / 1e3
+    line = {
+        "metric": "decode steps/sec over a growing context (append + keep set + sparse attn, "
+                  f"re-index every {R})",
+        "value": 1e6 / us, "unit": "steps/s", "n_gpus": 1, "steps": steps,
+        "warmup": args.warmup, "ms_per_step": us / 1e3, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": cfg.dtype, "data": "synthetic",
+        "config": {"workload": f"{args.config}: {WORKLOAD_TEXT[args.config]}; grows by "
+                               f"{steps} tokens per stream", "reindex_every": R,
+                   "max_recent": max_recent,
+                   "timing": "all steps captured in one HIP graph, replayed once",
+                   "cache": "warm: one K/V copy, whose kept chunks (about 146 MB at 16 x 128K) "
+                            "fit the 256 MB Infinity Cache and are re-read every step"},
+        "final_keep_chunks": np.diff(kept).tolist(),
+        "tokens_per_s": 1e6 / us * w.B,
+        "roofline": {"kernel": "attn (split-KV partial + merge) at the grown length",
+                     "bound": "hbm", "achieved": attn_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": attn_gbs / HBM_PEAK_GBS, "traffic": None,
+                     "algorithmic_bytes_per_launch": int(attn_bytes), "avg_launch_us": attn_us},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        from oracle import oracle
+
+        threads = max(1, len(os.sched_getaffinity(0)))
+        Kh = [w.K[w.tok_off[b]:w.tok_off[b + 1]] for b in range(w.B)]
+        Vh = None if w.V is None else [w.V[w.tok_off[b]:w.tok_off[b + 1]] for b in range(w.B)]
+        kn = dev.to_host(k_new)
+        vn = None if v_new is None else dev.to_host(v_new)
+        t_start = time.perf_counter()
+        n_done = 0
+        sel = None
+        while True:
+            t = n_done
+            if t % R == 0:
+                sel = oracle.select(oracle.score(w.q_idx, w.emb, w.chunk_off), w.chunk_off,
+                                    w.sel_off)
+            Kh = [np.concatenate([Kh[b], kn[t % steps][b:b + 1]]) for b in range(w.B)]
+            if Vh is not None:
+                Vh = [np.concatenate([Vh[b], vn[t % steps][b:b + 1]]) for b in range(w.B)]
+            lens = np.array([len(x) for x in Kh], np.int64)
+            off, ids = oracle.keep_recent(C, lens, w.chunk_off, sel, w.sel_off, max_recent)
+            tok = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+            oracle.attention(w.queries(t % 4), np.concatenate(Kh),
+                             None if Vh is None else np.concatenate(Vh), tok, ids, off, C,
+                             cfg.softmax_scale, dv=cfg.head_dim_v, nthreads=threads)
+            n_done += 1
+            el = time.perf_counter() - t_start
+            if el >= args.cpu_seconds or n_done >= steps:
+                break
+        line["cpu_baseline"] = {
+            "value": n_done / el, "unit": "steps/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n_done} growing-context decode step(s) of the same workload in "
+                      f"{el:.1f} s (append and keep set single-threaded, attention with OpenMP "
+                      f"over (stream, head))"}
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -579,8 +741,8 @@ def main():
     ap.add_argument("--tiles-per-block", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--mode", choices=["step", "copy", "scorer", "retriever", "residency"],
-                    default="step")
+    ap.add_argument("--mode", choices=["step", "copy", "scorer", "retriever", "residency",
+                                       "append"], default="step")
     ap.add_argument("--drift", type=float, default=0.5,
                     help="residency mode: indexer query drift per re-index epoch")
     ap.add_argument("--epochs", type=int, default=4, help="residency mode: timed re-index epochs")
@@ -613,6 +775,9 @@ def main():
         return
     if args.mode == "residency":
         run_residency(args)
+        return
+    if args.mode == "append":
+        run_append(args)
         return
 
     cfg = wl.CONFIGS[args.config]
