@@ -65,19 +65,75 @@ PartialLayout partial_layout(const lsa_shape& s, const AttnPlan& p) {
 
 namespace {
 
-constexpr int kMergeWaves = 8;
-constexpr int kMergeThreads = kMergeWaves * kWave;
-constexpr int kMergeBatch = 16;  // partials whose loads are in flight together
+constexpr int kMergeBatch = 16;   // partials whose loads are in flight together
+constexpr int kMergeGroups = 64;  // most groups of partials a stream is cut into
 
-// One workgroup per (stream, 64 consecutive output elements of the flattened
-// [H][dv] row); lane i owns element i of the block.  The eight waves split
-// the stream's partials into contiguous ranges and fold theirs into a running
-// (max, sum, output) state, kMergeBatch partials per round trip with one
-// rescale per batch; the eight states are then combined through LDS.  The
-// order of the arithmetic depends only on the plan, so reruns are
-// bit-identical.
-__global__ __launch_bounds__(kMergeThreads) void merge_kernel(AttnArgs a, int32_t nblk) {
-  __shared__ float s_state[3][kMergeWaves][kWave];
+// (max, sum, output) state of a set of partials, log2 domain.
+struct MergeState {
+  float m, l, acc;
+};
+
+// Folds partials [p_lo, p_hi) of the stream (rows first + p) into one state,
+// kMergeBatch loads in flight and one rescale per batch.
+__device__ __forceinline__ MergeState fold_partials(const AttnArgs& a, int64_t first,
+                                                    int32_t p_lo, int32_t p_hi, int32_t h,
+                                                    int32_t ec) {
+  const int32_t H = a.H, elems = a.H * a.dv;
+  MergeState st = {-INFINITY, 0.f, 0.f};
+  for (int32_t p0 = p_lo; p0 < p_hi; p0 += kMergeBatch) {
+    float mv[kMergeBatch], lv[kMergeBatch], ov[kMergeBatch];
+#pragma unroll
+    for (int u = 0; u < kMergeBatch; ++u) {
+      const int64_t row = first + min(p0 + u, p_hi - 1);
+      mv[u] = a.ws_m[row * H + h];
+      lv[u] = a.ws_l[row * H + h];
+      ov[u] = a.ws_o[row * elems + ec];
+    }
+    float mb = st.m;
+#pragma unroll
+    for (int u = 0; u < kMergeBatch; ++u)
+      if (p0 + u < p_hi) mb = fmaxf(mb, mv[u]);
+    const float mu = (mb == -INFINITY) ? 0.f : mb;
+    const float f = __builtin_amdgcn_exp2f(st.m - mu);
+    st.acc *= f;
+    st.l *= f;
+#pragma unroll
+    for (int u = 0; u < kMergeBatch; ++u) {
+      if (p0 + u < p_hi) {
+        const float w = __builtin_amdgcn_exp2f(mv[u] - mu);
+        st.acc = fmaf(ov[u], w, st.acc);
+        st.l = fmaf(lv[u], w, st.l);
+      }
+    }
+    st.m = mb;
+  }
+  return st;
+}
+
+// total <- total (+) g
+__device__ __forceinline__ void combine_state(MergeState& t, const MergeState& g) {
+  const float mx = fmaxf(t.m, g.m);
+  const float mu = (mx == -INFINITY) ? 0.f : mx;
+  const float ft = __builtin_amdgcn_exp2f(t.m - mu);
+  const float fg = __builtin_amdgcn_exp2f(g.m - mu);
+  t.l = fmaf(g.l, fg, t.l * ft);
+  t.acc = fmaf(g.acc, fg, t.acc * ft);
+  t.m = mx;
+}
+
+// One workgroup of MW waves per (stream, 64 consecutive output elements of the
+// flattened [H][dv] row); lane i owns element i of the block.  A stream's
+// partials are cut into groups (16, or more per group when a stream has over
+// 1024 partials, so that there are at most 64 groups); each group is folded
+// into one state, kMergeBatch partials per round trip with one rescale per
+// batch, and the group states are combined in group order.  With MW waves,
+// wave w folds groups w, w + MW, ... and the states meet in LDS; with one
+// wave the combine runs as the groups are folded.  The arithmetic is the same
+// for every MW and depends only on the plan, so reruns are bit-identical and
+// a stream's result does not depend on the launch shape the batch selects.
+template <int MW>
+__global__ __launch_bounds__(MW * kWave) void merge_kernel(AttnArgs a, int32_t nblk) {
+  __shared__ float s_state[MW > 1 ? 3 : 1][MW > 1 ? kMergeGroups : 1][kWave];
   const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
   const int32_t b = static_cast<int32_t>(blockIdx.x) / nblk;
   const int32_t blk = static_cast<int32_t>(blockIdx.x) - b * nblk;
@@ -89,59 +145,33 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(AttnArgs a, int32_
 
   int32_t first, count;
   stream_wg_range(a.sel_off, a.B, b, a.tiles_per_chunk, a.per, a.target, &first, &count);
-  const int32_t q = ceil_div_i(count, kMergeWaves);
-  const int32_t p_lo = min(count, wave * q);
-  const int32_t p_hi = min(count, p_lo + q);
+  const int32_t gs = max(kMergeBatch, ceil_div_i(count, kMergeGroups));
+  const int32_t ngroups = ceil_div_i(count, gs);
 
-  float m_run = -INFINITY, l_run = 0.f, acc = 0.f;
-  for (int32_t p0 = p_lo; p0 < p_hi; p0 += kMergeBatch) {
-    float mv[kMergeBatch], lv[kMergeBatch], ov[kMergeBatch];
-#pragma unroll
-    for (int u = 0; u < kMergeBatch; ++u) {
-      const int64_t row = static_cast<int64_t>(first) + min(p0 + u, p_hi - 1);
-      mv[u] = a.ws_m[row * H + h];
-      lv[u] = a.ws_l[row * H + h];
-      ov[u] = a.ws_o[row * elems + ec];
+  MergeState total = {-INFINITY, 0.f, 0.f};
+  if (MW == 1) {
+    for (int32_t g = 0; g < ngroups; ++g)
+      combine_state(total, fold_partials(a, first, g * gs, min(count, (g + 1) * gs), h, ec));
+  } else {
+    for (int32_t g = wave; g < ngroups; g += MW) {
+      const MergeState st = fold_partials(a, first, g * gs, min(count, (g + 1) * gs), h, ec);
+      s_state[0][g][lane] = st.m;
+      s_state[1][g][lane] = st.l;
+      s_state[2][g][lane] = st.acc;
     }
-    float mb = m_run;
-#pragma unroll
-    for (int u = 0; u < kMergeBatch; ++u)
-      if (p0 + u < p_hi) mb = fmaxf(mb, mv[u]);
-    const float mu = (mb == -INFINITY) ? 0.f : mb;
-    const float f = __builtin_amdgcn_exp2f(m_run - mu);
-    acc *= f;
-    l_run *= f;
-#pragma unroll
-    for (int u = 0; u < kMergeBatch; ++u) {
-      if (p0 + u < p_hi) {
-        const float w = __builtin_amdgcn_exp2f(mv[u] - mu);
-        acc = fmaf(ov[u], w, acc);
-        l_run = fmaf(lv[u], w, l_run);
-      }
-    }
-    m_run = mb;
+    __syncthreads();
+    if (wave != 0) return;
+    for (int32_t g = 0; g < ngroups; ++g)
+      combine_state(total, MergeState{s_state[0][g][lane], s_state[1][g][lane],
+                                      s_state[2][g][lane]});
   }
-  s_state[0][wave][lane] = m_run;
-  s_state[1][wave][lane] = l_run;
-  s_state[2][wave][lane] = acc;
-  __syncthreads();
-  if (wave != 0 || e >= elems) return;
-  float mx = -INFINITY;
-#pragma unroll
-  for (int w = 0; w < kMergeWaves; ++w) mx = fmaxf(mx, s_state[0][w][lane]);
-  const float mu = (mx == -INFINITY) ? 0.f : mx;
-  float l = 0.f, o = 0.f;
-#pragma unroll
-  for (int w = 0; w < kMergeWaves; ++w) {
-    const float f = __builtin_amdgcn_exp2f(s_state[0][w][lane] - mu);
-    l = fmaf(s_state[1][w][lane], f, l);
-    o = fmaf(s_state[2][w][lane], f, o);
-  }
+  if (e >= elems) return;
   const int64_t orow = static_cast<int64_t>(b) * H + h;
   const int32_t c = e - h * dv;
-  a.out[orow * dv + c] = (l > 0.f) ? o / l : 0.f;
+  a.out[orow * dv + c] = (total.l > 0.f) ? total.acc / total.l : 0.f;
   if (c == 0 && a.lse != nullptr)
-    a.lse[orow] = (l > 0.f) ? (mx + log2f(l)) * 0.69314718055994530942f : -INFINITY;
+    a.lse[orow] = (total.l > 0.f) ? (total.m + log2f(total.l)) * 0.69314718055994530942f
+                                  : -INFINITY;
 }
 
 }  // namespace
@@ -149,8 +179,15 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(AttnArgs a, int32_
 hipError_t launch_attn_merge(const lsa_shape& s, const AttnArgs& a, hipStream_t st) {
   const int32_t nblk = (s.num_q_heads * s.head_dim_v + kWave - 1) / kWave;
   const int64_t grid = static_cast<int64_t>(nblk) * s.batch;
-  hipLaunchKernelGGL(merge_kernel, dim3(static_cast<uint32_t>(grid)), dim3(kMergeThreads), 0, st,
-                     a, nblk);
+  // one wave per workgroup while a stream has a couple of groups of partials
+  // on average, eight when streams have many (a long single stream)
+  const AttnPlan plan = make_attn_plan(s, a.target);
+  if (plan.grid <= static_cast<int64_t>(2 * kMergeBatch) * s.batch)
+    hipLaunchKernelGGL(merge_kernel<1>, dim3(static_cast<uint32_t>(grid)), dim3(kWave), 0, st,
+                       a, nblk);
+  else
+    hipLaunchKernelGGL(merge_kernel<8>, dim3(static_cast<uint32_t>(grid)), dim3(8 * kWave), 0,
+                       st, a, nblk);
   return hipGetLastError();
 }
 
