@@ -200,6 +200,15 @@ __device__ __forceinline__ void find_stream_of_wg(const int32_t* sel_off, int32_
   if (sel0_out) *sel0_out = 0;
 }
 
+// A 64-bit value that is the same in every lane, as scalar registers (the two
+// halves are joined unsigned).
+__device__ __forceinline__ int64_t uniform_i64(int64_t x) {
+  const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int32_t>(x)));
+  const uint32_t hi =
+      static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int32_t>(x >> 32)));
+  return static_cast<int64_t>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
 // The run of tiles one attention workgroup owns.
 struct AttnRun {
   int32_t b;           // stream, or -1 when the workgroup has no work
@@ -240,7 +249,17 @@ __device__ __forceinline__ AttnRun attn_prologue(const AttnArgs& a, int32_t* s_s
     if (lane == 0) *s_run = r;
   }
   __syncthreads();
-  return *s_run;
+  // the run is uniform over the workgroup: scalar registers hold it
+  const AttnRun v = *s_run;
+  AttnRun u;
+  u.b = __builtin_amdgcn_readfirstlane(v.b);
+  u.t_begin = __builtin_amdgcn_readfirstlane(v.t_begin);
+  u.t_end = __builtin_amdgcn_readfirstlane(v.t_end);
+  u.sel0 = __builtin_amdgcn_readfirstlane(v.sel0);
+  u.slot_first = __builtin_amdgcn_readfirstlane(v.slot_first);
+  u.tb = uniform_i64(v.tb);
+  u.len = uniform_i64(v.len);
+  return u;
 }
 
 // Run by one full wave: index of the first workgroup of stream b and its
