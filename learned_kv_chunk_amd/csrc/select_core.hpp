@@ -18,6 +18,15 @@
 // exclusive scan of (#keys > T, #keys == T) then places every kept chunk at
 // its output position: ascending indices and the lower-index tie rule with no
 // sort.
+//
+// With eight or more keys per thread a bucket pass is tried first: the stream's finite
+// scores are spread over 1024 equal-width bins between their minimum and
+// maximum (a monotone map, so the bins are ordered like the keys), one
+// histogram finds the bin holding the k-th largest key, and when that bin has
+// at most 64 keys one wave ranks them exactly by (key desc, index asc).  For
+// scores from a continuous distribution the boundary bin holds a few keys, so
+// one histogram replaces four; otherwise (ties, infinities, a very skewed
+// spread) the radix passes run.
 #pragma once
 
 #include "lsa_internal.hpp"
@@ -32,11 +41,34 @@ __device__ __forceinline__ uint32_t order_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+constexpr int kSelectBins = 1024;     // bucket pass bins (the four radix histograms' words)
+constexpr int kSelectMaxCand = 64;    // keys the bucket pass ranks in one wave
+
 template <int THREADS>
 struct SelectLds {
   alignas(16) uint32_t hist[4][256];
   uint32_t tot[2 * (THREADS / kWave)];
+  uint32_t cand_key[kSelectMaxCand];
+  int32_t cand_idx[kSelectMaxCand];
+  uint32_t misc[4];  // candidate count; threshold key and its kept count
 };
+
+// Value of a non-zero order key (the inverse of order_key).
+__device__ __forceinline__ float key_value(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = min(v, static_cast<uint32_t>(__shfl_xor(static_cast<int>(v), o)));
+  return v;
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = max(v, static_cast<uint32_t>(__shfl_xor(static_cast<int>(v), o)));
+  return v;
+}
 
 // Barrier among the THREADS threads taking part (a single wave needs only
 // its LDS operations ordered).
@@ -103,13 +135,12 @@ __device__ __forceinline__ void select_load_keys(const float* __restrict__ score
   for (int i = 0; i < KPT; ++i) key[i] = (tid * KPT + i < n) ? order_key(sv[i]) : 0u;
 }
 
-// Top-k of the n keys held as select_load_keys leaves them, written ascending
-// to out[0..k); 0 < k < n.  Every one of the THREADS threads (threads
-// 0..THREADS-1 of the workgroup) must call it.
+// Radix passes: the key T of the k-th largest key (`prefix`) and how many
+// keys equal to T are kept (`remaining`).
 template <int THREADS, int KPT>
-__device__ __forceinline__ void select_topk_keys(const uint32_t (&key)[KPT], int32_t n,
-                                                 int32_t k, int32_t* __restrict__ out,
-                                                 SelectLds<THREADS>& lds) {
+__device__ __forceinline__ void select_radix(const uint32_t (&key)[KPT], int32_t n, int32_t k,
+                                             SelectLds<THREADS>& lds, uint32_t* prefix_out,
+                                             uint32_t* remaining_out) {
   const int tid = threadIdx.x;
   for (int i = tid; i < 4 * 256; i += THREADS) (&lds.hist[0][0])[i] = 0u;
   select_sync<THREADS>();
@@ -170,6 +201,146 @@ __device__ __forceinline__ void select_topk_keys(const uint32_t (&key)[KPT], int
     mask |= 0xffu << shift;
     remaining -= gt_pick;
   }
+
+  *prefix_out = prefix;
+  *remaining_out = remaining;
+}
+
+// Bucket pass (see the file comment): returns false, with the workgroup in
+// step and the histograms free, when the radix passes must decide instead.
+template <int THREADS, int KPT>
+__device__ __forceinline__ bool select_buckets(const uint32_t (&key)[KPT], int32_t n, int32_t k,
+                                               SelectLds<THREADS>& lds, uint32_t* prefix_out,
+                                               uint32_t* remaining_out) {
+  const int tid = threadIdx.x;
+  const int wave = tid / kWave;
+  const uint32_t lane = tid & (kWave - 1);
+  uint32_t* hist = &lds.hist[0][0];
+  uint32_t lo = 0xffffffffu, hi = 0u;
+#pragma unroll
+  for (int i = 0; i < KPT; ++i) {
+    if (tid * KPT + i < n && key[i] != 0u) {  // NaN (key 0) takes no part in the range
+      lo = min(lo, key[i]);
+      hi = max(hi, key[i]);
+    }
+  }
+  lo = wave_min_u32(lo);
+  hi = wave_max_u32(hi);
+  for (int i = tid; i < kSelectBins; i += THREADS) hist[i] = 0u;
+  if (tid == 0) lds.misc[0] = 0u;
+  if (THREADS > kWave) {
+    if (lane == 0) {
+      lds.tot[2 * wave] = lo;
+      lds.tot[2 * wave + 1] = hi;
+    }
+    select_sync<THREADS>();
+#pragma unroll
+    for (int w = 0; w < THREADS / kWave; ++w) {
+      lo = min(lo, lds.tot[2 * w]);
+      hi = max(hi, lds.tot[2 * w + 1]);
+    }
+  } else {
+    select_sync<THREADS>();
+  }
+  if (hi <= lo) return false;  // one distinct number (or none)
+  const float fl = key_value(lo), fh = key_value(hi);
+  const float range = fh - fl;
+  const float scale = static_cast<float>(kSelectBins) / range;
+  if (!(range > 0.f) || !__builtin_isfinite(range) || !__builtin_isfinite(scale)) return false;
+  // bin of a key: monotone in the key; NaN joins the lowest bin
+  auto bin_of = [&](uint32_t kv) -> int {
+    return kv == 0u ? 0
+                    : min(kSelectBins - 1, static_cast<int>((key_value(kv) - fl) * scale));
+  };
+#pragma unroll
+  for (int i = 0; i < KPT; ++i)
+    if (tid * KPT + i < n) atomicAdd(&hist[bin_of(key[i])], 1u);
+  select_sync<THREADS>();
+  // bin d* with #(bin > d*) < k <= #(bin >= d*); lane l owns bins 16l..16l+15
+  uint32_t cnt[16];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const uint4 c4 = reinterpret_cast<const uint4*>(hist)[4 * lane + q];
+    cnt[4 * q] = c4.x;
+    cnt[4 * q + 1] = c4.y;
+    cnt[4 * q + 2] = c4.z;
+    cnt[4 * q + 3] = c4.w;
+  }
+  uint32_t tot = 0;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) tot += cnt[j];
+  const uint32_t incl = wave_inclusive_scan(tot);
+  const uint32_t total = __builtin_amdgcn_readlane(incl, 63);
+  uint32_t ge = total - incl;
+  uint32_t pick = 0, gt_pick = 0;
+  bool found = false;
+#pragma unroll
+  for (int j = 15; j >= 0; --j) {
+    const uint32_t gt = ge;
+    ge += cnt[j];
+    if (!found && gt < static_cast<uint32_t>(k) && static_cast<uint32_t>(k) <= ge) {
+      found = true;
+      pick = 16u * lane + j;
+      gt_pick = gt;
+    }
+  }
+  const uint64_t hit = __ballot(found);
+  const int src = __ffsll(static_cast<long long>(hit)) - 1;
+  pick = __builtin_amdgcn_readlane(pick, src);
+  gt_pick = __builtin_amdgcn_readlane(gt_pick, src);
+  const uint32_t in_bin = hist[pick];
+  if (in_bin > static_cast<uint32_t>(kSelectMaxCand)) {
+    select_sync<THREADS>();  // every wave has read the histogram
+    return false;
+  }
+  const uint32_t remaining = static_cast<uint32_t>(k) - gt_pick;  // kept from bin d*
+#pragma unroll
+  for (int i = 0; i < KPT; ++i) {
+    if (tid * KPT + i < n && bin_of(key[i]) == static_cast<int>(pick)) {
+      const uint32_t slot = atomicAdd(&lds.misc[0], 1u);
+      lds.cand_key[slot] = key[i];
+      lds.cand_idx[slot] = tid * KPT + i;
+    }
+  }
+  select_sync<THREADS>();
+  if (wave == 0) {
+    // rank of each candidate by (key desc, index asc) among the in_bin ones
+    const bool mine = lane < in_bin;
+    const uint32_t kk = mine ? lds.cand_key[lane] : 0u;
+    const int32_t ii = mine ? lds.cand_idx[lane] : 0x7fffffff;
+    uint32_t rank = 0;
+    for (uint32_t j = 0; j < in_bin; ++j) {
+      const uint32_t kj = __builtin_amdgcn_readlane(kk, j);
+      const int32_t ij = __builtin_amdgcn_readlane(ii, j);
+      rank += (kj > kk || (kj == kk && ij < ii)) ? 1u : 0u;
+    }
+    const uint64_t at = __ballot(mine && rank == remaining - 1);
+    const uint32_t t_key = __builtin_amdgcn_readlane(kk, __ffsll(static_cast<long long>(at)) - 1);
+    const uint32_t above = static_cast<uint32_t>(__popcll(__ballot(mine && kk > t_key)));
+    if (lane == 0) {
+      lds.misc[1] = t_key;
+      lds.misc[2] = remaining - above;
+    }
+  }
+  select_sync<THREADS>();
+  *prefix_out = lds.misc[1];
+  *remaining_out = lds.misc[2];
+  return true;
+}
+
+// Top-k of the n keys held as select_load_keys leaves them, written ascending
+// to out[0..k); 0 < k < n.  Every one of the THREADS threads (threads
+// 0..THREADS-1 of the workgroup) must call it.
+template <int THREADS, int KPT>
+__device__ __forceinline__ void select_topk_keys(const uint32_t (&key)[KPT], int32_t n,
+                                                 int32_t k, int32_t* __restrict__ out,
+                                                 SelectLds<THREADS>& lds) {
+  const int tid = threadIdx.x;
+  uint32_t prefix, remaining;
+  // the bucket pass pays off from eight keys per thread (streams of several
+  // thousand chunks); below that the radix passes are as fast
+  if (KPT < 8 || !select_buckets<THREADS, KPT>(key, n, k, lds, &prefix, &remaining))
+    select_radix<THREADS, KPT>(key, n, k, lds, &prefix, &remaining);
 
   uint32_t n_gt = 0, n_eq = 0;
 #pragma unroll

@@ -183,6 +183,26 @@ def _select_case(scores_per_stream, keep):
     return got
 
 
+@pytest.mark.parametrize("n", [8192, 20000])
+def test_select_long_streams_bucket_and_radix_paths(n):
+    # long streams take the bucket pass first: continuous scores resolve there;
+    # ties, NaN and infinities, an outlier that crowds every other score into
+    # one bin, and a boundary bin over 64 keys send it to the radix passes
+    rng = np.random.default_rng(n)
+    cont = rng.standard_normal(n)
+    ties = np.round(rng.standard_normal(n) * 4) / 4
+    special = rng.standard_normal(n)
+    special[rng.choice(n, 40, replace=False)] = np.nan
+    special[:3] = [np.inf, -np.inf, -0.0]
+    outlier = rng.standard_normal(n) * 1e-3
+    outlier[n // 3] = 1e30
+    dense = np.concatenate([rng.standard_normal(n - 200), np.full(200, 0.5)])
+    subnormal = rng.standard_normal(n) * 1e-42
+    streams = [cont, ties, special, outlier, dense, subnormal]
+    for k in (1, 63, n // 8, n // 2, n - 1):
+        _select_case(streams, [k] * len(streams))
+
+
 def test_select_ties_nan_signed_zero_and_extremes():
     rng = np.random.default_rng(0)
     golden = np.array([0.5, 0.9, 0.5, 0.9, -0.0, 0.0, 0.1, np.nan], np.float32)
