@@ -21,7 +21,6 @@ sample of the same workload.
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import math
 import os
@@ -81,20 +80,17 @@ def kept_tokens(w, sel):
     return total
 
 
-def source_hash(path):
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
-
-
 def load_traffic(kernel_file, workload):
     """HBM bytes per launch from committed rocprofv3 counter runs, if they were
-    taken on the current kernel source; else None."""
+    taken on the current kernel sources; else None."""
+    from learned_kv_chunk_amd.profiling import kernel_sources, source_hash
+
     p = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
     if not os.path.exists(p):
         return None
     with open(p) as f:
         rec = json.load(f)
-    if rec.get("kernel_source_sha256_16") != source_hash(kernel_file):
+    if rec.get("kernel_source_sha256_16") != source_hash(kernel_sources(kernel_file)):
         return None
     return rec.get("bytes_per_launch")
 
@@ -864,9 +860,23 @@ def main():
     run(args.steps, t_first, evs)
     h1.record()
     torch.cuda.synchronize()
-    attn_us = float(np.mean([a.elapsed_time(b) for a, b in evs])) * 1e3
+    attn_us_events = float(np.mean([a.elapsed_time(b) for a, b in evs])) * 1e3
     ms_per_step_with_events = h0.elapsed_time(h1) / args.steps
 
+    # pass 3 (roofline.avg_launch_us): the attention partial kernel alone, the
+    # K launches (one per replica in turn, so each reads cold K/V) replayed
+    # back to back from a HIP graph with two events around the replay: no
+    # event record sits between the kernels
+    pool_mode = bool(cfg.materialize_pool)
+
+    def partial(i):
+        r = replicas[i % reps]
+        lsa.bench_attention_partial(
+            r.shape, qs[i % nq], r.k_pool if pool_mode else r.K,
+            r.v_pool if pool_mode else r.V, r.tok_off, r.sel_idx, r.sel_off,
+            lsa.KV_POOL if pool_mode else lsa.KV_STORE, r.workspace)
+
+    attn_us = _graph_us(partial, args.steps)
     attn_gbs = attn_bytes / attn_us / 1e3
     kernel_file = os.path.join(ROOT, "learned_kv_chunk_amd", "csrc",
                                "attn_mla.hip" if cfg.v_aliases_k else
@@ -912,6 +922,8 @@ def main():
             "traffic": traffic,
             "algorithmic_bytes_per_launch": int(attn_bytes),
             "avg_launch_us": attn_us,
+            "timing": "partial kernel alone, K cold launches replayed from a HIP graph",
+            "avg_launch_us_events_in_step": attn_us_events,
         },
         "cpu_baseline": None,
     }

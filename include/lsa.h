@@ -400,9 +400,19 @@ lsa_status lsa_decode_step(const lsa_shape* shape, const lsa_step_args* args,
  *   and achievable bandwidth are calibrated.
  * lsa_bench_flush: overwrites `bytes` of a caller buffer (multiple of 16) so
  *   that caches hold none of a workload's data afterwards.
+ * lsa_bench_attention_partial: enqueues only the split-KV partial kernel of
+ *   lsa_sparse_decode_attn (same arguments and checks, no outputs: the
+ *   partial results land in the workspace and are not merged), so that the
+ *   kernel can be timed back to back without anything recorded between
+ *   launches.
  * ------------------------------------------------------------------------- */
 lsa_status lsa_bench_copy(void* dst_dev, const void* src_dev, size_t bytes, void* hip_stream);
 lsa_status lsa_bench_flush(void* buf_dev, size_t bytes, void* hip_stream);
+lsa_status lsa_bench_attention_partial(const lsa_shape* shape, int32_t kv_mode, const void* q_dev,
+                                       const void* k_base_dev, const void* v_base_dev,
+                                       const int64_t* tok_off_dev, const int32_t* sel_idx_dev,
+                                       const int32_t* sel_off_dev, void* workspace_dev,
+                                       size_t workspace_bytes, void* hip_stream);
 
 #ifdef __cplusplus
 }

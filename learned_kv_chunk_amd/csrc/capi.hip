@@ -72,7 +72,7 @@ lsa_status enqueue_attention(const lsa_shape& s, int32_t kv_mode, const void* q,
                              const void* vbase, const int64_t* tok_off, const int32_t* sel_idx,
                              const int32_t* sel_off, float* out, float* lse, void* ws,
                              hipStream_t st, void* ev_begin = nullptr, void* ev_end = nullptr,
-                             const int64_t* seq_len = nullptr) {
+                             const int64_t* seq_len = nullptr, bool partial_only = false) {
   const AttnPlan plan = make_attn_plan(s, device_cu_count());
   const PartialLayout pl = partial_layout(s, plan);
   AttnArgs a;
@@ -109,6 +109,7 @@ lsa_status enqueue_attention(const lsa_shape& s, int32_t kv_mode, const void* q,
   if (e != hipSuccess) return LSA_ERR_HIP;
   if (ev_end && hipEventRecord(static_cast<hipEvent_t>(ev_end), st) != hipSuccess)
     return LSA_ERR_HIP;
+  if (partial_only) return LSA_OK;
   return hip_status(launch_attn_merge(s, a, st));
 }
 
@@ -444,6 +445,23 @@ lsa_status lsa_decode_step(const lsa_shape* shape, const lsa_step_args* args, vo
   return enqueue_attention(*shape, pool ? LSA_KV_POOL : LSA_KV_STORE, x.q_dev, kbase, vbase,
                            x.tok_off_dev, x.sel_idx_dev, x.sel_off_dev, x.out_dev, x.lse_dev,
                            workspace_dev, hs, x.ev_attn_begin, x.ev_attn_end);
+}
+
+lsa_status lsa_bench_attention_partial(const lsa_shape* shape, int32_t kv_mode, const void* q_dev,
+                                       const void* k_base_dev, const void* v_base_dev,
+                                       const int64_t* tok_off_dev, const int32_t* sel_idx_dev,
+                                       const int32_t* sel_off_dev, void* workspace_dev,
+                                       size_t workspace_bytes, void* hip_stream) {
+  // the checks of lsa_sparse_decode_attn, with the workspace standing in for
+  // the outputs it does not write
+  lsa_status st = check_attn_args(shape, kv_mode, q_dev, k_base_dev, v_base_dev, tok_off_dev,
+                                  sel_idx_dev, sel_off_dev, static_cast<const float*>(workspace_dev),
+                                  nullptr, workspace_dev, workspace_bytes);
+  if (st != LSA_OK) return st;
+  (void)hipGetLastError();
+  return enqueue_attention(*shape, kv_mode, q_dev, k_base_dev, v_base_dev, tok_off_dev,
+                           sel_idx_dev, sel_off_dev, nullptr, nullptr, workspace_dev,
+                           static_cast<hipStream_t>(hip_stream), nullptr, nullptr, nullptr, true);
 }
 
 lsa_status lsa_bench_copy(void* dst_dev, const void* src_dev, size_t bytes, void* hip_stream) {

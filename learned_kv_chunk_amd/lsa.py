@@ -111,6 +111,8 @@ _SIGNATURES = {
     "lsa_decode_step": ([ctypes.POINTER(Shape), ctypes.POINTER(StepArgs), _P, ctypes.c_size_t,
                          _P], _I32),
     "lsa_bench_copy": ([_P, _P, ctypes.c_size_t, _P], _I32),
+    "lsa_bench_attention_partial": ([ctypes.POINTER(Shape), _I32, _P, _P, _P, _P, _P, _P, _P,
+                                     ctypes.c_size_t, _P], _I32),
     "lsa_bench_flush": ([_P, ctypes.c_size_t, _P], _I32),
 }
 
@@ -543,6 +545,17 @@ def decode_step(shape: ProblemShape, *, q_idx, emb, chunk_off, scores, sel_off, 
     _check(library().lsa_decode_step(ctypes.byref(shape.c()), ctypes.byref(args),
                                      _ptr(workspace), workspace.numel(), _stream(stream)),
            "lsa_decode_step")
+
+
+def bench_attention_partial(shape: ProblemShape, q, k_base, v_base, tok_off, sel_idx, sel_off,
+                            kv_mode: int, workspace, stream=None) -> None:
+    """lsa_bench_attention_partial: the split-KV partial kernel alone (timing)."""
+    _dev(q, "q", shape.dtype, 3)
+    _dev(workspace, "workspace", torch.uint8, 1)
+    _check(library().lsa_bench_attention_partial(
+        ctypes.byref(shape.c()), int(kv_mode), _ptr(q), _ptr(k_base), _ptr(v_base),
+        _ptr(tok_off), _ptr(sel_idx), _ptr(sel_off), _ptr(workspace), workspace.numel(),
+        _stream(stream)), "lsa_bench_attention_partial")
 
 
 def bench_copy(dst: torch.Tensor, src: torch.Tensor, nbytes: int, stream=None) -> None:

@@ -59,9 +59,22 @@ def counter_per_dispatch(run_dir: str, counter: str, kernel: str) -> list[float]
     return vals
 
 
-def source_hash(path: str) -> str:
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def kernel_sources(kernel_file: str) -> list[str]:
+    """A kernel's source file and the headers every kernel file includes: a
+    traffic record is valid only while all of them are unchanged."""
+    csrc = os.path.dirname(os.path.abspath(kernel_file))
+    return [kernel_file, os.path.join(csrc, "lsa_internal.hpp"), os.path.join(csrc, "wave.hpp")]
+
+
+def source_hash(paths) -> str:
+    """First 16 hex digits of the SHA-256 of the files' contents, in order."""
+    if isinstance(paths, str):
+        paths = [paths]
+    h = hashlib.sha256()
+    for p in paths:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def cmd_stats(a) -> None:
@@ -90,8 +103,8 @@ def cmd_traffic(a) -> None:
     rec = {
         "kernel": a.kernel,
         "workload": a.workload,
-        "kernel_source": os.path.relpath(a.source),
-        "kernel_source_sha256_16": source_hash(a.source),
+        "kernel_source": [os.path.relpath(p) for p in kernel_sources(a.source)],
+        "kernel_source_sha256_16": source_hash(kernel_sources(a.source)),
         "fetch_bytes_counted": fetch,
         "write_bytes_counted": write,
         "copy_calibration": {"bytes_read": a.copy_bytes, "bytes_written": a.copy_bytes,
@@ -115,8 +128,8 @@ def cmd_traffic(a) -> None:
              f"| reads, calibrated (x{f_scale:.4f}) | {rec['read_bytes_per_launch']:.4g} |",
              f"| writes, calibrated (x{w_scale:.4f}) | {rec['write_bytes_per_launch']:.4g} |",
              f"| total | {rec['bytes_per_launch']:.4g} |", "",
-             f"Kernel source {rec['kernel_source']} sha256[:16] = "
-             f"{rec['kernel_source_sha256_16']}."]
+             f"Kernel sources {', '.join(rec['kernel_source'])}: sha256[:16] of their "
+             f"contents in that order = {rec['kernel_source_sha256_16']}."]
     text = "\n".join(lines) + "\n"
     if a.out:
         with open(a.out, "w") as f:
