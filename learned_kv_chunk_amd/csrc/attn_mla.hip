@@ -61,12 +61,15 @@ static_assert(kTileInsts == 4 * 5 + 4 * 4, "waves 0-3 issue 5 loads per tile, wa
 static_assert(kRowVecs % 8 == 0, "the swizzle permutes vectors inside aligned groups of 8");
 
 // LDS layout of a tile: row r (token) at r * kPitch, its 16-byte vector v at
-// slot v ^ swz(r) (swz < 8, so a vector stays in its aligned group of 8).  The
-// pitch is 288 words, so odd rows start half-way round the 64 banks; swz then
-// spreads both read patterns over all banks: the K operand reads (16
-// consecutive rows, one vector each, per 16-lane pass) and the transposed V
-// reads (8 consecutive rows, one aligned vector pair each, per 32-lane pass).
-__device__ __forceinline__ int swz(int r) { return (((r >> 1) & 3) << 1) | ((r >> 3) & 1); }
+// slot v ^ swz(r) with swz(r) = r & 7 (so a vector stays in its aligned group
+// of 8).  Both read patterns -- the K operand reads (16 consecutive rows, one
+// vector each, per 16-lane group) and the transposed V reads (8 consecutive
+// rows, one aligned vector pair each, per 32-lane group) -- then run without
+// bank conflicts; this was measured with the SQ_LDS_BANK_CONFLICT counter on
+// gfx950 for each pattern and several candidate swizzles (unpadded rows
+// conflict on both; other XOR patterns that a 64-bank, 16-lanes-per-cycle
+// model predicts conflict-free were not).
+__device__ __forceinline__ int swz(int r) { return r & 7; }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
@@ -164,7 +167,7 @@ struct ReadLane {
 // K operand of lane (r16, g): row r16, vector 4s + g.  V^T operand of lane
 // (r16, g): rows 4g + (r16 >> 2) (and +16), the 8-byte piece 8 * (r16 & 3) of
 // the 32-byte span of column group cg (vectors 2cg, 2cg + 1), in this wave's
-// column half.  swz(r) depends on r & 15 only, so rows r and r + 16 share it.
+// column half.  swz(r) depends on r & 7 only, so rows r and r + 16 share it.
 __device__ __forceinline__ ReadLane read_lane(int col_half, int lane) {
   ReadLane rl;
   const int r16 = lane & 15, g = lane >> 4;

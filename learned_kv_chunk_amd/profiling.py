@@ -12,7 +12,12 @@
         dispatch), each scaled by what the same counter reads for a plain copy
         kernel that reads and writes N bytes per launch
 
-Both read only rocprofv3's CSV files.
+    python -m learned_kv_chunk_amd.profiling counters DIR --kernel NAME ... --command "..."
+        per-dispatch averages of every counter of a `--pmc` run for the named
+        kernels, as a Markdown table (LDS bank conflicts, matrix-core busy
+        cycles, ...)
+
+All read only rocprofv3's CSV files.
 """
 from __future__ import annotations
 
@@ -137,6 +142,38 @@ def cmd_traffic(a) -> None:
     sys.stdout.write(text)
 
 
+def cmd_counters(a) -> None:
+    rows = _rows(os.path.join(a.dir, "run_counter_collection.csv"))
+    table = {}
+    for r in rows:
+        name = short_name(r["Kernel_Name"])
+        if not any(k in r["Kernel_Name"] for k in a.kernel):
+            continue
+        table.setdefault(name, {}).setdefault(r["Counter_Name"], []).append(
+            float(r["Counter_Value"]))
+    counters = sorted({c for v in table.values() for c in v})
+    lines = [f"# Counters: {a.title}", "", "Command:", "", "```", a.command, "```", "",
+             "Per-dispatch averages as rocprofv3 reports them (summed over the device).", "",
+             "| kernel | dispatches | " + " | ".join(counters) + " |",
+             "|---|---:|" + "---:|" * len(counters)]
+    for name, v in sorted(table.items()):
+        n = max(len(x) for x in v.values())
+        cells = [f"{statistics.mean(v[c]):.4g}" if c in v else "" for c in counters]
+        lines.append(f"| {name} | {n} | " + " | ".join(cells) + " |")
+    ratios = []
+    for name, v in sorted(table.items()):
+        if "SQ_LDS_BANK_CONFLICT" in v and "SQ_LDS_IDX_ACTIVE" in v:
+            ratios.append(f"* {name}: LDS bank-conflict cycles / LDS active cycles = "
+                          f"{statistics.mean(v['SQ_LDS_BANK_CONFLICT']) / max(1.0, statistics.mean(v['SQ_LDS_IDX_ACTIVE'])):.4f}")
+    if ratios:
+        lines += ["", "Ratios of the averages:", ""] + ratios
+    text = "\n".join(lines) + "\n"
+    if a.out:
+        with open(a.out, "w") as f:
+            f.write(text)
+    sys.stdout.write(text)
+
+
 def main(argv=None) -> None:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -158,9 +195,17 @@ def main(argv=None) -> None:
     t.add_argument("--command", required=True)
     t.add_argument("--out-json")
     t.add_argument("--out")
+    c = sub.add_parser("counters")
+    c.add_argument("dir")
+    c.add_argument("--kernel", action="append", required=True)
+    c.add_argument("--title", default="")
+    c.add_argument("--command", required=True)
+    c.add_argument("--out")
     a = ap.parse_args(argv)
     if a.cmd == "stats":
         cmd_stats(a)
+    elif a.cmd == "counters":
+        cmd_counters(a)
     else:
         cmd_traffic(a)
 
