@@ -10,8 +10,8 @@
 //
 // A workgroup owns a run of 32-token tiles of one stream and all (up to 64)
 // query heads.  Each tile is read from HBM once per workgroup, straight into
-// LDS with global_load_lds (no register staging), into one of three buffers,
-// so two tiles are in flight while a third is computed.  Eight waves (two per
+// LDS with global_load_lds (no register staging), into one of four buffers,
+// so three tiles are in flight while a fourth is computed.  Eight waves (two per
 // SIMD) work in pairs: the pair (2h, 2h+1) serves heads 16h..16h+15, each
 // wave of the pair computes S^T for one 16-token half of the tile
 //   S^T[token][head] = K_tile . Q^T     (v_mfma_f32_16x16x32_bf16, K = 576)
@@ -51,10 +51,6 @@ constexpr int kDmaMax = (kTileInsts + kMlaWaves - 1) / kMlaWaves;  // 5 (waves 0
 constexpr int kBufBytes = kTileSlots * 16;            // 36864
 constexpr int kBufs = 4;                              // three tiles in flight
 constexpr float kLazyLog2 = 8.f;  // reference-maximum slack of the online softmax (log2)
-
-// s_waitcnt immediate (gfx9 encoding) waiting for every vector-memory
-// operation, leaving the export and LDS/scalar counters unconstrained.
-constexpr int kWaitVmcnt0 = (7 << 4) | (15 << 8);
 
 static_assert(kTileInsts * kWave == kTileSlots, "DMA instructions must tile the buffer");
 static_assert(kTileInsts == 4 * 5 + 4 * 4, "waves 0-3 issue 5 loads per tile, waves 4-7 issue 4");
@@ -149,6 +145,30 @@ __device__ __forceinline__ void dma_tile(const unsigned char* __restrict__ kbyte
       const uint32_t voff = static_cast<uint32_t>(min(row, last) * row_bytes) + vec * 16;
       dma16(sbase, voff, __builtin_amdgcn_readfirstlane(lds0 + j * kMlaWaves * kWave * 16));
     }
+  }
+}
+
+// Copy the query rows of all heads (H rows of 1152 B, contiguous) into LDS
+// at `dst` (two tile buffers hold the 64-row maximum): instruction j of wave w
+// copies bytes (w + 8j) * 1024 .. +1023.  Every wave issues kQDma
+// instructions; a lane whose bytes lie past the H rows re-reads the last 16
+// bytes, so no read leaves the query array.
+constexpr int kQDma = kMlaDqk * 2 * 64 / (kWave * 16) / kMlaWaves;  // 9
+static_assert(kQDma * kMlaWaves * kWave * 16 == 2 * kBufBytes, "Q fills two tile buffers");
+
+__device__ __forceinline__ void dma_q(const unsigned char* __restrict__ qbytes, int32_t q_bytes,
+                                      const unsigned char* dst, int wave, int lane) {
+  const uint64_t addr = reinterpret_cast<uint64_t>(qbytes);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(addr));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(addr >> 32));
+  const unsigned char* sbase =
+      reinterpret_cast<const unsigned char*>((static_cast<uint64_t>(hi) << 32) | lo);
+  const uint32_t lds0 = lds_address(dst);
+#pragma unroll
+  for (int j = 0; j < kQDma; ++j) {
+    const int inst = wave + kMlaWaves * j;
+    const int32_t off = min(inst * kWave * 16 + lane * 16, q_bytes - 16);
+    dma16(sbase, static_cast<uint32_t>(off), __builtin_amdgcn_readfirstlane(lds0 + inst * kWave * 16));
   }
 }
 
@@ -336,7 +356,8 @@ __global__ __launch_bounds__(kMlaThreads, 1) void attn_mla_kernel(AttnArgs a) {
   // the loop, so "tile i has landed" is "at most nd times the number of later
   // tiles issued of this wave's loads outstanding", and the first barrier
   // makes every wave's part of tile i visible.  The buffer refilled with tile
-  // i+3 held tile i-1, which every wave finished before that barrier.  The
+  // i+3 held tile i-1 (for i = 0 the query), which every wave finished before
+  // that barrier.  The
   // second barrier publishes the S^T halves; a half is rewritten only after
   // the next first barrier, which its reader reaches after reading it.
   const DmaLane dl = dma_lane(row_bytes, wave, lane);
@@ -350,22 +371,39 @@ __global__ __launch_bounds__(kMlaThreads, 1) void attn_mla_kernel(AttnArgs a) {
   };
   const int32_t n = t_end - t_begin;
   int32_t nv[kBufs] = {0, 0, 0, 0};  // valid tokens of the tile in each buffer
-  for (int32_t t = 0; t < kBufs - 1; ++t)
-    if (t < n) nv[t] = issue(t, t);
 
-  // Q^T operand of this wave's heads: lane holds Q[head][s*32 + 8g .. +7].
-  // Loaded after the first tiles' copies are under way and waited for
-  // together with them, so the loop holds no compiler-tracked load.
+  // Start-up.  The query rows of the stream go to buffers 2-3 through the same
+  // copy path, ahead of tiles 0 and 1 (buffers 0-1); once the query has landed
+  // every wave takes its Q^T operand from LDS (lane (r16, g) holds
+  // Q[head][s*32 + 8g .. +7]), and only then is tile 2 issued into buffer 2,
+  // tile 3 following in the loop's first iteration.  So the first tile is
+  // waited for alone rather than with all three, and one coalesced copy per
+  // workgroup replaces per-wave query loads of 64-byte pieces.
   bf16x8 qf[kMlaDqk / 32];
   {
-    const uint16_t* __restrict__ qb = static_cast<const uint16_t*>(a.q);
-    const u32x4* src = reinterpret_cast<const u32x4*>(
-                           qb + (static_cast<int64_t>(b) * H + min(head, H - 1)) * kMlaDqk) + g;
+    const unsigned char* qbytes =
+        static_cast<const unsigned char*>(a.q) + static_cast<int64_t>(b) * H * kMlaDqk * 2;
+    const unsigned char* qs = smem + 2 * kBufBytes;
+    dma_q(qbytes, H * kMlaDqk * 2, qs, wave, lane);
+    if (0 < n) nv[0] = issue(0, 0);
+    if (1 < n) nv[1] = issue(1, 1);
+    if (n >= 2) {
+      if (five) LSA_MLA_WAIT_BARRIER(10);
+      else LSA_MLA_WAIT_BARRIER(8);
+    } else if (n == 1) {
+      if (five) LSA_MLA_WAIT_BARRIER(5);
+      else LSA_MLA_WAIT_BARRIER(4);
+    } else {
+      LSA_MLA_WAIT_BARRIER(0);
+    }
+    const unsigned char* qrow = qs + min(head, H - 1) * (kMlaDqk * 2) + 16 * g;
 #pragma unroll
     for (int s = 0; s < kMlaDqk / 32; ++s)
-      qf[s] = as_bf16x8(head < H ? src[s * 4] : u32x4{0u, 0u, 0u, 0u});
+      qf[s] = as_bf16x8(head < H ? *reinterpret_cast<const u32x4*>(qrow + 64 * s)
+                                 : u32x4{0u, 0u, 0u, 0u});
+    LSA_MLA_BARRIER();  // buffers 2-3 are free once every wave holds its Q
+    if (2 < n) nv[2] = issue(2, 2);
   }
-  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
 
   for (int32_t i = 0; i < n; ++i) {
     const int32_t later = min(n - 1 - i, kBufs - 2);  // tiles issued after tile i
