@@ -76,7 +76,9 @@ struct TileInfo {
 
 // One 16-byte-per-lane global -> LDS load: lane i's 16 bytes at sbase + voff
 // land at LDS address lds_addr + 16 i (the address is taken from M0, which is
-// restored afterwards).  Written as inline assembly so that the compiler, which
+// restored afterwards).  The load carries the non-temporal hint: each K row is
+// read once per step, and on cold rows at 1 x 1M the hint took the kernel from
+// 36.8 to 33.3 us and the decode step from 58.4 to 57.1 us.  Written as inline assembly so that the compiler, which
 // does not see the LDS write, adds no wait of its own for it before LDS reads:
 // the pipeline below does its own counting.
 __device__ __forceinline__ void dma16(const unsigned char* sbase, uint32_t voff,
@@ -86,7 +88,7 @@ __device__ __forceinline__ void dma16(const unsigned char* sbase, uint32_t voff,
       "s_mov_b32 %0, m0\n\t"
       "s_mov_b32 m0, %1\n\t"
       "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %2, %3\n\t"
+      "global_load_lds_dwordx4 %2, %3 nt\n\t"
       "s_mov_b32 m0, %0"
       : "=&s"(saved)
       : "s"(lds_addr), "v"(voff), "s"(sbase)

@@ -60,7 +60,10 @@ struct TileInfo {
 
 // Loads are unconditional so that the compiler can count them and keep the
 // next tile in flight: rows past the tile's valid tokens re-read its last
-// valid row (their logits are masked and their weights are zero).
+// valid row (their logits are masked and their weights are zero).  V is read
+// with the non-temporal hint and K without it: measured on cold K/V at
+// 16 x 128K, that pair streams fastest (30.1 us per launch against 31.8 with
+// no hint on either and 32.4 with the hint on both).
 template <int D>
 __device__ __forceinline__ void issue_tile(const uint16_t* __restrict__ kb,
                                            const uint16_t* __restrict__ vb, int32_t k_row,
@@ -80,7 +83,8 @@ __device__ __forceinline__ void issue_tile(const uint16_t* __restrict__ kb,
   for (int i = 0; i < D / 16; ++i) {
     const int flat = i * kWave + lane;
     const int row = min(flat / PR, last), c16 = flat % PR;
-    r.v[i] = reinterpret_cast<const u32x4*>(vb + (ti.row0 + row) * v_row)[c16];
+    r.v[i] = __builtin_nontemporal_load(
+        reinterpret_cast<const u32x4*>(vb + (ti.row0 + row) * v_row) + c16);
   }
 }
 
