@@ -6,7 +6,10 @@
 // The gather copies each kept chunk of the K (and V) history into its pool
 // slot; rows past the end of the stream are zero-filled.  One workgroup per
 // (kept slot, stream); each thread moves 16-byte vectors with several loads
-// in flight, so a chunk is read and written as whole cache lines.
+// in flight, so a chunk is read and written as whole cache lines.  Loads and
+// stores carry the non-temporal hint: at 4 x 512K (215 MB moved) that took
+// the gather from 45.5 to 38.0 us, against 41.2 with the hint on the loads
+// only and 40.0 on the stores only.
 #include "lsa_internal.hpp"
 
 namespace lsa {
@@ -27,13 +30,14 @@ __device__ __forceinline__ void copy_chunk(const char* __restrict__ src, char* _
 #pragma unroll
     for (int u = 0; u < kGatherUnroll; ++u) {
       const int64_t off = off0 + u * kStep;
-      v[u] = (off < valid_bytes) ? *reinterpret_cast<const u32x4*>(src + off)
-                                 : u32x4{0u, 0u, 0u, 0u};
+      v[u] = (off < valid_bytes)
+                 ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + off))
+                 : u32x4{0u, 0u, 0u, 0u};
     }
 #pragma unroll
     for (int u = 0; u < kGatherUnroll; ++u) {
       const int64_t off = off0 + u * kStep;
-      if (off < total_bytes) *reinterpret_cast<u32x4*>(dst + off) = v[u];
+      if (off < total_bytes) __builtin_nontemporal_store(v[u], reinterpret_cast<u32x4*>(dst + off));
     }
   }
 }
