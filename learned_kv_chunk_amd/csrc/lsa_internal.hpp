@@ -22,8 +22,9 @@ constexpr int kTileTokens = 32;        // tokens per attention tile
 //  * fixed split (per > 0): W_b = ceil(T_b / per), runs of `per` tiles;
 //  * proportional split (per == 0): the device's `target` workgroups (one per
 //    CU) are shared out in proportion to the streams' tiles,
-//    W_b = max(1, round(T_b * target / T)), and stream b's runs hold
-//    ceil(T_b / W_b) tiles, so every CU gets about T / target tiles.
+//    w_b = max(1, round(T_b * target / T)), stream b's runs hold
+//    per_b = ceil(T_b / w_b) tiles, so every CU gets about T / target tiles,
+//    and W_b = ceil(T_b / per_b) <= w_b workgroups carry them.
 // Either way a run holds at most run_tile_cap(tiles_per_chunk) tiles (W_b is
 // raised where needed), so that the kept-chunk indices of any run fit in
 // kMaxRunSlots LDS words.  Workgroup ids at or beyond sum_b W_b do nothing;
@@ -153,8 +154,11 @@ __device__ __forceinline__ StreamSplit stream_split(const int32_t* sel_off, int3
     const int32_t w_min = ceil_div_i(r.tiles, run_tile_cap(tpc));
     if (w < w_min) w = w_min;
     if (w > r.tiles) w = r.tiles;
-    r.wgs = w;
     r.per = w > 0 ? ceil_div_i(r.tiles, w) : 1;
+    // runs of `per` tiles may need fewer workgroups than w (e.g. 2620 tiles
+    // over 256: runs of 11 fill 239), and a workgroup with no tiles would
+    // still write a partial that the merge reads
+    r.wgs = w > 0 ? ceil_div_i(r.tiles, r.per) : 0;
   }
   return r;
 }
