@@ -865,6 +865,22 @@ def main():
     ms_per_step = g0.elapsed_time(g1) / args.steps
     steps_per_s = 1e3 / ms_per_step
 
+    # pass 1b: the same K steps captured once in a HIP graph and replayed
+    # between two events, as a decode loop that captures its step would issue
+    # them (no host launch cost between steps)
+    step_graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(step_graph):
+        run(args.steps, t_first)
+    step_graph.replay()
+    torch.cuda.synchronize()
+    gg0, gg1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    gg0.record()
+    step_graph.replay()
+    gg1.record()
+    torch.cuda.synchronize()
+    graph_ms_per_step = gg0.elapsed_time(gg1) / args.steps
+    del step_graph
+
     # pass 2: the same K steps with HIP events around the attention kernel of
     # every step (event records cost time between kernels, so this pass only
     # measures that kernel's duration)
@@ -1009,6 +1025,8 @@ def main():
         "step_hbm_frac": step_bytes * steps_per_s / 1e9 / HBM_PEAK_GBS,
         "wall_ms_per_step": wall * 1e3 / args.steps,
         "host_enqueue_ms_per_step": host_enqueue_s * 1e3 / args.steps,
+        "graph_ms_per_step": graph_ms_per_step,
+        "graph_steps_per_s": 1e3 / graph_ms_per_step,
         "ms_per_step_with_attn_events": ms_per_step_with_events,
         "resident_fraction": w.resident_fraction(),
         "roofline": {
