@@ -762,6 +762,9 @@ def main():
                     help="residency mode: indexer query drift per re-index epoch")
     ap.add_argument("--epochs", type=int, default=4, help="residency mode: timed re-index epochs")
     ap.add_argument("--copy-mib", type=int, default=1024)
+    ap.add_argument("--attention-only", action="store_true",
+                    help="step mode: time only the attention partial kernel (pass 3), so "
+                         "that a kernel trace of the run holds just those launches")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -846,6 +849,42 @@ def main():
             r.step(t, reindex=(t % R_idx == 0), materialize_pool=cfg.materialize_pool,
                    ev_begin=eb, ev_end=ee, q=qs[t % nq])
 
+    # pass 3 (roofline.avg_launch_us): the attention partial kernel alone, the
+    # K launches (one per replica in turn, so each reads cold K/V) replayed
+    # back to back from a HIP graph with two events around the replay: no
+    # event record sits between the kernels
+    pool_mode = bool(cfg.materialize_pool)
+
+    def partial(i):
+        r = replicas[i % reps]
+        lsa.bench_attention_partial(
+            r.shape, qs[i % nq], r.k_pool if pool_mode else r.K,
+            r.v_pool if pool_mode else r.V, r.tok_off, r.sel_idx, r.sel_off,
+            lsa.KV_POOL if pool_mode else lsa.KV_STORE, r.workspace)
+
+    kernel_file = os.path.join(ROOT, "learned_kv_chunk_amd", "csrc",
+                               "attn_mla.hip" if cfg.v_aliases_k else
+                               ("attn_mqa.hip" if cfg.dtype == "bf16" else "attn_portable.hip"))
+    if args.attention_only:
+        attn_us = _graph_us(partial, args.steps)
+        attn_gbs = attn_bytes / attn_us / 1e3
+        print(json.dumps({
+            "metric": "split-KV attention partial kernel launches/sec (cold K/V)",
+            "value": 1e6 / attn_us, "unit": "launches/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": 1, "higher_is_better": True, "dtype": cfg.dtype, "data": "synthetic",
+            "config": {"workload": f"{args.config}: {WORKLOAD_TEXT[args.config]}",
+                       "replicas": reps},
+            "roofline": {"kernel": os.path.basename(kernel_file).replace(".hip", ""),
+                         "bound": "hbm", "achieved": attn_gbs, "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": attn_gbs / HBM_PEAK_GBS,
+                         "algorithmic_bytes_per_launch": int(attn_bytes),
+                         "avg_launch_us": attn_us,
+                         "timing": "K cold launches replayed from a HIP graph (one untimed "
+                                   "replay first)"}}), flush=True)
+        return
+    attn_us = _graph_us(partial, args.steps)
+    attn_gbs = attn_bytes / attn_us / 1e3
+
     run(args.warmup, 0)
     torch.cuda.synchronize()
     # steps are numbered from a multiple of the re-index interval so that the
@@ -898,21 +937,8 @@ def main():
     attn_us_events = float(np.mean([a.elapsed_time(b) for a, b in evs])) * 1e3
     ms_per_step_with_events = h0.elapsed_time(h1) / args.steps
 
-    # pass 3 (roofline.avg_launch_us): the attention partial kernel alone, the
-    # K launches (one per replica in turn, so each reads cold K/V) replayed
-    # back to back from a HIP graph with two events around the replay: no
-    # event record sits between the kernels
-    pool_mode = bool(cfg.materialize_pool)
-
-    def partial(i):
-        r = replicas[i % reps]
-        lsa.bench_attention_partial(
-            r.shape, qs[i % nq], r.k_pool if pool_mode else r.K,
-            r.v_pool if pool_mode else r.V, r.tok_off, r.sel_idx, r.sel_off,
-            lsa.KV_POOL if pool_mode else lsa.KV_STORE, r.workspace)
-
-    attn_us = _graph_us(partial, args.steps)
-    attn_gbs = attn_bytes / attn_us / 1e3
+    # pass 3 (roofline.avg_launch_us, timed above): see the definition of
+    # `partial`
 
     # warm (Infinity-Cache-assisted) reference: the same steps on one replica
     warm_n = min(args.steps, 100)
@@ -993,9 +1019,6 @@ def main():
     torch.cuda.synchronize()
     copy_gbs = 3 * 2 * cb / (c0.elapsed_time(c1) * 1e-3) / 1e9
     del csrc, cdst
-    kernel_file = os.path.join(ROOT, "learned_kv_chunk_amd", "csrc",
-                               "attn_mla.hip" if cfg.v_aliases_k else
-                               ("attn_mqa.hip" if cfg.dtype == "bf16" else "attn_portable.hip"))
     traffic = load_traffic(kernel_file, args.config)
     line = {
         "metric": "LSA decode steps/sec at 128K ctx (score+top-k+attn); HBM GB/s vs peak",
