@@ -151,9 +151,11 @@ __device__ __forceinline__ void dma_tile(const unsigned char* __restrict__ kbyte
 }
 
 // Copy the query rows of all heads (H rows of 1152 B, contiguous) into LDS
-// at `dst` (two tile buffers hold the 64-row maximum): instruction j of wave w
-// copies bytes (w + 8j) * 1024 .. +1023.  Every wave issues kQDma
-// instructions; a lane whose bytes lie past the H rows re-reads the last 16
+// at `dst` (two tile buffers hold the 64-row maximum) in the tiles' layout:
+// LDS slot (row r, vector v) holds the row's vector v ^ swz(r), so that the
+// operand reads below are conflict-free like the K reads.  Instruction j of
+// wave w fills slots (w + 8j) * 64 .. +63.  Every wave issues kQDma
+// instructions; a lane whose slot lies past the H rows re-reads the last 16
 // bytes, so no read leaves the query array.
 constexpr int kQDma = kMlaDqk * 2 * 64 / (kWave * 16) / kMlaWaves;  // 9
 static_assert(kQDma * kMlaWaves * kWave * 16 == 2 * kBufBytes, "Q fills two tile buffers");
@@ -169,7 +171,10 @@ __device__ __forceinline__ void dma_q(const unsigned char* __restrict__ qbytes, 
 #pragma unroll
   for (int j = 0; j < kQDma; ++j) {
     const int inst = wave + kMlaWaves * j;
-    const int32_t off = min(inst * kWave * 16 + lane * 16, q_bytes - 16);
+    const int slot = inst * kWave + lane;
+    const int row = slot / kRowVecs;
+    const int32_t off =
+        min(row * kPitch + ((slot - row * kRowVecs) ^ swz(row)) * 16, q_bytes - 16);
     dma16(sbase, static_cast<uint32_t>(off), __builtin_amdgcn_readfirstlane(lds0 + inst * kWave * 16));
   }
 }
@@ -398,10 +403,12 @@ __global__ __launch_bounds__(kMlaThreads, 1) void attn_mla_kernel(AttnArgs a) {
     } else {
       LSA_MLA_WAIT_BARRIER(0);
     }
-    const unsigned char* qrow = qs + min(head, H - 1) * (kMlaDqk * 2) + 16 * g;
+    const int qr = min(head, H - 1);
+    const unsigned char* qrow = qs + qr * kPitch;
 #pragma unroll
     for (int s = 0; s < kMlaDqk / 32; ++s)
-      qf[s] = as_bf16x8(head < H ? *reinterpret_cast<const u32x4*>(qrow + 64 * s)
+      qf[s] = as_bf16x8(head < H ? *reinterpret_cast<const u32x4*>(
+                                       qrow + 16 * ((4 * s + g) ^ swz(qr)))
                                  : u32x4{0u, 0u, 0u, 0u});
     LSA_MLA_BARRIER();  // buffers 2-3 are free once every wave holds its Q
     if (2 < n) nv[2] = issue(2, 2);
