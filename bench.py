@@ -12,11 +12,15 @@ more than twice the 256 MB last-level (Infinity) cache: every step streams its
 bytes from HBM instead of re-reading what the previous step left in cache.
 `--replicas 1` gives the cache-assisted figure.
 
-Prints one JSON line (rank 0, one GPU).  `value` is decode steps per second;
-`roofline` reports the attention kernel's algorithmic bytes per launch over
-its average duration measured with HIP events around that kernel inside the
-timed steps; `cpu_baseline` times the CPU oracle on the host on a bounded
-sample of the same workload.
+Prints one JSON line (rank 0, one GPU).  `value` is decode steps per second
+(K steps issued eagerly between two events; `graph_ms_per_step` is the same
+steps replayed from a HIP graph); `roofline` reports the attention partial
+kernel's algorithmic bytes per launch over its average duration, K cold
+launches of that kernel alone replayed from a HIP graph between two events;
+`cpu_baseline` times the CPU oracle on the host on a bounded sample of the
+same workload.  `--attention-only` times just that kernel (for a kernel
+trace holding only its launches); `--mode` selects the retriever, residency,
+append, scorer and copy measurements.
 """
 from __future__ import annotations
 
