@@ -267,7 +267,7 @@ def test_mla_attention_split_variants(per):
     print(per, P.check_attention("bf16", out, lse, o_ref, l_ref))
 
 
-@pytest.mark.parametrize("heads", [16, 40, 64])
+@pytest.mark.parametrize("heads", [1, 7, 16, 40, 64])
 def test_mla_attention_head_counts(heads):
     w = wl.make_workload(_mla_cfg(num_q_heads=heads, kv_std=1.0, q_std=1.0))
     d = dev.upload(w, "cuda", attn_tiles_per_block=5)
