@@ -276,6 +276,7 @@ def run_retriever(args):
     shape = dev.problem_shape(w)
     shape.max_k = shape.max_chunks        # the kept counts are known on the device only
     shape.total_k = shape.total_chunks
+    shape.uniform = False
     B, n_total = w.B, int(w.chunk_off[-1])
     qd = torch.from_numpy(q.view(np.int16)).view(torch.bfloat16).cuda()
     wd = torch.from_numpy(hw).cuda()
@@ -639,7 +640,8 @@ def run_append(args):
     n_cap = (cap + C - 1) // C
     attn_shape = dataclasses.replace(
         shape, max_chunks=int(n_cap.max()), total_chunks=int(n_cap.sum()),
-        max_k=shape.max_k + max_recent, total_k=shape.total_k + w.B * max_recent)
+        max_k=shape.max_k + max_recent, total_k=shape.total_k + w.B * max_recent,
+        uniform=False)
     ws = lsa.allocate_workspace(attn_shape, "cuda")
     out_idx = torch.empty(attn_shape.total_k, dtype=torch.int32, device="cuda")
     out_off = torch.empty(w.B + 1, dtype=torch.int32, device="cuda")

@@ -90,8 +90,19 @@ typedef struct lsa_shape {
                              rounding (bf16 inputs: the attention weights are
                              rounded to bf16 relative to each split's running
                              maximum, about 2^-9 relative). */
-  int32_t reserved;       /* must be 0 */
+  int32_t flags;          /* 0, or LSA_SHAPE_UNIFORM */
 } lsa_shape;
+
+/* lsa_shape.flags: every stream has exactly max_chunks chunks and keeps
+ * exactly max_k of them, so chunk_off[b] = b * max_chunks and
+ * sel_off[b] = b * max_k (checked on the host against total_chunks and
+ * total_k; the offset arrays are still passed and must hold these values).
+ * The kernels then derive those offsets instead of reading them, which takes
+ * one dependent memory round trip out of the score, select, gather,
+ * attention and merge launches.  Leave it 0 for ragged batches and for keep
+ * sets whose sizes are known on the device only (lsa_select_threshold,
+ * lsa_keep_recent), whose shapes carry bounds. */
+#define LSA_SHAPE_UNIFORM 1
 
 /* Human-readable name of a status code (static storage). */
 const char* lsa_status_string(lsa_status status);

@@ -44,8 +44,8 @@ __global__ __launch_bounds__(kWave) void attn_portable_kernel(AttnArgs a) {
   {
     int32_t b, local;
     StreamSplit sp;
-    find_stream_of_wg(a.sel_off, a.B, a.tiles_per_chunk, a.per, a.target, blockIdx.x, &b,
-                      &local, &sp);
+    find_stream_of_wg(SelCsr{a.sel_off, a.uni_k}, a.B, a.tiles_per_chunk, a.per, a.target,
+                      blockIdx.x, &b, &local, &sp);
     if (lane == 0) {
       s_plan[0] = b;
       s_plan[1] = local * sp.per;
@@ -63,7 +63,7 @@ __global__ __launch_bounds__(kWave) void attn_portable_kernel(AttnArgs a) {
     s_q[i] = load_elem(q, static_cast<int64_t>(b) * H * dqk + i);
   __syncthreads();
 
-  const int32_t sel0 = a.sel_off[b];
+  const int32_t sel0 = SelCsr{a.sel_off, a.uni_k}.at(b);
   const int64_t cap = a.tok_off[b + 1] - a.tok_off[b];
   const int64_t sl = a.seq_len ? a.seq_len[b] : cap;
   const int64_t len = sl < 0 ? 0 : (sl < cap ? sl : cap);

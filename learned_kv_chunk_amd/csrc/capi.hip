@@ -24,13 +24,18 @@ lsa_status check_common(const lsa_shape* s) {
   if (s == nullptr) return LSA_ERR_INVALID_ARGUMENT;
   if (s->batch < 1 || s->chunk_size < 1 || s->chunk_size > kMaxChunkSize) return LSA_ERR_INVALID_ARGUMENT;
   if (s->dtype != LSA_DTYPE_F32 && s->dtype != LSA_DTYPE_BF16) return LSA_ERR_INVALID_ARGUMENT;
-  if (s->reserved != 0 || s->attn_tiles_per_block < 0) return LSA_ERR_INVALID_ARGUMENT;
+  if ((s->flags & ~LSA_SHAPE_UNIFORM) != 0 || s->attn_tiles_per_block < 0)
+    return LSA_ERR_INVALID_ARGUMENT;
   if (s->max_chunks < 1 || s->max_k < 1 || s->max_k > s->max_chunks) return LSA_ERR_INVALID_ARGUMENT;
   if (s->total_chunks < s->batch || s->total_chunks > static_cast<int64_t>(s->batch) * s->max_chunks ||
       s->total_chunks > INT32_MAX)
     return LSA_ERR_INVALID_ARGUMENT;
   if (s->total_k < s->batch || s->total_k > static_cast<int64_t>(s->batch) * s->max_k ||
       s->total_k > s->total_chunks)
+    return LSA_ERR_INVALID_ARGUMENT;
+  if ((s->flags & LSA_SHAPE_UNIFORM) &&
+      (s->total_chunks != static_cast<int64_t>(s->batch) * s->max_chunks ||
+       s->total_k != static_cast<int64_t>(s->batch) * s->max_k))
     return LSA_ERR_INVALID_ARGUMENT;
   return LSA_OK;
 }
@@ -99,6 +104,7 @@ lsa_status enqueue_attention(const lsa_shape& s, int32_t kv_mode, const void* q,
   a.tiles_per_chunk = plan.tiles_per_chunk;
   a.per = plan.per;
   a.target = plan.target;
+  a.uni_k = (s.flags & LSA_SHAPE_UNIFORM) ? s.max_k : 0;
   a.scale_log2 = s.softmax_scale * 1.4426950408889634f;
   if (ev_begin && hipEventRecord(static_cast<hipEvent_t>(ev_begin), st) != hipSuccess)
     return LSA_ERR_HIP;
@@ -131,7 +137,7 @@ const char* lsa_status_string(lsa_status status) {
   }
 }
 
-int32_t lsa_abi_version(void) { return 1; }
+int32_t lsa_abi_version(void) { return 2; }
 
 int32_t lsa_keep_count(int32_t n_chunks, int32_t ratio_num, int32_t ratio_den, int32_t round_up) {
   if (n_chunks <= 0 || ratio_num <= 0 || ratio_den <= 0) return 0;

@@ -46,12 +46,13 @@ __global__ __launch_bounds__(kGatherThreads) void gather_kernel(
     const char* __restrict__ store, int32_t row_bytes, const int64_t* __restrict__ tok_off,
     const int32_t* __restrict__ sel_idx, const int32_t* __restrict__ sel_off,
     char* __restrict__ pool, const char* __restrict__ store2, int32_t row_bytes2,
-    char* __restrict__ pool2, int32_t C) {
+    char* __restrict__ pool2, int32_t C, int32_t uni_k) {
   const int b = blockIdx.y;
   const int32_t j = blockIdx.x;
-  const int32_t k = sel_off[b + 1] - sel_off[b];
+  const int32_t s0 = uni_k > 0 ? b * uni_k : sel_off[b];  // uniform: not read
+  const int32_t k = uni_k > 0 ? uni_k : sel_off[b + 1] - s0;
   if (j >= k) return;
-  const int64_t slot = static_cast<int64_t>(sel_off[b]) + j;
+  const int64_t slot = static_cast<int64_t>(s0) + j;
   const int64_t len = tok_off[b + 1] - tok_off[b];
   const int64_t n = sel_idx[slot];
   int64_t valid = len - n * C;
@@ -92,7 +93,8 @@ hipError_t launch_gather(const lsa_shape& s, const void* store, int32_t row_byte
   hipLaunchKernelGGL(gather_kernel, grid, dim3(kGatherThreads), 0, st,
                      static_cast<const char*>(store), row_bytes, tok_off, sel_idx, sel_off,
                      static_cast<char*>(pool), static_cast<const char*>(store2), row_bytes2,
-                     static_cast<char*>(pool2), s.chunk_size);
+                     static_cast<char*>(pool2), s.chunk_size,
+                     (s.flags & LSA_SHAPE_UNIFORM) ? s.max_k : 0);
   return hipGetLastError();
 }
 

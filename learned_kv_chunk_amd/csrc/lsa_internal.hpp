@@ -76,6 +76,7 @@ struct AttnArgs {
   int32_t v_row;          // elements between consecutive V rows
   int32_t pool;           // 1: slot-indexed pool, 0: store indexed by chunk
   int32_t tiles_per_chunk, per, target;
+  int32_t uni_k;          // k of every stream when the shape is uniform, else 0
   float scale_log2;       // softmax_scale * log2(e)
 };
 
@@ -132,16 +133,24 @@ __device__ __forceinline__ float bf16_bits_to_float(uint16_t h) {
 
 __device__ __forceinline__ int32_t ceil_div_i(int32_t a, int32_t b) { return (a + b - 1) / b; }
 
+// The kept-chunk offsets sel_off[0..B]: read from memory, or b * uni for a
+// uniform shape (every stream keeps uni chunks), which needs no load.
+struct SelCsr {
+  const int32_t* off;
+  int32_t uni;
+  __device__ __forceinline__ int32_t at(int32_t i) const { return uni > 0 ? i * uni : off[i]; }
+};
+
 // Split geometry of one stream (device): tiles T_b, workgroups W_b and tiles
 // per workgroup, given the plan and the total tile count T.
 struct StreamSplit {
   int32_t tiles, wgs, per;
 };
-__device__ __forceinline__ StreamSplit stream_split(const int32_t* sel_off, int32_t b,
-                                                    int32_t tpc, int32_t per, int32_t target,
+__device__ __forceinline__ StreamSplit stream_split(SelCsr sel_off, int32_t b, int32_t tpc,
+                                                    int32_t per, int32_t target,
                                                     int32_t total_tiles) {
   StreamSplit r;
-  int32_t k = sel_off[b + 1] - sel_off[b];
+  int32_t k = sel_off.at(b + 1) - sel_off.at(b);
   if (k < 0) k = 0;
   r.tiles = k * tpc;
   if (per > 0) {
@@ -166,13 +175,28 @@ __device__ __forceinline__ StreamSplit stream_split(const int32_t* sel_off, int3
 // Run by one full wave: the stream owning workgroup `wg`, the workgroup's
 // index within that stream, and the stream's split.  b = -1 when wg is past
 // the last workgroup.
-__device__ __forceinline__ void find_stream_of_wg(const int32_t* sel_off, int32_t B,
-                                                  int32_t tpc, int32_t per, int32_t target,
-                                                  int32_t wg, int32_t* b_out, int32_t* local_out,
+__device__ __forceinline__ void find_stream_of_wg(SelCsr sel_off, int32_t B, int32_t tpc,
+                                                  int32_t per, int32_t target, int32_t wg,
+                                                  int32_t* b_out, int32_t* local_out,
                                                   StreamSplit* split_out,
                                                   int32_t* sel0_out = nullptr) {
   const int lane = threadIdx.x & (kWave - 1);
-  const int32_t total_tiles = (sel_off[B] - sel_off[0]) * tpc;
+  const int32_t total_tiles = (sel_off.at(B) - sel_off.at(0)) * tpc;
+  if (sel_off.uni > 0) {  // every stream has the same split
+    const StreamSplit sp = stream_split(sel_off, 0, tpc, per, target, total_tiles);
+    if (sp.wgs > 0 && wg < B * sp.wgs) {
+      *b_out = wg / sp.wgs;
+      *local_out = wg - *b_out * sp.wgs;
+      *split_out = sp;
+      if (sel0_out) *sel0_out = *b_out * sel_off.uni;
+      return;
+    }
+    *b_out = -1;
+    *local_out = 0;
+    *split_out = StreamSplit{0, 0, 1};
+    if (sel0_out) *sel0_out = 0;
+    return;
+  }
   int32_t base = 0;  // workgroups of streams before the current 64-stream window
   for (int32_t s0 = 0; s0 < B; s0 += kWave) {
     const int32_t s = s0 + lane;
@@ -180,7 +204,7 @@ __device__ __forceinline__ void find_stream_of_wg(const int32_t* sel_off, int32_
     int32_t so = 0;
     if (s < B) {
       sp = stream_split(sel_off, s, tpc, per, target, total_tiles);
-      so = sel_off[s];
+      so = sel_off.at(s);
     }
     const int32_t incl = static_cast<int32_t>(wave_inclusive_scan(static_cast<uint32_t>(sp.wgs)));
     const int32_t total = __builtin_amdgcn_readlane(incl, kWave - 1);
@@ -236,7 +260,8 @@ __device__ __forceinline__ AttnRun attn_prologue(const AttnArgs& a, int32_t* s_s
     const int32_t tpc = a.tiles_per_chunk;
     int32_t b, local, sel0;
     StreamSplit sp;
-    find_stream_of_wg(a.sel_off, a.B, tpc, a.per, a.target, blockIdx.x, &b, &local, &sp, &sel0);
+    find_stream_of_wg(SelCsr{a.sel_off, a.uni_k}, a.B, tpc, a.per, a.target, blockIdx.x, &b,
+                      &local, &sp, &sel0);
     AttnRun r = {b, 0, 0, 0, 0, 0, 0};
     if (b >= 0) {
       r.t_begin = local * sp.per;
@@ -268,11 +293,17 @@ __device__ __forceinline__ AttnRun attn_prologue(const AttnArgs& a, int32_t* s_s
 
 // Run by one full wave: index of the first workgroup of stream b and its
 // workgroup count.
-__device__ __forceinline__ void stream_wg_range(const int32_t* sel_off, int32_t B, int32_t b,
+__device__ __forceinline__ void stream_wg_range(SelCsr sel_off, int32_t B, int32_t b,
                                                 int32_t tpc, int32_t per, int32_t target,
                                                 int32_t* first_out, int32_t* count_out) {
   const int lane = threadIdx.x & (kWave - 1);
-  const int32_t total_tiles = (sel_off[B] - sel_off[0]) * tpc;
+  const int32_t total_tiles = (sel_off.at(B) - sel_off.at(0)) * tpc;
+  if (sel_off.uni > 0) {  // every stream has the same split
+    const int32_t w = stream_split(sel_off, 0, tpc, per, target, total_tiles).wgs;
+    *first_out = b * w;
+    *count_out = w;
+    return;
+  }
   uint32_t acc = 0;
   for (int32_t s0 = 0; s0 < b; s0 += kWave) {
     const int32_t s = s0 + lane;

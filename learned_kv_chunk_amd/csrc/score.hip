@@ -84,14 +84,16 @@ __device__ __forceinline__ void score_rows(const T* __restrict__ q, const T* __r
   }
 }
 
+// uni_n > 0: every stream has uni_n chunks (chunk_off[b] = b * uni_n, not read).
 template <typename T, int G, int NV>
 __global__ __launch_bounds__(kScoreThreads) void score_kernel(
     const T* __restrict__ q, const T* __restrict__ emb, const int32_t* __restrict__ chunk_off,
-    float* __restrict__ scores, int32_t D) {
+    float* __restrict__ scores, int32_t D, int32_t uni_n) {
   constexpr int kRowsPerBlock = (kScoreThreads / G) * kScorePasses;
   const int b = blockIdx.y;
-  const int32_t r_end = chunk_off[b + 1];
-  const int32_t r_begin = chunk_off[b] + static_cast<int32_t>(blockIdx.x) * kRowsPerBlock;
+  const int32_t r0 = uni_n > 0 ? b * uni_n : chunk_off[b];
+  const int32_t r_end = uni_n > 0 ? r0 + uni_n : chunk_off[b + 1];
+  const int32_t r_begin = r0 + static_cast<int32_t>(blockIdx.x) * kRowsPerBlock;
   if (r_begin >= r_end) return;
   score_rows<T, G, NV>(q, emb, scores, D, b, r_begin, r_end);
 }
@@ -114,7 +116,7 @@ hipError_t launch_score_t(const lsa_shape& s, const void* q, const void* emb,
   dim3 grid((s.max_chunks + kRowsPerBlock - 1) / kRowsPerBlock, s.batch);
   hipLaunchKernelGGL((score_kernel<T, G, NV>), grid, dim3(kScoreThreads), 0, st,
                      static_cast<const T*>(q), static_cast<const T*>(emb), chunk_off, scores,
-                     s.index_dim);
+                     s.index_dim, (s.flags & LSA_SHAPE_UNIFORM) ? s.max_chunks : 0);
   return hipGetLastError();
 }
 

@@ -17,19 +17,23 @@
 namespace lsa {
 namespace {
 
+// uni_n, uni_k > 0: every stream has uni_n chunks and keeps uni_k (the
+// offsets are b * uni_n and b * uni_k, not read).
 template <int THREADS, int KPT>
 __global__ __launch_bounds__(THREADS) void select_kernel(const float* __restrict__ scores,
                                                         const int32_t* __restrict__ chunk_off,
                                                         const int32_t* __restrict__ sel_off,
-                                                        int32_t* __restrict__ sel_idx) {
+                                                        int32_t* __restrict__ sel_idx,
+                                                        int32_t uni_n, int32_t uni_k) {
   __shared__ SelectLds<THREADS> lds;
   const int b = blockIdx.x;
-  const int32_t base = chunk_off[b];
-  const int32_t n = chunk_off[b + 1] - base;
-  int32_t k = sel_off[b + 1] - sel_off[b];
+  const int32_t base = uni_n > 0 ? b * uni_n : chunk_off[b];
+  const int32_t n = uni_n > 0 ? uni_n : chunk_off[b + 1] - base;
+  const int32_t s0 = uni_k > 0 ? b * uni_k : sel_off[b];
+  int32_t k = uni_k > 0 ? uni_k : sel_off[b + 1] - s0;
   if (n <= 0 || k <= 0) return;
   if (k > n) k = n;  // violated precondition: never write past the stream's range
-  int32_t* out = sel_idx + sel_off[b];
+  int32_t* out = sel_idx + s0;
   if (k == n) {
     for (int32_t i = threadIdx.x; i < n; i += THREADS) out[i] = i;
     return;
@@ -146,8 +150,9 @@ hipError_t launch_threshold_t(const lsa_shape& s, const float* scores, const int
 template <int THREADS, int KPT>
 hipError_t launch_select_t(const lsa_shape& s, const float* scores, const int32_t* chunk_off,
                            const int32_t* sel_off, int32_t* sel_idx, hipStream_t st) {
+  const bool uni = (s.flags & LSA_SHAPE_UNIFORM) != 0;
   hipLaunchKernelGGL((select_kernel<THREADS, KPT>), dim3(s.batch), dim3(THREADS), 0, st, scores,
-                     chunk_off, sel_off, sel_idx);
+                     chunk_off, sel_off, sel_idx, uni ? s.max_chunks : 0, uni ? s.max_k : 0);
   return hipGetLastError();
 }
 

@@ -39,7 +39,8 @@ def problem_shape(w: Workload, attn_tiles_per_block: int = 0) -> lsa.ProblemShap
         v_aliases_k=c.v_aliases_k, dtype=torch.bfloat16 if c.dtype == "bf16" else torch.float32,
         softmax_scale=c.softmax_scale, max_chunks=int(n_chunks.max()), max_k=int(w.keep.max()),
         total_chunks=int(w.chunk_off[-1]), total_k=int(w.sel_off[-1]),
-        attn_tiles_per_block=attn_tiles_per_block)
+        attn_tiles_per_block=attn_tiles_per_block,
+        uniform=bool((n_chunks == n_chunks[0]).all() and (w.keep == w.keep[0]).all()))
 
 
 @dataclasses.dataclass

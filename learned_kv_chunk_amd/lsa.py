@@ -31,6 +31,7 @@ DTYPE_F32 = 0
 DTYPE_BF16 = 1
 KV_STORE = 0
 KV_POOL = 1
+SHAPE_UNIFORM = 1  # lsa_shape.flags: LSA_SHAPE_UNIFORM
 
 
 class LsaError(RuntimeError):
@@ -55,7 +56,7 @@ class Shape(ctypes.Structure):
         ("total_chunks", ctypes.c_int64),
         ("total_k", ctypes.c_int64),
         ("attn_tiles_per_block", ctypes.c_int32),
-        ("reserved", ctypes.c_int32),
+        ("flags", ctypes.c_int32),
     ]
 
 
@@ -164,6 +165,10 @@ class ProblemShape:
     total_chunks: int
     total_k: int
     attn_tiles_per_block: int = 0
+    # every stream has max_chunks chunks and keeps max_k of them
+    # (LSA_SHAPE_UNIFORM): the kernels derive the offsets instead of reading
+    # them.  Set it to False for keep sets whose sizes the device decides.
+    uniform: bool = False
 
     def c(self) -> Shape:
         if self.dtype == torch.bfloat16:
@@ -175,7 +180,8 @@ class ProblemShape:
         return Shape(self.batch, self.chunk_size, self.index_dim, self.num_q_heads,
                       self.head_dim_qk, self.head_dim_v, int(bool(self.v_aliases_k)), dt,
                       float(self.softmax_scale), self.max_chunks, self.max_k,
-                      self.total_chunks, self.total_k, self.attn_tiles_per_block, 0)
+                      self.total_chunks, self.total_k, self.attn_tiles_per_block,
+                      SHAPE_UNIFORM if self.uniform else 0)
 
 
 def keep_count(n_chunks: int, ratio_num: int, ratio_den: int, round_up: bool) -> int:

@@ -36,7 +36,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_status_strings_and_version():
-    assert lsa.library().lsa_abi_version() == 1
+    assert lsa.library().lsa_abi_version() == 2
     for code, name in [(0, "LSA_OK"), (1, "LSA_ERR_INVALID_ARGUMENT"), (2, "LSA_ERR_UNSUPPORTED"),
                        (3, "LSA_ERR_WORKSPACE_TOO_SMALL"), (4, "LSA_ERR_HIP")]:
         assert lsa.status_string(code) == name
@@ -110,6 +110,8 @@ def _gather(s, v_store=DUMMY, v_pool=DUMMY):
     dict(batch=0), dict(chunk_size=0), dict(chunk_size=2048), dict(max_chunks=0),
     dict(max_k=0), dict(max_k=3000), dict(total_chunks=15), dict(total_chunks=16 * 2048 + 1),
     dict(total_k=15), dict(total_k=16 * 276 + 1), dict(attn_tiles_per_block=-1),
+    # a uniform shape must have total_chunks = B * max_chunks and total_k = B * max_k
+    dict(uniform=True, total_chunks=16 * 2048 - 1), dict(uniform=True, total_k=16 * 276 - 1),
 ])
 def test_invalid_shapes_rejected_everywhere(bad):
     s = shape(**bad)
@@ -117,6 +119,16 @@ def test_invalid_shapes_rejected_everywhere(bad):
     assert _select(s) == lsa.LSA_ERR_INVALID_ARGUMENT
     assert _attn(s) == lsa.LSA_ERR_INVALID_ARGUMENT
     assert _gather(s) == lsa.LSA_ERR_INVALID_ARGUMENT
+
+
+def test_shape_flags():
+    # LSA_SHAPE_UNIFORM is the only flag; a consistent uniform shape is accepted
+    c = shape(uniform=True).c()
+    assert c.flags == lsa.SHAPE_UNIFORM
+    assert lsa.library().lsa_workspace_bytes(ctypes.byref(c)) > 0
+    c.flags = 2
+    assert lsa.library().lsa_workspace_bytes(ctypes.byref(c)) == 0
+    assert shape().c().flags == 0
 
 
 def test_null_and_misaligned_pointers_rejected():

@@ -58,7 +58,8 @@ def test_append_decode_loop(name):
     n_cap = (cap + C - 1) // C
     attn_shape = dataclasses.replace(
         shape, max_chunks=int(n_cap.max()), total_chunks=int(n_cap.sum()),
-        max_k=shape.max_k + max_recent, total_k=shape.total_k + w.B * max_recent)
+        max_k=shape.max_k + max_recent, total_k=shape.total_k + w.B * max_recent,
+        uniform=False)
     kd, vd = _t(rows_k), None if rows_v is None else _t(rows_v)
     base_d = torch.from_numpy(base).cuda()
     seq_d = torch.from_numpy(L0.copy()).cuda()

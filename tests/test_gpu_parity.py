@@ -337,3 +337,33 @@ def test_workspace_is_reusable_across_calls_and_shapes():
             torch.cuda.synchronize()
             np.testing.assert_array_equal(dev.to_host(out), out_ref)
             np.testing.assert_array_equal(dev.to_host(lse), lse_ref)
+
+
+# ----------------------------------------------------------------------------- uniform shapes
+@pytest.mark.parametrize("name", ["cfg2", "cfg3", "cfg4"])
+def test_uniform_shape_flag_is_only_a_shortcut(name):
+    # equal stream lengths: every stream has the same chunk and kept counts, so
+    # the shape may carry LSA_SHAPE_UNIFORM; with and without it the decode
+    # step (score, select, gather, attention, merge) must give the same bits
+    L = wl.small_variant(name).lengths[0]
+    cfg = wl.small_variant(name, lengths=(L, L, L))
+    w = wl.make_workload(cfg)
+    d = dev.upload(w, "cuda")
+    assert d.shape.uniform
+    results = []
+    for uniform in (True, False):
+        d.shape.uniform = uniform
+        d.sel_idx.zero_()
+        d.out.zero_()
+        d.lse.zero_()
+        d.step(0, reindex=True, materialize_pool=cfg.materialize_pool)
+        torch.cuda.synchronize()
+        results.append([dev.to_host(t).copy() for t in (d.sel_idx, d.out, d.lse)])
+    d.shape.uniform = True
+    for a, b in zip(*results):
+        np.testing.assert_array_equal(a, b)
+    sel, out, lse = results[0]
+    s_gpu = dev.to_host(d.scores)
+    P.check_selection(w, s_gpu, sel, oracle.score(w.q_idx, w.emb, w.chunk_off))
+    o_ref, l_ref = P.oracle_attention_on(w, 0, sel)
+    P.check_attention(cfg.dtype, out, lse, o_ref, l_ref)

@@ -165,8 +165,9 @@ def _retriever_attention(w, q, hw, rec, combine, tau_quantile, cap, streams=None
     s_ref, _ = _check_scores(w, q, hw, rec, combine, s_gpu)
     tau = float(np.float32(np.quantile(s_ref, tau_quantile)))
     shape = dev.problem_shape(w)
-    shape.max_k = shape.max_chunks
+    shape.max_k = shape.max_chunks       # the kept counts are known on the device only
     shape.total_k = shape.total_chunks
+    shape.uniform = False
     off_d, idx_d, fb_d = lsa.select_threshold(shape, torch.from_numpy(s_gpu).cuda(), d.chunk_off,
                                               tau, cap)
     out, lse = lsa.sparse_decode_attn(shape, d.queries(0), d.K, d.V, d.tok_off, idx_d, off_d)
