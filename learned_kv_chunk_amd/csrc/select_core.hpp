@@ -252,9 +252,12 @@ __device__ __forceinline__ bool select_buckets(const uint32_t (&key)[KPT], int32
     return kv == 0u ? 0
                     : min(kSelectBins - 1, static_cast<int>((key_value(kv) - fl) * scale));
   };
+  int bin[KPT];  // kept for the candidate pass
 #pragma unroll
-  for (int i = 0; i < KPT; ++i)
-    if (tid * KPT + i < n) atomicAdd(&hist[bin_of(key[i])], 1u);
+  for (int i = 0; i < KPT; ++i) {
+    bin[i] = bin_of(key[i]);
+    if (tid * KPT + i < n) atomicAdd(&hist[bin[i]], 1u);
+  }
   select_sync<THREADS>();
   // bin d* with #(bin > d*) < k <= #(bin >= d*); lane l owns bins 16l..16l+15
   uint32_t cnt[16];
@@ -296,7 +299,7 @@ __device__ __forceinline__ bool select_buckets(const uint32_t (&key)[KPT], int32
   const uint32_t remaining = static_cast<uint32_t>(k) - gt_pick;  // kept from bin d*
 #pragma unroll
   for (int i = 0; i < KPT; ++i) {
-    if (tid * KPT + i < n && bin_of(key[i]) == static_cast<int>(pick)) {
+    if (tid * KPT + i < n && bin[i] == static_cast<int>(pick)) {
       const uint32_t slot = atomicAdd(&lds.misc[0], 1u);
       lds.cand_key[slot] = key[i];
       lds.cand_idx[slot] = tid * KPT + i;
