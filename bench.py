@@ -777,8 +777,8 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py: this build measures one GPU only (the LSA hot path has no "
-              "multi-GPU component here); run with --gpus 1", file=sys.stderr, flush=True)
+        print("bench.py: measures one GPU only (the LSA hot path here has no "
+              "multi-GPU component); run with --gpus 1", file=sys.stderr, flush=True)
         sys.exit(2)
 
     import numpy as np
