@@ -357,16 +357,16 @@ __global__ __launch_bounds__(kMlaThreads, 1) void attn_mla_kernel(AttnArgs a) {
 #pragma unroll
   for (int c = 0; c < kMlaDv / 32; ++c) o[c] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // Four-buffer pipeline: tiles i+1 .. i+3 are in flight while tile i is
-  // computed.  Each wave issues a fixed number nd of loads per tile (5 for
-  // waves 0-3, 4 for waves 4-7) and no other vector-memory operation inside
-  // the loop, so "tile i has landed" is "at most nd times the number of later
-  // tiles issued of this wave's loads outstanding", and the first barrier
-  // makes every wave's part of tile i visible.  The buffer refilled with tile
-  // i+3 held tile i-1 (for i = 0 the query), which every wave finished before
-  // that barrier.  The
-  // second barrier publishes the S^T halves; a half is rewritten only after
-  // the next first barrier, which its reader reaches after reading it.
+  // Four-buffer pipeline: tiles i+1, i+2 and (issued during iteration i)
+  // i+3 are in flight while tile i is computed.  Each wave issues a fixed
+  // number nd of loads per tile (5 for waves 0-3, 4 for waves 4-7) and no
+  // other vector-memory operation inside the loop, so "tile i has landed" is
+  // "at most nd times the number of later tiles issued of this wave's loads
+  // outstanding", and the first barrier makes every wave's part of tile i
+  // visible.  The buffer refilled with tile i+3 held tile i-1 (for i = 0 the
+  // query), which every wave finished before that barrier.  The second
+  // barrier publishes the S^T halves; a half is rewritten only after the next
+  // first barrier, which its reader reaches after reading it.
   const DmaLane dl = dma_lane(row_bytes, wave, lane);
   const ReadLane rl = read_lane(half, lane);
   const bool five = wave < 4;  // wave-uniform: 5 loads per tile, else 4
@@ -426,15 +426,18 @@ __global__ __launch_bounds__(kMlaThreads, 1) void attn_mla_kernel(AttnArgs a) {
       LSA_MLA_WAIT_BARRIER(0);
     }
     const int buf = i & (kBufs - 1);
-    if (i + kBufs - 1 < n) {
-      const int nb = (i + kBufs - 1) & (kBufs - 1);
-      nv[nb] = issue(i + kBufs - 1, nb);
-    }
     const unsigned char* kt = smem + buf * kBufBytes;
     f32x4 s_mine = {0.f, 0.f, 0.f, 0.f};
     if (active) {
       s_mine = qk_half(kt, half, rl, qf);
       s_xch[wave][lane] = s_mine;
+    }
+    // the copies of tile i+3 go out after this wave's S^T products, so that a
+    // wave stalled on a full memory queue does not hold up its products
+    // (measured: 1.2 % shorter at 1 x 1M than issuing them first)
+    if (i + kBufs - 1 < n) {
+      const int nb = (i + kBufs - 1) & (kBufs - 1);
+      nv[nb] = issue(i + kBufs - 1, nb);
     }
     LSA_MLA_BARRIER();
     if (active) {
