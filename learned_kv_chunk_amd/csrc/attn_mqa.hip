@@ -239,7 +239,6 @@ __global__ __launch_bounds__(mqa_waves<NHG>() * kWave, NHG == 1 ? 2 : 1) void at
   using L = MqaLds<D, NHG>;
   constexpr int NW = L::kWaves;
   constexpr int WPG = NW / HS;  // waves per team
-  constexpr int kThreads = NW * kWave;
   __shared__ __attribute__((aligned(16))) unsigned char smem[L::kBytes];
   __shared__ int32_t s_slot[kMaxRunSlots];  // the run's kept-chunk indices
   __shared__ AttnRun s_run;

@@ -79,7 +79,8 @@ __global__ __launch_bounds__(THREADS) void threshold_count_kernel(
     select_load_keys<THREADS, KPT>(scores + base, n, key);
     const uint32_t tkey = order_key(threshold);
 #pragma unroll
-    for (int i = 0; i < KPT; ++i) c += (threadIdx.x * KPT + i < n && key[i] >= tkey) ? 1u : 0u;
+    for (int i = 0; i < KPT; ++i)
+      c += (static_cast<int32_t>(threadIdx.x) * KPT + i < n && key[i] >= tkey) ? 1u : 0u;
   }
   c = block_sum<THREADS>(c, s_part);
   if (threadIdx.x == 0) {
@@ -117,7 +118,8 @@ __global__ __launch_bounds__(THREADS) void threshold_write_kernel(
   const uint32_t tkey = order_key(threshold);
   uint32_t c = 0;
 #pragma unroll
-  for (int i = 0; i < KPT; ++i) c += (threadIdx.x * KPT + i < n && key[i] >= tkey) ? 1u : 0u;
+  for (int i = 0; i < KPT; ++i)
+    c += (static_cast<int32_t>(threadIdx.x) * KPT + i < n && key[i] >= tkey) ? 1u : 0u;
   const uint32_t passing = block_sum<THREADS>(c, s_part[1]);
   if (passing == static_cast<uint32_t>(k)) {
     // the passing chunks in index order: thread t holds chunks [t*KPT, t*KPT+KPT)
