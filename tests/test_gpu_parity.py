@@ -367,3 +367,24 @@ def test_uniform_shape_flag_is_only_a_shortcut(name):
     P.check_selection(w, s_gpu, sel, oracle.score(w.q_idx, w.emb, w.chunk_off))
     o_ref, l_ref = P.oracle_attention_on(w, 0, sel)
     P.check_attention(cfg.dtype, out, lse, o_ref, l_ref)
+
+
+@pytest.mark.parametrize("uniform", [False, True])
+def test_more_than_64_streams(uniform):
+    # the work plan and the merge look streams up 64 at a time: 80 streams
+    # cross that window (ragged lengths, or all equal for the uniform shape)
+    rng = np.random.default_rng(80)
+    if uniform:
+        lengths = (64 * 70 + 13,) * 80
+    else:
+        lengths = tuple(int(x) for x in rng.integers(64 * 64, 64 * 90, size=80))
+    cfg = wl.small_variant("cfg2", lengths=lengths)
+    w = wl.make_workload(cfg)
+    d = dev.upload(w, "cuda")
+    assert d.shape.uniform == uniform
+    s_gpu, sel, out, lse = P.run_phases(d, 0)
+    s_ref = oracle.score(w.q_idx, w.emb, w.chunk_off)
+    P.check_scores(w, s_gpu, s_ref)
+    P.check_selection(w, s_gpu, sel, s_ref)
+    o_ref, l_ref = P.oracle_attention_on(w, 0, sel)
+    P.check_attention("bf16", out, lse, o_ref, l_ref)
