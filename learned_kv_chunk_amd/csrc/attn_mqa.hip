@@ -17,13 +17,17 @@
 // per-wave LDS buffer because the second product contracts over tokens,
 // which are strided in memory.  Each wave software-pipelines its tiles: the
 // next tile's loads are in flight while the current one is computed.
-// For up to 16 heads a workgroup has eight waves (two per SIMD, so one wave's
-// loads are in flight while the other computes); a wave serving two head
-// groups needs the registers of a whole SIMD, so up to 32 heads use four
-// waves, and up to 64 heads two teams of two such waves.  The waves of a team
-// take interleaved tiles of the workgroup's run, then merge their (max, sum,
-// output) states through LDS into one partial result, which the merge kernel
-// (attn_common.hip) combines with the stream's other partials.
+// A workgroup has four waves, one per SIMD: for up to 32 heads each wave
+// serves every head group, and up to 64 heads two teams of two waves each
+// serve half of them.  Measured on cold K/V, four waves stream faster than
+// eight (two per SIMD) even for one head group, where eight would fit: at
+// 16 x 128K, 30.2 us per launch against 31.6 for eight waves, each with the
+// load hints that suit it best; more loads in flight per CU only lengthen
+// the memory queues (a third register set per wave: 32.4 us).  The
+// waves of a team take interleaved tiles of the workgroup's run, then merge
+// their (max, sum, output) states through LDS into one partial result, which
+// the merge kernel (attn_common.hip) combines with the stream's other
+// partials.
 #include <math.h>
 
 #include "lsa_internal.hpp"
@@ -61,10 +65,13 @@ struct TileInfo {
 // Loads are unconditional so that the compiler can count them and keep the
 // next tile in flight: rows past the tile's valid tokens re-read its last
 // valid row (their logits are masked and their weights are zero).  V is read
-// with the non-temporal hint and K without it: measured on cold K/V at
-// 16 x 128K, that pair streams fastest (30.1 us per launch against 31.8 with
-// no hint on either and 32.4 with the hint on both).
-template <int D>
+// with the non-temporal hint.  K carries it too when a wave serves one head
+// group (KNT): each K load instruction covers half of every 128-byte line it
+// touches and the next one the other half, and measured on cold K/V the hint
+// pays only there (16 x 128K: 30.2 us against 31.4 without it; 32 ragged
+// streams: 65.5 against 64.7, a 1 % loss; eight waves per workgroup: 32.7
+// against 31.6; a wave serving two groups, 4 x 512K pool: 28.3 against 27.5).
+template <int D, bool KNT>
 __device__ __forceinline__ void issue_tile(const uint16_t* __restrict__ kb,
                                            const uint16_t* __restrict__ vb, int32_t k_row,
                                            int32_t v_row, const TileInfo& ti, TileRegs<D>& r,
@@ -77,7 +84,8 @@ __device__ __forceinline__ void issue_tile(const uint16_t* __restrict__ kb,
     const int row = min(blk * 16 + r16, last);
     const u32x4* src = reinterpret_cast<const u32x4*>(kb + (ti.row0 + row) * k_row) + g;
 #pragma unroll
-    for (int s = 0; s < D / 32; ++s) r.k[blk][s] = src[s * 4];
+    for (int s = 0; s < D / 32; ++s)
+      r.k[blk][s] = KNT ? __builtin_nontemporal_load(src + s * 4) : src[s * 4];
   }
 #pragma unroll
   for (int i = 0; i < D / 16; ++i) {
@@ -178,10 +186,9 @@ __device__ __forceinline__ void compute_tile(const TileRegs<D>& r, int32_t nvali
 
 constexpr int cmax(int a, int b) { return a > b ? a : b; }
 
-// Waves per workgroup: eight (two per SIMD) when a wave serves one head group,
-// four when it serves two (their registers allow one wave per SIMD).
+// Waves per workgroup: one per SIMD.
 template <int NHG>
-constexpr int mqa_waves() { return NHG == 1 ? 8 : 4; }
+constexpr int mqa_waves() { return 4; }
 
 template <int D, int NHG>
 struct MqaLds {
@@ -234,7 +241,7 @@ __device__ __forceinline__ void merge_state(const unsigned char* base, float (&m
 // interleave the run's tiles among themselves, so a tile is read once per team
 // (HS = 1 except for more than 32 heads).
 template <int D, int NHG, int HS>
-__global__ __launch_bounds__(mqa_waves<NHG>() * kWave, NHG == 1 ? 2 : 1) void attn_mqa_kernel(
+__global__ __launch_bounds__(mqa_waves<NHG>() * kWave, 1) void attn_mqa_kernel(
     AttnArgs a) {
   using L = MqaLds<D, NHG>;
   constexpr int NW = L::kWaves;
@@ -325,13 +332,13 @@ __global__ __launch_bounds__(mqa_waves<NHG>() * kWave, NHG == 1 ? 2 : 1) void at
     auto step = [&](TileRegs<D>& rc, const TileInfo& ic, TileRegs<D>& rn, TileInfo& in,
                     int32_t next) {
       in = tile_info(min(next, n_mine - 1));
-      issue_tile<D>(kb, vb, a.k_row, a.v_row, in, rn, lane);
+      issue_tile<D, NHG == 1>(kb, vb, a.k_row, a.v_row, in, rn, lane);
       __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the compute
       compute_tile<D, NHG>(rc, ic.nvalid, qf, m, l, o, sv, a.scale_log2, lane);
     };
     TileRegs<D> ra, rb;
     TileInfo ia = tile_info(0), ib;
-    issue_tile<D>(kb, vb, a.k_row, a.v_row, ia, ra, lane);
+    issue_tile<D, NHG == 1>(kb, vb, a.k_row, a.v_row, ia, ra, lane);
     for (int32_t i = 0;; i += 2) {
       step(ra, ia, rb, ib, i + 1);
       if (i + 1 >= n_mine) break;
