@@ -7,8 +7,9 @@
 //
 // THREADS threads (64: a single wave, no barriers) hold KPT consecutive
 // scores each ([t*KPT, t*KPT+KPT)) as order-preserving 32-bit keys.  An
-// MSB-first radix select runs four 8-bit digit passes, each into its own LDS
-// histogram.  In the first pass (sign and top exponent bits: few distinct
+// MSB-first radix select runs up to four 8-bit digit passes, each into its
+// own LDS histogram, and stops early once every key of the chosen digit is
+// kept (with continuous scores, usually after three).  In the first pass (sign and top exponent bits: few distinct
 // digits) the lanes holding the first participating lane's digit (usually the
 // wave's most common one) add their count once, so few lanes of a wave hit the
 // same LDS word; later passes only see keys that share the digits chosen so
@@ -136,11 +137,14 @@ __device__ __forceinline__ void select_load_keys(const float* __restrict__ score
 }
 
 // Radix passes: the key T of the k-th largest key (`prefix`) and how many
-// keys equal to T are kept (`remaining`).
+// keys equal to T are kept (`remaining`), T compared on the bits of `mask`.
+// The passes stop as soon as every key of the chosen digit is kept: then the
+// digits resolved so far already separate the kept keys (T is a prefix, and
+// all keys sharing it are kept).
 template <int THREADS, int KPT>
 __device__ __forceinline__ void select_radix(const uint32_t (&key)[KPT], int32_t n, int32_t k,
                                              SelectLds<THREADS>& lds, uint32_t* prefix_out,
-                                             uint32_t* remaining_out) {
+                                             uint32_t* remaining_out, uint32_t* mask_out) {
   const int tid = threadIdx.x;
   for (int i = tid; i < 4 * 256; i += THREADS) (&lds.hist[0][0])[i] = 0u;
   select_sync<THREADS>();
@@ -181,7 +185,7 @@ __device__ __forceinline__ void select_radix(const uint32_t (&key)[KPT], int32_t
     const uint32_t total = __builtin_amdgcn_readlane(incl, 63);
     uint32_t ge = total - incl;  // keys whose digit is above this lane's four
     const uint32_t cnt[4] = {c.x, c.y, c.z, c.w};
-    uint32_t pick = 0, gt_pick = 0;
+    uint32_t pick = 0, gt_pick = 0, n_pick = 0;
     bool found = false;
 #pragma unroll
     for (int j = 3; j >= 0; --j) {
@@ -191,19 +195,23 @@ __device__ __forceinline__ void select_radix(const uint32_t (&key)[KPT], int32_t
         found = true;
         pick = 4u * lane + j;
         gt_pick = gt;
+        n_pick = cnt[j];
       }
     }
     const uint64_t hit = __ballot(found);
     const int src = __ffsll(static_cast<long long>(hit)) - 1;
     pick = __builtin_amdgcn_readlane(pick, src);
     gt_pick = __builtin_amdgcn_readlane(gt_pick, src);
+    n_pick = __builtin_amdgcn_readlane(n_pick, src);
     prefix |= pick << shift;
     mask |= 0xffu << shift;
     remaining -= gt_pick;
+    if (n_pick == remaining) break;  // workgroup-uniform: every wave scanned the same counts
   }
 
   *prefix_out = prefix;
   *remaining_out = remaining;
+  *mask_out = mask;
 }
 
 // Bucket pass (see the file comment): returns false, with the workgroup in
@@ -339,18 +347,20 @@ __device__ __forceinline__ void select_topk_keys(const uint32_t (&key)[KPT], int
                                                  int32_t k, int32_t* __restrict__ out,
                                                  SelectLds<THREADS>& lds) {
   const int tid = threadIdx.x;
-  uint32_t prefix, remaining;
+  uint32_t prefix, remaining, mask = 0xffffffffu;
   // the bucket pass pays off from eight keys per thread (streams of several
   // thousand chunks); below that the radix passes are as fast
   if (KPT < 8 || !select_buckets<THREADS, KPT>(key, n, k, lds, &prefix, &remaining))
-    select_radix<THREADS, KPT>(key, n, k, lds, &prefix, &remaining);
+    select_radix<THREADS, KPT>(key, n, k, lds, &prefix, &remaining, &mask);
 
+  // keys above T (on the bits of mask) are kept, and the first `remaining`
+  // keys equal to T in index order
   uint32_t n_gt = 0, n_eq = 0;
 #pragma unroll
   for (int i = 0; i < KPT; ++i) {
     const bool v = tid * KPT + i < n;
-    n_gt += (v && key[i] > prefix) ? 1u : 0u;
-    n_eq += (v && key[i] == prefix) ? 1u : 0u;
+    n_gt += (v && (key[i] & mask) > prefix) ? 1u : 0u;
+    n_eq += (v && (key[i] & mask) == prefix) ? 1u : 0u;
   }
   uint32_t gt_before, eq_before;
   select_exclusive_scan2<THREADS>(n_gt, n_eq, &gt_before, &eq_before, lds.tot);
@@ -358,10 +368,10 @@ __device__ __forceinline__ void select_topk_keys(const uint32_t (&key)[KPT], int
   for (int i = 0; i < KPT; ++i) {
     const int32_t idx = tid * KPT + i;
     if (idx >= n) continue;
-    if (key[i] > prefix) {
+    if ((key[i] & mask) > prefix) {
       out[gt_before + min(eq_before, remaining)] = idx;
       ++gt_before;
-    } else if (key[i] == prefix) {
+    } else if ((key[i] & mask) == prefix) {
       if (eq_before < remaining) out[gt_before + eq_before] = idx;
       ++eq_before;
     }

@@ -217,6 +217,37 @@ def test_select_ties_nan_signed_zero_and_extremes():
         _select_case([rng.standard_normal(4096)], [k])
 
 
+def test_select_radix_passes_that_stop_early():
+    # the radix passes stop once every key of the chosen digit is kept; these
+    # streams resolve after the first digit (4.0 against 0.25), after the
+    # second (1.5 against 1.0: same leading byte), with a boundary digit that
+    # is kept whole (two of 1.5 under 1.75) or must be split by index (five
+    # of 1.5, two kept), with negative scores, and in a single-wave stream
+    rng = np.random.default_rng(7)
+
+    def mix(n, values, counts, rest):
+        v = np.full(n, rest)
+        idx = rng.permutation(n)
+        at = 0
+        for val, c in zip(values, counts):
+            v[idx[at:at + c]] = val
+            at += c
+        return v
+
+    cases = [(mix(2048, [4.0], [276], 0.25), 276),
+             (mix(2048, [1.5], [276], 1.0), 276),
+             (mix(2048, [1.75, 1.5], [274, 2], 1.0), 276),
+             (mix(2048, [1.75, 1.5], [274, 5], 1.0), 276),
+             (mix(3000, [-1.0, -1.5], [10, 90], -3.0), 100),
+             (mix(3000, [-1.0, -1.5], [10, 90], -3.0), 50),
+             (mix(40, [2.0, 1.5], [3, 4], 1.0), 7),
+             (mix(40, [2.0, 1.5], [3, 4], 1.0), 5),
+             (1.0 + rng.random(2048) * 2.0 ** -20, 276)]
+    for v, k in cases:
+        _select_case([v], [k])
+    _select_case([v for v, _ in cases], [k for _, k in cases])
+
+
 def test_select_large_streams():
     rng = np.random.default_rng(1)
     s = [rng.standard_normal(65536).astype(np.float32) * 1e-3,
