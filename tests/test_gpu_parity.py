@@ -260,6 +260,9 @@ def test_select_large_streams():
     dict(num_q_heads=8),                                   # padded head group
     dict(num_q_heads=24),                                  # two head groups, partially padded
     dict(num_q_heads=32, head_dim_qk=64, head_dim_v=64),   # d = 64
+    dict(num_q_heads=40),                                  # two teams, the second partly padded
+    dict(num_q_heads=64),                                  # two teams of two head groups
+    dict(num_q_heads=48, head_dim_qk=64, head_dim_v=64),   # two teams, d = 64
     dict(num_q_heads=12, head_dim_qk=96, head_dim_v=80),   # portable kernel, bf16
     dict(chunk_size=48),                                   # chunk not a multiple of the tile
     dict(chunk_size=128, index_dim=256),
