@@ -18,7 +18,11 @@ namespace lsa {
 namespace {
 
 constexpr int kScoreThreads = 256;
-constexpr int kScorePasses = 4;  // rows per group per workgroup (loads in flight)
+// Rows per group per workgroup.  One: more, smaller workgroups spread the
+// short cold read over every CU sooner (measured decode steps/s, interleaved
+// A/B: from 4 rows to 2 +0.4 % at 16 x 128K and +0.6 % at 1 x 1M, from 2 to
+// 1 another +0.5 % and +0.3 %; 8 rows 1 % slower than 4).
+constexpr int kScorePasses = 1;
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
