@@ -46,26 +46,27 @@ __global__ __launch_bounds__(kAppendThreads) void append_kv_kernel(
 
 // Chunks stream j attends to beyond its kept ones: the last scored chunk
 // M-1 unless kept (kept chunks ascend and lie below M, so only the last can
-// be M-1), then M .. ceil(L/C)-1; at most max_recent.
+// be M-1), then M .. ceil(L/C)-1; when more than max_recent qualify, the
+// newest max_recent (the chunk of the token being decoded is always one).
+// They are the consecutive chunks first .. first + count - 1.
 struct Recent {
-  int32_t m;         // scored chunks
-  int32_t with_last; // 1: chunk m-1 comes first
+  int32_t first;
   int32_t count;
 };
 
 __device__ __forceinline__ Recent recent_of(const int64_t* seq_len, const int32_t* chunk_off,
                                             const int32_t* sel_idx, const int32_t* sel_off,
                                             int32_t C, int32_t max_recent, int32_t j) {
-  Recent r;
-  r.m = chunk_off[j + 1] - chunk_off[j];
+  const int32_t m = chunk_off[j + 1] - chunk_off[j];
   const int32_t k = sel_off[j + 1] - sel_off[j];
   const int64_t len = seq_len[j] < 0 ? 0 : seq_len[j];
   const int64_t total = (len + C - 1) / C;
-  const bool last_kept = k > 0 && sel_idx[sel_off[j + 1] - 1] == r.m - 1;
-  r.with_last = (r.m > 0 && !last_kept) ? 1 : 0;
-  const int64_t later = total > r.m ? total - r.m : 0;
-  const int64_t c = r.with_last + later;
-  r.count = static_cast<int32_t>(c < max_recent ? c : max_recent);
+  const bool last_kept = k > 0 && sel_idx[sel_off[j + 1] - 1] == m - 1;
+  int64_t first = (m > 0 && !last_kept) ? m - 1 : m;
+  if (total - first > max_recent) first = total - max_recent;
+  Recent r;
+  r.first = static_cast<int32_t>(first);
+  r.count = static_cast<int32_t>(total > first ? total - first : 0);
   return r;
 }
 
@@ -97,7 +98,7 @@ __global__ __launch_bounds__(kRecentThreads) void keep_recent_kernel(
   }
   for (int32_t i = tid; i < k; i += kRecentThreads) out_idx[off + i] = sel_idx[s0 + i];
   for (int32_t i = tid; i < r.count; i += kRecentThreads)
-    out_idx[off + k + i] = r.with_last ? r.m - 1 + i : r.m + i;
+    out_idx[off + k + i] = r.first + i;
 }
 
 }  // namespace

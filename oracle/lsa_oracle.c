@@ -28,7 +28,8 @@
  *                     the swap between GPU and host memory).
  *   oracle_keep_recent  the attention keep set of a context that grew since
  *                     the last re-index: kept chunks, the last scored chunk
- *                     and the chunks not yet scored.
+ *                     and the chunks not yet scored (the newest max_recent
+ *                     of those two kinds when the bound binds).
  */
 #include "lsa_oracle.h"
 
@@ -347,15 +348,13 @@ void oracle_keep_recent(int32_t B, int32_t C, const int64_t* seq_len, const int3
       out[n++] = sel_idx[sel_off[b] + i];
       if (sel_idx[sel_off[b] + i] == m - 1) last_kept = 1;
     }
-    int32_t extra = 0;
-    if (m > 0 && !last_kept && extra < max_recent) {
-      out[n++] = m - 1;
-      ++extra;
-    }
-    for (int32_t c = m; c < total && extra < max_recent; ++c) {
-      out[n++] = c;
-      ++extra;
-    }
+    /* the chunks beyond the kept ones, oldest first: the last scored chunk
+     * (unless kept), then every unscored chunk; when there are more than
+     * max_recent of them the newest max_recent are the ones attended, since
+     * they hold the tokens written most recently, the current one included */
+    int32_t first = (m > 0 && !last_kept) ? m - 1 : m;
+    if (total - first > max_recent) first = total - max_recent;
+    for (int32_t c = first; c < total; ++c) out[n++] = c;
     out_off[b + 1] = out_off[b] + n;
   }
 }

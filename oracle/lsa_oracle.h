@@ -153,9 +153,10 @@ void oracle_pool_delta(int32_t B, const int32_t* chunk_off, const int32_t* sel_i
  * chunks the indexer has scored), plus the last scored chunk M_b-1 when it
  * was not kept (it was the partial tail when scored and may have grown
  * since), plus every chunk from M_b to ceil(seq_len[b]/C)-1 (not yet
- * scored): at most max_recent chunks beyond the kept ones per stream, in
- * that order.  Writes the ascending union to out_idx[out_off[b] ..] with
- * out_off[B+1] its running totals. */
+ * scored).  At most max_recent chunks beyond the kept ones per stream: when
+ * there are more, the newest max_recent of them (the highest indices, which
+ * hold the most recent tokens).  Writes the ascending union to
+ * out_idx[out_off[b] ..] with out_off[B+1] its running totals. */
 void oracle_keep_recent(int32_t B, int32_t C, const int64_t* seq_len, const int32_t* chunk_off,
                         const int32_t* sel_idx, const int32_t* sel_off, int32_t max_recent,
                         int32_t* out_idx, int32_t* out_off);

@@ -27,13 +27,15 @@ def _t(a):
     return torch.from_numpy(a).cuda()
 
 
-@pytest.mark.parametrize("name", ["cfg2", "cfg5", "cfg4", "cfg1"])
-def test_append_decode_loop(name):
+@pytest.mark.parametrize("name,max_recent", [("cfg2", 4), ("cfg5", 4), ("cfg4", 4), ("cfg1", 4),
+                                             ("cfg2", 2)])
+def test_append_decode_loop(name, max_recent):
+    # max_recent = 2 binds once a stream has three candidate chunks: the
+    # newest two must be attended
     w = wl.make_workload(wl.small_variant(name))
     c = w.cfg
     C = c.chunk_size
     steps = 2 * C + 9
-    max_recent = 4
     L0 = w.lengths.astype(np.int64)
     cap = L0 + steps + 3
     base = np.concatenate([[0], np.cumsum(cap)]).astype(np.int64)
@@ -85,6 +87,8 @@ def test_append_decode_loop(name):
         r_off, r_idx = oracle.keep_recent(C, seq_h, w.chunk_off, sel_h, w.sel_off, max_recent)
         np.testing.assert_array_equal(off_h, r_off)
         np.testing.assert_array_equal(idx_h, r_idx)
+        for b in range(w.B):  # the chunk of the token just written is attended
+            assert (seq_h[b] - 1) // C in idx_h[off_h[b]:off_h[b + 1]], (t, b)
         if t % 5 == 0 or t == steps - 1:
             # the grown context packed back to back for the oracle
             tok = np.concatenate([[0], np.cumsum(seq_h)]).astype(np.int64)
