@@ -854,7 +854,7 @@ def main():
             t = t_begin + i
             r = replicas[t % reps]
             eb, ee = (evs[i] if evs is not None else (None, None))
-            r.step(t, reindex=(t % R_idx == 0), materialize_pool=cfg.materialize_pool,
+            r.step(t, reindex_every=R_idx, materialize_pool=cfg.materialize_pool,
                    ev_begin=eb, ev_end=ee, q=qs[t % nq])
 
     # pass 3 (roofline.avg_launch_us): the attention partial kernel alone, the
@@ -955,7 +955,7 @@ def main():
     ww0.record()
     for i in range(warm_n):
         t = t_first + i
-        replicas[0].step(t, reindex=(t % R_idx == 0), materialize_pool=cfg.materialize_pool,
+        replicas[0].step(t, reindex_every=R_idx, materialize_pool=cfg.materialize_pool,
                          q=qs[t % nq])
     ww1.record()
     torch.cuda.synchronize()
@@ -973,7 +973,7 @@ def main():
     for i in range(spread_n):
         t = t_first + i
         sev[i][0].record()
-        replicas[t % reps].step(t, reindex=(t % R_idx == 0),
+        replicas[t % reps].step(t, reindex_every=R_idx,
                                 materialize_pool=cfg.materialize_pool, q=qs[t % nq])
         sev[i][1].record()
     torch.cuda.synchronize()

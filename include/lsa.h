@@ -31,7 +31,8 @@
  *   stated totals, 1 <= k_b <= N_b, kept indices in [0, N_b)) cannot be checked
  *   without reading device memory; kernels clamp so that a violation never
  *   writes outside the documented output ranges, but results are then
- *   unspecified.
+ *   unspecified.  lsa_check_tables checks them on the device (a debug aid,
+ *   not called by any other entry point).
  * Layout: all tensors are dense row-major.  Ragged per-stream data is packed
  *   back to back and described by CSR offset arrays of B+1 entries whose first
  *   entry is 0:
@@ -271,7 +272,9 @@ lsa_status lsa_gather_chunks(const lsa_shape* shape, const void* k_store_dev,
  *   chunk_off[b+1]-chunk_off[b], the chunks the indexer scored), then the
  *   last scored chunk M_b-1 unless kept (it was the partial tail when scored
  *   and may have grown since), then every chunk from M_b to
- *   ceil(seq_len[b]/C)-1; at most max_recent chunks beyond the kept ones.
+ *   ceil(seq_len[b]/C)-1; at most max_recent chunks beyond the kept ones,
+ *   the newest max_recent when more qualify (so the chunk holding the
+ *   latest token is always attended when max_recent >= 1).
  *   Writes the ascending union to out_sel_idx_dev (room for total_k +
  *   B*max_recent) and its CSR offsets to out_sel_off_dev [B+1], computed on
  *   the device.  Attention over it takes a shape whose total_k / max_k are
@@ -367,13 +370,20 @@ lsa_status lsa_sparse_decode_attn(const lsa_shape* shape, int32_t kv_mode, const
                                   void* hip_stream);
 
 /* ---------------------------------------------------------------------------
- * One decode step of the whole path in one call: when `reindex` is non-zero,
- * score -> select (-> gather into the pool when materialize_pool); then sparse
+ * One decode step of the whole path in one call: on a re-index step, score ->
+ * select (-> gather into the pool when materialize_pool); then sparse
  * attention (from the pool when materialize_pool, else in place from the
- * store).  With reindex == 0 the previous sel_idx (and pool) are reused, which
- * is the lookahead schedule of the review (section 3-1 table and section 4-3:
- * re-score about every 64 decode steps).  Every phase is one grid over all
- * streams; nothing returns to the host between phases.
+ * store).  On other steps the previous sel_idx (and pool) are reused.  This is
+ * the lookahead schedule of the review (section 3-2-3 steps 4-7; section 3-1
+ * table and section 4-3: re-score about every 64 decode steps): with
+ * reindex_every = R > 0 the call re-indexes exactly when step % R == 0
+ * (lsa_reindex_due) and `reindex` is ignored; with reindex_every = 0 the
+ * caller decides through `reindex` (non-zero: re-index).  A re-index step
+ * scores q_idx_dev as it is at that step, so a caller whose indexer query
+ * changes every step passes the current one.  Every phase is one grid over
+ * all streams; nothing returns to the host between phases.
+ * reindex_every < 0, or step < 0 with reindex_every > 0, is
+ * LSA_ERR_INVALID_ARGUMENT.
  * ev_attn_begin / ev_attn_end: optional hipEvent_t recorded on hip_stream
  * right before and right after the split-KV attention kernel (the merge pass
  * runs after ev_attn_end; NULL to skip), so a caller can time that kernel
@@ -399,10 +409,54 @@ typedef struct lsa_step_args {
   int32_t materialize_pool;     /* non-zero: gather kept chunks into the pool */
   void* ev_attn_begin;          /* hipEvent_t or NULL */
   void* ev_attn_end;            /* hipEvent_t or NULL */
+  int32_t reindex_every;        /* R > 0: re-index iff step % R == 0; 0: use `reindex` */
+  int32_t reserved;             /* 0 */
+  int64_t step;                 /* decode step number, counted from 0 */
 } lsa_step_args;
+
+/* 1 when decode step `step` re-scores and re-selects under re-index interval
+ * reindex_every (step % reindex_every == 0), else 0; -1 for reindex_every < 1
+ * or step < 0.  The schedule lsa_decode_step applies when its args carry
+ * reindex_every > 0. */
+int32_t lsa_reindex_due(int64_t step, int32_t reindex_every);
 
 lsa_status lsa_decode_step(const lsa_shape* shape, const lsa_step_args* args,
                            void* workspace_dev, size_t workspace_bytes, void* hip_stream);
+
+/* ---------------------------------------------------------------------------
+ * Debug check of the device-side preconditions (off the hot path; nothing
+ * else calls it).  The kernels read the offset tables and kept indices
+ * without checking them; a caller that wants a bad table reported instead of
+ * silently wrong results runs this first.  For every stream b it checks:
+ *   LSA_TABLE_ERR_CHUNK_OFF  chunk_off[0] == 0, chunk_off[B] == total_chunks,
+ *                            0 <= chunk_off[b] <= chunk_off[b+1] <= total_chunks,
+ *                            N_b <= max_chunks (and chunk_off[b] = b * max_chunks
+ *                            for a LSA_SHAPE_UNIFORM shape);
+ *   LSA_TABLE_ERR_SEL_OFF    the same of sel_off against total_k and max_k;
+ *   LSA_TABLE_ERR_KEEP       1 <= k_b <= N_b;
+ *   LSA_TABLE_ERR_TOK_OFF    tok_off[0] == 0, tok_off non-decreasing and
+ *                            N_b == ceil(L_b / C) (skipped when tok_off_dev is
+ *                            NULL);
+ *   LSA_TABLE_ERR_SEL_IDX    every kept index in [0, N_b), and strictly
+ *                            ascending within a stream when kept_ascending is
+ *                            non-zero (lsa_select_topk's output; a pool table
+ *                            of lsa_pool_delta_update is not ascending)
+ *                            (skipped when sel_idx_dev is NULL).
+ * *error_flags_dev (one int32 in device memory) receives the OR of the bits
+ * of every stream: 0 when every precondition holds.  Only entries inside the
+ * documented array sizes are read (sel_idx only where sel_off's range lies
+ * in [0, total_k]).  Two kernels: one clears the flag, one checks.
+ * ------------------------------------------------------------------------- */
+#define LSA_TABLE_ERR_CHUNK_OFF 1
+#define LSA_TABLE_ERR_SEL_OFF 2
+#define LSA_TABLE_ERR_KEEP 4
+#define LSA_TABLE_ERR_TOK_OFF 8
+#define LSA_TABLE_ERR_SEL_IDX 16
+
+lsa_status lsa_check_tables(const lsa_shape* shape, const int64_t* tok_off_dev,
+                            const int32_t* chunk_off_dev, const int32_t* sel_off_dev,
+                            const int32_t* sel_idx_dev, int32_t kept_ascending,
+                            int32_t* error_flags_dev, void* hip_stream);
 
 /* ---------------------------------------------------------------------------
  * Measurement helpers (not part of the method).

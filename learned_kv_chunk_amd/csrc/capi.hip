@@ -137,7 +137,12 @@ const char* lsa_status_string(lsa_status status) {
   }
 }
 
-int32_t lsa_abi_version(void) { return 2; }
+int32_t lsa_abi_version(void) { return 3; }
+
+int32_t lsa_reindex_due(int64_t step, int32_t reindex_every) {
+  if (reindex_every < 1 || step < 0) return -1;
+  return step % reindex_every == 0 ? 1 : 0;
+}
 
 int32_t lsa_keep_count(int32_t n_chunks, int32_t ratio_num, int32_t ratio_den, int32_t round_up) {
   if (n_chunks <= 0 || ratio_num <= 0 || ratio_den <= 0) return 0;
@@ -408,7 +413,13 @@ lsa_status lsa_keep_recent(const lsa_shape* shape, const int64_t* seq_len_dev,
 lsa_status lsa_decode_step(const lsa_shape* shape, const lsa_step_args* args, void* workspace_dev,
                            size_t workspace_bytes, void* hip_stream) {
   if (shape == nullptr || args == nullptr) return LSA_ERR_INVALID_ARGUMENT;
-  const lsa_step_args& x = *args;
+  lsa_step_args x = *args;
+  if (x.reindex_every < 0 || x.reserved != 0) return LSA_ERR_INVALID_ARGUMENT;
+  if (x.reindex_every > 0) {
+    const int32_t due = lsa_reindex_due(x.step, x.reindex_every);
+    if (due < 0) return LSA_ERR_INVALID_ARGUMENT;
+    x.reindex = due;
+  }
   const bool pool = x.materialize_pool != 0;
   const void* kbase = pool ? x.k_pool_dev : x.k_store_dev;
   const void* vbase = pool ? x.v_pool_dev : x.v_store_dev;
@@ -451,6 +462,23 @@ lsa_status lsa_decode_step(const lsa_shape* shape, const lsa_step_args* args, vo
   return enqueue_attention(*shape, pool ? LSA_KV_POOL : LSA_KV_STORE, x.q_dev, kbase, vbase,
                            x.tok_off_dev, x.sel_idx_dev, x.sel_off_dev, x.out_dev, x.lse_dev,
                            workspace_dev, hs, x.ev_attn_begin, x.ev_attn_end);
+}
+
+lsa_status lsa_check_tables(const lsa_shape* shape, const int64_t* tok_off_dev,
+                            const int32_t* chunk_off_dev, const int32_t* sel_off_dev,
+                            const int32_t* sel_idx_dev, int32_t kept_ascending,
+                            int32_t* error_flags_dev, void* hip_stream) {
+  lsa_status st = check_common(shape);
+  if (st != LSA_OK) return st;
+  if (!chunk_off_dev || !sel_off_dev || !error_flags_dev) return LSA_ERR_INVALID_ARGUMENT;
+  if ((tok_off_dev && !aligned(tok_off_dev, 8)) || !aligned(chunk_off_dev, 4) ||
+      !aligned(sel_off_dev, 4) || (sel_idx_dev && !aligned(sel_idx_dev, 4)) ||
+      !aligned(error_flags_dev, 4))
+    return LSA_ERR_INVALID_ARGUMENT;
+  (void)hipGetLastError();
+  return hip_status(launch_check_tables(*shape, tok_off_dev, chunk_off_dev, sel_off_dev,
+                                        sel_idx_dev, kept_ascending, error_flags_dev,
+                                        static_cast<hipStream_t>(hip_stream)));
 }
 
 lsa_status lsa_bench_attention_partial(const lsa_shape* shape, int32_t kv_mode, const void* q_dev,

@@ -121,6 +121,10 @@ bool portable_attn_supported(const lsa_shape& s);
 hipError_t launch_attn_portable(const lsa_shape& s, const AttnArgs& a, int64_t grid,
                                 hipStream_t st);
 hipError_t launch_attn_merge(const lsa_shape& s, const AttnArgs& a, hipStream_t st);
+hipError_t launch_check_tables(const lsa_shape& s, const int64_t* tok_off,
+                               const int32_t* chunk_off, const int32_t* sel_off,
+                               const int32_t* sel_idx, int32_t ascending, int32_t* flag,
+                               hipStream_t st);
 hipError_t launch_bench_copy(void* dst, const void* src, size_t bytes, hipStream_t st);
 hipError_t launch_bench_flush(void* buf, size_t bytes, hipStream_t st);
 

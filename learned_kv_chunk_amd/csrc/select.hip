@@ -13,6 +13,7 @@
 // order (one block-wide scan), or, when the cap binds, the radix top-k.
 #include "lsa_internal.hpp"
 #include "select_core.hpp"
+#include "table_check.hpp"
 
 namespace lsa {
 namespace {
@@ -28,11 +29,15 @@ __global__ __launch_bounds__(THREADS) void select_kernel(const float* __restrict
   __shared__ SelectLds<THREADS> lds;
   const int b = blockIdx.x;
   const int32_t base = uni_n > 0 ? b * uni_n : chunk_off[b];
-  const int32_t n = uni_n > 0 ? uni_n : chunk_off[b + 1] - base;
+  int32_t n = uni_n > 0 ? uni_n : chunk_off[b + 1] - base;
   const int32_t s0 = uni_k > 0 ? b * uni_k : sel_off[b];
   int32_t k = uni_k > 0 ? uni_k : sel_off[b + 1] - s0;
   if (n <= 0 || k <= 0) return;
-  if (k > n) k = n;  // violated precondition: never write past the stream's range
+  // violated preconditions (a stream longer than max_chunks, or k_b > N_b):
+  // rank only the keys a block holds and never write past them, so the
+  // result is still a deterministic function of the scores
+  n = select_clamp_keys(n, THREADS * KPT);
+  k = select_clamp_keys(k, n);
   int32_t* out = sel_idx + s0;
   if (k == n) {
     for (int32_t i = threadIdx.x; i < n; i += THREADS) out[i] = i;

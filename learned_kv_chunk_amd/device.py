@@ -68,15 +68,19 @@ class DeviceWorkload:
             self._q[step] = _to_device(self.w.queries(step), self.K.device)
         return self._q[step]
 
-    def step(self, t: int, reindex: bool, materialize_pool: bool = False, ev_begin=None,
-             ev_end=None, q: Optional[torch.Tensor] = None) -> None:
+    def step(self, t: int, reindex: bool = False, materialize_pool: bool = False,
+             ev_begin=None, ev_end=None, q: Optional[torch.Tensor] = None,
+             reindex_every: int = 0) -> None:
+        """Decode step t.  reindex_every > 0: the library's schedule decides
+        whether step t re-indexes (``reindex`` is ignored)."""
         lsa.decode_step(self.shape, q_idx=self.q_idx, emb=self.emb, chunk_off=self.chunk_off,
                         scores=self.scores, sel_off=self.sel_off, sel_idx=self.sel_idx,
                         q=self.queries(t) if q is None else q, k_store=self.K, v_store=self.V,
                         tok_off=self.tok_off, out=self.out, lse=self.lse,
                         workspace=self.workspace, reindex=reindex,
                         materialize_pool=materialize_pool, k_pool=self.k_pool,
-                        v_pool=self.v_pool, ev_attn_begin=ev_begin, ev_attn_end=ev_end)
+                        v_pool=self.v_pool, ev_attn_begin=ev_begin, ev_attn_end=ev_end,
+                        step=t, reindex_every=reindex_every)
 
 
 def upload(w: Workload, device="cuda", attn_tiles_per_block: int = 0,

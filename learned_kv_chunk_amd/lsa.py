@@ -80,6 +80,9 @@ class StepArgs(ctypes.Structure):
         ("materialize_pool", ctypes.c_int32),
         ("ev_attn_begin", ctypes.c_void_p),
         ("ev_attn_end", ctypes.c_void_p),
+        ("reindex_every", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+        ("step", ctypes.c_int64),
     ]
 
 
@@ -89,6 +92,8 @@ _I32 = ctypes.c_int32
 _SIGNATURES = {
     "lsa_status_string": ([_I32], ctypes.c_char_p),
     "lsa_abi_version": ([], _I32),
+    "lsa_check_tables": ([ctypes.POINTER(Shape), _P, _P, _P, _P, _I32, _P, _P], _I32),
+    "lsa_reindex_due": ([ctypes.c_int64, _I32], _I32),
     "lsa_keep_count": ([_I32, _I32, _I32, _I32], _I32),
     "lsa_workspace_bytes": ([ctypes.POINTER(Shape)], ctypes.c_size_t),
     "lsa_score": ([ctypes.POINTER(Shape), _P, _P, _P, _P, _P], _I32),
@@ -516,6 +521,46 @@ def sparse_decode_attn(shape: ProblemShape, q, k_base, v_base, tok_off, sel_idx,
     return out, lse
 
 
+TABLE_ERR_CHUNK_OFF = 1
+TABLE_ERR_SEL_OFF = 2
+TABLE_ERR_KEEP = 4
+TABLE_ERR_TOK_OFF = 8
+TABLE_ERR_SEL_IDX = 16
+
+# LSA_DEBUG_CHECKS=1: attention and decode-step calls first check their tables
+# on the device and raise on a violation (synchronises; debugging only)
+_DEBUG_CHECKS = os.environ.get("LSA_DEBUG_CHECKS", "0") == "1"
+
+
+def check_tables(shape: ProblemShape, chunk_off, sel_off, tok_off=None, sel_idx=None,
+                 kept_ascending: bool = True, flags=None, stream=None) -> int:
+    """lsa_check_tables: OR of the TABLE_ERR_* bits of every stream (0: the
+    device-side preconditions hold).  Synchronises the stream to read the
+    flag back; a debugging aid, not for the hot path."""
+    _dev(chunk_off, "chunk_off", torch.int32, 1)
+    _dev(sel_off, "sel_off", torch.int32, 1)
+    if tok_off is not None:
+        _dev(tok_off, "tok_off", torch.int64, 1)
+    if sel_idx is not None:
+        _dev(sel_idx, "sel_idx", torch.int32, 1)
+    if flags is None:
+        flags = torch.empty(1, dtype=torch.int32, device=chunk_off.device)
+    _dev(flags, "flags", torch.int32)
+    _check(library().lsa_check_tables(ctypes.byref(shape.c()), _ptr(tok_off), _ptr(chunk_off),
+                                      _ptr(sel_off), _ptr(sel_idx), int(bool(kept_ascending)),
+                                      _ptr(flags), _stream(stream)), "lsa_check_tables")
+    (stream if stream is not None else torch.cuda.current_stream()).synchronize()
+    return int(flags[0].item())
+
+
+def _debug_check(shape, chunk_off, sel_off, tok_off, sel_idx, where):
+    if chunk_off is None:  # attention calls carry no chunk table: rebuild it from the shape
+        return
+    bad = check_tables(shape, chunk_off, sel_off, tok_off, sel_idx, kept_ascending=False)
+    if bad:
+        raise ValueError(f"{where}: device tables violate the preconditions (flags {bad:#x})")
+
+
 def _event_ptr(ev):
     if ev is None:
         return None
@@ -527,9 +572,21 @@ def _event_ptr(ev):
 def decode_step(shape: ProblemShape, *, q_idx, emb, chunk_off, scores, sel_off, sel_idx, q,
                 k_store, v_store, tok_off, out, lse, workspace, reindex: bool = True,
                 materialize_pool: bool = False, k_pool=None, v_pool=None,
-                ev_attn_begin=None, ev_attn_end=None, stream=None) -> None:
+                ev_attn_begin=None, ev_attn_end=None, stream=None, step: int = 0,
+                reindex_every: int = 0) -> None:
     """lsa_decode_step: one whole decode step (score -> select -> [gather] ->
-    attention -> merge) enqueued by one call; outputs written in place."""
+    attention -> merge) enqueued by one call; outputs written in place.
+
+    reindex_every > 0 hands the schedule to the library (re-index iff
+    step % reindex_every == 0, ``reindex`` ignored); 0 leaves it to
+    ``reindex``."""
+    if reindex_every < 0 or (reindex_every > 0 and step < 0):
+        raise ValueError("reindex_every must be >= 0 and step >= 0")
+    if reindex_every > 0:
+        reindex = reindex_due(step, reindex_every)
+    if _DEBUG_CHECKS:
+        _debug_check(shape, chunk_off, sel_off, tok_off, None if reindex else sel_idx,
+                     "lsa_decode_step")
     for name, t, dt in [("q", q, shape.dtype), ("k_store", k_store, shape.dtype),
                         ("tok_off", tok_off, torch.int64), ("sel_off", sel_off, torch.int32),
                         ("sel_idx", sel_idx, torch.int32), ("out", out, torch.float32),
@@ -547,10 +604,19 @@ def decode_step(shape: ProblemShape, *, q_idx, emb, chunk_off, scores, sel_off, 
         _ptr(chunk_off) if reindex else None, _ptr(scores) if reindex else None,
         _ptr(sel_off), _ptr(sel_idx), _ptr(q), _ptr(k_store), _ptr(v_store), _ptr(tok_off),
         _ptr(k_pool), _ptr(v_pool), _ptr(out), _ptr(lse), int(bool(reindex)),
-        int(bool(materialize_pool)), _event_ptr(ev_attn_begin), _event_ptr(ev_attn_end))
+        int(bool(materialize_pool)), _event_ptr(ev_attn_begin), _event_ptr(ev_attn_end),
+        int(reindex_every), 0, int(step))
     _check(library().lsa_decode_step(ctypes.byref(shape.c()), ctypes.byref(args),
                                      _ptr(workspace), workspace.numel(), _stream(stream)),
            "lsa_decode_step")
+
+
+def reindex_due(step: int, reindex_every: int) -> bool:
+    """lsa_reindex_due: whether decode step `step` re-scores and re-selects."""
+    r = library().lsa_reindex_due(int(step), int(reindex_every))
+    if r < 0:
+        raise ValueError(f"invalid schedule: step={step}, reindex_every={reindex_every}")
+    return bool(r)
 
 
 def bench_attention_partial(shape: ProblemShape, q, k_base, v_base, tok_off, sel_idx, sel_off,

@@ -294,17 +294,31 @@ def all_chunks(tok_off: np.ndarray, C: int) -> tuple[np.ndarray, np.ndarray]:
     return sel_idx.astype(np.int32), sel_off
 
 
-def decode(q_idx: np.ndarray, emb: np.ndarray, chunk_off: np.ndarray, sel_off: np.ndarray,
+def decode(q_idx, emb: np.ndarray, chunk_off: np.ndarray, sel_off: np.ndarray,
            Qs: list, K: np.ndarray, V: np.ndarray | None, tok_off: np.ndarray, C: int,
            scale: float, reindex_every: int, dv: int | None = None, nthreads: int = 1):
-    """Multi-step decode: per step t, re-score and re-select when t % R == 0,
-    then attend with that step's queries Qs[t].  Returns a list of
-    (sel_idx, out, lse) per step."""
+    """The review's decode loop (section 3-2-3 steps 4-7, with the re-scoring
+    interval of the section 3-1 table and section 4-3): at step t the indexer
+    scores the chunks and a new kept set is selected only when t is a multiple
+    of ``reindex_every``; every step attends over the kept set of the most
+    recent re-index with that step's decode queries Qs[t].
+
+    ``q_idx`` is the indexer query embedding of every step: one [B, D] array
+    used at every re-index, or a sequence with one [B, D] array per step (the
+    query a real indexer computes from the current hidden state; only the
+    entries of re-index steps are read).  Returns a list of (sel_idx, out,
+    lse) per step."""
+    R = int(reindex_every)
+    if R < 1:
+        raise ValueError("reindex_every must be >= 1")
+    per_step = not (isinstance(q_idx, np.ndarray) and q_idx.ndim == 2)
+    if per_step and len(q_idx) < len(Qs):
+        raise ValueError("one indexer query per step is needed")
     results = []
     sel_idx = None
     for t, Q in enumerate(Qs):
-        if t % reindex_every == 0:
-            s = score(q_idx, emb, chunk_off)
+        if t % R == 0:
+            s = score(q_idx[t] if per_step else q_idx, emb, chunk_off)
             sel_idx = select(s, chunk_off, sel_off)
         out, lse = attention(Q, K, V, tok_off, sel_idx, sel_off, C, scale, dv=dv,
                              nthreads=nthreads)

@@ -36,7 +36,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_status_strings_and_version():
-    assert lsa.library().lsa_abi_version() == 2
+    assert lsa.library().lsa_abi_version() == 3
     for code, name in [(0, "LSA_OK"), (1, "LSA_ERR_INVALID_ARGUMENT"), (2, "LSA_ERR_UNSUPPORTED"),
                        (3, "LSA_ERR_WORKSPACE_TOO_SMALL"), (4, "LSA_ERR_HIP")]:
         assert lsa.status_string(code) == name
@@ -150,6 +150,31 @@ def test_null_and_misaligned_pointers_rejected():
     assert lsa.library().lsa_bench_flush(None, 16, None) == lsa.LSA_ERR_INVALID_ARGUMENT
 
 
+def test_reindex_schedule_helper_and_step_arg_checks():
+    lib = lsa.library()
+    assert [lib.lsa_reindex_due(t, 3) for t in range(8)] == [1, 0, 0, 1, 0, 0, 1, 0]
+    assert [lib.lsa_reindex_due(t, 1) for t in range(4)] == [1, 1, 1, 1]
+    assert lib.lsa_reindex_due(64 * 5, 64) == 1 and lib.lsa_reindex_due(64 * 5 + 1, 64) == 0
+    assert lib.lsa_reindex_due(2 ** 40, 64) == 1
+    assert lib.lsa_reindex_due(0, 0) == -1 and lib.lsa_reindex_due(-1, 4) == -1
+    assert lsa.reindex_due(6, 3) and not lsa.reindex_due(7, 3)
+    with pytest.raises(ValueError):
+        lsa.reindex_due(1, 0)
+    s = shape()
+    ws = lsa.workspace_bytes(s)
+    base = dict(q_idx_dev=DUMMY, emb_dev=DUMMY, chunk_off_dev=DUMMY, scores_dev=DUMMY,
+                sel_off_dev=DUMMY, sel_idx_dev=DUMMY, q_dev=DUMMY, k_store_dev=DUMMY,
+                v_store_dev=DUMMY, tok_off_dev=DUMMY, out_dev=DUMMY)
+    for bad in [dict(reindex_every=-1), dict(reindex_every=4, step=-3), dict(reserved=1)]:
+        a = lsa.StepArgs(**base, **bad)
+        assert lib.lsa_decode_step(ctypes.byref(s.c()), ctypes.byref(a), DUMMY, ws, None) == \
+            lsa.LSA_ERR_INVALID_ARGUMENT, bad
+    # with the schedule in charge, a re-index step needs the scoring inputs
+    a = lsa.StepArgs(**dict(base, q_idx_dev=None), reindex_every=4, step=8)
+    assert lib.lsa_decode_step(ctypes.byref(s.c()), ctypes.byref(a), DUMMY, ws, None) == \
+        lsa.LSA_ERR_INVALID_ARGUMENT
+
+
 def test_alias_requires_null_value_pointers():
     s = shape(v_aliases_k=True, head_dim_qk=576, head_dim_v=512, num_q_heads=64)
     assert _gather(s) == lsa.LSA_ERR_INVALID_ARGUMENT           # V pointers must be NULL
@@ -180,9 +205,9 @@ def test_python_layer_rejects_host_tensors():
                   torch.zeros(17, dtype=torch.int32))
 
 
-def test_workspace_holds_counters_and_every_partial():
+def test_workspace_holds_every_partial():
     # one partial (max, sum, output row) per head for every workgroup the plan
-    # can launch, plus the per-stream arrival counters
+    # can launch
     for per in [4, 8, 64, 256]:
         for B, k, H, dv in [(1, 8, 8, 64), (16, 276, 16, 128), (4, 819, 32, 128)]:
             s = shape(batch=B, max_k=k, total_k=B * k, num_q_heads=H, head_dim_qk=dv,

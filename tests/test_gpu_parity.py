@@ -84,19 +84,30 @@ def test_gather_is_bit_exact_and_pool_attention_matches_store(name):
     np.testing.assert_array_equal(dev.to_host(lse), lse_store)
 
 
-def test_reindex_schedule_over_several_steps():
-    cfg = wl.small_variant("cfg3", steps=5, reindex_every=2)
+@pytest.mark.parametrize("name,R,pool", [("cfg3", 3, True), ("cfg2", 3, False)])
+def test_reindex_schedule_over_several_steps(name, R, pool):
+    # The indexer query drifts every step and the device copy is updated every
+    # step; the library's schedule (lsa_decode_step with reindex_every = R) must
+    # re-score exactly on steps 0, R, 2R, ... and reuse the kept set (and pool)
+    # in between, so a schedule that re-indexes on any other step keeps a
+    # different set from the oracle's.
+    cfg = wl.small_variant(name, steps=8, reindex_every=R, n_needles=2)
     w = wl.make_workload(cfg)
-    d = dev.upload(w, "cuda")
+    d = dev.upload(w, "cuda", with_pool=pool)
+    q_steps = [wl.drift_query(w, t) for t in range(cfg.steps)]
     Qs = [w.queries(t) for t in range(cfg.steps)]
-    ref = oracle.decode(w.q_idx, w.emb, w.chunk_off, w.sel_off, Qs, w.K, w.V, w.tok_off,
-                        cfg.chunk_size, cfg.softmax_scale, cfg.reindex_every,
-                        nthreads=oracle.max_threads())
+    ref = oracle.decode(q_steps, w.emb, w.chunk_off, w.sel_off, Qs, w.K, w.V, w.tok_off,
+                        cfg.chunk_size, cfg.softmax_scale, R, nthreads=oracle.max_threads())
+    own = [oracle.select(oracle.score(q, w.emb, w.chunk_off), w.chunk_off, w.sel_off)
+           for q in q_steps]
     for t in range(cfg.steps):
-        d.step(t, reindex=(t % cfg.reindex_every == 0), materialize_pool=True)
+        if t % R:  # the test can see a wrong schedule only if this differs
+            assert not np.array_equal(own[t], ref[t][0]), t
+        d.q_idx.copy_(dev._to_device(q_steps[t], "cuda"))
+        d.step(t, materialize_pool=pool, reindex_every=R)
         torch.cuda.synchronize()
         sel = dev.to_host(d.sel_idx)
-        np.testing.assert_array_equal(sel, ref[t][0])   # no near-ties in this workload
+        np.testing.assert_array_equal(sel, ref[t][0], err_msg=f"step {t}")
         P.check_attention("bf16", dev.to_host(d.out), dev.to_host(d.lse), ref[t][1], ref[t][2])
 
 
@@ -367,7 +378,7 @@ def test_workspace_is_reusable_across_calls_and_shapes():
         for d, out_ref, lse_ref in [(da, out_a, lse_a), (db, out_b, lse_b)]:
             out, lse = lsa.sparse_decode_attn(d.shape, d.queries(0), d.K, d.V, d.tok_off,
                                               d.sel_idx, d.sel_off, workspace=big)
-            d.step(0, reindex=True)  # fused score+select uses the other counters
+            d.step(0, reindex=True)
             torch.cuda.synchronize()
             np.testing.assert_array_equal(dev.to_host(out), out_ref)
             np.testing.assert_array_equal(dev.to_host(lse), lse_ref)

@@ -334,20 +334,62 @@ def test_attention_threads_do_not_change_results():
     np.testing.assert_array_equal(a[1], b[1])
 
 
-def test_decode_reindex_schedule():
-    cfg = wl.small_variant("cfg2", lengths=(64 * 20 + 3, 64 * 9), steps=4)
-    w = wl.make_workload(cfg)
-    Qs = [w.queries(t) for t in range(4)]
-    res = oracle.decode(w.q_idx, w.emb, w.chunk_off, w.sel_off, Qs, w.K, w.V, w.tok_off,
-                        cfg.chunk_size, cfg.softmax_scale, reindex_every=2)
-    s = oracle.score(w.q_idx, w.emb, w.chunk_off)
-    sel = oracle.select(s, w.chunk_off, w.sel_off)
+def _schedule_golden():
+    g = _golden("reindex_schedule.json")
+    emb = _f32(g["emb"])
+    qs = [_f32(q) for q in g["q_idx_per_step"]]
+    V = _f32(g["V"])
+    K = np.zeros_like(V)
+    rng = np.random.default_rng(3)
+    Qs = [rng.standard_normal((2, 1, 2)).astype(np.float32) for _ in qs]
+    arr = {k: np.array(g[k], dtype=np.int64 if k == "tok_off" else np.int32)
+           for k in ("chunk_off", "sel_off", "tok_off")}
+    return g, emb, qs, K, V, Qs, arr
+
+
+def test_decode_reindex_schedule_golden():
+    g, emb, qs, K, V, Qs, a = _schedule_golden()
+    res = oracle.decode(qs, emb, a["chunk_off"], a["sel_off"], Qs, K, V, a["tok_off"],
+                        g["chunk_size"], 1.0, g["reindex_every"])
+    assert len(res) == len(qs)
     for t, (sel_t, out_t, lse_t) in enumerate(res):
-        np.testing.assert_array_equal(sel_t, sel)
-        o, l = oracle.attention(Qs[t], w.K, w.V, w.tok_off, sel, w.sel_off, cfg.chunk_size,
-                                cfg.softmax_scale)
-        np.testing.assert_array_equal(out_t, o)
-        np.testing.assert_array_equal(lse_t, l)
+        np.testing.assert_array_equal(sel_t, g["expected_sel_idx"][t])
+        np.testing.assert_allclose(out_t[:, 0, :], np.array(g["expected_out"][t]), rtol=1e-14)
+        np.testing.assert_allclose(lse_t[:, 0], np.array(g["expected_lse"][t]), rtol=1e-14)
+    # the fixture tells schedules apart: re-indexing every step, or one step late,
+    # gives other kept sets
+    every = oracle.decode(qs, emb, a["chunk_off"], a["sel_off"], Qs, K, V, a["tok_off"],
+                          g["chunk_size"], 1.0, 1)
+    np.testing.assert_array_equal(every[1][0], g["wrong_schedule_every_step_sel_idx_step1"])
+    late = oracle.decode(qs[1:] + qs[:1], emb, a["chunk_off"], a["sel_off"], Qs, K, V,
+                         a["tok_off"], g["chunk_size"], 1.0, g["reindex_every"])
+    assert any(not np.array_equal(x[0], e) for x, e in zip(late, g["expected_sel_idx"]))
+    assert any(not np.array_equal(x[0], e) for x, e in zip(every, g["expected_sel_idx"]))
+
+
+def test_decode_reindex_schedule_with_drifting_indexer_queries():
+    # the indexer query changes every step; only re-index steps may use it
+    cfg = wl.small_variant("cfg2", lengths=(64 * 40 + 3, 64 * 33, 64 * 52 + 17), steps=8)
+    w = wl.make_workload(cfg)
+    R = 3
+    q_steps = [wl.drift_query(w, t) for t in range(cfg.steps)]
+    Qs = [w.queries(t) for t in range(cfg.steps)]
+    res = oracle.decode(q_steps, w.emb, w.chunk_off, w.sel_off, Qs, w.K, w.V, w.tok_off,
+                        cfg.chunk_size, cfg.softmax_scale, R)
+    own = [oracle.select(oracle.score(q, w.emb, w.chunk_off), w.chunk_off, w.sel_off)
+           for q in q_steps]
+    for t, (sel_t, out_t, lse_t) in enumerate(res):
+        np.testing.assert_array_equal(sel_t, own[R * (t // R)])
+        if t % R:
+            # the step's own query would keep another set: re-indexing here is visible
+            assert not np.array_equal(own[t], sel_t), t
+    for e in range(1, (cfg.steps - 1) // R + 1):
+        assert not np.array_equal(own[R * e], own[R * (e - 1)]), e
+    # a fixed query (one [B, D] array) is read at every re-index
+    fixed = oracle.decode(w.q_idx, w.emb, w.chunk_off, w.sel_off, Qs[:4], w.K, w.V, w.tok_off,
+                          cfg.chunk_size, cfg.softmax_scale, 2)
+    for sel_t, _, _ in fixed:
+        np.testing.assert_array_equal(sel_t, own[0])
 
 
 def test_workload_shapes_of_the_five_configs():
@@ -668,6 +710,16 @@ def test_keep_recent_properties_and_grown_attention():
         want = set(sel[so[b]:so[b + 1]].tolist()) | {int(M[b]) - 1} | \
             set(range(int(M[b]), int((L[b] + C - 1) // C)))
         assert got == sorted(want)
+    # a binding bound keeps the newest candidates: the chunk holding the
+    # latest token (ceil(L/C) - 1) is always attended
+    for mr in (1, 2, 3):
+        off_b, idx_b = oracle.keep_recent(C, L, co, sel, so, mr)
+        for b in range(4):
+            kept = sel[so[b]:so[b + 1]].tolist()
+            cand = sorted((({int(M[b]) - 1} - set(kept)) |
+                           set(range(int(M[b]), int((L[b] + C - 1) // C)))))
+            assert idx_b[off_b[b]:off_b[b + 1]].tolist() == kept + cand[max(0, len(cand) - mr):]
+            assert int((L[b] + C - 1) // C) - 1 in idx_b[off_b[b]:off_b[b + 1]].tolist()
     # attention over the keep set of the grown context equals attention over
     # the kept chunks' tokens plus every token appended since (all of them lie
     # in the last scored chunk or in unscored chunks)
