@@ -291,6 +291,48 @@ def test_attention_shape_variants(variant):
     print(variant, P.check_attention("bf16", out, lse, o_ref, l_ref))
 
 
+# ----------------------------------------------------------------------------- degenerate streams
+# One ragged batch holding a stream shorter than a chunk (one partial chunk,
+# N_b = 1, k_b = 1), a single full chunk, a single token, a stream with a
+# one-token last chunk whose keep count rounds to 1, and a longer stream, run
+# through every attention kernel family: the matrix-core MQA kernel (d = 128,
+# d = 64, and two teams of head groups), absorbed MLA, and the fp32 kernel.
+# Review section 3-2-3 step 6: the unselected chunks are masked, whatever
+# their count.
+_EDGE = [
+    ("cfg2", {}),
+    ("cfg2", dict(num_q_heads=32, head_dim_qk=64, head_dim_v=64)),
+    ("cfg2", dict(num_q_heads=40)),
+    ("cfg4", {}),
+    ("cfg1", {}),
+]
+
+
+@pytest.mark.parametrize("name,variant", _EDGE, ids=lambda x: str(x))
+def test_attention_degenerate_streams(name, variant):
+    C = wl.CONFIGS[name].chunk_size
+    lengths = (17, C, 1, 3 * C + 1, 41 * C + 5, C + 1)
+    cfg = wl.small_variant(name, lengths=lengths, n_needles=0, keep_num=135, keep_den=1000,
+                           keep_round_up=True, **variant)
+    w = wl.make_workload(cfg)
+    assert list(w.keep[:4]) == [1, 1, 1, 1] and np.diff(w.chunk_off)[:3].tolist() == [1, 1, 1]
+    for per in (0, 1, 3):
+        d = dev.upload(w, "cuda", attn_tiles_per_block=per)
+        s_gpu, sel, out, lse = P.run_phases(d, 0)
+        s_ref = oracle.score(w.q_idx, w.emb, w.chunk_off)
+        P.check_scores(w, s_gpu, s_ref)
+        P.check_selection(w, s_gpu, sel, s_ref)
+        o_ref, l_ref = P.oracle_attention_on(w, 0, sel)
+        print(name, variant, per, P.check_attention(cfg.dtype, out, lse, o_ref, l_ref))
+        # the one-token stream attends to its single token: out = V of that token
+        t = int(w.tok_off[2])
+        v = wl.as_f32(w.V[t] if w.V is not None else w.K[t, :cfg.head_dim_v])
+        np.testing.assert_allclose(out[2], np.broadcast_to(v, out[2].shape), rtol=1e-6,
+                                   atol=1e-7)
+        np.testing.assert_allclose(lse[2], wl.as_f32(w.queries(0))[2] @ wl.as_f32(
+            w.K[t]) * cfg.softmax_scale, rtol=1e-4, atol=1e-6)
+
+
 # ----------------------------------------------------------------------------- MLA (absorbed latent)
 def _mla_cfg(**kw):
     # three ragged streams with partial last chunks, a quarter of the chunks kept,
