@@ -17,8 +17,9 @@
  * Ownership: the caller owns every buffer.  Pointers named *_dev are device
  *   (HBM) pointers; the lsa_shape / lsa_step_args structs themselves are read
  *   on the host during the call and may be freed when it returns.  The library
- *   keeps no global mutable state, never allocates device or host memory and
- *   is reentrant; scratch memory is the caller's workspace.
+ *   never allocates device or host memory and is reentrant; scratch memory is
+ *   the caller's workspace, except for lsa_decode_step_static, whose scratch
+ *   is a static device array.
  * Asynchrony: a call validates its arguments on the host, enqueues kernels on
  *   `hip_stream` (a hipStream_t; NULL means the legacy null stream) and
  *   returns.  Results are valid once the stream reaches that point.  No call
@@ -422,6 +423,25 @@ int32_t lsa_reindex_due(int64_t step, int32_t reindex_every);
 
 lsa_status lsa_decode_step(const lsa_shape* shape, const lsa_step_args* args,
                            void* workspace_dev, size_t workspace_bytes, void* hip_stream);
+
+/* ---------------------------------------------------------------------------
+ * lsa_decode_step without a workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same arguments, checks, kernels and
+ * results as lsa_decode_step; the split-KV partials go to a static device
+ * array of LSA_STATIC_SCRATCH_BYTES that the library holds on every device
+ * it runs on until the process ends.  A shape whose lsa_workspace_bytes
+ * exceeds that size returns LSA_ERR_WORKSPACE_TOO_SMALL before anything is
+ * enqueued.  The call allocates nothing.  All calls on one device share that
+ * device's array: calls that overlap on one device (concurrent streams, or
+ * host threads) race and must be serialised by the caller.  The first call
+ * on a device looks up the array's device address (LSA_ERR_HIP if that
+ * fails).
+ * ------------------------------------------------------------------------- */
+#define LSA_STATIC_SCRATCH_BYTES (64u << 20)
+
+lsa_status lsa_decode_step_static(const lsa_shape* shape, const lsa_step_args* args,
+                                  void* hip_stream);
 
 /* ---------------------------------------------------------------------------
  * Debug check of the device-side preconditions (off the hot path; nothing

@@ -4,6 +4,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "lsa_internal.hpp"
 
 namespace lsa {
@@ -270,21 +272,37 @@ lsa_status lsa_gather_chunks(const lsa_shape* shape, const void* k_store_dev,
                                   static_cast<hipStream_t>(hip_stream)));
 }
 
+// Checks of an attention call's arguments other than the workspace.
+static lsa_status check_attn_io(const lsa_shape* shape, int32_t kv_mode, const void* q,
+                                const void* kb, const void* vb, const int64_t* tok_off,
+                                const int32_t* sel_idx, const int32_t* sel_off, const float* out,
+                                const float* lse) {
+  lsa_status st = check_attn_shape(shape);
+  if (st != LSA_OK) return st;
+  if (kv_mode != LSA_KV_STORE && kv_mode != LSA_KV_POOL) return LSA_ERR_INVALID_ARGUMENT;
+  if (!q || !kb || !tok_off || !sel_idx || !sel_off || !out) return LSA_ERR_INVALID_ARGUMENT;
+  if (shape->v_aliases_k ? (vb != nullptr) : (vb == nullptr)) return LSA_ERR_INVALID_ARGUMENT;
+  if (!aligned(q, 16) || !aligned(kb, 16) || (vb && !aligned(vb, 16)) || !aligned(tok_off, 8) ||
+      !aligned(sel_idx, 4) || !aligned(sel_off, 4) || !aligned(out, 16) ||
+      (lse && !aligned(lse, 4)))
+    return LSA_ERR_INVALID_ARGUMENT;
+  return LSA_OK;
+}
+
+// Workspace of a validated attention shape: present, 256-byte aligned, large enough.
+static lsa_status check_workspace(const lsa_shape* shape, const void* ws, size_t ws_bytes) {
+  if (!ws || !aligned(ws, 256)) return LSA_ERR_INVALID_ARGUMENT;
+  if (ws_bytes < lsa_workspace_bytes(shape)) return LSA_ERR_WORKSPACE_TOO_SMALL;
+  return LSA_OK;
+}
+
 static lsa_status check_attn_args(const lsa_shape* shape, int32_t kv_mode, const void* q,
                                   const void* kb, const void* vb, const int64_t* tok_off,
                                   const int32_t* sel_idx, const int32_t* sel_off, const float* out,
                                   const float* lse, const void* ws, size_t ws_bytes) {
-  lsa_status st = check_attn_shape(shape);
+  const lsa_status st = check_attn_io(shape, kv_mode, q, kb, vb, tok_off, sel_idx, sel_off, out, lse);
   if (st != LSA_OK) return st;
-  if (kv_mode != LSA_KV_STORE && kv_mode != LSA_KV_POOL) return LSA_ERR_INVALID_ARGUMENT;
-  if (!q || !kb || !tok_off || !sel_idx || !sel_off || !out || !ws) return LSA_ERR_INVALID_ARGUMENT;
-  if (shape->v_aliases_k ? (vb != nullptr) : (vb == nullptr)) return LSA_ERR_INVALID_ARGUMENT;
-  if (!aligned(q, 16) || !aligned(kb, 16) || (vb && !aligned(vb, 16)) || !aligned(tok_off, 8) ||
-      !aligned(sel_idx, 4) || !aligned(sel_off, 4) || !aligned(out, 16) ||
-      (lse && !aligned(lse, 4)) || !aligned(ws, 256))
-    return LSA_ERR_INVALID_ARGUMENT;
-  if (ws_bytes < lsa_workspace_bytes(shape)) return LSA_ERR_WORKSPACE_TOO_SMALL;
-  return LSA_OK;
+  return check_workspace(shape, ws, ws_bytes);
 }
 
 // Device address of page-locked host memory, or null when `p` is not such memory.
@@ -410,22 +428,14 @@ lsa_status lsa_keep_recent(const lsa_shape* shape, const int64_t* seq_len_dev,
                                        static_cast<hipStream_t>(hip_stream)));
 }
 
-lsa_status lsa_decode_step(const lsa_shape* shape, const lsa_step_args* args, void* workspace_dev,
-                           size_t workspace_bytes, void* hip_stream) {
-  if (shape == nullptr || args == nullptr) return LSA_ERR_INVALID_ARGUMENT;
-  lsa_step_args x = *args;
-  if (x.reindex_every < 0 || x.reserved != 0) return LSA_ERR_INVALID_ARGUMENT;
-  if (x.reindex_every > 0) {
-    const int32_t due = lsa_reindex_due(x.step, x.reindex_every);
-    if (due < 0) return LSA_ERR_INVALID_ARGUMENT;
-    x.reindex = due;
-  }
+// Checks of a decode step's arguments other than the workspace (x.reindex
+// already set by the schedule).
+static lsa_status check_step(const lsa_shape* shape, const lsa_step_args& x) {
   const bool pool = x.materialize_pool != 0;
   const void* kbase = pool ? x.k_pool_dev : x.k_store_dev;
   const void* vbase = pool ? x.v_pool_dev : x.v_store_dev;
-  lsa_status st = check_attn_args(shape, pool ? LSA_KV_POOL : LSA_KV_STORE, x.q_dev, kbase, vbase,
-                                  x.tok_off_dev, x.sel_idx_dev, x.sel_off_dev, x.out_dev,
-                                  x.lse_dev, workspace_dev, workspace_bytes);
+  lsa_status st = check_attn_io(shape, pool ? LSA_KV_POOL : LSA_KV_STORE, x.q_dev, kbase, vbase,
+                                x.tok_off_dev, x.sel_idx_dev, x.sel_off_dev, x.out_dev, x.lse_dev);
   if (st != LSA_OK) return st;
   if (pool && (!x.k_store_dev || (shape->v_aliases_k ? x.v_store_dev != nullptr : !x.v_store_dev)))
     return LSA_ERR_INVALID_ARGUMENT;
@@ -442,6 +452,13 @@ lsa_status lsa_decode_step(const lsa_shape* shape, const lsa_step_args* args, vo
         !aligned(x.scores_dev, 4))
       return LSA_ERR_INVALID_ARGUMENT;
   }
+  return LSA_OK;
+}
+
+// Enqueues a validated decode step with its split-KV partials in `ws`.
+static lsa_status enqueue_step(const lsa_shape* shape, const lsa_step_args& x, void* ws,
+                               void* hip_stream) {
+  const bool pool = x.materialize_pool != 0;
   const hipStream_t hs = static_cast<hipStream_t>(hip_stream);
   (void)hipGetLastError();
   if (x.reindex) {
@@ -459,9 +476,86 @@ lsa_status lsa_decode_step(const lsa_shape* shape, const lsa_step_args* args, vo
         return LSA_ERR_HIP;
     }
   }
-  return enqueue_attention(*shape, pool ? LSA_KV_POOL : LSA_KV_STORE, x.q_dev, kbase, vbase,
-                           x.tok_off_dev, x.sel_idx_dev, x.sel_off_dev, x.out_dev, x.lse_dev,
-                           workspace_dev, hs, x.ev_attn_begin, x.ev_attn_end);
+  return enqueue_attention(*shape, pool ? LSA_KV_POOL : LSA_KV_STORE, x.q_dev,
+                           pool ? x.k_pool_dev : x.k_store_dev,
+                           pool ? x.v_pool_dev : x.v_store_dev, x.tok_off_dev, x.sel_idx_dev,
+                           x.sel_off_dev, x.out_dev, x.lse_dev, ws, hs, x.ev_attn_begin,
+                           x.ev_attn_end);
+}
+
+// The step's arguments with the lookahead schedule applied to x.reindex.
+static lsa_status resolve_schedule(const lsa_step_args* args, lsa_step_args* x) {
+  if (args == nullptr) return LSA_ERR_INVALID_ARGUMENT;
+  *x = *args;
+  if (x->reindex_every < 0 || x->reserved != 0) return LSA_ERR_INVALID_ARGUMENT;
+  if (x->reindex_every > 0) {
+    const int32_t due = lsa_reindex_due(x->step, x->reindex_every);
+    if (due < 0) return LSA_ERR_INVALID_ARGUMENT;
+    x->reindex = due;
+  }
+  return LSA_OK;
+}
+
+lsa_status lsa_decode_step(const lsa_shape* shape, const lsa_step_args* args, void* workspace_dev,
+                           size_t workspace_bytes, void* hip_stream) {
+  if (shape == nullptr) return LSA_ERR_INVALID_ARGUMENT;
+  lsa_step_args x;
+  lsa_status st = resolve_schedule(args, &x);
+  if (st != LSA_OK) return st;
+  st = check_step(shape, x);
+  if (st != LSA_OK) return st;
+  st = check_workspace(shape, workspace_dev, workspace_bytes);
+  if (st != LSA_OK) return st;
+  return enqueue_step(shape, x, workspace_dev, hip_stream);
+}
+
+// ---------------------------------------------------------------------------
+// lsa_decode_step_static: lsa_decode_step for callers that cannot allocate.
+// Its split-KV partials (the only scratch memory of a step) live in the
+// file-scope device array below: each device holds its own copy, from when
+// the library's code object is loaded on it until the process ends.  In host
+// code `scratch` names a host-side stand-in, never a device address; the
+// device address of each device's copy comes from hipGetSymbolAddress, taken
+// once per device with that device current, and only that address reaches
+// the kernels.  Every call on a device shares its copy (overlapping calls on
+// one device race); nothing in it has to start at zero, since every partial
+// the merge reads is written first by the same step.
+static __device__ __align__(256) unsigned char scratch[LSA_STATIC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxScratchDevices = 64;
+std::once_flag g_scratch_once[kMaxScratchDevices];
+void* g_scratch_dev[kMaxScratchDevices];
+hipError_t g_scratch_err[kMaxScratchDevices];
+}  // namespace
+
+// Device address of the current device's copy of `scratch`, or null.
+static void* static_scratch_address() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxScratchDevices) return nullptr;
+  std::call_once(g_scratch_once[dev], [dev] {
+    void* p = nullptr;
+    g_scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    g_scratch_dev[dev] = g_scratch_err[dev] == hipSuccess ? p : nullptr;
+  });
+  return g_scratch_dev[dev];
+}
+
+lsa_status lsa_decode_step_static(const lsa_shape* shape, const lsa_step_args* args,
+                                  void* hip_stream) {
+  if (shape == nullptr) return LSA_ERR_INVALID_ARGUMENT;
+  lsa_step_args x;
+  lsa_status st = resolve_schedule(args, &x);
+  if (st != LSA_OK) return st;
+  st = check_step(shape, x);
+  if (st != LSA_OK) return st;
+  if (lsa_workspace_bytes(shape) > LSA_STATIC_SCRATCH_BYTES) return LSA_ERR_WORKSPACE_TOO_SMALL;
+  void* ws = static_scratch_address();
+  if (ws == nullptr) {
+    (void)hipGetLastError();
+    return LSA_ERR_HIP;
+  }
+  return enqueue_step(shape, x, ws, hip_stream);
 }
 
 lsa_status lsa_check_tables(const lsa_shape* shape, const int64_t* tok_off_dev,

@@ -93,6 +93,7 @@ _SIGNATURES = {
     "lsa_status_string": ([_I32], ctypes.c_char_p),
     "lsa_abi_version": ([], _I32),
     "lsa_check_tables": ([ctypes.POINTER(Shape), _P, _P, _P, _P, _I32, _P, _P], _I32),
+    "lsa_decode_step_static": ([ctypes.POINTER(Shape), ctypes.POINTER(StepArgs), _P], _I32),
     "lsa_reindex_due": ([ctypes.c_int64, _I32], _I32),
     "lsa_keep_count": ([_I32, _I32, _I32, _I32], _I32),
     "lsa_workspace_bytes": ([ctypes.POINTER(Shape)], ctypes.c_size_t),
@@ -569,6 +570,35 @@ def _event_ptr(ev):
     return ctypes.c_void_p(ev.cuda_event)
 
 
+def _step_args(shape: ProblemShape, q_idx, emb, chunk_off, scores, sel_off, sel_idx, q,
+               k_store, v_store, tok_off, out, lse, reindex, materialize_pool, k_pool, v_pool,
+               ev_attn_begin, ev_attn_end, step, reindex_every, where) -> StepArgs:
+    if reindex_every < 0 or (reindex_every > 0 and step < 0):
+        raise ValueError("reindex_every must be >= 0 and step >= 0")
+    if reindex_every > 0:
+        reindex = reindex_due(step, reindex_every)
+    if _DEBUG_CHECKS:
+        _debug_check(shape, chunk_off, sel_off, tok_off, None if reindex else sel_idx, where)
+    for name, t, dt in [("q", q, shape.dtype), ("k_store", k_store, shape.dtype),
+                        ("tok_off", tok_off, torch.int64), ("sel_off", sel_off, torch.int32),
+                        ("sel_idx", sel_idx, torch.int32), ("out", out, torch.float32)]:
+        _dev(t, name, dt)
+    if lse is not None:
+        _dev(lse, "lse", torch.float32)
+    if reindex:
+        for name, t, dt in [("q_idx", q_idx, shape.dtype), ("emb", emb, shape.dtype),
+                            ("chunk_off", chunk_off, torch.int32),
+                            ("scores", scores, torch.float32)]:
+            _dev(t, name, dt)
+    return StepArgs(
+        _ptr(q_idx) if reindex else None, _ptr(emb) if reindex else None,
+        _ptr(chunk_off) if reindex else None, _ptr(scores) if reindex else None,
+        _ptr(sel_off), _ptr(sel_idx), _ptr(q), _ptr(k_store), _ptr(v_store), _ptr(tok_off),
+        _ptr(k_pool), _ptr(v_pool), _ptr(out), _ptr(lse), int(bool(reindex)),
+        int(bool(materialize_pool)), _event_ptr(ev_attn_begin), _event_ptr(ev_attn_end),
+        int(reindex_every), 0, int(step))
+
+
 def decode_step(shape: ProblemShape, *, q_idx, emb, chunk_off, scores, sel_off, sel_idx, q,
                 k_store, v_store, tok_off, out, lse, workspace, reindex: bool = True,
                 materialize_pool: bool = False, k_pool=None, v_pool=None,
@@ -580,35 +610,31 @@ def decode_step(shape: ProblemShape, *, q_idx, emb, chunk_off, scores, sel_off, 
     reindex_every > 0 hands the schedule to the library (re-index iff
     step % reindex_every == 0, ``reindex`` ignored); 0 leaves it to
     ``reindex``."""
-    if reindex_every < 0 or (reindex_every > 0 and step < 0):
-        raise ValueError("reindex_every must be >= 0 and step >= 0")
-    if reindex_every > 0:
-        reindex = reindex_due(step, reindex_every)
-    if _DEBUG_CHECKS:
-        _debug_check(shape, chunk_off, sel_off, tok_off, None if reindex else sel_idx,
-                     "lsa_decode_step")
-    for name, t, dt in [("q", q, shape.dtype), ("k_store", k_store, shape.dtype),
-                        ("tok_off", tok_off, torch.int64), ("sel_off", sel_off, torch.int32),
-                        ("sel_idx", sel_idx, torch.int32), ("out", out, torch.float32),
-                        ("workspace", workspace, torch.uint8)]:
-        _dev(t, name, dt)
-    if lse is not None:
-        _dev(lse, "lse", torch.float32)
-    if reindex:
-        for name, t, dt in [("q_idx", q_idx, shape.dtype), ("emb", emb, shape.dtype),
-                            ("chunk_off", chunk_off, torch.int32),
-                            ("scores", scores, torch.float32)]:
-            _dev(t, name, dt)
-    args = StepArgs(
-        _ptr(q_idx) if reindex else None, _ptr(emb) if reindex else None,
-        _ptr(chunk_off) if reindex else None, _ptr(scores) if reindex else None,
-        _ptr(sel_off), _ptr(sel_idx), _ptr(q), _ptr(k_store), _ptr(v_store), _ptr(tok_off),
-        _ptr(k_pool), _ptr(v_pool), _ptr(out), _ptr(lse), int(bool(reindex)),
-        int(bool(materialize_pool)), _event_ptr(ev_attn_begin), _event_ptr(ev_attn_end),
-        int(reindex_every), 0, int(step))
+    args = _step_args(shape, q_idx, emb, chunk_off, scores, sel_off, sel_idx, q, k_store,
+                      v_store, tok_off, out, lse, reindex, materialize_pool, k_pool, v_pool,
+                      ev_attn_begin, ev_attn_end, step, reindex_every, "lsa_decode_step")
+    _dev(workspace, "workspace", torch.uint8)
     _check(library().lsa_decode_step(ctypes.byref(shape.c()), ctypes.byref(args),
                                      _ptr(workspace), workspace.numel(), _stream(stream)),
            "lsa_decode_step")
+
+
+STATIC_SCRATCH_BYTES = 64 << 20  # LSA_STATIC_SCRATCH_BYTES
+
+
+def decode_step_static(shape: ProblemShape, *, q_idx, emb, chunk_off, scores, sel_off, sel_idx,
+                       q, k_store, v_store, tok_off, out, lse, reindex: bool = True,
+                       materialize_pool: bool = False, k_pool=None, v_pool=None,
+                       ev_attn_begin=None, ev_attn_end=None, stream=None, step: int = 0,
+                       reindex_every: int = 0) -> None:
+    """lsa_decode_step_static: lsa_decode_step with no workspace argument (the
+    library's static per-device scratch holds the split partials); allocates
+    nothing.  Calls on one device must not overlap."""
+    args = _step_args(shape, q_idx, emb, chunk_off, scores, sel_off, sel_idx, q, k_store,
+                      v_store, tok_off, out, lse, reindex, materialize_pool, k_pool, v_pool,
+                      ev_attn_begin, ev_attn_end, step, reindex_every, "lsa_decode_step_static")
+    _check(library().lsa_decode_step_static(ctypes.byref(shape.c()), ctypes.byref(args),
+                                            _stream(stream)), "lsa_decode_step_static")
 
 
 def reindex_due(step: int, reindex_every: int) -> bool:

@@ -175,6 +175,31 @@ def test_reindex_schedule_helper_and_step_arg_checks():
         lsa.LSA_ERR_INVALID_ARGUMENT
 
 
+def test_static_step_checks_before_touching_the_device():
+    # no GPU is needed: every refusal happens before the scratch is looked up
+    lib = lsa.library()
+    base = dict(q_idx_dev=DUMMY, emb_dev=DUMMY, chunk_off_dev=DUMMY, scores_dev=DUMMY,
+                sel_off_dev=DUMMY, sel_idx_dev=DUMMY, q_dev=DUMMY, k_store_dev=DUMMY,
+                v_store_dev=DUMMY, tok_off_dev=DUMMY, out_dev=DUMMY, reindex=1)
+    s = shape()
+    assert lib.lsa_decode_step_static(None, ctypes.byref(lsa.StepArgs(**base)), None) == \
+        lsa.LSA_ERR_INVALID_ARGUMENT
+    assert lib.lsa_decode_step_static(ctypes.byref(s.c()), None, None) == \
+        lsa.LSA_ERR_INVALID_ARGUMENT
+    a = lsa.StepArgs(**dict(base, q_dev=None))
+    assert lib.lsa_decode_step_static(ctypes.byref(s.c()), ctypes.byref(a), None) == \
+        lsa.LSA_ERR_INVALID_ARGUMENT
+    a = lsa.StepArgs(**base, reindex_every=-2)
+    assert lib.lsa_decode_step_static(ctypes.byref(s.c()), ctypes.byref(a), None) == \
+        lsa.LSA_ERR_INVALID_ARGUMENT
+    big = shape(attn_tiles_per_block=1)   # one partial per 32-token tile: 73 MB
+    assert lsa.workspace_bytes(big) > lsa.STATIC_SCRATCH_BYTES
+    a = lsa.StepArgs(**base)
+    assert lib.lsa_decode_step_static(ctypes.byref(big.c()), ctypes.byref(a), None) == \
+        lsa.LSA_ERR_WORKSPACE_TOO_SMALL
+    assert lsa.workspace_bytes(shape()) <= lsa.STATIC_SCRATCH_BYTES
+
+
 def test_alias_requires_null_value_pointers():
     s = shape(v_aliases_k=True, head_dim_qk=576, head_dim_v=512, num_q_heads=64)
     assert _gather(s) == lsa.LSA_ERR_INVALID_ARGUMENT           # V pointers must be NULL
