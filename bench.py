@@ -843,8 +843,9 @@ def main():
         replicas.append(r)
     nq = 8
     qs = [base.queries(t) for t in range(nq)]
-    for r in replicas:  # fill every replica's kept set (and pool) once
-        r.step(0, reindex=True, materialize_pool=cfg.materialize_pool, q=qs[0])
+    for r in replicas:  # fill every replica's kept set (and pool) once; this also
+        # marshals each replica's step arguments (PreparedStep) outside the timing
+        r.step(0, materialize_pool=cfg.materialize_pool, q=qs[0], reindex_every=R_idx)
     torch.cuda.synchronize()
     print(f"bench: {reps} replica(s), {step_bytes / 1e6:.1f} MB per step", file=sys.stderr,
           flush=True)
@@ -857,24 +858,47 @@ def main():
             r.step(t, reindex_every=R_idx, materialize_pool=cfg.materialize_pool,
                    ev_begin=eb, ev_end=ee, q=qs[t % nq])
 
-    # pass 3 (roofline.avg_launch_us): the attention partial kernel alone, the
-    # K launches (one per replica in turn, so each reads cold K/V) replayed
-    # back to back from a HIP graph with two events around the replay: no
-    # event record sits between the kernels
+    # pass 3 (roofline.avg_launch_us): the attention phase alone (one
+    # lsa_sparse_decode_attn call: split-KV partials and their log-sum-exp
+    # merge), the K calls (one per replica in turn, so each reads cold K/V)
+    # replayed back to back from a HIP graph with two events around the
+    # replay: no event record sits between the kernels
     pool_mode = bool(cfg.materialize_pool)
 
-    def partial(i):
+    def attention(i):
+        r = replicas[i % reps]
+        lsa.sparse_decode_attn(
+            r.shape, qs[i % nq], r.k_pool if pool_mode else r.K,
+            r.v_pool if pool_mode else r.V, r.tok_off, r.sel_idx, r.sel_off,
+            lsa.KV_POOL if pool_mode else lsa.KV_STORE, out=r.out, lse=r.lse,
+            workspace=r.workspace)
+
+    def partial(i):  # the partial kernel without any merge (dominant kernel of MLA)
         r = replicas[i % reps]
         lsa.bench_attention_partial(
             r.shape, qs[i % nq], r.k_pool if pool_mode else r.K,
             r.v_pool if pool_mode else r.V, r.tok_off, r.sel_idx, r.sel_off,
             lsa.KV_POOL if pool_mode else lsa.KV_STORE, r.workspace)
 
+    def score(i):
+        r = replicas[i % reps]
+        lsa.score(r.shape, r.q_idx, r.emb, r.chunk_off, scores=r.scores)
+
     kernel_file = os.path.join(ROOT, "learned_kv_chunk_amd", "csrc",
                                "attn_mla.hip" if cfg.v_aliases_k else
                                ("attn_mqa.hip" if cfg.dtype == "bf16" else "attn_portable.hip"))
+    # the MQA kernel merges each stream itself when streams average at most
+    # eight of the device's workgroups (the library's rule)
+    tpc = -(-cfg.chunk_size // 32)
+    wgs_expected = (-(-int(w.sel_off[-1]) * tpc // args.tiles_per_block) if args.tiles_per_block
+                    else torch.cuda.get_device_properties(0).multi_processor_count)
+    fused = (cfg.dtype == "bf16" and not cfg.v_aliases_k and
+             cfg.num_q_heads * cfg.head_dim_v <= 2048 and wgs_expected <= 8 * cfg.batch)
+    attn_desc = ("attn_mqa: split-KV partials and their LSE merge in one kernel" if fused else
+                 os.path.basename(kernel_file).replace(".hip", "") +
+                 " partial kernel + LSE merge kernel (the attention phase)")
     if args.attention_only:
-        attn_us = _graph_us(partial, args.steps, warm=4)
+        attn_us = _graph_us(attention, args.steps, warm=4)
         attn_gbs = attn_bytes / attn_us / 1e3
         print(json.dumps({
             "metric": "split-KV attention partial kernel launches/sec (cold K/V)",
@@ -882,7 +906,7 @@ def main():
             "warmup": 4, "higher_is_better": True, "dtype": cfg.dtype, "data": "synthetic",
             "config": {"workload": f"{args.config}: {WORKLOAD_TEXT[args.config]}",
                        "replicas": reps},
-            "roofline": {"kernel": os.path.basename(kernel_file).replace(".hip", ""),
+            "roofline": {"kernel": attn_desc,
                          "bound": "hbm", "achieved": attn_gbs, "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": attn_gbs / HBM_PEAK_GBS,
                          "algorithmic_bytes_per_launch": int(attn_bytes),
@@ -943,10 +967,14 @@ def main():
     attn_us_events = float(np.mean([a.elapsed_time(b) for a, b in evs])) * 1e3
     ms_per_step_with_events = h0.elapsed_time(h1) / args.steps
 
-    # pass 3 (roofline.avg_launch_us): see the definition of `partial`; run
-    # after the step passes, with the clocks up
-    attn_us = _graph_us(partial, args.steps)
+    # pass 3 (roofline.avg_launch_us): see the definition of `attention`; run
+    # after the step passes, with the clocks up; the partial kernel alone and
+    # the score kernel alone the same way
+    attn_us = _graph_us(attention, args.steps)
     attn_gbs = attn_bytes / attn_us / 1e3
+    partial_us = attn_us if fused else _graph_us(partial, args.steps)
+    score_us = _graph_us(score, args.steps)
+    score_bytes = ab["score"]
 
     # warm (Infinity-Cache-assisted) reference: the same steps on one replica
     warm_n = min(args.steps, 100)
@@ -1061,7 +1089,7 @@ def main():
         "ms_per_step_with_attn_events": ms_per_step_with_events,
         "resident_fraction": w.resident_fraction(),
         "roofline": {
-            "kernel": os.path.basename(kernel_file).replace(".hip", "") + " (split-KV attention)",
+            "kernel": attn_desc,
             "bound": "hbm",
             "achieved": attn_gbs,
             "peak": HBM_PEAK_GBS,
@@ -1070,11 +1098,17 @@ def main():
             "traffic": traffic,
             "algorithmic_bytes_per_launch": int(attn_bytes),
             "avg_launch_us": attn_us,
-            "timing": "partial kernel alone, K cold launches replayed from a HIP graph",
+            "timing": "the attention phase (one lsa_sparse_decode_attn call), K cold calls "
+                      "replayed from a HIP graph",
+            "partial_kernel_us": partial_us,
             "avg_launch_us_events_in_step": attn_us_events,
             "measured_copy_gbs": copy_gbs,
             "frac_of_measured_copy": attn_gbs / copy_gbs,
         },
+        "score_kernel": {"us": score_us, "algorithmic_bytes": int(score_bytes),
+                         "gbs": score_bytes / score_us / 1e3,
+                         "frac": score_bytes / score_us / 1e3 / HBM_PEAK_GBS,
+                         "timing": "K cold launches replayed from a HIP graph"},
         "warm_ms_per_step": warm_ms,
         "warm_note": "one replica, back to back: Infinity-Cache-assisted",
         "step_us_p10_p50_p90_with_events": [float(np.percentile(per_step, q)) for q in

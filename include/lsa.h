@@ -123,7 +123,10 @@ int32_t lsa_keep_count(int32_t n_chunks, int32_t ratio_num, int32_t ratio_den,
 
 /* Bytes of workspace lsa_sparse_decode_attn / lsa_decode_step need for this
  * shape (0 if the shape is invalid).  Monotone in batch, total_k, max_k,
- * num_q_heads and head_dim_v; any buffer at least this large works. */
+ * num_q_heads and head_dim_v; any buffer at least this large works.  The
+ * buffer must be zero-filled once before its first use (it holds one arrival
+ * counter per stream); every call leaves it zero-filled again, so a workspace
+ * is zeroed once when allocated, not per call. */
 size_t lsa_workspace_bytes(const lsa_shape* shape);
 
 /* ---------------------------------------------------------------------------
@@ -346,17 +349,21 @@ lsa_status lsa_pool_delta_update(const lsa_shape* shape, const void* k_host, con
  *   out[b][h][:] = sum_t exp(x_t) V_t / sum_t exp(x_t)
  *   lse[b][h]    = log(sum_t exp(x_t))          (natural log)
  * computed split-KV: workgroups own runs of 32-token tiles, keep an fp32
- * online softmax, and a merge pass combines their partial (max, sum, output)
- * by log-sum-exp.
+ * online softmax, and their partial (max, sum, output) results are combined
+ * by log-sum-exp (by the last workgroup of each stream to finish, or by a
+ * merge pass).
  * q_dev: [B][H][head_dim_qk].  kv_mode LSA_KV_STORE: k_base/v_base are the
  * stores ([sum L][d]) and chunk sel_idx[s] of stream b is read in place.
  * kv_mode LSA_KV_POOL: k_base/v_base are pools written by lsa_gather_chunks
  * and slot s is read (sel_idx is still needed for the valid-token count of
  * partial chunks).  v_base must be NULL when v_aliases_k.
  * out_dev: [B][H][head_dim_v] fp32; lse_dev: [B][H] fp32 (may be NULL).
- * workspace_dev: >= lsa_workspace_bytes(shape) bytes, 256-byte aligned; it
- * holds the split partial results, its contents on entry do not matter, and
- * calls that share a workspace must not run concurrently.
+ * workspace_dev: >= lsa_workspace_bytes(shape) bytes, 256-byte aligned,
+ * zero-filled before its first use (see lsa_workspace_bytes); it holds the
+ * split partial results and the per-stream arrival counters of the kernels
+ * that merge a stream in its last workgroup (the multi-query kernel; the
+ * others run a separate merge pass); calls that share a workspace must not
+ * run concurrently.
  * Supported: bf16 with num_q_heads <= 64 and head_dim_qk == head_dim_v in
  * {64, 128} (multi-query); bf16 with head_dim_qk 576, head_dim_v 512,
  * v_aliases_k = 1 and 1 to 64 query heads (absorbed latent attention); fp32

@@ -10,6 +10,8 @@
 // out = sum_p f_p o_p / sum_p f_p l_p, lse = ln2 * (m* + log2 sum_p f_p l_p).
 #include <math.h>
 
+#include <atomic>
+
 #include "lsa_internal.hpp"
 
 namespace lsa {
@@ -20,12 +22,29 @@ constexpr int32_t kDefaultTarget = 256;  // compute units of an MI355X
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 }  // namespace
 
+// The compute-unit count of each device is queried once and kept: a device
+// attribute that never changes, so every later call (one per attention
+// enqueue) costs only hipGetDevice.
 int32_t device_cu_count() {
-  int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-      cus <= 0)
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int32_t> cached[kMaxDevices];  // 0: not queried yet
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
     return kDefaultTarget;
+  }
+  const bool keep = dev >= 0 && dev < kMaxDevices;
+  if (keep) {
+    const int32_t c = cached[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus <= 0) {
+    (void)hipGetLastError();
+    return kDefaultTarget;
+  }
+  if (keep) cached[dev].store(cus, std::memory_order_relaxed);
   return cus;
 }
 
@@ -56,7 +75,8 @@ AttnPlan make_attn_plan(const lsa_shape& s, int32_t target) {
 PartialLayout partial_layout(const lsa_shape& s, const AttnPlan& p) {
   PartialLayout L;
   const size_t rows = static_cast<size_t>(p.ws_rows) * static_cast<size_t>(s.num_q_heads);
-  L.m_off = 0;
+  L.cnt_off = 0;  // same place for every shape (see kCounterStreams)
+  L.m_off = static_cast<size_t>(kCounterStreams) * sizeof(int32_t);
   L.l_off = L.m_off + align256(rows * sizeof(float));
   L.o_off = L.l_off + align256(rows * sizeof(float));
   L.total = L.o_off + align256(rows * static_cast<size_t>(s.head_dim_v) * sizeof(float));
@@ -198,12 +218,12 @@ __global__ __launch_bounds__(MW * kWave) void merge_kernel(AttnArgs a, int32_t n
 
 }  // namespace
 
-hipError_t launch_attn_merge(const lsa_shape& s, const AttnArgs& a, hipStream_t st) {
+hipError_t launch_attn_merge(const lsa_shape& s, const AttnArgs& a, const AttnPlan& plan,
+                             hipStream_t st) {
   const int32_t nblk = (s.num_q_heads * s.head_dim_v + kWave - 1) / kWave;
   const int64_t grid = static_cast<int64_t>(nblk) * s.batch;
   // one wave per workgroup while a stream has a couple of groups of partials
   // on average, eight when streams have many (a long single stream)
-  const AttnPlan plan = make_attn_plan(s, a.target);
   const bool one = plan.grid <= static_cast<int64_t>(2 * kMergeBatch) * s.batch;
   // a block of 64 output elements lies inside one head when dv is a multiple of 64
   const bool hu = s.head_dim_v % kWave == 0;

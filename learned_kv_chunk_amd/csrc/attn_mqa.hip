@@ -25,9 +25,11 @@
 // load hints that suit it best; more loads in flight per CU only lengthen
 // the memory queues (a third register set per wave: 32.4 us).  The
 // waves of a team take interleaved tiles of the workgroup's run, then merge
-// their (max, sum, output) states through LDS into one partial result, which
-// the merge kernel (attn_common.hip) combines with the stream's other
-// partials.
+// their (max, sum, output) states through LDS into one partial result.  The
+// stream's partials are combined by the stream's last workgroup to finish
+// (arrival counter with release / acquire ordering at device scope,
+// merge_stream_block), so attention is one launch; a stream served by a
+// single workgroup writes its output directly.
 #include <math.h>
 
 #include "lsa_internal.hpp"
@@ -359,21 +361,61 @@ __global__ __launch_bounds__(mqa_waves<NHG>() * kWave, 1) void attn_mqa_kernel(
       merge_state<D, NHG>(smem + (grp * (WPG / 2) + wl) * L::kStateBytes, m, l, o, lane);
   }
   const int64_t wg = blockIdx.x;
+  if (a.fuse_merge && run.wgs == 1) {
+    // the stream's only workgroup holds its whole softmax state: normalise
+    // and write the output directly, no partial and no merge
+    if (wl == 0) {
+#pragma unroll
+      for (int hg = 0; hg < NHG; ++hg) {
+        const int head = head0 + hg * 16;
+        if (head >= H) continue;
+        const float lt = xor32_sum(xor16_sum(l[hg]));
+        const float inv = lt > 0.f ? 1.f / lt : 0.f;
+        const int64_t orow = static_cast<int64_t>(b) * H + head;
+        if (g == 0 && a.lse != nullptr)
+          a.lse[orow] = lt > 0.f ? (m[hg] + log2f(lt)) * 0.69314718055994530942f : -INFINITY;
+#pragma unroll
+        for (int cg = 0; cg < D / 16; ++cg)
+          *reinterpret_cast<f32x4*>(a.out + orow * D + cg * 16 + 4 * g) = o[hg][cg] * inv;
+      }
+    }
+    return;
+  }
   if (wl == 0) {
 #pragma unroll
     for (int hg = 0; hg < NHG; ++hg) {
       const int head = head0 + hg * 16;
       if (head >= H) continue;
       const float lt = xor32_sum(xor16_sum(l[hg]));
-      if (g == 0) {
-        a.ws_m[wg * H + head] = m[hg];
-        a.ws_l[wg * H + head] = lt;
-      }
+      float* om = a.ws_m + wg * H + head;
+      float* ol = a.ws_l + wg * H + head;
+      float* oo = a.ws_o + (wg * H + head) * D + 4 * g;
+      if (a.fuse_merge) {  // the stream's last workgroup reads these at device scope
+        if (g == 0) {
+          store_coherent(om, m[hg]);
+          store_coherent(ol, lt);
+        }
 #pragma unroll
-      for (int cg = 0; cg < D / 16; ++cg)
-        *reinterpret_cast<f32x4*>(a.ws_o + (wg * H + head) * D + cg * 16 + 4 * g) = o[hg][cg];
+        for (int cg = 0; cg < D / 16; ++cg)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) store_coherent(oo + cg * 16 + j, o[hg][cg][j]);
+      } else {
+        if (g == 0) {
+          *om = m[hg];
+          *ol = lt;
+        }
+#pragma unroll
+        for (int cg = 0; cg < D / 16; ++cg) *reinterpret_cast<f32x4*>(oo + cg * 16) = o[hg][cg];
+      }
     }
   }
+  if (!a.fuse_merge) return;
+  // the stream's last workgroup to finish merges its partials (no merge launch)
+  __shared__ int32_t s_last;
+  if (!arrive_last(a, b, run.wgs, &s_last)) return;
+  merge_stream_block<NW * kWave>(a, b, wg - run.local, run.wgs);
+  if (tid == 0)
+    __hip_atomic_store(a.counters + b, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <int D>

@@ -75,13 +75,28 @@ lsa_status hip_status(hipError_t e) { return e == hipSuccess ? LSA_OK : LSA_ERR_
 
 // Enqueue the attention partial kernel and the merge; arguments validated.
 // ev_begin / ev_end (may be null) bracket the partial kernel.
-lsa_status enqueue_attention(const lsa_shape& s, int32_t kv_mode, const void* q, const void* kbase,
-                             const void* vbase, const int64_t* tok_off, const int32_t* sel_idx,
+// The split-KV plan of a validated attention shape on the current device and
+// the workspace layout it implies (computed once per call).
+struct AttnSetup {
+  AttnPlan plan;
+  PartialLayout layout;
+};
+
+AttnSetup attn_setup(const lsa_shape& s) {
+  AttnSetup x;
+  x.plan = make_attn_plan(s, device_cu_count());
+  x.layout = partial_layout(s, x.plan);
+  return x;
+}
+
+lsa_status enqueue_attention(const lsa_shape& s, const AttnSetup& setup, int32_t kv_mode,
+                             const void* q, const void* kbase, const void* vbase,
+                             const int64_t* tok_off, const int32_t* sel_idx,
                              const int32_t* sel_off, float* out, float* lse, void* ws,
                              hipStream_t st, void* ev_begin = nullptr, void* ev_end = nullptr,
                              const int64_t* seq_len = nullptr, bool partial_only = false) {
-  const AttnPlan plan = make_attn_plan(s, device_cu_count());
-  const PartialLayout pl = partial_layout(s, plan);
+  const AttnPlan& plan = setup.plan;
+  const PartialLayout& pl = setup.layout;
   AttnArgs a;
   a.q = q;
   a.k = kbase;
@@ -95,6 +110,22 @@ lsa_status enqueue_attention(const lsa_shape& s, int32_t kv_mode, const void* q,
   a.ws_m = reinterpret_cast<float*>(static_cast<char*>(ws) + pl.m_off);
   a.ws_l = reinterpret_cast<float*>(static_cast<char*>(ws) + pl.l_off);
   a.ws_o = reinterpret_cast<float*>(static_cast<char*>(ws) + pl.o_off);
+  a.counters = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + pl.cnt_off);
+  // the MQA kernel merges each stream's partials in its last workgroup; the
+  // other kernels leave that to the merge launch
+  // when streams average at most eight workgroups (so a last workgroup reads
+  // few partials) and H * dv <= 8 * 256 (one load round trip covers them);
+  // otherwise the merge launch reads them with many workgroups in parallel.
+  // Measured: 32 ragged streams (eight workgroups each on average) 82.1 ->
+  // 79.2 us per step fused, their merges overlapping other streams' tiles;
+  // 16 x 128K (sixteen each, all streams ending together) 42.9 -> 45.2 us
+  // fused, so that shape keeps the merge launch.
+  const int64_t wgs_expected =
+      plan.per > 0 ? (s.total_k * plan.tiles_per_chunk + plan.per - 1) / plan.per : plan.target;
+  const bool fused = mqa_attn_supported(s) && !mla_attn_supported(s) && !partial_only &&
+                     s.batch <= kCounterStreams && s.num_q_heads * s.head_dim_v <= 8 * 256 &&
+                     wgs_expected <= 8 * static_cast<int64_t>(s.batch);
+  a.fuse_merge = fused ? 1 : 0;
   a.B = s.batch;
   a.H = s.num_q_heads;
   a.dqk = s.head_dim_qk;
@@ -117,8 +148,8 @@ lsa_status enqueue_attention(const lsa_shape& s, int32_t kv_mode, const void* q,
   if (e != hipSuccess) return LSA_ERR_HIP;
   if (ev_end && hipEventRecord(static_cast<hipEvent_t>(ev_end), st) != hipSuccess)
     return LSA_ERR_HIP;
-  if (partial_only) return LSA_OK;
-  return hip_status(launch_attn_merge(s, a, st));
+  if (partial_only || fused) return LSA_OK;
+  return hip_status(launch_attn_merge(s, a, plan, st));
 }
 
 }  // namespace
@@ -289,20 +320,23 @@ static lsa_status check_attn_io(const lsa_shape* shape, int32_t kv_mode, const v
   return LSA_OK;
 }
 
-// Workspace of a validated attention shape: present, 256-byte aligned, large enough.
-static lsa_status check_workspace(const lsa_shape* shape, const void* ws, size_t ws_bytes) {
+// Workspace of a validated attention call: present, 256-byte aligned, large enough.
+static lsa_status check_workspace(const AttnSetup& setup, const void* ws, size_t ws_bytes) {
   if (!ws || !aligned(ws, 256)) return LSA_ERR_INVALID_ARGUMENT;
-  if (ws_bytes < lsa_workspace_bytes(shape)) return LSA_ERR_WORKSPACE_TOO_SMALL;
+  if (ws_bytes < setup.layout.total) return LSA_ERR_WORKSPACE_TOO_SMALL;
   return LSA_OK;
 }
 
+// Checks of an attention call; on success *setup holds its plan and layout.
 static lsa_status check_attn_args(const lsa_shape* shape, int32_t kv_mode, const void* q,
                                   const void* kb, const void* vb, const int64_t* tok_off,
                                   const int32_t* sel_idx, const int32_t* sel_off, const float* out,
-                                  const float* lse, const void* ws, size_t ws_bytes) {
+                                  const float* lse, const void* ws, size_t ws_bytes,
+                                  AttnSetup* setup) {
   const lsa_status st = check_attn_io(shape, kv_mode, q, kb, vb, tok_off, sel_idx, sel_off, out, lse);
   if (st != LSA_OK) return st;
-  return check_workspace(shape, ws, ws_bytes);
+  *setup = attn_setup(*shape);
+  return check_workspace(*setup, ws, ws_bytes);
 }
 
 // Device address of page-locked host memory, or null when `p` is not such memory.
@@ -356,12 +390,13 @@ lsa_status lsa_sparse_decode_attn(const lsa_shape* shape, int32_t kv_mode, const
                                   const int64_t* tok_off_dev, const int32_t* sel_idx_dev,
                                   const int32_t* sel_off_dev, float* out_dev, float* lse_dev,
                                   void* workspace_dev, size_t workspace_bytes, void* hip_stream) {
+  AttnSetup setup;
   lsa_status st = check_attn_args(shape, kv_mode, q_dev, k_base_dev, v_base_dev, tok_off_dev,
                                   sel_idx_dev, sel_off_dev, out_dev, lse_dev, workspace_dev,
-                                  workspace_bytes);
+                                  workspace_bytes, &setup);
   if (st != LSA_OK) return st;
   (void)hipGetLastError();
-  return enqueue_attention(*shape, kv_mode, q_dev, k_base_dev, v_base_dev, tok_off_dev,
+  return enqueue_attention(*shape, setup, kv_mode, q_dev, k_base_dev, v_base_dev, tok_off_dev,
                            sel_idx_dev, sel_off_dev, out_dev, lse_dev, workspace_dev,
                            static_cast<hipStream_t>(hip_stream));
 }
@@ -373,13 +408,14 @@ lsa_status lsa_sparse_decode_attn_varlen(const lsa_shape* shape, int32_t kv_mode
                                          const int32_t* sel_off_dev, float* out_dev,
                                          float* lse_dev, void* workspace_dev,
                                          size_t workspace_bytes, void* hip_stream) {
+  AttnSetup setup;
   lsa_status st = check_attn_args(shape, kv_mode, q_dev, k_base_dev, v_base_dev, base_off_dev,
                                   sel_idx_dev, sel_off_dev, out_dev, lse_dev, workspace_dev,
-                                  workspace_bytes);
+                                  workspace_bytes, &setup);
   if (st != LSA_OK) return st;
   if (!seq_len_dev || !aligned(seq_len_dev, 8)) return LSA_ERR_INVALID_ARGUMENT;
   (void)hipGetLastError();
-  return enqueue_attention(*shape, kv_mode, q_dev, k_base_dev, v_base_dev, base_off_dev,
+  return enqueue_attention(*shape, setup, kv_mode, q_dev, k_base_dev, v_base_dev, base_off_dev,
                            sel_idx_dev, sel_off_dev, out_dev, lse_dev, workspace_dev,
                            static_cast<hipStream_t>(hip_stream), nullptr, nullptr, seq_len_dev);
 }
@@ -456,8 +492,8 @@ static lsa_status check_step(const lsa_shape* shape, const lsa_step_args& x) {
 }
 
 // Enqueues a validated decode step with its split-KV partials in `ws`.
-static lsa_status enqueue_step(const lsa_shape* shape, const lsa_step_args& x, void* ws,
-                               void* hip_stream) {
+static lsa_status enqueue_step(const lsa_shape* shape, const AttnSetup& setup,
+                               const lsa_step_args& x, void* ws, void* hip_stream) {
   const bool pool = x.materialize_pool != 0;
   const hipStream_t hs = static_cast<hipStream_t>(hip_stream);
   (void)hipGetLastError();
@@ -476,7 +512,7 @@ static lsa_status enqueue_step(const lsa_shape* shape, const lsa_step_args& x, v
         return LSA_ERR_HIP;
     }
   }
-  return enqueue_attention(*shape, pool ? LSA_KV_POOL : LSA_KV_STORE, x.q_dev,
+  return enqueue_attention(*shape, setup, pool ? LSA_KV_POOL : LSA_KV_STORE, x.q_dev,
                            pool ? x.k_pool_dev : x.k_store_dev,
                            pool ? x.v_pool_dev : x.v_store_dev, x.tok_off_dev, x.sel_idx_dev,
                            x.sel_off_dev, x.out_dev, x.lse_dev, ws, hs, x.ev_attn_begin,
@@ -504,9 +540,10 @@ lsa_status lsa_decode_step(const lsa_shape* shape, const lsa_step_args* args, vo
   if (st != LSA_OK) return st;
   st = check_step(shape, x);
   if (st != LSA_OK) return st;
-  st = check_workspace(shape, workspace_dev, workspace_bytes);
+  const AttnSetup setup = attn_setup(*shape);
+  st = check_workspace(setup, workspace_dev, workspace_bytes);
   if (st != LSA_OK) return st;
-  return enqueue_step(shape, x, workspace_dev, hip_stream);
+  return enqueue_step(shape, setup, x, workspace_dev, hip_stream);
 }
 
 // ---------------------------------------------------------------------------
@@ -549,13 +586,14 @@ lsa_status lsa_decode_step_static(const lsa_shape* shape, const lsa_step_args* a
   if (st != LSA_OK) return st;
   st = check_step(shape, x);
   if (st != LSA_OK) return st;
-  if (lsa_workspace_bytes(shape) > LSA_STATIC_SCRATCH_BYTES) return LSA_ERR_WORKSPACE_TOO_SMALL;
+  const AttnSetup setup = attn_setup(*shape);
+  if (setup.layout.total > LSA_STATIC_SCRATCH_BYTES) return LSA_ERR_WORKSPACE_TOO_SMALL;
   void* ws = static_scratch_address();
   if (ws == nullptr) {
     (void)hipGetLastError();
     return LSA_ERR_HIP;
   }
-  return enqueue_step(shape, x, ws, hip_stream);
+  return enqueue_step(shape, setup, x, ws, hip_stream);
 }
 
 lsa_status lsa_check_tables(const lsa_shape* shape, const int64_t* tok_off_dev,
@@ -582,12 +620,13 @@ lsa_status lsa_bench_attention_partial(const lsa_shape* shape, int32_t kv_mode, 
                                        size_t workspace_bytes, void* hip_stream) {
   // the checks of lsa_sparse_decode_attn, with the workspace standing in for
   // the outputs it does not write
+  AttnSetup setup;
   lsa_status st = check_attn_args(shape, kv_mode, q_dev, k_base_dev, v_base_dev, tok_off_dev,
                                   sel_idx_dev, sel_off_dev, static_cast<const float*>(workspace_dev),
-                                  nullptr, workspace_dev, workspace_bytes);
+                                  nullptr, workspace_dev, workspace_bytes, &setup);
   if (st != LSA_OK) return st;
   (void)hipGetLastError();
-  return enqueue_attention(*shape, kv_mode, q_dev, k_base_dev, v_base_dev, tok_off_dev,
+  return enqueue_attention(*shape, setup, kv_mode, q_dev, k_base_dev, v_base_dev, tok_off_dev,
                            sel_idx_dev, sel_off_dev, nullptr, nullptr, workspace_dev,
                            static_cast<hipStream_t>(hip_stream), nullptr, nullptr, nullptr, true);
 }

@@ -48,13 +48,20 @@ struct AttnPlan {
 
 // `target` is the number of compute units of the device that will run it.
 AttnPlan make_attn_plan(const lsa_shape& s, int32_t target);
-// Compute units of the current device (host).
+// Compute units of the current device (host; queried once per device).
 int32_t device_cu_count();
 
-// Workspace layout: split-KV partials m[rows][H], l[rows][H] (fp32, log2
-// domain max and sum) and o[rows][H][dv] (fp32, unnormalised), rows = ws_rows.
+// Workspace layout: first the arrival counters of the kernels that merge a
+// stream's partials in its last workgroup, int32 [kCounterStreams] at offset
+// 0 for every shape (so that no shape's partials ever overlap another shape's
+// counters in a shared workspace; they are zero between calls, every launch
+// leaves them as it found them); then the split-KV partials m[rows][H],
+// l[rows][H] (fp32, log2 domain max and sum) and o[rows][H][dv] (fp32,
+// unnormalised), rows = ws_rows.  Batches of more than kCounterStreams
+// streams merge in a separate launch.
+constexpr int32_t kCounterStreams = 16384;
 struct PartialLayout {
-  size_t m_off, l_off, o_off, total;
+  size_t m_off, l_off, o_off, cnt_off, total;
 };
 PartialLayout partial_layout(const lsa_shape& s, const AttnPlan& p);
 
@@ -71,6 +78,8 @@ struct AttnArgs {
   float* ws_m;
   float* ws_l;
   float* ws_o;
+  int32_t* counters;      // per-stream arrival counters (zero between calls)
+  int32_t fuse_merge;     // 1: the partial kernel merges each stream itself
   int32_t B, H, dqk, dv, C;
   int32_t k_row;          // elements between consecutive K rows
   int32_t v_row;          // elements between consecutive V rows
@@ -120,7 +129,8 @@ hipError_t launch_attn_mla(const lsa_shape& s, const AttnArgs& a, int64_t grid, 
 bool portable_attn_supported(const lsa_shape& s);
 hipError_t launch_attn_portable(const lsa_shape& s, const AttnArgs& a, int64_t grid,
                                 hipStream_t st);
-hipError_t launch_attn_merge(const lsa_shape& s, const AttnArgs& a, hipStream_t st);
+hipError_t launch_attn_merge(const lsa_shape& s, const AttnArgs& a, const AttnPlan& plan,
+                             hipStream_t st);
 hipError_t launch_check_tables(const lsa_shape& s, const int64_t* tok_off,
                                const int32_t* chunk_off, const int32_t* sel_off,
                                const int32_t* sel_idx, int32_t ascending, int32_t* flag,
@@ -248,6 +258,8 @@ struct AttnRun {
   int32_t t_end;
   int32_t sel0;        // sel_off[b]
   int32_t slot_first;  // the run's first kept chunk, counted within the stream
+  int32_t local;       // this workgroup's index among the stream's
+  int32_t wgs;         // the stream's workgroups (partials)
   int64_t tb;          // tok_off[b]
   int64_t len;         // L_b
 };
@@ -266,8 +278,10 @@ __device__ __forceinline__ AttnRun attn_prologue(const AttnArgs& a, int32_t* s_s
     StreamSplit sp;
     find_stream_of_wg(SelCsr{a.sel_off, a.uni_k}, a.B, tpc, a.per, a.target, blockIdx.x, &b,
                       &local, &sp, &sel0);
-    AttnRun r = {b, 0, 0, 0, 0, 0, 0};
+    AttnRun r = {b, 0, 0, 0, 0, 0, 0, 0, 0};
     if (b >= 0) {
+      r.local = local;
+      r.wgs = sp.wgs;
       r.t_begin = local * sp.per;
       r.t_end = min(sp.tiles, (local + 1) * sp.per);
       r.sel0 = sel0;
@@ -290,6 +304,8 @@ __device__ __forceinline__ AttnRun attn_prologue(const AttnArgs& a, int32_t* s_s
   u.t_end = __builtin_amdgcn_readfirstlane(v.t_end);
   u.sel0 = __builtin_amdgcn_readfirstlane(v.sel0);
   u.slot_first = __builtin_amdgcn_readfirstlane(v.slot_first);
+  u.local = __builtin_amdgcn_readfirstlane(v.local);
+  u.wgs = __builtin_amdgcn_readfirstlane(v.wgs);
   u.tb = uniform_i64(v.tb);
   u.len = uniform_i64(v.len);
   return u;
@@ -315,6 +331,101 @@ __device__ __forceinline__ void stream_wg_range(SelCsr sel_off, int32_t B, int32
   }
   *first_out = static_cast<int32_t>(wave_sum_u32(acc));
   *count_out = stream_split(sel_off, b, tpc, per, target, total_tiles).wgs;
+}
+
+// Device-scope (all XCDs' L2s) coherent stores of the split partials that a
+// stream's last workgroup merges: they write through to the device's
+// coherence point (global_store with the sc1 bit), so publishing a partial
+// needs no write-back of the L2.
+__device__ __forceinline__ void store_coherent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Merge of one stream's split-KV partials by the NT threads of the stream's
+// last workgroup to finish (after arrive_last): rows first .. first + count -
+// 1 of the workspace are combined into out[b] and lse[b].  Thread i owns
+// EPT = 8 consecutive output elements of the flattened [H][dv] row (the
+// caller guarantees H * dv <= 8 * NT and dv % 8 == 0, so the eight share a
+// head), and the loads of a batch of kBlockMergeBatch partials (two 16-byte
+// vectors, the maximum and the sum each) are all issued before any is used:
+// one memory round trip per batch.  Partials are folded in row order, one
+// rescale per batch, so the result is a deterministic function of the plan.
+constexpr int kBlockMergeBatch = 16;
+
+template <int NT>
+__device__ __forceinline__ void merge_stream_block(const AttnArgs& a, int32_t b, int64_t first,
+                                                   int32_t count) {
+  typedef float f4 __attribute__((ext_vector_type(4)));
+  const int32_t H = a.H, dv = a.dv, elems = H * dv;
+  const int32_t e = static_cast<int32_t>(threadIdx.x) * 8;
+  if (e >= elems) return;
+  const int32_t h = e / dv;
+  float m = -INFINITY, l = 0.f;
+  f4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
+  for (int32_t p0 = 0; p0 < count; p0 += kBlockMergeBatch) {
+    f4 o0[kBlockMergeBatch], o1[kBlockMergeBatch];
+    float mv[kBlockMergeBatch], lv[kBlockMergeBatch];
+#pragma unroll
+    for (int u = 0; u < kBlockMergeBatch; ++u) {
+      const int64_t row = first + min(p0 + u, count - 1);
+      const f4* src = reinterpret_cast<const f4*>(a.ws_o + row * elems + e);
+      o0[u] = src[0];
+      o1[u] = src[1];
+      mv[u] = a.ws_m[row * H + h];
+      lv[u] = a.ws_l[row * H + h];
+    }
+    float mb = m;
+#pragma unroll
+    for (int u = 0; u < kBlockMergeBatch; ++u)
+      if (p0 + u < count) mb = fmaxf(mb, mv[u]);
+    const float mu = (mb == -INFINITY) ? 0.f : mb;
+    const float f = __builtin_amdgcn_exp2f(m - mu);
+    acc0 *= f;
+    acc1 *= f;
+    l *= f;
+#pragma unroll
+    for (int u = 0; u < kBlockMergeBatch; ++u) {
+      if (p0 + u < count) {
+        const float w = __builtin_amdgcn_exp2f(mv[u] - mu);
+        acc0 += o0[u] * w;
+        acc1 += o1[u] * w;
+        l = fmaf(lv[u], w, l);
+      }
+    }
+    m = mb;
+  }
+  const int64_t orow = static_cast<int64_t>(b) * H + h;
+  const int32_t c = e - h * dv;
+  const float inv = l > 0.f ? 1.f / l : 0.f;
+  f4* dst = reinterpret_cast<f4*>(a.out + orow * dv + c);
+  dst[0] = acc0 * inv;
+  dst[1] = acc1 * inv;
+  if (c == 0 && a.lse != nullptr)
+    a.lse[orow] = l > 0.f ? (m + log2f(l)) * 0.69314718055994530942f : -INFINITY;
+}
+
+// Arrival of a workgroup whose partial for stream b has been written with
+// store_coherent: every wave waits until its own stores are acknowledged at
+// the device's coherence point, then one thread increments the stream's
+// counter (a device-scope atomic).  The workgroup that sees the count reach
+// wgs - 1 arrived last: every other partial is already at the coherence
+// point, and an acquire at device scope (an invalidation of this XCD's
+// caches) makes its plain loads find them.  Returns true in every thread of
+// that workgroup, which resets the counter once it has read the partials.
+// s_flag: one LDS word.
+__device__ __forceinline__ bool arrive_last(const AttnArgs& a, int32_t b, int32_t wgs,
+                                            int32_t* s_flag) {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int32_t old =
+        __hip_atomic_fetch_add(a.counters + b, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *s_flag = (old == wgs - 1) ? 1 : 0;
+  }
+  __syncthreads();
+  if (*s_flag == 0) return false;
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  return true;
 }
 
 }  // namespace lsa

@@ -62,17 +62,40 @@ class DeviceWorkload:
     k_pool: Optional[torch.Tensor] = None
     v_pool: Optional[torch.Tensor] = None
     _q: dict = dataclasses.field(default_factory=dict)
+    _prepared: dict = dataclasses.field(default_factory=dict)
 
     def queries(self, step: int) -> torch.Tensor:
         if step not in self._q:
             self._q[step] = _to_device(self.w.queries(step), self.K.device)
         return self._q[step]
 
+    def prepared(self, materialize_pool: bool, reindex_every: int) -> lsa.PreparedStep:
+        """The step's arguments marshalled once (cached per pool mode and
+        re-index interval)."""
+        key = (bool(materialize_pool), int(reindex_every))
+        p = self._prepared.get(key)
+        if p is None:
+            p = lsa.PreparedStep(self.shape, q_idx=self.q_idx, emb=self.emb,
+                                 chunk_off=self.chunk_off, scores=self.scores,
+                                 sel_off=self.sel_off, sel_idx=self.sel_idx, q=self.queries(0),
+                                 k_store=self.K, v_store=self.V, tok_off=self.tok_off,
+                                 out=self.out, lse=self.lse, workspace=self.workspace,
+                                 materialize_pool=materialize_pool, k_pool=self.k_pool,
+                                 v_pool=self.v_pool, reindex_every=reindex_every)
+            self._prepared[key] = p
+        return p
+
     def step(self, t: int, reindex: bool = False, materialize_pool: bool = False,
              ev_begin=None, ev_end=None, q: Optional[torch.Tensor] = None,
              reindex_every: int = 0) -> None:
         """Decode step t.  reindex_every > 0: the library's schedule decides
-        whether step t re-indexes (``reindex`` is ignored)."""
+        whether step t re-indexes (``reindex`` is ignored), through the
+        prepared arguments."""
+        if reindex_every > 0:
+            self.prepared(materialize_pool, reindex_every).run(
+                t, q=self.queries(t) if q is None else q, ev_attn_begin=ev_begin,
+                ev_attn_end=ev_end)
+            return
         lsa.decode_step(self.shape, q_idx=self.q_idx, emb=self.emb, chunk_off=self.chunk_off,
                         scores=self.scores, sel_off=self.sel_off, sel_idx=self.sel_idx,
                         q=self.queries(t) if q is None else q, k_store=self.K, v_store=self.V,

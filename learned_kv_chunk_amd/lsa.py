@@ -199,8 +199,8 @@ def workspace_bytes(shape: ProblemShape) -> int:
 
 
 def allocate_workspace(shape: ProblemShape, device) -> torch.Tensor:
-    """Workspace for lsa_sparse_decode_attn / lsa_decode_step (its contents
-    need no initialisation; zero-filled for reproducible debugging)."""
+    """Workspace for lsa_sparse_decode_attn / lsa_decode_step, zero-filled
+    as the library requires before first use (calls leave it zeroed)."""
     n = workspace_bytes(shape)
     if n == 0:
         raise LsaError(LSA_ERR_UNSUPPORTED, "lsa_workspace_bytes")
@@ -217,8 +217,11 @@ def _ptr(t: Optional[torch.Tensor]):
 
 
 def _stream(stream=None):
-    s = stream if stream is not None else torch.cuda.current_stream()
-    return ctypes.c_void_p(s.cuda_stream)
+    if stream is not None:
+        return ctypes.c_void_p(stream.cuda_stream)
+    # torch's current HIP stream of the current device (the capture stream
+    # under graph capture), read without building a Stream object
+    return ctypes.c_void_p(torch._C._cuda_getCurrentRawStream(torch.cuda.current_device()))
 
 
 def _dev(t: torch.Tensor, name: str, dtype=None, ndim=None):
@@ -575,28 +578,89 @@ def _step_args(shape: ProblemShape, q_idx, emb, chunk_off, scores, sel_off, sel_
                ev_attn_begin, ev_attn_end, step, reindex_every, where) -> StepArgs:
     if reindex_every < 0 or (reindex_every > 0 and step < 0):
         raise ValueError("reindex_every must be >= 0 and step >= 0")
-    if reindex_every > 0:
-        reindex = reindex_due(step, reindex_every)
+    # with the schedule in the library's hands every step may re-index: the
+    # scoring inputs are always checked and passed
+    scoring = bool(reindex) or reindex_every > 0
     if _DEBUG_CHECKS:
-        _debug_check(shape, chunk_off, sel_off, tok_off, None if reindex else sel_idx, where)
+        due = reindex_due(step, reindex_every) if reindex_every > 0 else bool(reindex)
+        _debug_check(shape, chunk_off, sel_off, tok_off, None if due else sel_idx, where)
     for name, t, dt in [("q", q, shape.dtype), ("k_store", k_store, shape.dtype),
                         ("tok_off", tok_off, torch.int64), ("sel_off", sel_off, torch.int32),
                         ("sel_idx", sel_idx, torch.int32), ("out", out, torch.float32)]:
         _dev(t, name, dt)
     if lse is not None:
         _dev(lse, "lse", torch.float32)
-    if reindex:
+    if scoring:
         for name, t, dt in [("q_idx", q_idx, shape.dtype), ("emb", emb, shape.dtype),
                             ("chunk_off", chunk_off, torch.int32),
                             ("scores", scores, torch.float32)]:
             _dev(t, name, dt)
     return StepArgs(
-        _ptr(q_idx) if reindex else None, _ptr(emb) if reindex else None,
-        _ptr(chunk_off) if reindex else None, _ptr(scores) if reindex else None,
+        _ptr(q_idx) if scoring else None, _ptr(emb) if scoring else None,
+        _ptr(chunk_off) if scoring else None, _ptr(scores) if scoring else None,
         _ptr(sel_off), _ptr(sel_idx), _ptr(q), _ptr(k_store), _ptr(v_store), _ptr(tok_off),
         _ptr(k_pool), _ptr(v_pool), _ptr(out), _ptr(lse), int(bool(reindex)),
         int(bool(materialize_pool)), _event_ptr(ev_attn_begin), _event_ptr(ev_attn_end),
         int(reindex_every), 0, int(step))
+
+
+class PreparedStep:
+    """The arguments of lsa_decode_step (or, static=True, of
+    lsa_decode_step_static) checked and marshalled once, for a decode loop
+    that issues a step over the same buffers again and again: run() only sets
+    the step number, the decode queries and the optional events, then calls
+    the library (the re-index schedule, reindex_every >= 1, stays the
+    library's).  Argument marshalling only, as everywhere in this module."""
+
+    def __init__(self, shape: ProblemShape, *, q_idx, emb, chunk_off, scores, sel_off, sel_idx,
+                 q, k_store, v_store, tok_off, out, lse, workspace=None,
+                 materialize_pool: bool = False, k_pool=None, v_pool=None,
+                 reindex_every: int = 1, static: bool = False):
+        if reindex_every < 1:
+            raise ValueError("a prepared step runs the library's schedule: reindex_every >= 1")
+        self.shape = shape
+        self._args = _step_args(shape, q_idx, emb, chunk_off, scores, sel_off, sel_idx, q,
+                                k_store, v_store, tok_off, out, lse, True, materialize_pool,
+                                k_pool, v_pool, None, None, 0, reindex_every,
+                                "lsa_decode_step")
+        self._tables = (chunk_off, sel_off, tok_off, sel_idx)
+        self._keep = [q_idx, emb, scores, q, k_store, v_store, out, lse, k_pool, v_pool,
+                      workspace]
+        self._shape_c = shape.c()
+        self._shape_ref = ctypes.byref(self._shape_c)
+        self._args_ref = ctypes.byref(self._args)
+        self._static = static
+        if static:
+            self._fn = library().lsa_decode_step_static
+        else:
+            _dev(workspace, "workspace", torch.uint8)
+            self._fn = library().lsa_decode_step
+            self._ws = ctypes.c_void_p(workspace.data_ptr())
+            self._ws_n = workspace.numel()
+        self._q = q
+
+    def run(self, step: int, q=None, ev_attn_begin=None, ev_attn_end=None, stream=None):
+        a = self._args
+        if step < 0:
+            raise ValueError("step must be >= 0")
+        a.step = step
+        if q is not None and q is not self._q:
+            if not q.is_cuda or q.dtype != self.shape.dtype or not q.is_contiguous():
+                raise ValueError("q must be a contiguous device tensor of the shape's dtype")
+            a.q_dev = q.data_ptr()
+            self._q = q
+        a.ev_attn_begin = _event_ptr(ev_attn_begin)
+        a.ev_attn_end = _event_ptr(ev_attn_end)
+        if _DEBUG_CHECKS:
+            co, so, to, si = self._tables
+            due = reindex_due(step, a.reindex_every)
+            _debug_check(self.shape, co, so, to, None if due else si, "PreparedStep.run")
+        if self._static:
+            st = self._fn(self._shape_ref, self._args_ref, _stream(stream))
+        else:
+            st = self._fn(self._shape_ref, self._args_ref, self._ws, self._ws_n, _stream(stream))
+        if st != LSA_OK:
+            raise LsaError(st, "lsa_decode_step_static" if self._static else "lsa_decode_step")
 
 
 def decode_step(shape: ProblemShape, *, q_idx, emb, chunk_off, scores, sel_off, sel_idx, q,

@@ -409,15 +409,20 @@ def test_hot_token_dominates():
 
 
 def test_workspace_is_reusable_across_calls_and_shapes():
-    # one workspace serves calls of different shapes, repeatedly
-    wa, da = small_workload("cfg2")
-    wb, db = small_workload("cfg5")
-    big = torch.zeros(max(da.workspace.numel(), db.workspace.numel()), dtype=torch.uint8,
+    # one workspace serves calls of different shapes, repeatedly: head counts
+    # and value widths differ (so one shape's partials cover bytes where
+    # another shape's partials start), some kernels merge through the
+    # per-stream arrival counters and some through a merge launch; the
+    # counters stay at zero between calls
+    cases = []
+    for name in ["cfg2", "cfg5", "cfg3", "cfg4"]:
+        w, d = small_workload(name)
+        _, _, out_r, lse_r = P.run_phases(d, 0)
+        cases.append((d, out_r, lse_r))
+    big = torch.zeros(max(d.workspace.numel() for d, _, _ in cases), dtype=torch.uint8,
                       device="cuda")
-    _, _, out_a, lse_a = P.run_phases(da, 0)
-    _, _, out_b, lse_b = P.run_phases(db, 0)
     for _ in range(3):
-        for d, out_ref, lse_ref in [(da, out_a, lse_a), (db, out_b, lse_b)]:
+        for d, out_ref, lse_ref in cases:
             out, lse = lsa.sparse_decode_attn(d.shape, d.queries(0), d.K, d.V, d.tok_off,
                                               d.sel_idx, d.sel_off, workspace=big)
             d.step(0, reindex=True)
@@ -475,3 +480,35 @@ def test_more_than_64_streams(uniform):
     P.check_selection(w, s_gpu, sel, s_ref)
     o_ref, l_ref = P.oracle_attention_on(w, 0, sel)
     P.check_attention("bf16", out, lse, o_ref, l_ref)
+
+
+# ----------------------------------------------------------------------------- in-kernel merge
+@pytest.mark.parametrize("heads,dim", [(16, 128), (8, 128), (32, 64), (16, 64)])
+def test_streams_merged_by_their_last_workgroup(heads, dim):
+    # 40 ragged streams average at most eight workgroups each, so the MQA
+    # kernel merges every stream in the last of its workgroups to finish
+    # (arrival counters in the workspace) and a one-workgroup stream writes
+    # its output directly; results match the oracle, reruns are bit-identical
+    # (the counters are back at zero after every call) and equal the same
+    # batch through the merge launch (a fixed split with many workgroups per
+    # stream) up to the weights' rounding.
+    rng = np.random.default_rng(40 + heads + dim)
+    lengths = tuple(int(x) for x in rng.integers(40, 64 * 120, size=40))
+    cfg = wl.small_variant("cfg2", lengths=lengths, n_needles=0, num_q_heads=heads,
+                           head_dim_qk=dim, head_dim_v=dim, keep_round_up=True)
+    w = wl.make_workload(cfg)
+    d = dev.upload(w, "cuda")
+    s_gpu, sel, out, lse = P.run_phases(d, 0)
+    o_ref, l_ref = P.oracle_attention_on(w, 0, sel)
+    print(heads, dim, P.check_attention("bf16", out, lse, o_ref, l_ref))
+    for _ in range(3):
+        _, _, out2, lse2 = P.run_phases(d, 0)
+        np.testing.assert_array_equal(out2, out)
+        np.testing.assert_array_equal(lse2, lse)
+    s = dev.problem_shape(w, attn_tiles_per_block=1)   # > 8 workgroups per stream: merge launch
+    o3, l3 = lsa.sparse_decode_attn(s, d.queries(0), d.K, d.V, d.tok_off, d.sel_idx, d.sel_off)
+    torch.cuda.synchronize()
+    o3, l3 = dev.to_host(o3), dev.to_host(l3)
+    P.check_attention("bf16", o3, l3, o_ref, l_ref)
+    rel = np.linalg.norm(o3 - out, axis=-1) / np.linalg.norm(out, axis=-1)
+    assert rel.max() <= 5e-3 and np.abs(l3 - lse).max() <= 1e-5
