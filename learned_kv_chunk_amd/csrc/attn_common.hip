@@ -18,6 +18,7 @@ namespace lsa {
 
 namespace {
 constexpr int32_t kDefaultTarget = 256;  // compute units of an MI355X
+constexpr int64_t kPortTilesPerWg = 4;
 
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 }  // namespace
@@ -53,6 +54,16 @@ AttnPlan make_attn_plan(const lsa_shape& s, int32_t target) {
   p.tiles_per_chunk = (s.chunk_size + kTileTokens - 1) / kTileTokens;
   const int64_t total_tiles = s.total_k * p.tiles_per_chunk;
   p.target = target > 0 ? target : kDefaultTarget;
+  // The vector-ALU kernel on small inputs: a workgroup of four waves gets
+  // four tiles (one per wave) rather than one tile per CU, so that few
+  // workgroups cover a short stream and it merges in its last one.  More
+  // tiles per wave cost more than they save there (measured on the 4K-token
+  // fp32 workload, 16 tiles: partial kernel 14.5 us with one tile per wave,
+  // 22.4 with two, 37.9 with four).
+  if (!mqa_attn_supported(s) && !mla_attn_supported(s)) {
+    const int64_t want = (total_tiles + kPortTilesPerWg - 1) / kPortTilesPerWg;
+    if (want < p.target) p.target = want > 0 ? static_cast<int32_t>(want) : 1;
+  }
   const int64_t cap = run_tile_cap(p.tiles_per_chunk);
   if (s.attn_tiles_per_block > 0) {
     int64_t per = s.attn_tiles_per_block;

@@ -1,189 +1,444 @@
-// attn_portable.hip -- portable split-KV sparse decode attention on the
-// vector ALUs, for fp32 inputs and for head shapes the matrix-core kernels do
-// not cover (up to 16 query heads, head dims up to 256).
+// attn_portable.hip -- split-KV sparse decode attention on the vector ALUs,
+// for fp32 inputs and for head shapes the matrix-core kernels do not cover
+// (up to 16 query heads, head dims up to 256).
 //
 // Dimensionstp review, section 3-2-3 steps 6-7: softmax attention over the
-// tokens of the kept chunks.  One wave per workgroup owns a run of 32-token
-// tiles of one stream: lane t computes the logits of token t for every head
-// (queries staged in LDS as fp32), the wave keeps an fp32 online softmax per
-// head (wave-wide max / sum reductions), the tile's weights go through LDS,
-// and lanes accumulate output columns c, c+64, ... reading value rows with
-// coalesced loads.  Key and value reads are issued kPortBatch at a time so
-// that their memory latency overlaps.  The wave's (m, l, o) is its workgroup's partial result.
+// tokens of the kept chunks.  A workgroup owns a run of 32-token tiles of one
+// stream; its waves take the run's tiles in turn (wave w: tiles w, w + NW,
+// ...).  Per tile a wave
+//   * loads the tile's K and V rows as 16-byte vectors of consecutive
+//     addresses (a tile of a chunk is contiguous in memory: one round trip
+//     for the whole tile), the next tile's loads already in flight in a
+//     second register set while the current tile is computed from LDS,
+//   * computes the logits with lane = token (lanes 0-31 and 32-63 take
+//     alternate heads) from its LDS copy of K and the stream's queries,
+//   * updates the per-head online softmax (half-wave max and sum
+//     reductions), writing the weights to LDS,
+//   * accumulates O with lane = output column, reading V rows from LDS
+//     (consecutive lanes, consecutive words).
+// The waves' (max, sum, output) states are tree-merged through LDS into the
+// workgroup's partial result; a stream served by one workgroup writes its
+// output directly, otherwise the stream's last workgroup to finish merges
+// the partials (when the library chose that, see capi.hip) or a merge launch
+// does.
 #include <math.h>
 
-#include "wave.hpp"
 #include "lsa_internal.hpp"
+#include "wave.hpp"
 
 namespace lsa {
 namespace {
 
 constexpr int kPortHeads = 16;
 constexpr int kPortMaxDim = 256;
-constexpr int kPortBatch = 16;  // independent loads in flight per lane
+constexpr int kPortMaxRowBytes = kPortMaxDim * 4;
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 template <typename T>
-__device__ __forceinline__ float load_elem(const T* p, int64_t i);
+__device__ __forceinline__ f32x4 widen4(const unsigned char* p);
 template <>
-__device__ __forceinline__ float load_elem<float>(const float* p, int64_t i) {
-  return p[i];
+__device__ __forceinline__ f32x4 widen4<float>(const unsigned char* p) {
+  return *reinterpret_cast<const f32x4*>(p);
 }
 template <>
-__device__ __forceinline__ float load_elem<uint16_t>(const uint16_t* p, int64_t i) {
-  return bf16_bits_to_float(p[i]);
+__device__ __forceinline__ f32x4 widen4<uint16_t>(const unsigned char* p) {
+  const uint2 w = *reinterpret_cast<const uint2*>(p);
+  return f32x4{__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xffff0000u),
+               __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xffff0000u)};
 }
 
-// HM: heads held in registers (>= H); CV: output columns per lane / 64.
-template <typename T, int HM, int CV>
-__global__ __launch_bounds__(kWave) void attn_portable_kernel(AttnArgs a) {
+template <typename T>
+__device__ __forceinline__ float widen1(const unsigned char* p);
+template <>
+__device__ __forceinline__ float widen1<float>(const unsigned char* p) {
+  return *reinterpret_cast<const float*>(p);
+}
+template <>
+__device__ __forceinline__ float widen1<uint16_t>(const unsigned char* p) {
+  return __uint_as_float(static_cast<uint32_t>(*reinterpret_cast<const uint16_t*>(p)) << 16);
+}
+
+// Max / sum over each half-wave (lanes 0-31, 32-63), in every lane: DPP
+// steps within each 16-lane row, then one row swap (no LDS round trips; the
+// shuffle form cost five dependent LDS accesses per reduction).
+__device__ __forceinline__ float half_max(float v) {
+  v = fmaxf(v, dpp_f32<kDppQuadXor1>(v));
+  v = fmaxf(v, dpp_f32<kDppQuadXor2>(v));
+  v = fmaxf(v, dpp_f32<kDppRowRor4>(v));
+  v = fmaxf(v, dpp_f32<kDppRowRor8>(v));
+  return xor16_max(v);
+}
+__device__ __forceinline__ float half_sum(float v) {
+  v += dpp_f32<kDppQuadXor1>(v);
+  v += dpp_f32<kDppQuadXor2>(v);
+  v += dpp_f32<kDppRowRor4>(v);
+  v += dpp_f32<kDppRowRor8>(v);
+  return xor16_sum(v);
+}
+
+// Geometry of one wave's tile loads: row bytes of K and V (multiples of 16),
+// their 16-byte vectors per row, and the vectors per lane of a 32-row tile.
+struct PortGeom {
+  int32_t kb, vb;      // row bytes read per token (K: dqk elements, V: dv elements)
+  int32_t kvec, vvec;  // 16-byte vectors per row
+  int64_t kstride, vstride;  // bytes between consecutive rows in memory
+};
+
+// 16-byte vectors of a 32-row tile per lane, at most: 32 * 1024 / 16 / 64.
+constexpr int kPortLoads = kTileTokens * kPortMaxRowBytes / 16 / kWave;
+
+// LP: loads per lane of K and of V (compile-time bound of vec * 32 / 64).
+template <int LP>
+struct PortRegs {
+  u32x4 k[LP];
+  u32x4 v[LP];
+};
+
+// Issues the loads of one tile (rows row0 .. row0 + 31, rows past nvalid
+// re-read the last valid row; nvalid == 0 reads row0): lane l takes vectors
+// l, l + 64, ... of the tile.
+template <int LP>
+__device__ __forceinline__ void port_issue(const unsigned char* __restrict__ kbase,
+                                           const unsigned char* __restrict__ vbase,
+                                           const PortGeom& g, int64_t row0, int32_t nvalid,
+                                           PortRegs<LP>& r, int lane) {
+  const int32_t last = nvalid > 0 ? nvalid - 1 : 0;
+#pragma unroll
+  for (int i = 0; i < LP; ++i) {
+    const int32_t v = i * kWave + lane;
+    const int32_t rk = min(v / g.kvec, last), sk = v % g.kvec;
+    const int32_t rv = min(v / g.vvec, last), sv = v % g.vvec;
+    if (v < kTileTokens * g.kvec)
+      r.k[i] = *reinterpret_cast<const u32x4*>(kbase + (row0 + rk) * g.kstride + sk * 16);
+    if (v < kTileTokens * g.vvec)
+      r.v[i] = *reinterpret_cast<const u32x4*>(vbase + (row0 + rv) * g.vstride + sv * 16);
+  }
+}
+
+// The registers of a tile into this wave's LDS tiles (rows padded by 16
+// bytes so that the 32 lanes reading one column of different rows spread
+// over the banks).
+template <int LP>
+__device__ __forceinline__ void port_stage(const PortRegs<LP>& r, const PortGeom& g,
+                                           unsigned char* sk_tile, unsigned char* sv_tile,
+                                           int lane) {
+#pragma unroll
+  for (int i = 0; i < LP; ++i) {
+    const int32_t v = i * kWave + lane;
+    if (v < kTileTokens * g.kvec)
+      *reinterpret_cast<u32x4*>(sk_tile + (v / g.kvec) * (g.kb + 16) + (v % g.kvec) * 16) = r.k[i];
+    if (v < kTileTokens * g.vvec)
+      *reinterpret_cast<u32x4*>(sv_tile + (v / g.vvec) * (g.vb + 16) + (v % g.vvec) * 16) = r.v[i];
+  }
+}
+
+template <int HM, int CV>
+struct PortState {
+  float acc[HM][CV];  // lane's output columns lane + 64 i, unnormalised
+};
+
+// Waves per workgroup: four while four waves' K and V tiles fit the LDS
+// beside the queries (rows up to 256 bytes), else two.
+template <int LP>
+constexpr int port_waves() { return LP <= 8 ? 4 : 2; }
+
+// HM heads (>= H, even); CV output columns per lane / 64; LP tile loads per
+// lane (rows of up to LP * 32 bytes).
+template <typename T, int HM, int CV, int LP>
+__global__ __launch_bounds__(port_waves<LP>() * kWave) void attn_portable_kernel(AttnArgs a) {
+  constexpr int NW = port_waves<LP>();
+  constexpr int kWaveTileBytes = 2 * kTileTokens * (LP * 32 + 16);  // K and V tiles
+  constexpr bool kDoubleBuffer = LP <= 8;  // two register sets fit beside the accumulators
+  __shared__ __attribute__((aligned(16))) unsigned char smem[NW * kWaveTileBytes];
+  __shared__ int32_t s_slot[kMaxRunSlots];
+  __shared__ AttnRun s_run;
   __shared__ float s_q[HM * kPortMaxDim];
-  __shared__ float s_p[HM][kTileTokens];
-  __shared__ int32_t s_plan[3];
+  __shared__ float s_p[NW][HM][kTileTokens];
+  __shared__ float s_stat[NW][3][HM];  // per wave: running max, sum, this tile's rescale
+  __shared__ int32_t s_last;
 
-  const int lane = threadIdx.x;
-  {
-    int32_t b, local;
-    StreamSplit sp;
-    find_stream_of_wg(SelCsr{a.sel_off, a.uni_k}, a.B, a.tiles_per_chunk, a.per, a.target,
-                      blockIdx.x, &b, &local, &sp);
-    if (lane == 0) {
-      s_plan[0] = b;
-      s_plan[1] = local * sp.per;
-      s_plan[2] = min(sp.tiles, (local + 1) * sp.per);
-    }
-  }
-  __syncthreads();
-  const int32_t b = s_plan[0];
-  if (b < 0) return;
-  const T* __restrict__ q = static_cast<const T*>(a.q);
-  const T* __restrict__ kb = static_cast<const T*>(a.k);
-  const T* __restrict__ vb = static_cast<const T*>(a.v);
+  const int tid = threadIdx.x;
+  const int wave = tid / kWave, lane = tid & (kWave - 1);
+  const AttnRun run = attn_prologue(a, s_slot, &s_run);
+  if (run.b < 0) return;
+  const int32_t b = run.b;
   const int32_t H = a.H, dqk = a.dqk, dv = a.dv, C = a.C, tpc = a.tiles_per_chunk;
-  for (int32_t i = lane; i < H * dqk; i += kWave)
-    s_q[i] = load_elem(q, static_cast<int64_t>(b) * H * dqk + i);
-  __syncthreads();
+  constexpr int ES = sizeof(T);
+  PortGeom g;
+  g.kb = dqk * ES;
+  g.vb = dv * ES;
+  g.kvec = g.kb / 16;
+  g.vvec = g.vb / 16;
+  g.kstride = static_cast<int64_t>(a.k_row) * ES;
+  g.vstride = static_cast<int64_t>(a.v_row) * ES;
+  unsigned char* sk_tile = smem + wave * kWaveTileBytes;
+  unsigned char* sv_tile = sk_tile + kTileTokens * (g.kb + 16);
 
-  const int32_t sel0 = SelCsr{a.sel_off, a.uni_k}.at(b);
-  const int64_t cap = a.tok_off[b + 1] - a.tok_off[b];
-  const int64_t sl = a.seq_len ? a.seq_len[b] : cap;
-  const int64_t len = sl < 0 ? 0 : (sl < cap ? sl : cap);
-  const int32_t t_begin = s_plan[1];
-  const int32_t t_end = s_plan[2];
-
-  float m[HM], l[HM], o[HM][CV];
-#pragma unroll
-  for (int h = 0; h < HM; ++h) {
-    m[h] = -INFINITY;
-    l[h] = 0.f;
-#pragma unroll
-    for (int i = 0; i < CV; ++i) o[h][i] = 0.f;
-  }
-
-  for (int32_t t = t_begin; t < t_end; ++t) {
-    const int32_t slot = sel0 + t / tpc;
-    const int32_t sub = t - (t / tpc) * tpc;
-    const int64_t n = a.sel_idx[slot];
-    int64_t valid = len - n * C;
-    if (n < 0 || valid < 0) valid = 0;
+  const unsigned char* __restrict__ kbase = static_cast<const unsigned char*>(a.k);
+  const unsigned char* __restrict__ vbase = static_cast<const unsigned char*>(a.v);
+  const int64_t last_chunk = run.len > 0 ? (run.len - 1) / C : 0;
+  // tile i of this wave: (first row, valid tokens)
+  auto tile_of = [&](int32_t i, int64_t* row0, int32_t* nvalid) {
+    const int32_t t = run.t_begin + wave + NW * i;
+    const int32_t j = t / tpc;
+    const int32_t sub = t - j * tpc;
+    int64_t n = s_slot[min(j - run.slot_first, kMaxRunSlots - 1)];
+    n = n < 0 ? 0 : (n > last_chunk ? last_chunk : n);
+    int64_t valid = run.len - n * C;
     if (valid > C) valid = C;
     valid -= static_cast<int64_t>(sub) * kTileTokens;
-    if (valid <= 0) continue;
-    const int32_t nv = valid > kTileTokens ? kTileTokens : static_cast<int32_t>(valid);
-    const int64_t row0 = a.pool ? static_cast<int64_t>(slot) * C + sub * kTileTokens
-                                : a.tok_off[b] + n * C + sub * kTileTokens;
+    const int64_t chunk_row = a.pool ? static_cast<int64_t>(run.sel0 + j) * C : run.tb + n * C;
+    if (valid <= 0) {
+      *nvalid = 0;
+      *row0 = chunk_row;
+    } else {
+      *nvalid = valid > kTileTokens ? kTileTokens : static_cast<int32_t>(valid);
+      *row0 = chunk_row + sub * kTileTokens;
+    }
+  };
+  const int32_t n_mine = (run.t_end - run.t_begin - wave + NW - 1) / NW;
 
-    float x[HM];
+  // the first tile's loads go out before the queries are staged
+  PortRegs<LP> ra;
+  int64_t row_a = 0, row_b = 0;
+  int32_t nv_a = 0, nv_b = 0;
+  if (n_mine > 0) {
+    tile_of(0, &row_a, &nv_a);
+    port_issue<LP>(kbase, vbase, g, row_a, nv_a, ra, lane);
+  }
+  {
+    const unsigned char* qb = static_cast<const unsigned char*>(a.q) +
+                              static_cast<int64_t>(b) * H * dqk * ES;
+    for (int32_t i = tid; i < H * dqk; i += NW * kWave) s_q[i] = widen1<T>(qb + i * ES);
+    for (int32_t i = H * dqk + tid; i < HM * dqk; i += NW * kWave) s_q[i] = 0.f;
+  }
+  if (lane < HM) {
+    s_stat[wave][0][lane] = -INFINITY;
+    s_stat[wave][1][lane] = 0.f;
+  }
+  __syncthreads();
+
+  PortState<HM, CV> st;
 #pragma unroll
-    for (int h = 0; h < HM; ++h) x[h] = 0.f;
-    if (lane < nv) {
-      // the token's key row, kPortBatch elements per round trip
-      const int64_t kr = (row0 + lane) * a.k_row;
-      for (int32_t j0 = 0; j0 < dqk; j0 += kPortBatch) {
-        float kv[kPortBatch];
+  for (int h = 0; h < HM; ++h)
 #pragma unroll
-        for (int u = 0; u < kPortBatch; ++u) kv[u] = load_elem(kb, kr + min(j0 + u, dqk - 1));
+    for (int i = 0; i < CV; ++i) st.acc[h][i] = 0.f;
+
+  const int tok = lane & (kTileTokens - 1), half = lane >> 5;
+  auto compute = [&](const PortRegs<LP>& r, int32_t nv) {
+    port_stage<LP>(r, g, sk_tile, sv_tile, lane);
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes done
+    __builtin_amdgcn_wave_barrier();
+    // logits: lane = token, heads half, half + 2, ...
+    float x[HM / 2];
 #pragma unroll
-        for (int u = 0; u < kPortBatch; ++u) {
-          if (j0 + u < dqk) {
+    for (int j = 0; j < HM / 2; ++j) x[j] = 0.f;
+    const unsigned char* krow = sk_tile + tok * (g.kb + 16);
+#pragma unroll 4
+    for (int32_t d0 = 0; d0 < dqk; d0 += 4) {
+      const f32x4 kv = widen4<T>(krow + d0 * ES);
 #pragma unroll
-            for (int h = 0; h < HM; ++h)
-              if (h < H) x[h] = fmaf(s_q[h * dqk + j0 + u], kv[u], x[h]);
-          }
-        }
+      for (int j = 0; j < HM / 2; ++j) {
+        const f32x4 qv = *reinterpret_cast<const f32x4*>(s_q + (2 * j + half) * dqk + d0);
+        x[j] = fmaf(qv.x, kv.x, fmaf(qv.y, kv.y, fmaf(qv.z, kv.z, fmaf(qv.w, kv.w, x[j]))));
       }
     }
-    float alpha[HM];
+    // online softmax per head (the lanes of a half share the head)
+#pragma unroll
+    for (int j = 0; j < HM / 2; ++j) {
+      const int h = 2 * j + half;
+      const float xs = tok < nv ? x[j] * a.scale_log2 : -INFINITY;
+      const float m_old = s_stat[wave][0][h];
+      const float m_new = fmaxf(m_old, half_max(xs));
+      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+      const float p = tok < nv ? __builtin_amdgcn_exp2f(xs - m_use) : 0.f;
+      const float ps = half_sum(p);
+      s_p[wave][h][tok] = p;
+      if (tok == 0) {
+        const float alpha = __builtin_amdgcn_exp2f(m_old - m_use);
+        s_stat[wave][0][h] = m_new;
+        s_stat[wave][1][h] = s_stat[wave][1][h] * alpha + ps;
+        s_stat[wave][2][h] = alpha;
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);
+    __builtin_amdgcn_wave_barrier();
+    // O += P V: lane = column; four tokens per step (weights past nv are 0
+    // and their V rows hold finite values)
 #pragma unroll
     for (int h = 0; h < HM; ++h) {
-      if (h >= H) {
-        alpha[h] = 1.f;
-        continue;
-      }
-      const float xs = (lane < nv) ? x[h] * a.scale_log2 : -INFINITY;
-      const float m_new = fmaxf(m[h], wave_max(xs));
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      alpha[h] = __builtin_amdgcn_exp2f(m[h] - m_use);
-      const float p = (lane < nv) ? __builtin_amdgcn_exp2f(xs - m_use) : 0.f;
-      l[h] = l[h] * alpha[h] + wave_sum(p);
-      m[h] = m_new;
-      if (lane < kTileTokens) s_p[h][lane] = p;
+      const float alpha = s_stat[wave][2][h];
+#pragma unroll
+      for (int i = 0; i < CV; ++i) st.acc[h][i] *= alpha;
     }
-    __syncthreads();
+#pragma unroll 4
+    for (int32_t t0 = 0; t0 < nv; t0 += 4) {
+      float vv[4][CV];
 #pragma unroll
-    for (int i = 0; i < CV; ++i) {
-      const int32_t c = lane + i * kWave;
-      if (c >= dv) continue;
-      float acc[HM];
+      for (int u = 0; u < 4; ++u) {
+        const unsigned char* vrow = sv_tile + (t0 + u) * (g.vb + 16);
 #pragma unroll
-      for (int h = 0; h < HM; ++h) acc[h] = o[h][i] * alpha[h];
-      for (int32_t t0 = 0; t0 < nv; t0 += kPortBatch) {
-        float vv[kPortBatch];
-#pragma unroll
-        for (int u = 0; u < kPortBatch; ++u)
-          vv[u] = load_elem(vb, (row0 + min(t0 + u, nv - 1)) * a.v_row + c);
-#pragma unroll
-        for (int u = 0; u < kPortBatch; ++u) {
-          if (t0 + u < nv) {
-#pragma unroll
-            for (int h = 0; h < HM; ++h)
-              if (h < H) acc[h] = fmaf(s_p[h][t0 + u], vv[u], acc[h]);
-          }
+        for (int i = 0; i < CV; ++i) {
+          const int32_t c = min(lane + i * kWave, dv - 1);
+          vv[u][i] = widen1<T>(vrow + c * ES);
         }
       }
 #pragma unroll
-      for (int h = 0; h < HM; ++h) o[h][i] = acc[h];
+      for (int h = 0; h < HM; ++h) {
+        const f32x4 p = *reinterpret_cast<const f32x4*>(&s_p[wave][h][t0]);
+#pragma unroll
+        for (int i = 0; i < CV; ++i)
+          st.acc[h][i] = fmaf(p.x, vv[0][i], fmaf(p.y, vv[1][i],
+                              fmaf(p.z, vv[2][i], fmaf(p.w, vv[3][i], st.acc[h][i]))));
+      }
     }
-    __syncthreads();
+    __builtin_amdgcn_wave_barrier();  // LDS tiles are rewritten by the next stage
+  };
+
+  if constexpr (kDoubleBuffer) {
+    PortRegs<LP> rb;
+    for (int32_t i = 0; i < n_mine; i += 2) {
+      if (i + 1 < n_mine) {
+        tile_of(i + 1, &row_b, &nv_b);
+        port_issue<LP>(kbase, vbase, g, row_b, nv_b, rb, lane);
+      }
+      compute(ra, nv_a);
+      if (i + 1 >= n_mine) break;
+      if (i + 2 < n_mine) {
+        tile_of(i + 2, &row_a, &nv_a);
+        port_issue<LP>(kbase, vbase, g, row_a, nv_a, ra, lane);
+      }
+      compute(rb, nv_b);
+    }
+  } else {  // rows over 256 bytes: one register set, tiles loaded one at a time
+    for (int32_t i = 0; i < n_mine; ++i) {
+      if (i > 0) {
+        tile_of(i, &row_a, &nv_a);
+        port_issue<LP>(kbase, vbase, g, row_a, nv_a, ra, lane);
+      }
+      compute(ra, nv_a);
+    }
   }
 
-  const int64_t wg = blockIdx.x;
+  // tree-merge the waves' states into wave 0 (output columns through LDS,
+  // reusing the tile buffers)
+  float* so = reinterpret_cast<float*>(smem);  // [NW/2][HM][CV][64]
 #pragma unroll
-  for (int h = 0; h < HM; ++h) {
-    if (h >= H) continue;
-    if (lane == 0) {
-      a.ws_m[wg * H + h] = m[h];
-      a.ws_l[wg * H + h] = l[h];
+  for (int stride = NW / 2; stride >= 1; stride /= 2) {
+    __syncthreads();
+    if (wave >= stride && wave < 2 * stride) {
+      float* dst = so + (wave - stride) * HM * CV * kWave;
+#pragma unroll
+      for (int h = 0; h < HM; ++h)
+#pragma unroll
+        for (int i = 0; i < CV; ++i) dst[(h * CV + i) * kWave + lane] = st.acc[h][i];
     }
+    __syncthreads();
+    if (wave < stride) {
+      const float* src = so + wave * HM * CV * kWave;
+      const int other = wave + stride;
 #pragma unroll
-    for (int i = 0; i < CV; ++i) {
-      const int32_t c = lane + i * kWave;
-      if (c < dv) a.ws_o[(wg * H + h) * dv + c] = o[h][i];
+      for (int h = 0; h < HM; ++h) {
+        const float m0 = s_stat[wave][0][h], m1 = s_stat[other][0][h];
+        const float mx = fmaxf(m0, m1);
+        const float mu = (mx == -INFINITY) ? 0.f : mx;
+        const float f0 = __builtin_amdgcn_exp2f(m0 - mu), f1 = __builtin_amdgcn_exp2f(m1 - mu);
+#pragma unroll
+        for (int i = 0; i < CV; ++i)
+          st.acc[h][i] = st.acc[h][i] * f0 + src[(h * CV + i) * kWave + lane] * f1;
+      }
+    }
+    __syncthreads();
+    if (wave < stride && lane < HM) {
+      const int h = lane, other = wave + stride;
+      const float m0 = s_stat[wave][0][h], m1 = s_stat[other][0][h];
+      const float mx = fmaxf(m0, m1);
+      const float mu = (mx == -INFINITY) ? 0.f : mx;
+      s_stat[wave][1][h] = s_stat[wave][1][h] * __builtin_amdgcn_exp2f(m0 - mu) +
+                           s_stat[other][1][h] * __builtin_amdgcn_exp2f(m1 - mu);
+      s_stat[wave][0][h] = mx;
     }
   }
+  __syncthreads();
+
+  const int64_t wg = blockIdx.x;
+  if (a.fuse_merge && run.wgs == 1) {  // the stream's whole state: output directly
+    if (wave == 0) {
+#pragma unroll
+      for (int h = 0; h < HM; ++h) {
+        if (h >= H) continue;
+        const float lt = s_stat[0][1][h];
+        const float inv = lt > 0.f ? 1.f / lt : 0.f;
+        const int64_t orow = static_cast<int64_t>(b) * H + h;
+#pragma unroll
+        for (int i = 0; i < CV; ++i) {
+          const int32_t c = lane + i * kWave;
+          if (c < dv) a.out[orow * dv + c] = st.acc[h][i] * inv;
+        }
+        if (lane == 0 && a.lse != nullptr)
+          a.lse[orow] = lt > 0.f ? (s_stat[0][0][h] + log2f(lt)) * 0.69314718055994530942f
+                                 : -INFINITY;
+      }
+    }
+    return;
+  }
+  if (wave == 0) {
+#pragma unroll
+    for (int h = 0; h < HM; ++h) {
+      if (h >= H) continue;
+      float* om = a.ws_m + wg * H + h;
+      float* ol = a.ws_l + wg * H + h;
+      float* oo = a.ws_o + (wg * H + h) * dv;
+      if (lane == 0) {
+        if (a.fuse_merge) {
+          store_coherent(om, s_stat[0][0][h]);
+          store_coherent(ol, s_stat[0][1][h]);
+        } else {
+          *om = s_stat[0][0][h];
+          *ol = s_stat[0][1][h];
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < CV; ++i) {
+        const int32_t c = lane + i * kWave;
+        if (c >= dv) continue;
+        if (a.fuse_merge) store_coherent(oo + c, st.acc[h][i]);
+        else oo[c] = st.acc[h][i];
+      }
+    }
+  }
+  if (!a.fuse_merge) return;
+  if (!arrive_last(a, b, run.wgs, &s_last)) return;
+  merge_stream_block<NW * kWave>(a, b, wg - run.local, run.wgs);
+  if (tid == 0)
+    __hip_atomic_store(a.counters + b, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <typename T, int HM, int CV>
+hipError_t launch_portable_l(const AttnArgs& a, int64_t grid, hipStream_t st) {
+  const int kb = a.dqk * static_cast<int>(sizeof(T)), vb = a.dv * static_cast<int>(sizeof(T));
+  const int vec = (kb > vb ? kb : vb) / 16;
+  const int lp = (kTileTokens * vec + kWave - 1) / kWave;
+  const dim3 g(static_cast<uint32_t>(grid));
+#define LSA_PORT_LP(LP_)                                                                   \
+  if (lp <= LP_) {                                                                         \
+    hipLaunchKernelGGL((attn_portable_kernel<T, HM, CV, LP_>), g,                          \
+                       dim3(port_waves<LP_>() * kWave), 0, st, a);                         \
+    return hipGetLastError();                                                              \
+  }
+  LSA_PORT_LP(4) LSA_PORT_LP(8) LSA_PORT_LP(16) LSA_PORT_LP(kPortLoads)
+#undef LSA_PORT_LP
+  return hipErrorNotSupported;
 }
 
 template <typename T, int HM>
 hipError_t launch_portable_h(const AttnArgs& a, int64_t grid, hipStream_t st) {
   const int cv = (a.dv + kWave - 1) / kWave;
-#define LSA_PORT_CASE(CV_)                                                                  \
-  if (cv == CV_) {                                                                          \
-    hipLaunchKernelGGL((attn_portable_kernel<T, HM, CV_>), dim3(static_cast<uint32_t>(grid)), \
-                       dim3(kWave), 0, st, a);                                              \
-    return hipGetLastError();                                                               \
-  }
-  LSA_PORT_CASE(1) LSA_PORT_CASE(2) LSA_PORT_CASE(3) LSA_PORT_CASE(4)
-#undef LSA_PORT_CASE
-  return hipErrorNotSupported;
+  if (cv == 1) return launch_portable_l<T, HM, 1>(a, grid, st);
+  if (cv == 2) return launch_portable_l<T, HM, 2>(a, grid, st);
+  return launch_portable_l<T, HM, 4>(a, grid, st);
 }
 
 template <typename T>

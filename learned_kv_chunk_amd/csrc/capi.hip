@@ -75,6 +75,30 @@ lsa_status hip_status(hipError_t e) { return e == hipSuccess ? LSA_OK : LSA_ERR_
 
 // Enqueue the attention partial kernel and the merge; arguments validated.
 // ev_begin / ev_end (may be null) bracket the partial kernel.
+// Whether the attention kernel merges each stream's partials in the stream's
+// last workgroup (no merge launch): the multi-query and vector-ALU kernels
+// can, when streams average at most eight workgroups (so a last workgroup
+// reads few partials) and its threads hold the output row in one pass
+// (H * dv <= 8 * threads, dv a multiple of 8); otherwise the merge launch
+// reads the partials with many workgroups in parallel.  Measured: 32 ragged
+// streams (eight workgroups each on average) 82.1 -> 79.2 us per step fused,
+// their merges overlapping other streams' tiles; 16 x 128K (sixteen each,
+// all streams ending together) 42.9 -> 45.2 us fused, so that shape keeps
+// the merge launch.
+bool fuse_merge_in_kernel(const lsa_shape& s, const AttnPlan& plan) {
+  if (mla_attn_supported(s) || s.batch > kCounterStreams || s.head_dim_v % 8 != 0) return false;
+  int32_t threads = 256;
+  if (!mqa_attn_supported(s)) {  // vector-ALU kernel: four waves up to 256-byte rows, else two
+    const int32_t es = s.dtype == LSA_DTYPE_BF16 ? 2 : 4;
+    const int32_t rb = (s.head_dim_qk > s.head_dim_v ? s.head_dim_qk : s.head_dim_v) * es;
+    threads = rb <= 256 ? 256 : 128;
+  }
+  if (s.num_q_heads * s.head_dim_v > 8 * threads) return false;
+  const int64_t wgs_expected =
+      plan.per > 0 ? (s.total_k * plan.tiles_per_chunk + plan.per - 1) / plan.per : plan.target;
+  return wgs_expected <= 8 * static_cast<int64_t>(s.batch);
+}
+
 // The split-KV plan of a validated attention shape on the current device and
 // the workspace layout it implies (computed once per call).
 struct AttnSetup {
@@ -111,20 +135,8 @@ lsa_status enqueue_attention(const lsa_shape& s, const AttnSetup& setup, int32_t
   a.ws_l = reinterpret_cast<float*>(static_cast<char*>(ws) + pl.l_off);
   a.ws_o = reinterpret_cast<float*>(static_cast<char*>(ws) + pl.o_off);
   a.counters = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + pl.cnt_off);
-  // the MQA kernel merges each stream's partials in its last workgroup; the
-  // other kernels leave that to the merge launch
-  // when streams average at most eight workgroups (so a last workgroup reads
-  // few partials) and H * dv <= 8 * 256 (one load round trip covers them);
-  // otherwise the merge launch reads them with many workgroups in parallel.
-  // Measured: 32 ragged streams (eight workgroups each on average) 82.1 ->
-  // 79.2 us per step fused, their merges overlapping other streams' tiles;
-  // 16 x 128K (sixteen each, all streams ending together) 42.9 -> 45.2 us
-  // fused, so that shape keeps the merge launch.
-  const int64_t wgs_expected =
-      plan.per > 0 ? (s.total_k * plan.tiles_per_chunk + plan.per - 1) / plan.per : plan.target;
-  const bool fused = mqa_attn_supported(s) && !mla_attn_supported(s) && !partial_only &&
-                     s.batch <= kCounterStreams && s.num_q_heads * s.head_dim_v <= 8 * 256 &&
-                     wgs_expected <= 8 * static_cast<int64_t>(s.batch);
+  // in-kernel merge, or the merge launch after the partial kernel
+  const bool fused = !partial_only && fuse_merge_in_kernel(s, plan);
   a.fuse_merge = fused ? 1 : 0;
   a.B = s.batch;
   a.H = s.num_q_heads;

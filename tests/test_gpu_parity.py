@@ -377,6 +377,28 @@ def test_fp32_portable_attention_ragged():
     P.check_attention("f32", out, lse, o_ref, l_ref)
 
 
+@pytest.mark.parametrize("variant", [
+    dict(),                                                     # cfg1 heads, d = 64
+    dict(num_q_heads=16, head_dim_qk=128, head_dim_v=128),      # 512-byte rows, two waves
+    dict(num_q_heads=3, head_dim_qk=256, head_dim_v=256),       # 1 KiB rows
+    dict(num_q_heads=5, head_dim_qk=32, head_dim_v=96),         # d_v > d_qk, odd heads
+    dict(num_q_heads=1, head_dim_qk=64, head_dim_v=8),          # one head, narrow values
+])
+@pytest.mark.parametrize("per", [0, 1, 3])
+def test_fp32_portable_attention_head_shapes(variant, per):
+    # the vector-ALU kernel at its supported extremes: the four-wave double
+    # buffered form and the two-wave form for long rows, padded head counts,
+    # and every split (one workgroup per stream writing its output directly,
+    # several merging in the last one, or the merge launch)
+    cfg = wl.small_variant("cfg1", lengths=(64 * 37 + 17, 300, 64 * 20, 45), keep_num=1,
+                           keep_den=4, **variant)
+    w = wl.make_workload(cfg)
+    d = dev.upload(w, "cuda", attn_tiles_per_block=per)
+    s_gpu, sel, out, lse = P.run_phases(d, 0)
+    o_ref, l_ref = P.oracle_attention_on(w, 0, sel)
+    print(variant, per, P.check_attention("f32", out, lse, o_ref, l_ref))
+
+
 @pytest.mark.parametrize("std", [1.0, 3.0])
 def test_stress_large_logits(std):
     # unscaled keys and queries: logits of O(10)-O(100), far from uniform weights
