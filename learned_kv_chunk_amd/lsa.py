@@ -16,7 +16,9 @@ from typing import Optional
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "liblsa.so")
+# LSA_LIBRARY may name another build of the same sources (the host-sanitizer
+# build of sanitize.py); there is still no fallback when it is missing
+LIB_PATH = os.environ.get("LSA_LIBRARY") or os.path.join(_HERE, "liblsa.so")
 
 LSA_OK = 0
 LSA_ERR_INVALID_ARGUMENT = 1

@@ -38,6 +38,9 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "lsa_oracle.c")
 _LIB_PATH = os.path.join(_HERE, "liblsa_oracle.so")
+# another build of the same source (the sanitizer run of
+# learned_kv_chunk_amd/sanitize.py) may be named here; it is loaded as is
+_LIB_OVERRIDE = os.environ.get("LSA_ORACLE_LIBRARY")
 
 F32 = 0
 BF16 = 1
@@ -61,8 +64,9 @@ def build(force: bool = False) -> str:
 def _load():
     global _lib
     if _lib is None:
-        build()
-        lib = ctypes.CDLL(_LIB_PATH)
+        if not _LIB_OVERRIDE:
+            build()
+        lib = ctypes.CDLL(_LIB_OVERRIDE or _LIB_PATH)
         P = ctypes.c_void_p
         i32, i64, f64 = ctypes.c_int32, ctypes.c_int64, ctypes.c_double
         lib.oracle_keep_count.argtypes = [i32, i32, i32, i32]
