@@ -166,6 +166,32 @@ def run_copy(args):
                       "gbs": 2 * nbytes / us / 1e3}), flush=True)
 
 
+def run_read(args):
+    """Streams --copy-mib MiB through lsa_bench_read in access pattern
+    --read-pattern (0 plain, 1 non-temporal, 2 the MQA K operand pattern):
+    the reference of the HBM read counters for each pattern."""
+    import torch
+
+    from learned_kv_chunk_amd import lsa
+
+    nbytes = args.copy_mib * 2 ** 20
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    sink = torch.empty(lsa.BENCH_READ_SINK_BYTES, dtype=torch.uint8, device="cuda")
+    lsa.bench_flush(src)
+    for _ in range(3):
+        lsa.bench_read(src, nbytes, args.read_pattern, sink)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        lsa.bench_read(src, nbytes, args.read_pattern, sink)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / args.steps
+    print(json.dumps({"mode": "read", "pattern": args.read_pattern, "read_bytes": nbytes,
+                      "us_per_launch": us, "gbs": nbytes / us / 1e3}), flush=True)
+
+
 def run_scorer(args):
     """Times lsa_score_fp8_multihead (the released retriever's multi-head scorer
     over float8 compressed-key records) on the chunks of a workload, cold: each
@@ -764,7 +790,9 @@ def main():
     ap.add_argument("--tiles-per-block", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--mode", choices=["step", "copy", "scorer", "retriever", "residency",
+    ap.add_argument("--read-pattern", type=int, default=1, choices=[0, 1, 2],
+                    help="--mode read: 0 plain, 1 non-temporal, 2 the MQA K operand pattern")
+    ap.add_argument("--mode", choices=["step", "copy", "read", "scorer", "retriever", "residency",
                                        "append"], default="step")
     ap.add_argument("--drift", type=float, default=0.5,
                     help="residency mode: indexer query drift per re-index epoch")
@@ -790,6 +818,9 @@ def main():
 
     lsa.library()  # fail loudly without the HIP library
     torch.cuda.set_device(0)
+    if args.mode == "read":
+        run_read(args)
+        return
     if args.mode == "copy":
         run_copy(args)
         return

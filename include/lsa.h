@@ -490,6 +490,14 @@ lsa_status lsa_check_tables(const lsa_shape* shape, const int64_t* tok_off_dev,
  * lsa_bench_copy: streaming device copy of `bytes` (a multiple of 16, both
  *   pointers 16-byte aligned); the reference kernel against which HBM counters
  *   and achievable bandwidth are calibrated.
+ * lsa_bench_read: reads `bytes` of a device buffer without writing it (the
+ *   reference for the HBM read counters): pattern 0 plain 16-byte loads,
+ *   each wave instruction covering 1 KiB of consecutive bytes; 1 the same
+ *   with the non-temporal hint; 2 the multi-query attention kernel's K
+ *   operand pattern (256-byte rows in blocks of 16, one instruction covering
+ *   64 bytes of each of 16 rows, non-temporal).  bytes: a multiple of 16
+ *   (4096 for pattern 2).  sink_dev: one uint32 per thread of the launch,
+ *   LSA_BENCH_READ_SINK_BYTES bytes (else LSA_ERR_WORKSPACE_TOO_SMALL).
  * lsa_bench_flush: overwrites `bytes` of a caller buffer (multiple of 16) so
  *   that caches hold none of a workload's data afterwards.
  * lsa_bench_attention_partial: enqueues only the split-KV partial kernel of
@@ -499,6 +507,9 @@ lsa_status lsa_check_tables(const lsa_shape* shape, const int64_t* tok_off_dev,
  *   launches.
  * ------------------------------------------------------------------------- */
 lsa_status lsa_bench_copy(void* dst_dev, const void* src_dev, size_t bytes, void* hip_stream);
+#define LSA_BENCH_READ_SINK_BYTES (256u * 32u * 256u * 4u)
+lsa_status lsa_bench_read(const void* src_dev, size_t bytes, int32_t pattern, void* sink_dev,
+                          size_t sink_bytes, void* hip_stream);
 lsa_status lsa_bench_flush(void* buf_dev, size_t bytes, void* hip_stream);
 lsa_status lsa_bench_attention_partial(const lsa_shape* shape, int32_t kv_mode, const void* q_dev,
                                        const void* k_base_dev, const void* v_base_dev,

@@ -328,12 +328,21 @@ __global__ __launch_bounds__(mqa_waves<NHG>() * kWave, 1) void attn_mqa_kernel(
   }
 
   // Software pipeline, two register sets: the loads of tile i+1 are in flight
-  // while tile i is computed.  Past the last tile the prefetch repeats the last
-  // tile (a cache hit) so that every step issues the same loads.
+  // while tile i is computed.  Past the last tile the prefetch still issues
+  // the same loads, all of them at the current tile's first row (nvalid = 0:
+  // every row re-reads row 0), so that the compiler can count them; a re-read
+  // of the whole last tile instead, with the non-temporal hint, missed the
+  // caches and fetched 16 KiB per wave again (16 x 128K: 158.6 MB counted
+  // against 145.7 MB expected per launch).
   if (n_mine > 0) {
     auto step = [&](TileRegs<D>& rc, const TileInfo& ic, TileRegs<D>& rn, TileInfo& in,
                     int32_t next) {
-      in = tile_info(min(next, n_mine - 1));
+      if (next < n_mine) {
+        in = tile_info(next);
+      } else {
+        in.row0 = ic.row0;
+        in.nvalid = 0;
+      }
       issue_tile<D, NHG == 1>(kb, vb, a.k_row, a.v_row, in, rn, lane);
       __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the compute
       compute_tile<D, NHG>(rc, ic.nvalid, qf, m, l, o, sv, a.scale_log2, lane);

@@ -650,6 +650,18 @@ lsa_status lsa_bench_copy(void* dst_dev, const void* src_dev, size_t bytes, void
   return hip_status(launch_bench_copy(dst_dev, src_dev, bytes, static_cast<hipStream_t>(hip_stream)));
 }
 
+lsa_status lsa_bench_read(const void* src_dev, size_t bytes, int32_t pattern, void* sink_dev,
+                          size_t sink_bytes, void* hip_stream) {
+  if (!src_dev || !sink_dev || !aligned(src_dev, 16) || !aligned(sink_dev, 4) ||
+      pattern < 0 || pattern > 2 || bytes % (pattern == 2 ? 4096 : 16) != 0)
+    return LSA_ERR_INVALID_ARGUMENT;
+  if (sink_bytes < static_cast<size_t>(kBenchReadBlocks) * 256 * sizeof(uint32_t))
+    return LSA_ERR_WORKSPACE_TOO_SMALL;
+  (void)hipGetLastError();
+  return hip_status(launch_bench_read(src_dev, bytes, pattern, static_cast<uint32_t*>(sink_dev),
+                                      static_cast<hipStream_t>(hip_stream)));
+}
+
 lsa_status lsa_bench_flush(void* buf_dev, size_t bytes, void* hip_stream) {
   if (!buf_dev || bytes % 16 != 0 || !aligned(buf_dev, 16)) return LSA_ERR_INVALID_ARGUMENT;
   (void)hipGetLastError();

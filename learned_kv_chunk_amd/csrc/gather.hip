@@ -82,7 +82,53 @@ __global__ __launch_bounds__(256) void flush_kernel(u32x4* __restrict__ buf, int
     buf[i] = u32x4{salt, static_cast<uint32_t>(i), salt ^ 0x5bd1e995u, 1u};
 }
 
+// Read-only streaming of n 16-byte vectors in one of three access patterns
+// (the calibration references of the HBM read counters):
+//   0  plain loads, each wave instruction covering 1 KiB of consecutive bytes;
+//   1  the same with the non-temporal hint;
+//   2  the multi-query attention kernel's K operand pattern: the buffer seen
+//      as 256-byte rows in blocks of 16 rows, a wave instruction covering 64
+//      bytes of each of the 16 rows and the next instruction the next 64,
+//      with the non-temporal hint.
+// Every loaded word is folded into one value per thread, written to
+// sink[thread] so that no load can be removed.
+__global__ __launch_bounds__(256) void read_kernel(const u32x4* __restrict__ src, int64_t n,
+                                                   int32_t pattern, uint32_t* __restrict__ sink) {
+  const int64_t tid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  uint32_t acc = 0;
+  if (pattern == 2) {
+    const int lane = threadIdx.x & 63;
+    const int r16 = lane & 15, g = lane >> 4;
+    const int64_t waves = static_cast<int64_t>(gridDim.x) * (blockDim.x / 64);
+    const int64_t wave = tid / 64;
+    const int64_t blocks = n / 256;  // 16 rows x 16 vectors
+    for (int64_t blk = wave; blk < blocks; blk += waves) {
+      const u32x4* rowp = src + blk * 256 + r16 * 16 + g;
+      u32x4 v[4];
+#pragma unroll
+      for (int s2 = 0; s2 < 4; ++s2) v[s2] = __builtin_nontemporal_load(rowp + 4 * s2);
+#pragma unroll
+      for (int s2 = 0; s2 < 4; ++s2) acc ^= v[s2].x ^ v[s2].y ^ v[s2].z ^ v[s2].w;
+    }
+  } else {
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+    for (int64_t i = tid; i < n; i += stride) {
+      const u32x4 v = pattern == 1 ? __builtin_nontemporal_load(src + i) : src[i];
+      acc ^= v.x ^ v.y ^ v.z ^ v.w;
+    }
+  }
+  sink[tid] = acc;
+}
+
 }  // namespace
+
+hipError_t launch_bench_read(const void* src, size_t bytes, int32_t pattern, uint32_t* sink,
+                             hipStream_t st) {
+  const int64_t n = static_cast<int64_t>(bytes / 16);
+  hipLaunchKernelGGL(read_kernel, dim3(kBenchReadBlocks), dim3(256), 0, st,
+                     static_cast<const u32x4*>(src), n, pattern, sink);
+  return hipGetLastError();
+}
 
 hipError_t launch_gather(const lsa_shape& s, const void* store, int32_t row_bytes,
                          const int64_t* tok_off, const int32_t* sel_idx,

@@ -136,6 +136,9 @@ hipError_t launch_check_tables(const lsa_shape& s, const int64_t* tok_off,
                                const int32_t* sel_idx, int32_t ascending, int32_t* flag,
                                hipStream_t st);
 hipError_t launch_bench_copy(void* dst, const void* src, size_t bytes, hipStream_t st);
+constexpr int32_t kBenchReadBlocks = 256 * 32;  // workgroups of 256 threads of lsa_bench_read
+hipError_t launch_bench_read(const void* src, size_t bytes, int32_t pattern, uint32_t* sink,
+                             hipStream_t st);
 hipError_t launch_bench_flush(void* buf, size_t bytes, hipStream_t st);
 
 // ---------------------------------------------------------------------------

@@ -123,6 +123,7 @@ _SIGNATURES = {
     "lsa_bench_attention_partial": ([ctypes.POINTER(Shape), _I32, _P, _P, _P, _P, _P, _P, _P,
                                      ctypes.c_size_t, _P], _I32),
     "lsa_bench_flush": ([_P, ctypes.c_size_t, _P], _I32),
+    "lsa_bench_read": ([_P, ctypes.c_size_t, _I32, _P, ctypes.c_size_t, _P], _I32),
 }
 
 _lib = None
@@ -725,6 +726,19 @@ def bench_attention_partial(shape: ProblemShape, q, k_base, v_base, tok_off, sel
 def bench_copy(dst: torch.Tensor, src: torch.Tensor, nbytes: int, stream=None) -> None:
     _check(library().lsa_bench_copy(_ptr(dst), _ptr(src), nbytes, _stream(stream)),
            "lsa_bench_copy")
+
+
+BENCH_READ_SINK_BYTES = 256 * 32 * 256 * 4  # LSA_BENCH_READ_SINK_BYTES
+
+
+def bench_read(src: torch.Tensor, nbytes: int, pattern: int, sink: torch.Tensor,
+               stream=None) -> None:
+    """lsa_bench_read: stream-read nbytes of src in access pattern 0, 1 or 2."""
+    _dev(src, "src")
+    _dev(sink, "sink")
+    _check(library().lsa_bench_read(_ptr(src), nbytes, int(pattern), _ptr(sink),
+                                    sink.numel() * sink.element_size(), _stream(stream)),
+           "lsa_bench_read")
 
 
 def bench_flush(buf: torch.Tensor, stream=None) -> None:
