@@ -33,6 +33,7 @@
 #include <math.h>
 
 #include "lsa_internal.hpp"
+#include "select_core.hpp"
 #include "wave.hpp"
 
 namespace lsa {
@@ -191,6 +192,7 @@ constexpr int cmax(int a, int b) { return a > b ? a : b; }
 // Waves per workgroup: one per SIMD.
 template <int NHG>
 constexpr int mqa_waves() { return 4; }
+constexpr int kMqaThreads = 4 * kWave;
 
 template <int D, int NHG>
 struct MqaLds {
@@ -242,7 +244,9 @@ __device__ __forceinline__ void merge_state(const unsigned char* base, float (&m
 // teams; team t serves head groups t*NHG .. t*NHG + NHG - 1 and its waves
 // interleave the run's tiles among themselves, so a tile is read once per team
 // (HS = 1 except for more than 32 heads).
-template <int D, int NHG, int HS>
+// KSEL > 0: the workgroup ranks its stream's kept chunks itself in the
+// prologue (KSEL keys per thread, attn_select_stream) instead of reading them.
+template <int D, int NHG, int HS, int KSEL>
 __global__ __launch_bounds__(mqa_waves<NHG>() * kWave, 1) void attn_mqa_kernel(
     AttnArgs a) {
   using L = MqaLds<D, NHG>;
@@ -263,16 +267,10 @@ __global__ __launch_bounds__(mqa_waves<NHG>() * kWave, 1) void attn_mqa_kernel(
   if (run.b < 0) return;
   const int32_t b = run.b;
   const int32_t tpc = a.tiles_per_chunk, C = a.C, H = a.H;
-  const int32_t sel0 = run.sel0;
-  const int32_t t_begin = run.t_begin;
-  const int32_t t_end = run.t_end;
-  const int32_t slot_first = run.slot_first;
-  const int64_t tb = run.tb;
-  const int64_t len = run.len;
-  const int64_t last_chunk = len > 0 ? (len - 1) / C : 0;
 
   // Q^T operand: lane holds Q[head][s*32 + 8*(lane/16) + 0..7] for the heads
-  // (grp*NHG + hg)*16 + lane%16 of its team
+  // (grp*NHG + hg)*16 + lane%16 of its team (loaded before an in-kernel
+  // top-k, whose latency then covers theirs)
   const int head0 = grp * NHG * 16 + r16;
   const uint16_t* __restrict__ qb = static_cast<const uint16_t*>(a.q);
   bf16x8 qf[NHG][D / 32];
@@ -285,6 +283,17 @@ __global__ __launch_bounds__(mqa_waves<NHG>() * kWave, 1) void attn_mqa_kernel(
     for (int s = 0; s < D / 32; ++s)
       qf[hg][s] = as_bf16x8(head < H ? src[s * 4] : u32x4{0u, 0u, 0u, 0u});
   }
+  if constexpr (KSEL > 0)  // the V tile buffers are free until the first tile
+    attn_select_stream<NW * kWave, KSEL>(a, run, s_slot,
+                                         *reinterpret_cast<SelectLds<NW * kWave>*>(smem));
+  const int32_t sel0 = run.sel0;
+  const int32_t t_begin = run.t_begin;
+  const int32_t t_end = run.t_end;
+  // s_slot holds the run's kept chunks, or the whole stream's when selected here
+  const int32_t slot_first = KSEL > 0 ? 0 : run.slot_first;
+  const int64_t tb = run.tb;
+  const int64_t len = run.len;
+  const int64_t last_chunk = len > 0 ? (len - 1) / C : 0;
 
   // Tile i of this wave is t_begin + wl + WPG*i.  An empty tile (past the end
   // of a partial chunk) points at its chunk's first row with nvalid = 0.
@@ -427,21 +436,37 @@ __global__ __launch_bounds__(mqa_waves<NHG>() * kWave, 1) void attn_mqa_kernel(
     __hip_atomic_store(a.counters + b, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int D>
-hipError_t launch_mqa_d(const AttnArgs& a, int64_t grid, hipStream_t st) {
+template <int D, int KSEL>
+hipError_t launch_mqa_dk(const AttnArgs& a, int64_t grid, hipStream_t st) {
   const int nhg = (a.H + 15) / 16;
   dim3 g(static_cast<uint32_t>(grid));
   if (nhg == 1)
-    hipLaunchKernelGGL((attn_mqa_kernel<D, 1, 1>), g, dim3(mqa_waves<1>() * kWave), 0, st, a);
+    hipLaunchKernelGGL((attn_mqa_kernel<D, 1, 1, KSEL>), g, dim3(mqa_waves<1>() * kWave), 0, st,
+                       a);
   else if (nhg == 2)
-    hipLaunchKernelGGL((attn_mqa_kernel<D, 2, 1>), g, dim3(mqa_waves<2>() * kWave), 0, st, a);
+    hipLaunchKernelGGL((attn_mqa_kernel<D, 2, 1, KSEL>), g, dim3(mqa_waves<2>() * kWave), 0, st,
+                       a);
   else if (nhg <= 4)
-    hipLaunchKernelGGL((attn_mqa_kernel<D, 2, 2>), g, dim3(mqa_waves<2>() * kWave), 0, st, a);
+    hipLaunchKernelGGL((attn_mqa_kernel<D, 2, 2, KSEL>), g, dim3(mqa_waves<2>() * kWave), 0, st,
+                       a);
   else return hipErrorNotSupported;
   return hipGetLastError();
 }
 
+template <int D>
+hipError_t launch_mqa_d(const AttnArgs& a, int32_t max_chunks, hipStream_t st,
+                        int64_t grid) {
+  if (a.sel_scores == nullptr) return launch_mqa_dk<D, 0>(a, grid, st);
+  if (max_chunks <= kMqaThreads * 8) return launch_mqa_dk<D, 8>(a, grid, st);
+  if (max_chunks <= kMqaThreads * 16) return launch_mqa_dk<D, 16>(a, grid, st);
+  return hipErrorNotSupported;
+}
+
 }  // namespace
+
+bool mqa_select_in_kernel_supported(const lsa_shape& s) {
+  return mqa_attn_supported(s) && s.max_chunks <= kMqaThreads * 16 && s.max_k <= kMaxRunSlots;
+}
 
 bool mqa_attn_supported(const lsa_shape& s) {
   return s.dtype == LSA_DTYPE_BF16 && !s.v_aliases_k && s.head_dim_qk == s.head_dim_v &&
@@ -450,8 +475,9 @@ bool mqa_attn_supported(const lsa_shape& s) {
 }
 
 hipError_t launch_attn_mqa(const lsa_shape& s, const AttnArgs& a, int64_t grid, hipStream_t st) {
-  if (s.head_dim_qk == 128) return launch_mqa_d<128>(a, grid, st);
-  if (s.head_dim_qk == 64) return launch_mqa_d<64>(a, grid, st);
+  if (a.sel_scores != nullptr && !mqa_select_in_kernel_supported(s)) return hipErrorNotSupported;
+  if (s.head_dim_qk == 128) return launch_mqa_d<128>(a, s.max_chunks, st, grid);
+  if (s.head_dim_qk == 64) return launch_mqa_d<64>(a, s.max_chunks, st, grid);
   return hipErrorNotSupported;
 }
 

@@ -118,10 +118,18 @@ lsa_status enqueue_attention(const lsa_shape& s, const AttnSetup& setup, int32_t
                              const int64_t* tok_off, const int32_t* sel_idx,
                              const int32_t* sel_off, float* out, float* lse, void* ws,
                              hipStream_t st, void* ev_begin = nullptr, void* ev_end = nullptr,
-                             const int64_t* seq_len = nullptr, bool partial_only = false) {
+                             const int64_t* seq_len = nullptr, bool partial_only = false,
+                             const float* sel_scores = nullptr,
+                             const int32_t* chunk_off = nullptr) {
   const AttnPlan& plan = setup.plan;
   const PartialLayout& pl = setup.layout;
   AttnArgs a;
+  // sel_scores non-null: the attention kernel ranks the kept chunks itself and
+  // writes them to sel_idx (which it then does not read)
+  a.sel_scores = sel_scores;
+  a.chunk_off = chunk_off;
+  a.sel_idx_out = const_cast<int32_t*>(sel_idx);
+  a.uni_n = (s.flags & LSA_SHAPE_UNIFORM) ? s.max_chunks : 0;
   a.q = q;
   a.k = kbase;
   a.v = s.v_aliases_k ? kbase : vbase;
@@ -509,12 +517,17 @@ static lsa_status enqueue_step(const lsa_shape* shape, const AttnSetup& setup,
   const bool pool = x.materialize_pool != 0;
   const hipStream_t hs = static_cast<hipStream_t>(hip_stream);
   (void)hipGetLastError();
+  // the multi-query kernel ranks each stream's kept chunks in its prologue
+  // (no select launch, no kept-index round trip) when it reads the store
+  const bool select_in_attention =
+      x.reindex && !pool && !mla_attn_supported(*shape) && mqa_select_in_kernel_supported(*shape);
   if (x.reindex) {
     if (launch_score(*shape, x.q_idx_dev, x.emb_dev, x.chunk_off_dev, x.scores_dev, hs) !=
         hipSuccess)
       return LSA_ERR_HIP;
-    if (launch_select(*shape, x.scores_dev, x.chunk_off_dev, x.sel_off_dev, x.sel_idx_dev, hs) !=
-        hipSuccess)
+    if (!select_in_attention &&
+        launch_select(*shape, x.scores_dev, x.chunk_off_dev, x.sel_off_dev, x.sel_idx_dev, hs) !=
+            hipSuccess)
       return LSA_ERR_HIP;
     if (pool) {
       const int32_t kb = shape->head_dim_qk * elem_bytes(*shape);
@@ -528,7 +541,8 @@ static lsa_status enqueue_step(const lsa_shape* shape, const AttnSetup& setup,
                            pool ? x.k_pool_dev : x.k_store_dev,
                            pool ? x.v_pool_dev : x.v_store_dev, x.tok_off_dev, x.sel_idx_dev,
                            x.sel_off_dev, x.out_dev, x.lse_dev, ws, hs, x.ev_attn_begin,
-                           x.ev_attn_end);
+                           x.ev_attn_end, nullptr, false,
+                           select_in_attention ? x.scores_dev : nullptr, x.chunk_off_dev);
 }
 
 // The step's arguments with the lookahead schedule applied to x.reindex.

@@ -80,6 +80,13 @@ struct AttnArgs {
   float* ws_o;
   int32_t* counters;      // per-stream arrival counters (zero between calls)
   int32_t fuse_merge;     // 1: the partial kernel merges each stream itself
+  // In-kernel top-k (sel_scores non-null): every workgroup ranks its
+  // stream's scores itself instead of reading sel_idx, and the stream's
+  // first workgroup writes the kept set to sel_idx_out.
+  const float* sel_scores;   // [total_chunks] fp32 scores, or null
+  const int32_t* chunk_off;  // [B+1] (read unless uni_n > 0)
+  int32_t* sel_idx_out;      // [total_k]
+  int32_t uni_n;             // chunks of every stream when the shape is uniform, else 0
   int32_t B, H, dqk, dv, C;
   int32_t k_row;          // elements between consecutive K rows
   int32_t v_row;          // elements between consecutive V rows
@@ -123,6 +130,8 @@ hipError_t launch_pool_delta(const lsa_shape& s, const void* k_host_dev, int32_t
                              hipStream_t st);
 // Attention partial kernels (one per kernel family) and the merge.
 bool mqa_attn_supported(const lsa_shape& s);
+// The MQA kernel can rank each stream's kept chunks itself (in-kernel top-k).
+bool mqa_select_in_kernel_supported(const lsa_shape& s);
 hipError_t launch_attn_mqa(const lsa_shape& s, const AttnArgs& a, int64_t grid, hipStream_t st);
 bool mla_attn_supported(const lsa_shape& s);
 hipError_t launch_attn_mla(const lsa_shape& s, const AttnArgs& a, int64_t grid, hipStream_t st);
@@ -263,6 +272,9 @@ struct AttnRun {
   int32_t slot_first;  // the run's first kept chunk, counted within the stream
   int32_t local;       // this workgroup's index among the stream's
   int32_t wgs;         // the stream's workgroups (partials)
+  int32_t cbase;       // chunk_off[b] (in-kernel top-k only)
+  int32_t cn;          // N_b (in-kernel top-k only)
+  int32_t kb;          // k_b
   int64_t tb;          // tok_off[b]
   int64_t len;         // L_b
 };
@@ -281,10 +293,11 @@ __device__ __forceinline__ AttnRun attn_prologue(const AttnArgs& a, int32_t* s_s
     StreamSplit sp;
     find_stream_of_wg(SelCsr{a.sel_off, a.uni_k}, a.B, tpc, a.per, a.target, blockIdx.x, &b,
                       &local, &sp, &sel0);
-    AttnRun r = {b, 0, 0, 0, 0, 0, 0, 0, 0};
+    AttnRun r = {b, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
     if (b >= 0) {
       r.local = local;
       r.wgs = sp.wgs;
+      r.kb = sp.tiles / tpc;
       r.t_begin = local * sp.per;
       r.t_end = min(sp.tiles, (local + 1) * sp.per);
       r.sel0 = sel0;
@@ -292,7 +305,13 @@ __device__ __forceinline__ AttnRun attn_prologue(const AttnArgs& a, int32_t* s_s
       const int32_t nslots = min((r.t_end - 1) / tpc - r.slot_first + 1, kMaxRunSlots);
       const int64_t t0 = a.tok_off[b], t1 = a.tok_off[b + 1];
       const int64_t sl = a.seq_len ? a.seq_len[b] : t1 - t0;
-      for (int32_t i = lane; i < nslots; i += kWave) s_slot[i] = a.sel_idx[sel0 + r.slot_first + i];
+      if (a.sel_scores == nullptr) {
+        for (int32_t i = lane; i < nslots; i += kWave)
+          s_slot[i] = a.sel_idx[sel0 + r.slot_first + i];
+      } else {  // the kept set is ranked in the kernel: the stream's chunk range
+        r.cbase = a.uni_n > 0 ? b * a.uni_n : a.chunk_off[b];
+        r.cn = a.uni_n > 0 ? a.uni_n : a.chunk_off[b + 1] - r.cbase;
+      }
       r.tb = t0;
       r.len = sl < 0 ? 0 : (sl < t1 - t0 ? sl : t1 - t0);
     }
@@ -309,6 +328,9 @@ __device__ __forceinline__ AttnRun attn_prologue(const AttnArgs& a, int32_t* s_s
   u.slot_first = __builtin_amdgcn_readfirstlane(v.slot_first);
   u.local = __builtin_amdgcn_readfirstlane(v.local);
   u.wgs = __builtin_amdgcn_readfirstlane(v.wgs);
+  u.cbase = __builtin_amdgcn_readfirstlane(v.cbase);
+  u.cn = __builtin_amdgcn_readfirstlane(v.cn);
+  u.kb = __builtin_amdgcn_readfirstlane(v.kb);
   u.tb = uniform_i64(v.tb);
   u.len = uniform_i64(v.len);
   return u;

@@ -342,7 +342,7 @@ __device__ __forceinline__ bool select_buckets(const uint32_t (&key)[KPT], int32
 // Top-k of the n keys held as select_load_keys leaves them, written ascending
 // to out[0..k); 0 < k < n.  Every one of the THREADS threads (threads
 // 0..THREADS-1 of the workgroup) must call it.
-template <int THREADS, int KPT>
+template <int THREADS, int KPT, bool BUCKETS = (KPT >= 8)>
 __device__ __forceinline__ void select_topk_keys(const uint32_t (&key)[KPT], int32_t n,
                                                  int32_t k, int32_t* __restrict__ out,
                                                  SelectLds<THREADS>& lds) {
@@ -350,7 +350,7 @@ __device__ __forceinline__ void select_topk_keys(const uint32_t (&key)[KPT], int
   uint32_t prefix, remaining, mask = 0xffffffffu;
   // the bucket pass pays off from eight keys per thread (streams of several
   // thousand chunks); below that the radix passes are as fast
-  if (KPT < 8 || !select_buckets<THREADS, KPT>(key, n, k, lds, &prefix, &remaining))
+  if (!BUCKETS || !select_buckets<THREADS, KPT>(key, n, k, lds, &prefix, &remaining))
     select_radix<THREADS, KPT>(key, n, k, lds, &prefix, &remaining, &mask);
 
   // keys above T (on the bits of mask) are kept, and the first `remaining`
@@ -379,13 +379,38 @@ __device__ __forceinline__ void select_topk_keys(const uint32_t (&key)[KPT], int
 }
 
 // Top-k of scores[0..n) written ascending to out[0..k); 0 < k < n.
-template <int THREADS, int KPT>
+template <int THREADS, int KPT, bool BUCKETS = (KPT >= 8)>
 __device__ __forceinline__ void select_topk_block(const float* __restrict__ scores, int32_t n,
                                                   int32_t k, int32_t* __restrict__ out,
                                                   SelectLds<THREADS>& lds) {
   uint32_t key[KPT];
   select_load_keys<THREADS, KPT>(scores, n, key);
-  select_topk_keys<THREADS, KPT>(key, n, k, out, lds);
+  select_topk_keys<THREADS, KPT, BUCKETS>(key, n, k, out, lds);
+}
+
+// The kept set of an attention workgroup's stream, ranked in its prologue by
+// all THREADS threads (the same keys, rule and algorithm as lsa_select_topk,
+// so the same set): kept[0 .. k_b) (LDS) receives the stream's kept chunk
+// indices in ascending order, and the stream's first workgroup also writes
+// them to sel_idx_out.  Requires N_b <= THREADS * KPT and k_b <= kMaxRunSlots
+// (checked on the host); ends with a barrier.  lds may alias LDS that the
+// caller uses only afterwards.
+template <int THREADS, int KPT>
+__device__ __forceinline__ void attn_select_stream(const AttnArgs& a, const AttnRun& run,
+                                                   int32_t* kept, SelectLds<THREADS>& lds) {
+  const int32_t n = run.cn < 0 ? 0 : (run.cn > THREADS * KPT ? THREADS * KPT : run.cn);
+  int32_t k = run.kb < 0 ? 0 : (run.kb > kMaxRunSlots ? kMaxRunSlots : run.kb);
+  if (k > n) k = n;
+  if (k > 0 && k < n) {
+    // the radix passes: the bucket pass is slower for streams of up to
+    // 2048 chunks (eight keys per thread here)
+    select_topk_block<THREADS, KPT, (KPT > 8)>(a.sel_scores + run.cbase, n, k, kept, lds);
+  } else {
+    for (int32_t i = threadIdx.x; i < k; i += THREADS) kept[i] = i;
+  }
+  __syncthreads();
+  if (run.local == 0)
+    for (int32_t i = threadIdx.x; i < k; i += THREADS) a.sel_idx_out[run.sel0 + i] = kept[i];
 }
 
 }  // namespace lsa
