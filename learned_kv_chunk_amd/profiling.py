@@ -65,10 +65,22 @@ def counter_per_dispatch(run_dir: str, counter: str, kernel: str) -> list[float]
 
 
 def kernel_sources(kernel_file: str) -> list[str]:
-    """A kernel's source file and the headers every kernel file includes: a
-    traffic record is valid only while all of them are unchanged."""
-    csrc = os.path.dirname(os.path.abspath(kernel_file))
-    return [kernel_file, os.path.join(csrc, "lsa_internal.hpp"), os.path.join(csrc, "wave.hpp")]
+    """A kernel's source file and every header it includes from this
+    repository, recursively (first-seen order): a traffic record is valid
+    only while all of them are unchanged."""
+    import re
+
+    out, todo = [], [kernel_file]
+    while todo:
+        f = todo.pop(0)
+        if f in out or not os.path.exists(f):
+            continue
+        out.append(f)
+        base = os.path.dirname(os.path.abspath(f))
+        with open(f) as fh:
+            for inc in re.findall(r'^\s*#\s*include\s+"([^"]+)"', fh.read(), flags=re.M):
+                todo.append(os.path.relpath(os.path.normpath(os.path.join(base, inc))))
+    return out
 
 
 def source_hash(paths) -> str:
