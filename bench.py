@@ -14,13 +14,16 @@ bytes from HBM instead of re-reading what the previous step left in cache.
 
 Prints one JSON line (rank 0, one GPU).  `value` is decode steps per second
 (K steps issued eagerly between two events; `graph_ms_per_step` is the same
-steps replayed from a HIP graph); `roofline` reports the attention partial
-kernel's algorithmic bytes per launch over its average duration, K cold
-launches of that kernel alone replayed from a HIP graph between two events;
+steps replayed from a HIP graph); `roofline` reports the attention phase's
+algorithmic bytes per call over its average duration: K cold calls of
+lsa_sparse_decode_attn (the split-KV partial kernel and the log-sum-exp
+merge, or the one kernel that merges in its last workgroups) replayed from a
+HIP graph between two events, with the partial kernel alone beside it
+(`partial_kernel_us`); `score_kernel` does the same for the score kernel;
 `cpu_baseline` times the CPU oracle on the host on a bounded sample of the
-same workload.  `--attention-only` times just that kernel (for a kernel
-trace holding only its launches); `--mode` selects the retriever, residency,
-append, scorer and copy measurements.
+same workload.  `--attention-only` times just the attention phase (for a
+kernel trace holding only its launches); `--mode` selects the retriever,
+residency, append, scorer, copy and read measurements.
 """
 from __future__ import annotations
 
