@@ -55,7 +55,7 @@ WORKLOAD_TEXT = {
 
 
 def algorithmic_bytes(w):
-    """Bytes the method must move per step, by phase."""
+    """Bytes the method must move per step, by phase (split partials excluded)."""
     import numpy as np
 
     c = w.cfg

@@ -131,7 +131,7 @@ void oracle_select_threshold(int32_t B, const double* scores, const int32_t* chu
 /* Delta residency of the chunk pool (wiki note flowchart: only the selected
  * chunks stay on the GPU, the rest live in host memory and are swapped in
  * when needed; dimensionstp review section 3-2-5: that offload engine is
- * unreleased, so the rule below is this build's plain reading).  Stream b
+ * unreleased, so the rule below is the plainest one that fits).  Stream b
  * owns the k_b pool slots sel_off[b] .. sel_off[b+1]-1; table[slot] is the
  * chunk a slot holds (-1: none).  Given the new kept set sel_idx (ascending,
  * k_b chunks per stream) and the old table:
@@ -148,7 +148,7 @@ void oracle_pool_delta(int32_t B, const int32_t* chunk_off, const int32_t* sel_i
 /* Attention keep set of a growing context (dimensionstp review section
  * 3-2-3 steps 2 and 7: history goes to the cache and decode attends to the
  * kept chunks; the pages say nothing of tokens added after the last
- * re-index, so this is this build's reading): the chunks of the last
+ * re-index, so this is the plainest rule that fits): the chunks of the last
  * selection (ascending, all below M_b = chunk_off[b+1]-chunk_off[b], the
  * chunks the indexer has scored), plus the last scored chunk M_b-1 when it
  * was not kept (it was the partial tail when scored and may have grown
