@@ -2,6 +2,7 @@
 workloads: the same structure, dtypes and head shapes as the five benchmark
 workloads, at lengths the oracle finishes in seconds, spanning many tiles and
 ragged partial last chunks.  Tolerances are those of tests/parity.py."""
+import dataclasses
 import math
 
 import numpy as np
@@ -264,6 +265,113 @@ def test_select_large_streams():
     s = [rng.standard_normal(65536).astype(np.float32) * 1e-3,
          np.round(rng.standard_normal(20000), 2), rng.standard_normal(8192)]
     _select_case(s, [6000, 19999, 655])
+
+
+# ----------------------------------------------------------------------------- top-k inside attention
+def _bf16_exact(v):
+    v = np.asarray(v, dtype=np.float32)
+    back = wl.bf16_bits_to_f32(wl.to_bf16_bits(v))
+    np.testing.assert_array_equal(back, v)  # NaN matches NaN
+    return v
+
+
+def _mix(rng, n, values, counts, rest):
+    v = np.full(n, rest, dtype=np.float32)
+    idx = rng.permutation(n)
+    at = 0
+    for val, c in zip(values, counts):
+        v[idx[at:at + c]] = val
+        at += c
+    return v
+
+
+def _scored_workload(scores_per_stream, keep, C=32):
+    """A bf16 MQA workload (16 heads, d = 64) whose chunk scores are exactly
+    the given bf16-representable values: the indexer query is the first unit
+    vector and chunk n's embedding holds its score in its first component
+    (every other product is 0 x 0, so the fp32 sum is the value itself)."""
+    lengths = tuple(len(v) * C for v in scores_per_stream)
+    cfg = wl.small_variant("cfg2", lengths=lengths, n_needles=0, chunk_size=C, num_q_heads=16,
+                           head_dim_qk=64, head_dim_v=64)
+    w = wl.make_workload(cfg)
+    vals = np.concatenate([_bf16_exact(v) for v in scores_per_stream])
+    emb = np.zeros((len(vals), cfg.index_dim), np.float32)
+    emb[:, 0] = vals
+    q_idx = np.zeros((cfg.batch, cfg.index_dim), np.float32)
+    q_idx[:, 0] = 1.0
+    keep = np.asarray(keep, np.int32)
+    sel_off = np.concatenate([[0], np.cumsum(keep)]).astype(np.int32)
+    return dataclasses.replace(w, emb=wl.to_bf16_bits(emb), q_idx=wl.to_bf16_bits(q_idx),
+                               keep=keep, sel_off=sel_off), vals
+
+
+def _select_in_attention_case(scores_per_stream, keep):
+    w, vals = _scored_workload(scores_per_stream, keep)
+    for per in (0, 1):  # per = 1: one tile per workgroup, so each stream ranks in many
+        d = dev.upload(w, "cuda", attn_tiles_per_block=per, with_pool=False)
+        s = d.shape
+        # the shapes the decode step ranks inside the attention kernel
+        assert s.dtype == torch.bfloat16 and s.max_chunks <= 4096 and s.max_k <= 1024
+        d.sel_idx.fill_(-1)
+        d.step(0, reindex=True, materialize_pool=False)
+        torch.cuda.synchronize()
+        s_gpu = dev.to_host(d.scores)
+        np.testing.assert_array_equal(s_gpu, vals)
+        sel = dev.to_host(d.sel_idx)
+        np.testing.assert_array_equal(
+            sel, oracle.select(s_gpu.astype(np.float64), w.chunk_off, w.sel_off))
+        alone = lsa.select_topk(s, d.scores, d.chunk_off, d.sel_off)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(dev.to_host(alone), sel)
+        # every workgroup of a stream attended over the same kept set
+        o_ref, l_ref = P.oracle_attention_on(w, 0, sel)
+        P.check_attention("bf16", dev.to_host(d.out), dev.to_host(d.lse), o_ref, l_ref)
+
+
+def test_select_in_attention_ties_nan_and_early_stop():
+    # streams of up to 2048 chunks (eight keys per thread: the radix passes):
+    # quarter-step ties, NaN and infinities, bf16-rounded normals (many equal
+    # values), the early-stop mixes of the standalone test, one value
+    # everywhere, keep one and keep all
+    rng = np.random.default_rng(11)
+    ties = np.round(rng.standard_normal(2048) * 4) / 4
+    special = wl.bf16_bits_to_f32(wl.to_bf16_bits(rng.standard_normal(1500).astype(np.float32)))
+    special[rng.choice(1500, 40, replace=False)] = np.nan
+    special[:3] = [np.inf, -np.inf, -0.0]
+    normal = wl.bf16_bits_to_f32(wl.to_bf16_bits(rng.standard_normal(2000).astype(np.float32)))
+    streams = [ties, special, normal,
+               _mix(rng, 2048, [4.0], [276], 0.25), _mix(rng, 2048, [1.5], [276], 1.0),
+               _mix(rng, 2048, [1.75, 1.5], [274, 2], 1.0),
+               _mix(rng, 2048, [1.75, 1.5], [274, 5], 1.0),
+               _mix(rng, 1000, [-1.0, -1.5], [10, 90], -3.0),
+               _mix(rng, 1000, [-1.0, -1.5], [10, 90], -3.0),
+               _mix(rng, 40, [2.0, 1.5], [3, 4], 1.0), np.full(300, 0.25, np.float32),
+               normal[:64].copy(), normal[:97].copy()]
+    keep = [276, 203, 270, 276, 276, 276, 276, 100, 50, 5, 7, 64, 1]
+    _select_in_attention_case(streams, keep)
+
+
+def test_select_in_attention_long_streams():
+    # 2049-4096 chunks (sixteen keys per thread: the bucket pass first, the
+    # radix passes when ties, NaN, infinities, an outlier or a crowded
+    # boundary bin send it there), and the uniform-shape case
+    rng = np.random.default_rng(12)
+    n = 4096
+    normal = wl.bf16_bits_to_f32(wl.to_bf16_bits(rng.standard_normal(n).astype(np.float32)))
+    cont = wl.bf16_bits_to_f32(wl.to_bf16_bits(
+        (rng.standard_normal(n) * 2.0 ** rng.integers(-8, 8, n)).astype(np.float32)))
+    special = normal.copy()
+    special[rng.choice(n, 40, replace=False)] = np.nan
+    special[:3] = [np.inf, -np.inf, -0.0]
+    outlier = wl.bf16_bits_to_f32(wl.to_bf16_bits(
+        (rng.standard_normal(3000) * 1e-3).astype(np.float32)))
+    outlier[1000] = wl.bf16_bits_to_f32(wl.to_bf16_bits(np.float32([1e30])))[0]
+    dense = np.concatenate([normal[:2800], np.full(200, 0.5, np.float32)])
+    streams = [normal, cont, special, outlier, dense, np.round(normal * 4) / 4]
+    for k in (1, 63, 512, 1024):
+        _select_in_attention_case(streams, [k] * len(streams))
+    uniform = [normal, cont, special, np.round(normal * 4) / 4]
+    _select_in_attention_case(uniform, [409] * len(uniform))
 
 
 # ----------------------------------------------------------------------------- shape coverage
