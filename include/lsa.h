@@ -443,7 +443,9 @@ lsa_status lsa_decode_step(const lsa_shape* shape, const lsa_step_args* args,
  * device's array: calls that overlap on one device (concurrent streams, or
  * host threads) race and must be serialised by the caller.  The first call
  * on a device looks up the array's device address (LSA_ERR_HIP if that
- * fails).
+ * fails) and enqueues, ahead of its step, a fill kernel that zeroes the
+ * array's per-stream arrival counters (a kernel, not a memset, so that the
+ * call can be captured in a graph); every step leaves them at zero.
  * ------------------------------------------------------------------------- */
 #define LSA_STATIC_SCRATCH_BYTES (64u << 20)
 

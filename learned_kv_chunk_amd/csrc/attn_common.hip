@@ -227,7 +227,18 @@ __global__ __launch_bounds__(MW * kWave) void merge_kernel(AttnArgs a, int32_t n
                                   : -INFINITY;
 }
 
+__global__ __launch_bounds__(256) void clear_counters_kernel(int32_t* counters) {
+  const int32_t i = static_cast<int32_t>(blockIdx.x) * 256 + static_cast<int32_t>(threadIdx.x);
+  if (i < kCounterStreams) counters[i] = 0;
+}
+
 }  // namespace
+
+hipError_t launch_clear_counters(void* ws, hipStream_t st) {
+  hipLaunchKernelGGL(clear_counters_kernel, dim3((kCounterStreams + 255) / 256), dim3(256), 0, st,
+                     static_cast<int32_t*>(ws));
+  return hipGetLastError();
+}
 
 hipError_t launch_attn_merge(const lsa_shape& s, const AttnArgs& a, const AttnPlan& plan,
                              hipStream_t st) {

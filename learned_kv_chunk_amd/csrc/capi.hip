@@ -4,6 +4,7 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <atomic>
 #include <mutex>
 
 #include "lsa_internal.hpp"
@@ -581,8 +582,11 @@ lsa_status lsa_decode_step(const lsa_shape* shape, const lsa_step_args* args, vo
 // device address of each device's copy comes from hipGetSymbolAddress, taken
 // once per device with that device current, and only that address reaches
 // the kernels.  Every call on a device shares its copy (overlapping calls on
-// one device race); nothing in it has to start at zero, since every partial
-// the merge reads is written first by the same step.
+// one device race).  Of its contents only the per-stream arrival counters
+// (the first 64 KiB) must start at zero: the first call on each device
+// clears them with a fill kernel on its stream, ahead of its step, and every
+// attention launch leaves them at zero; every partial the merge reads is
+// written first by the same step.
 static __device__ __align__(256) unsigned char scratch[LSA_STATIC_SCRATCH_BYTES];
 
 namespace {
@@ -590,10 +594,12 @@ constexpr int kMaxScratchDevices = 64;
 std::once_flag g_scratch_once[kMaxScratchDevices];
 void* g_scratch_dev[kMaxScratchDevices];
 hipError_t g_scratch_err[kMaxScratchDevices];
+std::atomic<bool> g_scratch_cleared[kMaxScratchDevices];
 }  // namespace
 
-// Device address of the current device's copy of `scratch`, or null.
-static void* static_scratch_address() {
+// Device address of the current device's copy of `scratch`, or null; *dev_out
+// receives the device.
+static void* static_scratch_address(int* dev_out) {
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxScratchDevices) return nullptr;
   std::call_once(g_scratch_once[dev], [dev] {
@@ -601,6 +607,7 @@ static void* static_scratch_address() {
     g_scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
     g_scratch_dev[dev] = g_scratch_err[dev] == hipSuccess ? p : nullptr;
   });
+  *dev_out = dev;
   return g_scratch_dev[dev];
 }
 
@@ -614,10 +621,17 @@ lsa_status lsa_decode_step_static(const lsa_shape* shape, const lsa_step_args* a
   if (st != LSA_OK) return st;
   const AttnSetup setup = attn_setup(*shape);
   if (setup.layout.total > LSA_STATIC_SCRATCH_BYTES) return LSA_ERR_WORKSPACE_TOO_SMALL;
-  void* ws = static_scratch_address();
+  int dev = -1;
+  void* ws = static_scratch_address(&dev);
   if (ws == nullptr) {
     (void)hipGetLastError();
     return LSA_ERR_HIP;
+  }
+  if (!g_scratch_cleared[dev].load(std::memory_order_acquire)) {
+    (void)hipGetLastError();
+    if (launch_clear_counters(ws, static_cast<hipStream_t>(hip_stream)) != hipSuccess)
+      return LSA_ERR_HIP;
+    g_scratch_cleared[dev].store(true, std::memory_order_release);
   }
   return enqueue_step(shape, setup, x, ws, hip_stream);
 }

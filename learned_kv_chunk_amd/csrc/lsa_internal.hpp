@@ -140,6 +140,9 @@ hipError_t launch_attn_portable(const lsa_shape& s, const AttnArgs& a, int64_t g
                                 hipStream_t st);
 hipError_t launch_attn_merge(const lsa_shape& s, const AttnArgs& a, const AttnPlan& plan,
                              hipStream_t st);
+// Zeroes the per-stream arrival counters at the start of a workspace (a
+// fill kernel: no memset node if the caller captures the stream in a graph).
+hipError_t launch_clear_counters(void* ws, hipStream_t st);
 hipError_t launch_check_tables(const lsa_shape& s, const int64_t* tok_off,
                                const int32_t* chunk_off, const int32_t* sel_off,
                                const int32_t* sel_idx, int32_t ascending, int32_t* flag,
