@@ -60,8 +60,14 @@ AttnPlan make_attn_plan(const lsa_shape& s, int32_t target) {
   // tiles per wave cost more than they save there (measured on the 4K-token
   // fp32 workload, 16 tiles: partial kernel 14.5 us with one tile per wave,
   // 22.4 with two, 37.9 with four).
+  // With few tiles and at least five heads the waves of a workgroup share
+  // each tile and split its heads instead (portable_split_heads): then one
+  // tile per workgroup.
+  p.split_heads = 0;
   if (!mqa_attn_supported(s) && !mla_attn_supported(s)) {
-    const int64_t want = (total_tiles + kPortTilesPerWg - 1) / kPortTilesPerWg;
+    p.split_heads = portable_split_heads(s, total_tiles, p.target) ? 1 : 0;
+    const int64_t per_wg = p.split_heads ? 1 : kPortTilesPerWg;
+    const int64_t want = (total_tiles + per_wg - 1) / per_wg;
     if (want < p.target) p.target = want > 0 ? static_cast<int32_t>(want) : 1;
   }
   const int64_t cap = run_tile_cap(p.tiles_per_chunk);

@@ -416,6 +416,276 @@ __global__ __launch_bounds__(port_waves<LP>() * kWave) void attn_portable_kernel
     __hip_atomic_store(a.counters + b, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// ---------------------------------------------------------------------------
+// Split-heads form, for inputs of few tiles (the plan then gives a workgroup
+// one tile) with 5-16 heads and rows of at most 256 bytes: the four waves of
+// the workgroup share each tile -- its 256 threads load it and stage it once
+// in LDS -- and wave w takes heads w * HPW .. w * HPW + HPW - 1 (its two
+// half-waves alternate between them).  A tile then costs each wave a quarter
+// of the logits and of P.V, and the waves' states need no merging: each wave
+// owns the whole state of its heads.
+constexpr int kShWaves = 4;
+constexpr int kShThreads = kShWaves * kWave;
+constexpr int kShMaxRowBytes = 256;
+constexpr int kShLoads = kTileTokens * (kShMaxRowBytes / 16) / kShThreads;  // per thread per array
+
+template <typename T, int HM, int CV>
+__global__ __launch_bounds__(kShThreads) void attn_portable_sh_kernel(AttnArgs a) {
+  constexpr int HPW = HM / kShWaves;  // heads per wave
+  constexpr int JH = HPW / 2;         // heads per half-wave
+  constexpr int kPitchMax = kShMaxRowBytes + 16;
+  __shared__ __attribute__((aligned(16))) unsigned char s_k[kTileTokens * kPitchMax];
+  __shared__ __attribute__((aligned(16))) unsigned char s_v[kTileTokens * kPitchMax];
+  __shared__ int32_t s_slot[kMaxRunSlots];
+  __shared__ AttnRun s_run;
+  __shared__ __attribute__((aligned(16))) float s_q[HM * (kShMaxRowBytes / 2)];
+  __shared__ __attribute__((aligned(16))) float s_p[HM][kTileTokens];
+  __shared__ float s_stat[3][HM];  // per head: running max, sum, this tile's rescale
+  __shared__ int32_t s_last;
+
+  const int tid = threadIdx.x;
+  const int wave = tid / kWave, lane = tid & (kWave - 1);
+  const AttnRun run = attn_prologue(a, s_slot, &s_run);
+  if (run.b < 0) return;
+  const int32_t b = run.b;
+  const int32_t H = a.H, dqk = a.dqk, dv = a.dv, C = a.C, tpc = a.tiles_per_chunk;
+  constexpr int ES = sizeof(T);
+  PortGeom g;
+  g.kb = dqk * ES;
+  g.vb = dv * ES;
+  g.kvec = g.kb / 16;
+  g.vvec = g.vb / 16;
+  g.kstride = static_cast<int64_t>(a.k_row) * ES;
+  g.vstride = static_cast<int64_t>(a.v_row) * ES;
+  const int32_t kpitch = g.kb + 16, vpitch = g.vb + 16;
+
+  const unsigned char* __restrict__ kbase = static_cast<const unsigned char*>(a.k);
+  const unsigned char* __restrict__ vbase = static_cast<const unsigned char*>(a.v);
+  const int64_t last_chunk = run.len > 0 ? (run.len - 1) / C : 0;
+  // tile i of the run: (first row, valid tokens), as in the kernel above
+  auto tile_of = [&](int32_t i, int64_t* row0, int32_t* nvalid) {
+    const int32_t t = run.t_begin + i;
+    const int32_t j = t / tpc;
+    const int32_t sub = t - j * tpc;
+    int64_t n = s_slot[min(j - run.slot_first, kMaxRunSlots - 1)];
+    n = n < 0 ? 0 : (n > last_chunk ? last_chunk : n);
+    int64_t valid = run.len - n * C;
+    if (valid > C) valid = C;
+    valid -= static_cast<int64_t>(sub) * kTileTokens;
+    const int64_t chunk_row = a.pool ? static_cast<int64_t>(run.sel0 + j) * C : run.tb + n * C;
+    if (valid <= 0) {
+      *nvalid = 0;
+      *row0 = chunk_row;
+    } else {
+      *nvalid = valid > kTileTokens ? kTileTokens : static_cast<int32_t>(valid);
+      *row0 = chunk_row + sub * kTileTokens;
+    }
+  };
+  const int32_t n_tiles = run.t_end - run.t_begin;
+
+  // thread tid loads vectors tid, tid + 256, ... of the tile's K and V rows
+  // (rows past nvalid re-read the last valid row)
+  struct ShRegs {
+    u32x4 k[kShLoads];
+    u32x4 v[kShLoads];
+  };
+  auto issue = [&](int64_t row0, int32_t nvalid, ShRegs& r) {
+    const int32_t last = nvalid > 0 ? nvalid - 1 : 0;
+#pragma unroll
+    for (int i = 0; i < kShLoads; ++i) {
+      const int32_t v = i * kShThreads + tid;
+      if (v < kTileTokens * g.kvec)
+        r.k[i] = *reinterpret_cast<const u32x4*>(
+            kbase + (row0 + min(v / g.kvec, last)) * g.kstride + (v % g.kvec) * 16);
+      if (v < kTileTokens * g.vvec)
+        r.v[i] = *reinterpret_cast<const u32x4*>(
+            vbase + (row0 + min(v / g.vvec, last)) * g.vstride + (v % g.vvec) * 16);
+    }
+  };
+  auto stage = [&](const ShRegs& r) {
+#pragma unroll
+    for (int i = 0; i < kShLoads; ++i) {
+      const int32_t v = i * kShThreads + tid;
+      if (v < kTileTokens * g.kvec)
+        *reinterpret_cast<u32x4*>(s_k + (v / g.kvec) * kpitch + (v % g.kvec) * 16) = r.k[i];
+      if (v < kTileTokens * g.vvec)
+        *reinterpret_cast<u32x4*>(s_v + (v / g.vvec) * vpitch + (v % g.vvec) * 16) = r.v[i];
+    }
+  };
+
+  // the first tile's loads go out before the queries are staged
+  ShRegs ra, rb;
+  int64_t row_a = 0, row_b = 0;
+  int32_t nv_a = 0, nv_b = 0;
+  if (n_tiles > 0) {
+    tile_of(0, &row_a, &nv_a);
+    issue(row_a, nv_a, ra);
+  }
+  {
+    const unsigned char* qb = static_cast<const unsigned char*>(a.q) +
+                              static_cast<int64_t>(b) * H * dqk * ES;
+    for (int32_t i = tid; i < H * dqk; i += kShThreads) s_q[i] = widen1<T>(qb + i * ES);
+    for (int32_t i = H * dqk + tid; i < HM * dqk; i += kShThreads) s_q[i] = 0.f;
+  }
+  if (tid < HM) {
+    s_stat[0][tid] = -INFINITY;
+    s_stat[1][tid] = 0.f;
+  }
+
+  float acc[HPW][CV];
+#pragma unroll
+  for (int hh = 0; hh < HPW; ++hh)
+#pragma unroll
+    for (int i = 0; i < CV; ++i) acc[hh][i] = 0.f;
+
+  const int tok = lane & (kTileTokens - 1), half = lane >> 5;
+  const int h0 = wave * HPW;  // this wave's first head
+  auto compute = [&](int32_t nv) {
+    // logits: lane = token, heads h0 + half, h0 + 2 + half, ...
+    float x[JH];
+#pragma unroll
+    for (int j = 0; j < JH; ++j) x[j] = 0.f;
+    const unsigned char* krow = s_k + tok * kpitch;
+#pragma unroll 4
+    for (int32_t d0 = 0; d0 < dqk; d0 += 4) {
+      const f32x4 kv = widen4<T>(krow + d0 * ES);
+#pragma unroll
+      for (int j = 0; j < JH; ++j) {
+        const f32x4 qv = *reinterpret_cast<const f32x4*>(s_q + (h0 + 2 * j + half) * dqk + d0);
+        x[j] = fmaf(qv.x, kv.x, fmaf(qv.y, kv.y, fmaf(qv.z, kv.z, fmaf(qv.w, kv.w, x[j]))));
+      }
+    }
+    // online softmax per head (the lanes of a half share the head)
+#pragma unroll
+    for (int j = 0; j < JH; ++j) {
+      const int h = h0 + 2 * j + half;
+      const float xs = tok < nv ? x[j] * a.scale_log2 : -INFINITY;
+      const float m_old = s_stat[0][h];
+      const float m_new = fmaxf(m_old, half_max(xs));
+      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+      const float p = tok < nv ? __builtin_amdgcn_exp2f(xs - m_use) : 0.f;
+      const float ps = half_sum(p);
+      s_p[h][tok] = p;
+      if (tok == 0) {
+        const float alpha = __builtin_amdgcn_exp2f(m_old - m_use);
+        s_stat[0][h] = m_new;
+        s_stat[1][h] = s_stat[1][h] * alpha + ps;
+        s_stat[2][h] = alpha;
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the weights are in LDS
+    __builtin_amdgcn_wave_barrier();
+    // O += P V for this wave's heads: lane = column, four tokens per step
+#pragma unroll
+    for (int hh = 0; hh < HPW; ++hh) {
+      const float alpha = s_stat[2][h0 + hh];
+#pragma unroll
+      for (int i = 0; i < CV; ++i) acc[hh][i] *= alpha;
+    }
+#pragma unroll 4
+    for (int32_t t0 = 0; t0 < nv; t0 += 4) {
+      float vv[4][CV];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const unsigned char* vrow = s_v + (t0 + u) * vpitch;
+#pragma unroll
+        for (int i = 0; i < CV; ++i) vv[u][i] = widen1<T>(vrow + min(lane + i * kWave, dv - 1) * ES);
+      }
+#pragma unroll
+      for (int hh = 0; hh < HPW; ++hh) {
+        const f32x4 p = *reinterpret_cast<const f32x4*>(&s_p[h0 + hh][t0]);
+#pragma unroll
+        for (int i = 0; i < CV; ++i)
+          acc[hh][i] = fmaf(p.x, vv[0][i], fmaf(p.y, vv[1][i],
+                            fmaf(p.z, vv[2][i], fmaf(p.w, vv[3][i], acc[hh][i]))));
+      }
+    }
+  };
+
+  // every wave stages its share of a tile, then every wave computes on it;
+  // the barrier after the products frees the tile buffers for the next one
+  __syncthreads();
+  for (int32_t i = 0; i < n_tiles; i += 2) {
+    if (i + 1 < n_tiles) {
+      tile_of(i + 1, &row_b, &nv_b);
+      issue(row_b, nv_b, rb);
+    }
+    stage(ra);
+    __syncthreads();
+    compute(nv_a);
+    __syncthreads();
+    if (i + 1 >= n_tiles) break;
+    if (i + 2 < n_tiles) {
+      tile_of(i + 2, &row_a, &nv_a);
+      issue(row_a, nv_a, ra);
+    }
+    stage(rb);
+    __syncthreads();
+    compute(nv_b);
+    __syncthreads();
+  }
+
+  const int64_t wg = blockIdx.x;
+  if (a.fuse_merge && run.wgs == 1) {  // the stream's whole state: output directly
+#pragma unroll
+    for (int hh = 0; hh < HPW; ++hh) {
+      const int h = h0 + hh;
+      if (h >= H) continue;
+      const float lt = s_stat[1][h];
+      const float inv = lt > 0.f ? 1.f / lt : 0.f;
+      const int64_t orow = static_cast<int64_t>(b) * H + h;
+#pragma unroll
+      for (int i = 0; i < CV; ++i) {
+        const int32_t c = lane + i * kWave;
+        if (c < dv) a.out[orow * dv + c] = acc[hh][i] * inv;
+      }
+      if (lane == 0 && a.lse != nullptr)
+        a.lse[orow] = lt > 0.f ? (s_stat[0][h] + log2f(lt)) * 0.69314718055994530942f
+                               : -INFINITY;
+    }
+    return;
+  }
+#pragma unroll
+  for (int hh = 0; hh < HPW; ++hh) {
+    const int h = h0 + hh;
+    if (h >= H) continue;
+    float* om = a.ws_m + wg * H + h;
+    float* ol = a.ws_l + wg * H + h;
+    float* oo = a.ws_o + (wg * H + h) * dv;
+    if (lane == 0) {
+      if (a.fuse_merge) {
+        store_coherent(om, s_stat[0][h]);
+        store_coherent(ol, s_stat[1][h]);
+      } else {
+        *om = s_stat[0][h];
+        *ol = s_stat[1][h];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < CV; ++i) {
+      const int32_t c = lane + i * kWave;
+      if (c >= dv) continue;
+      if (a.fuse_merge) store_coherent(oo + c, acc[hh][i]);
+      else oo[c] = acc[hh][i];
+    }
+  }
+  if (!a.fuse_merge) return;
+  if (!arrive_last(a, b, run.wgs, &s_last)) return;
+  merge_stream_block<kShThreads>(a, b, wg - run.local, run.wgs);
+  if (tid == 0)
+    __hip_atomic_store(a.counters + b, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <typename T, int HM>
+hipError_t launch_portable_sh(const AttnArgs& a, int64_t grid, hipStream_t st) {
+  const dim3 g(static_cast<uint32_t>(grid));
+  if (a.dv <= kWave)
+    hipLaunchKernelGGL((attn_portable_sh_kernel<T, HM, 1>), g, dim3(kShThreads), 0, st, a);
+  else
+    hipLaunchKernelGGL((attn_portable_sh_kernel<T, HM, 2>), g, dim3(kShThreads), 0, st, a);
+  return hipGetLastError();
+}
+
 template <typename T, int HM, int CV>
 hipError_t launch_portable_l(const AttnArgs& a, int64_t grid, hipStream_t st) {
   const int kb = a.dqk * static_cast<int>(sizeof(T)), vb = a.dv * static_cast<int>(sizeof(T));
@@ -443,6 +713,13 @@ hipError_t launch_portable_h(const AttnArgs& a, int64_t grid, hipStream_t st) {
 
 template <typename T>
 hipError_t launch_portable_t(const AttnArgs& a, int64_t grid, hipStream_t st) {
+  if (a.split_heads) {
+    if (a.H <= 4 || a.H > kPortHeads || a.dqk * static_cast<int>(sizeof(T)) > kShMaxRowBytes ||
+        a.dv * static_cast<int>(sizeof(T)) > kShMaxRowBytes)
+      return hipErrorNotSupported;
+    if (a.H <= 8) return launch_portable_sh<T, 8>(a, grid, st);
+    return launch_portable_sh<T, 16>(a, grid, st);
+  }
   if (a.H <= 4) return launch_portable_h<T, 4>(a, grid, st);
   if (a.H <= 8) return launch_portable_h<T, 8>(a, grid, st);
   return launch_portable_h<T, 16>(a, grid, st);
@@ -453,6 +730,13 @@ hipError_t launch_portable_t(const AttnArgs& a, int64_t grid, hipStream_t st) {
 bool portable_attn_supported(const lsa_shape& s) {
   return s.num_q_heads >= 1 && s.num_q_heads <= kPortHeads && s.head_dim_qk >= 1 &&
          s.head_dim_qk <= kPortMaxDim && s.head_dim_v >= 1 && s.head_dim_v <= kPortMaxDim;
+}
+
+bool portable_split_heads(const lsa_shape& s, int64_t total_tiles, int32_t target) {
+  const int es = s.dtype == LSA_DTYPE_BF16 ? 2 : 4;
+  return portable_attn_supported(s) && s.num_q_heads > 4 &&
+         s.head_dim_qk * es <= kShMaxRowBytes && s.head_dim_v * es <= kShMaxRowBytes &&
+         total_tiles <= target;
 }
 
 hipError_t launch_attn_portable(const lsa_shape& s, const AttnArgs& a, int64_t grid,

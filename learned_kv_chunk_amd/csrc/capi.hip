@@ -97,7 +97,10 @@ bool fuse_merge_in_kernel(const lsa_shape& s, const AttnPlan& plan) {
   if (s.num_q_heads * s.head_dim_v > 8 * threads) return false;
   const int64_t wgs_expected =
       plan.per > 0 ? (s.total_k * plan.tiles_per_chunk + plan.per - 1) / plan.per : plan.target;
-  return wgs_expected <= 8 * static_cast<int64_t>(s.batch);
+  // the split-heads form has one tile per workgroup and small partials: its
+  // last workgroup merges up to 32 per stream on average
+  const int64_t per_stream = plan.split_heads ? 32 : 8;
+  return wgs_expected <= per_stream * static_cast<int64_t>(s.batch);
 }
 
 // The split-KV plan of a validated attention shape on the current device and
@@ -159,6 +162,7 @@ lsa_status enqueue_attention(const lsa_shape& s, const AttnSetup& setup, int32_t
   a.per = plan.per;
   a.target = plan.target;
   a.uni_k = (s.flags & LSA_SHAPE_UNIFORM) ? s.max_k : 0;
+  a.split_heads = plan.split_heads;
   a.scale_log2 = s.softmax_scale * 1.4426950408889634f;
   if (ev_begin && hipEventRecord(static_cast<hipEvent_t>(ev_begin), st) != hipSuccess)
     return LSA_ERR_HIP;

@@ -44,6 +44,7 @@ struct AttnPlan {
   int32_t target;   // workgroups the proportional split aims at
   int64_t grid;     // workgroups launched (upper bound of sum_b W_b)
   int64_t ws_rows;  // partial results the workspace holds (>= grid)
+  int32_t split_heads;  // vector-ALU kernel: the waves share each tile, split its heads
 };
 
 // `target` is the number of compute units of the device that will run it.
@@ -93,6 +94,7 @@ struct AttnArgs {
   int32_t pool;           // 1: slot-indexed pool, 0: store indexed by chunk
   int32_t tiles_per_chunk, per, target;
   int32_t uni_k;          // k of every stream when the shape is uniform, else 0
+  int32_t split_heads;    // AttnPlan::split_heads
   float scale_log2;       // softmax_scale * log2(e)
 };
 
@@ -136,6 +138,10 @@ hipError_t launch_attn_mqa(const lsa_shape& s, const AttnArgs& a, int64_t grid, 
 bool mla_attn_supported(const lsa_shape& s);
 hipError_t launch_attn_mla(const lsa_shape& s, const AttnArgs& a, int64_t grid, hipStream_t st);
 bool portable_attn_supported(const lsa_shape& s);
+// Whether the vector-ALU kernel runs its split-heads form for a shape with
+// total_tiles tiles on `target` compute units (small inputs, 5-16 heads,
+// rows of at most 256 bytes).
+bool portable_split_heads(const lsa_shape& s, int64_t total_tiles, int32_t target);
 hipError_t launch_attn_portable(const lsa_shape& s, const AttnArgs& a, int64_t grid,
                                 hipStream_t st);
 hipError_t launch_attn_merge(const lsa_shape& s, const AttnArgs& a, const AttnPlan& plan,

@@ -473,6 +473,21 @@ def test_mla_attention_head_counts(heads):
     assert (np.abs(lse - l_ref) / np.abs(l_ref)).max() <= 1e-4
 
 
+@pytest.mark.parametrize("heads", [8, 16])
+def test_fp32_portable_attention_many_tiles(heads):
+    # more tiles than compute units: the tile-parallel form of the kernel
+    # (waves take alternate tiles, states tree-merged) for head counts that
+    # take the split-heads form on short inputs
+    cfg = wl.small_variant("cfg1", lengths=(64 * 1300 + 9, 64 * 700), keep_num=1, keep_den=4,
+                           num_q_heads=heads)
+    w = wl.make_workload(cfg)
+    assert (w.keep.sum() * 2) > 256  # tiles of 32 tokens, chunks of 64
+    d = dev.upload(w, "cuda")
+    s_gpu, sel, out, lse = P.run_phases(d, 0)
+    o_ref, l_ref = P.oracle_attention_on(w, 0, sel)
+    print(heads, P.check_attention("f32", out, lse, o_ref, l_ref))
+
+
 def test_fp32_portable_attention_ragged():
     cfg = wl.small_variant("cfg1", lengths=(4096 + 17, 300, 64 * 40), keep_num=1, keep_den=4)
     w = wl.make_workload(cfg)
@@ -486,7 +501,9 @@ def test_fp32_portable_attention_ragged():
 
 
 @pytest.mark.parametrize("variant", [
-    dict(),                                                     # cfg1 heads, d = 64
+    dict(),                                                     # cfg1 heads, d = 64: split heads
+    dict(num_q_heads=16, head_dim_qk=64, head_dim_v=64),        # split heads, four per wave
+    dict(num_q_heads=5, head_dim_qk=32, head_dim_v=64),         # split heads, odd heads
     dict(num_q_heads=16, head_dim_qk=128, head_dim_v=128),      # 512-byte rows, two waves
     dict(num_q_heads=3, head_dim_qk=256, head_dim_v=256),       # 1 KiB rows
     dict(num_q_heads=5, head_dim_qk=32, head_dim_v=96),         # d_v > d_qk, odd heads
@@ -494,7 +511,8 @@ def test_fp32_portable_attention_ragged():
 ])
 @pytest.mark.parametrize("per", [0, 1, 3])
 def test_fp32_portable_attention_head_shapes(variant, per):
-    # the vector-ALU kernel at its supported extremes: the four-wave double
+    # the vector-ALU kernel at its supported extremes: the split-heads form
+    # (few tiles, 5-16 heads, rows up to 256 bytes), the four-wave double
     # buffered form and the two-wave form for long rows, padded head counts,
     # and every split (one workgroup per stream writing its output directly,
     # several merging in the last one, or the merge launch)
