@@ -24,6 +24,7 @@
 #include <math.h>
 
 #include "lsa_internal.hpp"
+#include "select_core.hpp"
 #include "wave.hpp"
 
 namespace lsa {
@@ -423,13 +424,15 @@ __global__ __launch_bounds__(port_waves<LP>() * kWave) void attn_portable_kernel
 // in LDS -- and wave w takes heads w * HPW .. w * HPW + HPW - 1 (its two
 // half-waves alternate between them).  A tile then costs each wave a quarter
 // of the logits and of P.V, and the waves' states need no merging: each wave
-// owns the whole state of its heads.
+// owns the whole state of its heads.  KSEL > 0: the workgroup ranks its
+// stream's kept chunks itself before its first tile (KSEL keys per thread,
+// attn_select_stream) instead of reading them.
 constexpr int kShWaves = 4;
 constexpr int kShThreads = kShWaves * kWave;
 constexpr int kShMaxRowBytes = 256;
 constexpr int kShLoads = kTileTokens * (kShMaxRowBytes / 16) / kShThreads;  // per thread per array
 
-template <typename T, int HM, int CV>
+template <typename T, int HM, int CV, int KSEL>
 __global__ __launch_bounds__(kShThreads) void attn_portable_sh_kernel(AttnArgs a) {
   constexpr int HPW = HM / kShWaves;  // heads per wave
   constexpr int JH = HPW / 2;         // heads per half-wave
@@ -442,6 +445,7 @@ __global__ __launch_bounds__(kShThreads) void attn_portable_sh_kernel(AttnArgs a
   __shared__ __attribute__((aligned(16))) float s_p[HM][kTileTokens];
   __shared__ float s_stat[3][HM];  // per head: running max, sum, this tile's rescale
   __shared__ int32_t s_last;
+  static_assert(sizeof(SelectLds<kShThreads>) <= sizeof(s_k), "the top-k scratch aliases s_k");
 
   const int tid = threadIdx.x;
   const int wave = tid / kWave, lane = tid & (kWave - 1);
@@ -450,6 +454,26 @@ __global__ __launch_bounds__(kShThreads) void attn_portable_sh_kernel(AttnArgs a
   const int32_t b = run.b;
   const int32_t H = a.H, dqk = a.dqk, dv = a.dv, C = a.C, tpc = a.tiles_per_chunk;
   constexpr int ES = sizeof(T);
+
+  // the stream's queries, HM x dqk (rows past H zero), kQPer values per thread
+  constexpr int kQPer = HM * (kShMaxRowBytes / 2) / kShThreads;
+  float qreg[kQPer];
+  auto load_q = [&]() {
+    const unsigned char* qb = static_cast<const unsigned char*>(a.q) +
+                              static_cast<int64_t>(b) * H * dqk * ES;
+#pragma unroll
+    for (int u = 0; u < kQPer; ++u) {
+      const int32_t i = u * kShThreads + tid;
+      qreg[u] = i < H * dqk ? widen1<T>(qb + i * ES) : 0.f;
+    }
+  };
+  if constexpr (KSEL > 0) {  // the query loads are in flight while the top-k runs
+    load_q();
+    attn_select_stream<kShThreads, KSEL>(a, run, s_slot,
+                                         *reinterpret_cast<SelectLds<kShThreads>*>(s_k));
+  }
+  // s_slot holds the run's kept chunks, or the whole stream's when ranked here
+  const int32_t slot_first = KSEL > 0 ? 0 : run.slot_first;
   PortGeom g;
   g.kb = dqk * ES;
   g.vb = dv * ES;
@@ -467,7 +491,7 @@ __global__ __launch_bounds__(kShThreads) void attn_portable_sh_kernel(AttnArgs a
     const int32_t t = run.t_begin + i;
     const int32_t j = t / tpc;
     const int32_t sub = t - j * tpc;
-    int64_t n = s_slot[min(j - run.slot_first, kMaxRunSlots - 1)];
+    int64_t n = s_slot[min(j - slot_first, kMaxRunSlots - 1)];
     n = n < 0 ? 0 : (n > last_chunk ? last_chunk : n);
     int64_t valid = run.len - n * C;
     if (valid > C) valid = C;
@@ -521,11 +545,11 @@ __global__ __launch_bounds__(kShThreads) void attn_portable_sh_kernel(AttnArgs a
     tile_of(0, &row_a, &nv_a);
     issue(row_a, nv_a, ra);
   }
-  {
-    const unsigned char* qb = static_cast<const unsigned char*>(a.q) +
-                              static_cast<int64_t>(b) * H * dqk * ES;
-    for (int32_t i = tid; i < H * dqk; i += kShThreads) s_q[i] = widen1<T>(qb + i * ES);
-    for (int32_t i = H * dqk + tid; i < HM * dqk; i += kShThreads) s_q[i] = 0.f;
+  if constexpr (KSEL == 0) load_q();
+#pragma unroll
+  for (int u = 0; u < kQPer; ++u) {
+    const int32_t i = u * kShThreads + tid;
+    if (i < HM * dqk) s_q[i] = qreg[u];
   }
   if (tid < HM) {
     s_stat[0][tid] = -INFINITY;
@@ -676,14 +700,25 @@ __global__ __launch_bounds__(kShThreads) void attn_portable_sh_kernel(AttnArgs a
     __hip_atomic_store(a.counters + b, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <typename T, int HM>
-hipError_t launch_portable_sh(const AttnArgs& a, int64_t grid, hipStream_t st) {
+template <typename T, int HM, int KSEL>
+hipError_t launch_portable_sh_k(const AttnArgs& a, int64_t grid, hipStream_t st) {
   const dim3 g(static_cast<uint32_t>(grid));
   if (a.dv <= kWave)
-    hipLaunchKernelGGL((attn_portable_sh_kernel<T, HM, 1>), g, dim3(kShThreads), 0, st, a);
+    hipLaunchKernelGGL((attn_portable_sh_kernel<T, HM, 1, KSEL>), g, dim3(kShThreads), 0, st, a);
   else
-    hipLaunchKernelGGL((attn_portable_sh_kernel<T, HM, 2>), g, dim3(kShThreads), 0, st, a);
+    hipLaunchKernelGGL((attn_portable_sh_kernel<T, HM, 2, KSEL>), g, dim3(kShThreads), 0, st, a);
   return hipGetLastError();
+}
+
+// KSEL from the longest stream when the kernel ranks the kept chunks itself
+template <typename T, int HM>
+hipError_t launch_portable_sh(const AttnArgs& a, int32_t max_chunks, int64_t grid,
+                              hipStream_t st) {
+  if (a.sel_scores == nullptr) return launch_portable_sh_k<T, HM, 0>(a, grid, st);
+  if (max_chunks <= kShThreads) return launch_portable_sh_k<T, HM, 1>(a, grid, st);
+  if (max_chunks <= kShThreads * 8) return launch_portable_sh_k<T, HM, 8>(a, grid, st);
+  if (max_chunks <= kShThreads * 16) return launch_portable_sh_k<T, HM, 16>(a, grid, st);
+  return hipErrorNotSupported;
 }
 
 template <typename T, int HM, int CV>
@@ -712,14 +747,16 @@ hipError_t launch_portable_h(const AttnArgs& a, int64_t grid, hipStream_t st) {
 }
 
 template <typename T>
-hipError_t launch_portable_t(const AttnArgs& a, int64_t grid, hipStream_t st) {
+hipError_t launch_portable_t(const AttnArgs& a, int32_t max_chunks, int64_t grid,
+                             hipStream_t st) {
   if (a.split_heads) {
     if (a.H <= 4 || a.H > kPortHeads || a.dqk * static_cast<int>(sizeof(T)) > kShMaxRowBytes ||
         a.dv * static_cast<int>(sizeof(T)) > kShMaxRowBytes)
       return hipErrorNotSupported;
-    if (a.H <= 8) return launch_portable_sh<T, 8>(a, grid, st);
-    return launch_portable_sh<T, 16>(a, grid, st);
+    if (a.H <= 8) return launch_portable_sh<T, 8>(a, max_chunks, grid, st);
+    return launch_portable_sh<T, 16>(a, max_chunks, grid, st);
   }
+  if (a.sel_scores != nullptr) return hipErrorNotSupported;
   if (a.H <= 4) return launch_portable_h<T, 4>(a, grid, st);
   if (a.H <= 8) return launch_portable_h<T, 8>(a, grid, st);
   return launch_portable_h<T, 16>(a, grid, st);
@@ -732,6 +769,10 @@ bool portable_attn_supported(const lsa_shape& s) {
          s.head_dim_qk <= kPortMaxDim && s.head_dim_v >= 1 && s.head_dim_v <= kPortMaxDim;
 }
 
+bool portable_select_in_kernel_supported(const lsa_shape& s, const AttnPlan& plan) {
+  return plan.split_heads != 0 && s.max_chunks <= kShThreads * 16 && s.max_k <= kMaxRunSlots;
+}
+
 bool portable_split_heads(const lsa_shape& s, int64_t total_tiles, int32_t target) {
   const int es = s.dtype == LSA_DTYPE_BF16 ? 2 : 4;
   return portable_attn_supported(s) && s.num_q_heads > 4 &&
@@ -741,8 +782,8 @@ bool portable_split_heads(const lsa_shape& s, int64_t total_tiles, int32_t targe
 
 hipError_t launch_attn_portable(const lsa_shape& s, const AttnArgs& a, int64_t grid,
                                 hipStream_t st) {
-  if (s.dtype == LSA_DTYPE_BF16) return launch_portable_t<uint16_t>(a, grid, st);
-  return launch_portable_t<float>(a, grid, st);
+  if (s.dtype == LSA_DTYPE_BF16) return launch_portable_t<uint16_t>(a, s.max_chunks, grid, st);
+  return launch_portable_t<float>(a, s.max_chunks, grid, st);
 }
 
 }  // namespace lsa

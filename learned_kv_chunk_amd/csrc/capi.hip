@@ -522,10 +522,13 @@ static lsa_status enqueue_step(const lsa_shape* shape, const AttnSetup& setup,
   const bool pool = x.materialize_pool != 0;
   const hipStream_t hs = static_cast<hipStream_t>(hip_stream);
   (void)hipGetLastError();
-  // the multi-query kernel ranks each stream's kept chunks in its prologue
-  // (no select launch, no kept-index round trip) when it reads the store
+  // the multi-query kernel and the split-heads vector-ALU kernel rank each
+  // stream's kept chunks in their prologue (no select launch, no kept-index
+  // round trip) when they read the store
   const bool select_in_attention =
-      x.reindex && !pool && !mla_attn_supported(*shape) && mqa_select_in_kernel_supported(*shape);
+      x.reindex && !pool && !mla_attn_supported(*shape) &&
+      (mqa_attn_supported(*shape) ? mqa_select_in_kernel_supported(*shape)
+                                  : portable_select_in_kernel_supported(*shape, setup.plan));
   if (x.reindex) {
     if (launch_score(*shape, x.q_idx_dev, x.emb_dev, x.chunk_off_dev, x.scores_dev, hs) !=
         hipSuccess)

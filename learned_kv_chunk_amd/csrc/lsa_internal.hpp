@@ -142,6 +142,9 @@ bool portable_attn_supported(const lsa_shape& s);
 // total_tiles tiles on `target` compute units (small inputs, 5-16 heads,
 // rows of at most 256 bytes).
 bool portable_split_heads(const lsa_shape& s, int64_t total_tiles, int32_t target);
+// Whether that form can rank the kept chunks in its prologue (streams of up
+// to 4096 chunks keeping up to kMaxRunSlots).
+bool portable_select_in_kernel_supported(const lsa_shape& s, const AttnPlan& plan);
 hipError_t launch_attn_portable(const lsa_shape& s, const AttnArgs& a, int64_t grid,
                                 hipStream_t st);
 hipError_t launch_attn_merge(const lsa_shape& s, const AttnArgs& a, const AttnPlan& plan,

@@ -285,33 +285,40 @@ def _mix(rng, n, values, counts, rest):
     return v
 
 
-def _scored_workload(scores_per_stream, keep, C=32):
-    """A bf16 MQA workload (16 heads, d = 64) whose chunk scores are exactly
-    the given bf16-representable values: the indexer query is the first unit
-    vector and chunk n's embedding holds its score in its first component
-    (every other product is 0 x 0, so the fp32 sum is the value itself)."""
+def _scored_workload(scores_per_stream, keep, C=32, base="cfg2"):
+    """A workload whose chunk scores are exactly the given values (for bf16,
+    bf16-representable ones): the indexer query is the first unit vector and
+    chunk n's embedding holds its score in its first component (every other
+    product is 0 x 0, so the fp32 sum is the value itself).  base "cfg2": bf16
+    MQA, 16 heads, d = 64; "cfg1": fp32, 8 heads, d = 64 (the vector-ALU
+    kernel)."""
     lengths = tuple(len(v) * C for v in scores_per_stream)
-    cfg = wl.small_variant("cfg2", lengths=lengths, n_needles=0, chunk_size=C, num_q_heads=16,
-                           head_dim_qk=64, head_dim_v=64)
+    heads = dict(num_q_heads=16, head_dim_qk=64, head_dim_v=64) if base == "cfg2" else {}
+    cfg = wl.small_variant(base, lengths=lengths, n_needles=0, chunk_size=C, **heads)
     w = wl.make_workload(cfg)
-    vals = np.concatenate([_bf16_exact(v) for v in scores_per_stream])
+    bf16 = cfg.dtype == "bf16"
+    vals = np.concatenate([_bf16_exact(v) if bf16 else np.asarray(v, np.float32)
+                           for v in scores_per_stream])
     emb = np.zeros((len(vals), cfg.index_dim), np.float32)
     emb[:, 0] = vals
     q_idx = np.zeros((cfg.batch, cfg.index_dim), np.float32)
     q_idx[:, 0] = 1.0
+    enc = wl.to_bf16_bits if bf16 else (lambda x: x)
     keep = np.asarray(keep, np.int32)
     sel_off = np.concatenate([[0], np.cumsum(keep)]).astype(np.int32)
-    return dataclasses.replace(w, emb=wl.to_bf16_bits(emb), q_idx=wl.to_bf16_bits(q_idx),
-                               keep=keep, sel_off=sel_off), vals
+    return dataclasses.replace(w, emb=enc(emb), q_idx=enc(q_idx), keep=keep,
+                               sel_off=sel_off), vals
 
 
-def _select_in_attention_case(scores_per_stream, keep):
-    w, vals = _scored_workload(scores_per_stream, keep)
+def _select_in_attention_case(scores_per_stream, keep, base="cfg2"):
+    w, vals = _scored_workload(scores_per_stream, keep, base=base)
     for per in (0, 1):  # per = 1: one tile per workgroup, so each stream ranks in many
         d = dev.upload(w, "cuda", attn_tiles_per_block=per, with_pool=False)
         s = d.shape
-        # the shapes the decode step ranks inside the attention kernel
-        assert s.dtype == torch.bfloat16 and s.max_chunks <= 4096 and s.max_k <= 1024
+        # the shapes the decode step ranks inside the attention kernel (the
+        # vector-ALU kernel: in its split-heads form, at most one tile per CU)
+        assert s.max_chunks <= 4096 and s.max_k <= 1024
+        assert s.dtype == torch.bfloat16 or int(w.sel_off[-1]) <= 256
         d.sel_idx.fill_(-1)
         d.step(0, reindex=True, materialize_pool=False)
         torch.cuda.synchronize()
@@ -325,7 +332,26 @@ def _select_in_attention_case(scores_per_stream, keep):
         np.testing.assert_array_equal(dev.to_host(alone), sel)
         # every workgroup of a stream attended over the same kept set
         o_ref, l_ref = P.oracle_attention_on(w, 0, sel)
-        P.check_attention("bf16", dev.to_host(d.out), dev.to_host(d.lse), o_ref, l_ref)
+        P.check_attention(w.cfg.dtype, dev.to_host(d.out), dev.to_host(d.lse), o_ref, l_ref)
+
+
+def test_select_in_split_heads_attention():
+    # the fp32 vector-ALU kernel in its split-heads form (few kept tiles)
+    # ranks the kept chunks too: streams of up to 256, 2048 and 4096 chunks
+    # (one, eight and sixteen keys per thread) with ties, NaN, infinities and
+    # the early-stop mixes, keeping few chunks each
+    rng = np.random.default_rng(13)
+    normal = rng.standard_normal(4096).astype(np.float32)
+    special = normal[:3000].copy()
+    special[rng.choice(3000, 40, replace=False)] = np.nan
+    special[:3] = [np.inf, -np.inf, -0.0]
+    ties = (np.round(normal * 4) / 4).astype(np.float32)
+    short = [ties[:200], special[:256], _mix(rng, 64, [2.0, 1.5], [3, 4], 1.0), normal[:17]]
+    _select_in_attention_case(short, [20, 9, 5, 17], base="cfg1")
+    mid = [ties[:2048], special[:1500], _mix(rng, 2048, [1.75, 1.5], [40, 5], 1.0), normal[:300]]
+    _select_in_attention_case(mid, [63, 30, 42, 1], base="cfg1")
+    long = [normal, special, ties, _mix(rng, 2500, [4.0], [50], 0.25)]
+    _select_in_attention_case(long, [63, 40, 60, 50], base="cfg1")
 
 
 def test_select_in_attention_ties_nan_and_early_stop():
