@@ -291,7 +291,7 @@ def _scored_workload(scores_per_stream, keep, C=32, base="cfg2"):
     chunk n's embedding holds its score in its first component (every other
     product is 0 x 0, so the fp32 sum is the value itself).  base "cfg2": bf16
     MQA, 16 heads, d = 64; "cfg1": fp32, 8 heads, d = 64 (the vector-ALU
-    kernel)."""
+    kernel); "cfg4": absorbed MLA, 64 heads."""
     lengths = tuple(len(v) * C for v in scores_per_stream)
     heads = dict(num_q_heads=16, head_dim_qk=64, head_dim_v=64) if base == "cfg2" else {}
     cfg = wl.small_variant(base, lengths=lengths, n_needles=0, chunk_size=C, **heads)
@@ -315,9 +315,10 @@ def _select_in_attention_case(scores_per_stream, keep, base="cfg2"):
     for per in (0, 1):  # per = 1: one tile per workgroup, so each stream ranks in many
         d = dev.upload(w, "cuda", attn_tiles_per_block=per, with_pool=False)
         s = d.shape
-        # the shapes the decode step ranks inside the attention kernel (the
-        # vector-ALU kernel: in its split-heads form, at most one tile per CU)
-        assert s.max_chunks <= 4096 and s.max_k <= 1024
+        # within the shapes whose decode step ranks inside the attention
+        # kernel (MQA up to 4096 chunks; the vector-ALU kernel in its
+        # split-heads form: at most one tile per CU); MLA runs the select launch
+        assert s.max_chunks <= (8192 if base == "cfg4" else 4096) and s.max_k <= 1024
         assert s.dtype == torch.bfloat16 or int(w.sel_off[-1]) <= 256
         d.sel_idx.fill_(-1)
         d.step(0, reindex=True, materialize_pool=False)
@@ -333,6 +334,22 @@ def _select_in_attention_case(scores_per_stream, keep, base="cfg2"):
         # every workgroup of a stream attended over the same kept set
         o_ref, l_ref = P.oracle_attention_on(w, 0, sel)
         P.check_attention(w.cfg.dtype, dev.to_host(d.out), dev.to_host(d.lse), o_ref, l_ref)
+
+
+def test_decode_step_mla_adversarial_scores():
+    # the decode step of absorbed MLA (the select launch, then the MLA kernel)
+    # on the same kinds of scores: ties, NaN, infinities and the early-stop
+    # mixes up to 2048 chunks, one stream of 8192 (the bucket pass), keep one
+    rng = np.random.default_rng(14)
+    normal = wl.bf16_bits_to_f32(wl.to_bf16_bits(rng.standard_normal(8192).astype(np.float32)))
+    special = normal[:2048].copy()
+    special[rng.choice(2048, 30, replace=False)] = np.nan
+    special[:3] = [np.inf, -np.inf, -0.0]
+    ties = np.round(normal * 4) / 4
+    short = [special, ties[:1500], _mix(rng, 900, [1.75, 1.5], [60, 9], 1.0), normal[:40]]
+    _select_in_attention_case(short, [164, 120, 64, 1], base="cfg4")
+    _select_in_attention_case([normal], [655], base="cfg4")
+    _select_in_attention_case([ties], [700], base="cfg4")
 
 
 def test_select_in_split_heads_attention():
