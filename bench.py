@@ -918,19 +918,14 @@ def main():
         r = replicas[i % reps]
         lsa.score(r.shape, r.q_idx, r.emb, r.chunk_off, scores=r.scores)
 
-    kernel_file = os.path.join(ROOT, "learned_kv_chunk_amd", "csrc",
-                               "attn_mla.hip" if cfg.v_aliases_k else
-                               ("attn_mqa.hip" if cfg.dtype == "bf16" else "attn_portable.hip"))
-    # the MQA kernel merges each stream itself when streams average at most
-    # eight of the device's workgroups (the library's rule)
-    tpc = -(-cfg.chunk_size // 32)
-    wgs_expected = (-(-int(w.sel_off[-1]) * tpc // args.tiles_per_block) if args.tiles_per_block
-                    else torch.cuda.get_device_properties(0).multi_processor_count)
-    fused = (cfg.dtype == "bf16" and not cfg.v_aliases_k and
-             cfg.num_q_heads * cfg.head_dim_v <= 2048 and wgs_expected <= 8 * cfg.batch)
-    attn_desc = ("attn_mqa: split-KV partials and their LSE merge in one kernel" if fused else
-                 os.path.basename(kernel_file).replace(".hip", "") +
-                 " partial kernel + LSE merge kernel (the attention phase)")
+    # how the library runs attention for this shape (kernel, merge in the
+    # kernel or a merge launch), as lsa_attention_plan reports it
+    attn_plan = lsa.attention_plan(replicas[0].shape)
+    fused = attn_plan["merge_in_kernel"]
+    kernel_file = os.path.join(ROOT, "learned_kv_chunk_amd", "csrc", attn_plan["kernel"] + ".hip")
+    kname = attn_plan["kernel"] + (" (split heads)" if attn_plan["split_heads"] else "")
+    attn_desc = (kname + ": split-KV partials and their LSE merge in one kernel" if fused else
+                 kname + " partial kernel + LSE merge kernel (the attention phase)")
     if args.attention_only:
         attn_us = _graph_us(attention, args.steps, warm=4)
         attn_gbs = attn_bytes / attn_us / 1e3
@@ -1138,6 +1133,7 @@ def main():
             "avg_launch_us_events_in_step": attn_us_events,
             "measured_copy_gbs": copy_gbs,
             "frac_of_measured_copy": attn_gbs / copy_gbs,
+            "attention_plan": attn_plan,
         },
         "score_kernel": {"us": score_us, "algorithmic_bytes": int(score_bytes),
                          "gbs": score_bytes / score_us / 1e3,

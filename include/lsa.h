@@ -129,6 +129,32 @@ int32_t lsa_keep_count(int32_t n_chunks, int32_t ratio_num, int32_t ratio_den,
  * is zeroed once when allocated, not per call. */
 size_t lsa_workspace_bytes(const lsa_shape* shape);
 
+/* How lsa_sparse_decode_attn / lsa_decode_step would run attention for this
+ * shape on the current device (a description for measurement and
+ * diagnostics; nothing is enqueued).  Wiki note "Key points": the cost of
+ * decode is the KV traffic; this names the kernel that streams it and
+ * whether its split-KV partials are merged by a separate launch. */
+enum { LSA_ATTN_KERNEL_MQA = 0, LSA_ATTN_KERNEL_MLA = 1, LSA_ATTN_KERNEL_VECTOR = 2 };
+typedef struct {
+  int64_t grid;             /* workgroups of the attention launch (an upper bound
+                               of the ones that do work) */
+  int64_t partial_rows;     /* split-KV partial results the workspace holds */
+  int32_t kernel;           /* LSA_ATTN_KERNEL_* */
+  int32_t tiles_per_chunk;  /* 32-token tiles per chunk */
+  int32_t merge_in_kernel;  /* 1: each stream's last workgroup merges its
+                               partials (no merge launch); 0: a merge launch */
+  int32_t split_heads;      /* 1: the vector-ALU kernel's split-heads form */
+  int32_t select_in_kernel; /* 1: a re-indexing lsa_decode_step over the store
+                               ranks the kept chunks inside the attention
+                               kernel (no select launch) */
+  int32_t reserved;         /* 0 */
+} lsa_attn_plan_info;
+
+/* Fills *info; LSA_ERR_INVALID_ARGUMENT for a null pointer or a shape
+ * lsa_sparse_decode_attn would refuse, LSA_ERR_UNSUPPORTED for an
+ * unsupported one (then *info is untouched). */
+lsa_status lsa_attention_plan(const lsa_shape* shape, lsa_attn_plan_info* info);
+
 /* ---------------------------------------------------------------------------
  * Chunk scoring (dual-encoder relevance).  Wiki note flowchart and "Key
  * points"; dimensionstp review sections 2-1 and 3-2-4; abstract v2: the

@@ -103,6 +103,15 @@ bool fuse_merge_in_kernel(const lsa_shape& s, const AttnPlan& plan) {
   return wgs_expected <= per_stream * static_cast<int64_t>(s.batch);
 }
 
+// Whether a re-indexing decode step over the store ranks the kept chunks in
+// the attention kernel's prologue (no select launch, no kept-index round
+// trip): the multi-query kernel and the split-heads vector-ALU kernel can.
+bool select_in_attention_kernel(const lsa_shape& s, const AttnPlan& plan) {
+  if (mla_attn_supported(s)) return false;
+  return mqa_attn_supported(s) ? mqa_select_in_kernel_supported(s)
+                               : portable_select_in_kernel_supported(s, plan);
+}
+
 // The split-KV plan of a validated attention shape on the current device and
 // the workspace layout it implies (computed once per call).
 struct AttnSetup {
@@ -195,7 +204,7 @@ const char* lsa_status_string(lsa_status status) {
   }
 }
 
-int32_t lsa_abi_version(void) { return 3; }
+int32_t lsa_abi_version(void) { return 4; }
 
 int32_t lsa_reindex_due(int64_t step, int32_t reindex_every) {
   if (reindex_every < 1 || step < 0) return -1;
@@ -214,6 +223,27 @@ int32_t lsa_keep_count(int32_t n_chunks, int32_t ratio_num, int32_t ratio_den, i
 size_t lsa_workspace_bytes(const lsa_shape* shape) {
   if (check_attn_shape(shape) != LSA_OK) return 0;
   return partial_layout(*shape, make_attn_plan(*shape, device_cu_count())).total;
+}
+
+lsa_status lsa_attention_plan(const lsa_shape* shape, lsa_attn_plan_info* info) {
+  if (info == nullptr) return LSA_ERR_INVALID_ARGUMENT;
+  const lsa_status st = check_attn_shape(shape);
+  if (st != LSA_OK) return st;
+  const lsa_shape& s = *shape;
+  const AttnPlan plan = make_attn_plan(s, device_cu_count());
+  lsa_attn_plan_info r;
+  r.grid = plan.grid;
+  r.partial_rows = plan.ws_rows;
+  r.kernel = mla_attn_supported(s)   ? LSA_ATTN_KERNEL_MLA
+             : mqa_attn_supported(s) ? LSA_ATTN_KERNEL_MQA
+                                     : LSA_ATTN_KERNEL_VECTOR;
+  r.tiles_per_chunk = plan.tiles_per_chunk;
+  r.merge_in_kernel = fuse_merge_in_kernel(s, plan) ? 1 : 0;
+  r.split_heads = plan.split_heads;
+  r.select_in_kernel = select_in_attention_kernel(s, plan) ? 1 : 0;
+  r.reserved = 0;
+  *info = r;
+  return LSA_OK;
 }
 
 lsa_status lsa_score(const lsa_shape* shape, const void* q_idx_dev, const void* emb_dev,
@@ -522,13 +552,8 @@ static lsa_status enqueue_step(const lsa_shape* shape, const AttnSetup& setup,
   const bool pool = x.materialize_pool != 0;
   const hipStream_t hs = static_cast<hipStream_t>(hip_stream);
   (void)hipGetLastError();
-  // the multi-query kernel and the split-heads vector-ALU kernel rank each
-  // stream's kept chunks in their prologue (no select launch, no kept-index
-  // round trip) when they read the store
   const bool select_in_attention =
-      x.reindex && !pool && !mla_attn_supported(*shape) &&
-      (mqa_attn_supported(*shape) ? mqa_select_in_kernel_supported(*shape)
-                                  : portable_select_in_kernel_supported(*shape, setup.plan));
+      x.reindex && !pool && select_in_attention_kernel(*shape, setup.plan);
   if (x.reindex) {
     if (launch_score(*shape, x.q_idx_dev, x.emb_dev, x.chunk_off_dev, x.scores_dev, hs) !=
         hipSuccess)

@@ -88,6 +88,22 @@ class StepArgs(ctypes.Structure):
     ]
 
 
+class AttnPlanInfo(ctypes.Structure):
+    _fields_ = [
+        ("grid", ctypes.c_int64),
+        ("partial_rows", ctypes.c_int64),
+        ("kernel", ctypes.c_int32),
+        ("tiles_per_chunk", ctypes.c_int32),
+        ("merge_in_kernel", ctypes.c_int32),
+        ("split_heads", ctypes.c_int32),
+        ("select_in_kernel", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+    ]
+
+
+ATTN_KERNEL_NAMES = {0: "attn_mqa", 1: "attn_mla", 2: "attn_portable"}
+
+
 # Exported symbols of include/lsa.h with their (argtypes, restype).
 _P = ctypes.c_void_p
 _I32 = ctypes.c_int32
@@ -99,6 +115,7 @@ _SIGNATURES = {
     "lsa_reindex_due": ([ctypes.c_int64, _I32], _I32),
     "lsa_keep_count": ([_I32, _I32, _I32, _I32], _I32),
     "lsa_workspace_bytes": ([ctypes.POINTER(Shape)], ctypes.c_size_t),
+    "lsa_attention_plan": ([ctypes.POINTER(Shape), ctypes.POINTER(AttnPlanInfo)], _I32),
     "lsa_score": ([ctypes.POINTER(Shape), _P, _P, _P, _P, _P], _I32),
     "lsa_score_fp8_multihead": ([ctypes.POINTER(Shape), _I32, _I32, _P, _P, _P, _P, _P, _P],
                                 _I32),
@@ -199,6 +216,19 @@ def keep_count(n_chunks: int, ratio_num: int, ratio_den: int, round_up: bool) ->
 
 def workspace_bytes(shape: ProblemShape) -> int:
     return int(library().lsa_workspace_bytes(ctypes.byref(shape.c())))
+
+
+def attention_plan(shape: ProblemShape) -> dict:
+    """lsa_attention_plan: how attention runs for this shape on the current
+    device (kernel, launch grid, whether the partials merge in the kernel,
+    split-heads form, top-k inside the kernel)."""
+    info = AttnPlanInfo()
+    _check(library().lsa_attention_plan(ctypes.byref(shape.c()), ctypes.byref(info)),
+           "lsa_attention_plan")
+    return {"kernel": ATTN_KERNEL_NAMES.get(info.kernel, str(info.kernel)), "grid": info.grid,
+            "partial_rows": info.partial_rows, "tiles_per_chunk": info.tiles_per_chunk,
+            "merge_in_kernel": bool(info.merge_in_kernel), "split_heads": bool(info.split_heads),
+            "select_in_kernel": bool(info.select_in_kernel)}
 
 
 def allocate_workspace(shape: ProblemShape, device) -> torch.Tensor:

@@ -36,7 +36,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_status_strings_and_version():
-    assert lsa.library().lsa_abi_version() == 3
+    assert lsa.library().lsa_abi_version() == 4
     for code, name in [(0, "LSA_OK"), (1, "LSA_ERR_INVALID_ARGUMENT"), (2, "LSA_ERR_UNSUPPORTED"),
                        (3, "LSA_ERR_WORKSPACE_TOO_SMALL"), (4, "LSA_ERR_HIP")]:
         assert lsa.status_string(code) == name
@@ -59,6 +59,35 @@ def shape(**kw):
                 total_k=16 * 276)
     base.update(kw)
     return lsa.ProblemShape(**base)
+
+
+def test_attention_plan_names_kernel_merge_and_form():
+    # no GPU here: the plan is made for the 256 compute units of an MI355X
+    p = lsa.attention_plan(shape())
+    assert p["kernel"] == "attn_mqa" and not p["split_heads"] and p["tiles_per_chunk"] == 2
+    assert not p["merge_in_kernel"] and p["select_in_kernel"]  # 16 workgroups per stream
+    assert p["grid"] >= 256 and p["partial_rows"] >= p["grid"]
+    # 32 ragged streams: eight workgroups each on average, merged in the kernel
+    p = lsa.attention_plan(shape(batch=32, max_chunks=4096, max_k=553, total_chunks=68733,
+                                 total_k=9294))
+    assert p["merge_in_kernel"] and p["select_in_kernel"]
+    mla = lsa.attention_plan(shape(batch=1, chunk_size=128, index_dim=256, num_q_heads=64,
+                                   head_dim_qk=576, head_dim_v=512, v_aliases_k=True,
+                                   max_chunks=8192, max_k=655, total_chunks=8192, total_k=655))
+    assert mla["kernel"] == "attn_mla" and not mla["merge_in_kernel"]
+    assert not mla["select_in_kernel"] and mla["tiles_per_chunk"] == 4
+    # the 4K fp32 workload: 16 tiles, the split-heads form, merged in the kernel
+    f32 = dict(batch=1, index_dim=64, num_q_heads=8, head_dim_qk=64, head_dim_v=64,
+               dtype=torch.float32, max_chunks=64, max_k=8, total_chunks=64, total_k=8)
+    p = lsa.attention_plan(shape(**f32))
+    assert p["kernel"] == "attn_portable" and p["split_heads"] and p["merge_in_kernel"]
+    assert p["select_in_kernel"]
+    # more tiles than compute units: the tile-parallel form, no top-k inside
+    p = lsa.attention_plan(shape(**dict(f32, max_chunks=4096, max_k=600, total_chunks=4096,
+                                        total_k=600)))
+    assert not p["split_heads"] and not p["select_in_kernel"]
+    with pytest.raises(lsa.LsaError):
+        lsa.attention_plan(shape(num_q_heads=100))
 
 
 def test_workspace_sizes_positive_and_monotone():
