@@ -25,11 +25,12 @@
 // load hints that suit it best; more loads in flight per CU only lengthen
 // the memory queues (a third register set per wave: 32.4 us).  The
 // waves of a team take interleaved tiles of the workgroup's run, then merge
-// their (max, sum, output) states through LDS into one partial result.  The
-// stream's partials are combined by the stream's last workgroup to finish
-// (arrival counter with release / acquire ordering at device scope,
-// merge_stream_block), so attention is one launch; a stream served by a
-// single workgroup writes its output directly.
+// their (max, sum, output) states through LDS into one partial result.  When
+// streams average few workgroups the stream's partials are combined by its
+// last workgroup to finish (arrival counter with release / acquire ordering
+// at device scope, merge_stream_block), so attention is one launch, and a
+// stream served by a single workgroup writes its output directly; otherwise
+// the merge launch of attn_common.hip combines them.
 #include <math.h>
 
 #include "lsa_internal.hpp"

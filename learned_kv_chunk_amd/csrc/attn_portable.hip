@@ -4,8 +4,10 @@
 //
 // Dimensionstp review, section 3-2-3 steps 6-7: softmax attention over the
 // tokens of the kept chunks.  A workgroup owns a run of 32-token tiles of one
-// stream; its waves take the run's tiles in turn (wave w: tiles w, w + NW,
-// ...).  Per tile a wave
+// stream.  Two forms: on short inputs with 5-16 heads the split-heads form
+// further below (the waves share each tile and split its heads); otherwise
+// the tile-parallel form here, whose waves take the run's tiles in turn
+// (wave w: tiles w, w + NW, ...).  Per tile a wave
 //   * loads the tile's K and V rows as 16-byte vectors of consecutive
 //     addresses (a tile of a chunk is contiguous in memory: one round trip
 //     for the whole tile), the next tile's loads already in flight in a
