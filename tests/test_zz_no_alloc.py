@@ -70,6 +70,41 @@ def test_static_step_equals_workspace_step_twice(first, second):
     assert sizes[1] < sizes[0] <= lsa.STATIC_SCRATCH_BYTES, sizes
 
 
+@pytest.mark.parametrize("name", ["cfg5", "cfg2"])
+def test_static_step_replayed_from_a_graph(name):
+    # the callers it is for capture it: a re-indexing step (its partials merged
+    # in the kernel for the ragged batch, by the merge launch for 16 x 128K)
+    # captured once, replayed three times with eager work and a different
+    # eager step between the replays; every replay equals the eager step bit
+    # for bit
+    w = wl.make_workload(_cfg(name))
+    d = dev.upload(w, "cuda")
+    _static_step(d, 0)
+    sel_e, out_e, lse_e = _host(d)
+    d.queries(1)  # every input the loop uses exists before the capture
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        _static_step(d, 0)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        _static_step(d, 0)
+    for _ in range(3):
+        d.sel_idx.fill_(-1)
+        d.out.fill_(float("nan"))
+        d.lse.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        sel_r, out_r, lse_r = _host(d)
+        np.testing.assert_array_equal(sel_r, sel_e)
+        np.testing.assert_array_equal(out_r, out_e)
+        np.testing.assert_array_equal(lse_r, lse_e)
+        _static_step(d, 1, reindex=False)
+        torch.cuda.synchronize()
+
+
 def test_static_step_refuses_partials_beyond_the_scratch():
     w = wl.make_workload(wl.small_variant("cfg2"))
     d = dev.upload(w, "cuda")
