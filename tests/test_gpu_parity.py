@@ -152,6 +152,31 @@ def test_reruns_are_bit_identical():
         np.testing.assert_array_equal(x, y)
 
 
+def test_concurrent_steps_on_two_streams_match_sequential_ones():
+    # the library keeps no state between calls: two workloads (each its own
+    # workspace) stepped on two HIP streams at once give what each gives alone
+    loads = [small_workload(n) for n in ("cfg5", "cfg2", "cfg1")]
+    alone = []
+    for w, d in loads:
+        d.step(0, reindex=True)
+        torch.cuda.synchronize()
+        alone.append((dev.to_host(d.sel_idx), dev.to_host(d.out), dev.to_host(d.lse)))
+    for w, d in loads:
+        d.out.fill_(float("nan"))
+        d.sel_idx.fill_(-1)
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream() for _ in loads]
+    for rep in range(3):
+        for (w, d), st in zip(loads, streams):
+            with torch.cuda.stream(st):
+                d.step(0, reindex=True)
+        torch.cuda.synchronize()
+        for (w, d), (sel, out, lse) in zip(loads, alone):
+            np.testing.assert_array_equal(dev.to_host(d.sel_idx), sel)
+            np.testing.assert_array_equal(dev.to_host(d.out), out)
+            np.testing.assert_array_equal(dev.to_host(d.lse), lse)
+
+
 def _single_stream(w: wl.Workload, b: int) -> wl.Workload:
     r0, r1 = int(w.tok_off[b]), int(w.tok_off[b + 1])
     c0, c1 = int(w.chunk_off[b]), int(w.chunk_off[b + 1])
