@@ -48,11 +48,15 @@ def test_phases_match_oracle(name):
 
 @pytest.mark.parametrize("name", SMALL)
 def test_fused_step_equals_phases_and_reuses_selection(name):
+    # the fused step (whose attention kernel may rank the kept chunks itself)
+    # gives the phases' scores, kept set and outputs bit for bit
     w, d = small_workload(name)
-    _, sel_a, out_a, lse_a = P.run_phases(d, 0)
+    s_a, sel_a, out_a, lse_a = P.run_phases(d, 0)
     d.sel_idx.fill_(-1)
+    d.scores.fill_(float("nan"))
     d.step(0, reindex=True, materialize_pool=w.cfg.materialize_pool)
     torch.cuda.synchronize()
+    np.testing.assert_array_equal(dev.to_host(d.scores), s_a)
     np.testing.assert_array_equal(dev.to_host(d.sel_idx), sel_a)
     np.testing.assert_array_equal(dev.to_host(d.out), out_a)
     np.testing.assert_array_equal(dev.to_host(d.lse), lse_a)
