@@ -390,3 +390,22 @@ def test_append_and_keep_recent_validation():
         DUMMY, DUMMY, need, None)
     assert av(s, sl=None) == lsa.LSA_ERR_INVALID_ARGUMENT
     assert av(s, sl=ctypes.c_void_p(0x100004)) == lsa.LSA_ERR_INVALID_ARGUMENT
+
+
+def test_header_compiles_as_c_and_links(tmp_path):
+    # include/lsa.h from plain C99, linked against liblsa.so: the host-side
+    # calls that need no GPU behave as the header states
+    import shutil
+    import subprocess
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("gcc not available")
+    src = os.path.join(os.path.dirname(os.path.abspath(__file__)), "native", "abi_from_c.c")
+    exe = str(tmp_path / "abi_from_c")
+    libdir = os.path.dirname(lsa.LIB_PATH)
+    r = subprocess.run([gcc, "-std=c99", "-Wall", "-Wextra", "-Werror", "-o", exe, src,
+                        "-L" + libdir, "-llsa", "-Wl,-rpath," + libdir],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0 and "abi_from_c ok" in r.stdout, r.stdout + r.stderr
