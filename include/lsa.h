@@ -382,14 +382,17 @@ lsa_status lsa_pool_delta_update(const lsa_shape* shape, const void* k_host, con
  * stores ([sum L][d]) and chunk sel_idx[s] of stream b is read in place.
  * kv_mode LSA_KV_POOL: k_base/v_base are pools written by lsa_gather_chunks
  * and slot s is read (sel_idx is still needed for the valid-token count of
- * partial chunks).  v_base must be NULL when v_aliases_k.
+ * partial chunks).  A stream's kept indices may come in any order (the
+ * select writes them ascending): the order changes only how the sums are
+ * split and rounded.  v_base must be NULL when v_aliases_k.
  * out_dev: [B][H][head_dim_v] fp32; lse_dev: [B][H] fp32 (may be NULL).
  * workspace_dev: >= lsa_workspace_bytes(shape) bytes, 256-byte aligned,
  * zero-filled before its first use (see lsa_workspace_bytes); it holds the
  * split partial results and the per-stream arrival counters of the kernels
- * that merge a stream in its last workgroup (the multi-query kernel; the
- * others run a separate merge pass); calls that share a workspace must not
- * run concurrently.
+ * that merge a stream in its last workgroup (the multi-query and vector-ALU
+ * kernels, for shapes whose streams have few workgroups; otherwise, and for
+ * absorbed latent attention, a separate merge pass runs); calls that share a
+ * workspace must not run concurrently.
  * Supported: bf16 with num_q_heads <= 64 and head_dim_qk == head_dim_v in
  * {64, 128} (multi-query); bf16 with head_dim_qk 576, head_dim_v 512,
  * v_aliases_k = 1 and 1 to 64 query heads (absorbed latent attention); fp32

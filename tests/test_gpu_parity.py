@@ -610,6 +610,36 @@ def test_stress_large_logits(std):
     assert (np.abs(lse - l_ref) / np.abs(l_ref)).max() <= 1e-4
 
 
+@pytest.mark.parametrize("name,variant", [("cfg2", {}), ("cfg3", {}), ("cfg4", {}),
+                                          ("cfg1", {}), ("cfg1", dict(num_q_heads=3))])
+def test_kept_index_order_changes_attention_only_by_rounding(name, variant):
+    # attention over a stream's kept chunks is a softmax over a set of tokens:
+    # the order of the kept indices in sel_idx (ascending from the select)
+    # changes the split and the summation order, never the set
+    w = wl.make_workload(wl.small_variant(name, **variant) if name != "cfg1" or variant
+                         else wl.CONFIGS["cfg1"])
+    d = dev.upload(w, "cuda")
+    _, sel, out_a, lse_a = P.run_phases(d, 0)
+    rng = np.random.default_rng(5)
+    perm = sel.copy()
+    for b in range(w.B):
+        s0, s1 = int(w.sel_off[b]), int(w.sel_off[b + 1])
+        perm[s0:s1] = rng.permutation(perm[s0:s1])
+    assert not np.array_equal(perm, sel)
+    sel_t = torch.from_numpy(perm).cuda()
+    out, lse = lsa.sparse_decode_attn(d.shape, d.queries(0), d.K, d.V, d.tok_off, sel_t,
+                                      d.sel_off, lsa.KV_STORE, workspace=d.workspace)
+    torch.cuda.synchronize()
+    out, lse = dev.to_host(out), dev.to_host(lse)
+    o_ref, l_ref = P.oracle_attention_on(w, 0, sel)
+    P.check_attention(w.cfg.dtype, out, lse, o_ref, l_ref)
+    scale = np.abs(out_a).max()
+    tol = 1e-5 if w.cfg.dtype == "f32" else 1e-2  # bf16: the weights are rounded to bf16
+    assert np.abs(out - out_a).max() <= tol * scale
+    assert np.abs(lse - lse_a).max() <= (1e-5 if w.cfg.dtype == "f32" else 1e-3) * np.abs(
+        lse_a).max()
+
+
 def test_hot_token_dominates():
     cfg = wl.small_variant("cfg2", n_needles=8)
     w = wl.make_workload(cfg)
