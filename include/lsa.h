@@ -418,7 +418,12 @@ lsa_status lsa_sparse_decode_attn(const lsa_shape* shape, int32_t kv_mode, const
  * caller decides through `reindex` (non-zero: re-index).  A re-index step
  * scores q_idx_dev as it is at that step, so a caller whose indexer query
  * changes every step passes the current one.  Every phase is one grid over
- * all streams; nothing returns to the host between phases.
+ * all streams; nothing returns to the host between phases.  Over the store,
+ * the multi-query kernel and the vector-ALU kernel on short inputs rank each
+ * stream's kept chunks in their own prologue (same keys, rule and algorithm
+ * as lsa_select_topk, so the same sel_idx, which the stream's first
+ * workgroup writes) instead of a select launch; lsa_attention_plan reports
+ * which.
  * reindex_every < 0, or step < 0 with reindex_every > 0, is
  * LSA_ERR_INVALID_ARGUMENT.
  * ev_attn_begin / ev_attn_end: optional hipEvent_t recorded on hip_stream
