@@ -202,8 +202,8 @@ __global__ __launch_bounds__(MW * kWave) void merge_kernel(AttnArgs a, int32_t n
   const int32_t h = ec / dv;
 
   int32_t first, count;
-  stream_wg_range(SelCsr{a.sel_off, a.uni_k}, a.B, b, a.tiles_per_chunk, a.per, a.target,
-                  &first, &count);
+  stream_wg_range(SelCsr{a.sel_off, a.uni_k, a.uni_wgs, a.uni_per}, a.B, b, a.tiles_per_chunk,
+                  a.per, a.target, &first, &count);
   const int32_t gs = max(kMergeBatch, ceil_div_i(count, kMergeGroups));
   const int32_t ngroups = ceil_div_i(count, gs);
 

@@ -171,6 +171,17 @@ lsa_status enqueue_attention(const lsa_shape& s, const AttnSetup& setup, int32_t
   a.per = plan.per;
   a.target = plan.target;
   a.uni_k = (s.flags & LSA_SHAPE_UNIFORM) ? s.max_k : 0;
+  a.uni_wgs = 0;
+  a.uni_per = 1;
+  if (a.uni_k > 0) {  // the split every stream of a uniform batch takes
+    const int32_t t = s.max_k * plan.tiles_per_chunk;
+    const int32_t total = static_cast<int32_t>(s.total_k) * plan.tiles_per_chunk;
+    const StreamSplit sp =
+        split_of_tiles(t, plan.tiles_per_chunk, plan.per, plan.target, total,
+                       uniform_balanced_run(s.batch, t, plan.per, plan.target));
+    a.uni_wgs = sp.wgs;
+    a.uni_per = sp.per;
+  }
   a.split_heads = plan.split_heads;
   a.scale_log2 = s.softmax_scale * 1.4426950408889634f;
   if (ev_begin && hipEventRecord(static_cast<hipEvent_t>(ev_begin), st) != hipSuccess)

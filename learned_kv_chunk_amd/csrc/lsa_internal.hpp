@@ -20,8 +20,16 @@ constexpr int kTileTokens = 32;        // tokens per attention tile
 // workgroup owns a run of consecutive tiles of one stream, and the W_b
 // workgroups of stream b are numbered consecutively in stream order.
 //  * fixed split (per > 0): W_b = ceil(T_b / per), runs of `per` tiles;
-//  * proportional split (per == 0): the device's `target` workgroups (one per
-//    CU) are shared out in proportion to the streams' tiles,
+//  * balanced split (per == 0, at most 64 streams): one run length p for the
+//    whole batch, the smallest for which the streams' ceil(T_b / p) runs
+//    number at most `target` (the device's CUs); stream b's W_b =
+//    ceil(T_b / p) workgroups then hold per_b = ceil(T_b / W_b) <= p tiles
+//    each.  The longest run is what the launch waits for, and a stream whose
+//    share of the CUs is fractional would otherwise get one workgroup
+//    carrying up to 1.5 times the average (32 ragged streams: 102 tiles
+//    against 72.6, where this plan's longest run is 79);
+//  * proportional split (per == 0, more than 64 streams): the `target`
+//    workgroups are shared out in proportion to the streams' tiles,
 //    w_b = max(1, round(T_b * target / T)), stream b's runs hold
 //    per_b = ceil(T_b / w_b) tiles, so every CU gets about T / target tiles,
 //    and W_b = ceil(T_b / per_b) <= w_b workgroups carry them.
@@ -94,6 +102,7 @@ struct AttnArgs {
   int32_t pool;           // 1: slot-indexed pool, 0: store indexed by chunk
   int32_t tiles_per_chunk, per, target;
   int32_t uni_k;          // k of every stream when the shape is uniform, else 0
+  int32_t uni_wgs, uni_per;  // uniform shape: every stream's workgroups and run length
   int32_t split_heads;    // AttnPlan::split_heads
   float scale_log2;       // softmax_scale * log2(e)
 };
@@ -176,38 +185,100 @@ __device__ __forceinline__ int32_t ceil_div_i(int32_t a, int32_t b) { return (a 
 struct SelCsr {
   const int32_t* off;
   int32_t uni;
+  int32_t uwgs, uper;  // uniform batch: every stream's W_b and run length (host-computed)
   __device__ __forceinline__ int32_t at(int32_t i) const { return uni > 0 ? i * uni : off[i]; }
 };
 
-// Split geometry of one stream (device): tiles T_b, workgroups W_b and tiles
-// per workgroup, given the plan and the total tile count T.
+// Split geometry of a stream of `tiles` tiles (host and device): workgroups
+// W_b and tiles per workgroup, given the plan, the total tile count T and the
+// balanced run length (0: not the balanced split).
 struct StreamSplit {
   int32_t tiles, wgs, per;
 };
-__device__ __forceinline__ StreamSplit stream_split(SelCsr sel_off, int32_t b, int32_t tpc,
-                                                    int32_t per, int32_t target,
-                                                    int32_t total_tiles) {
+__host__ __device__ inline int32_t ceil_div_hd(int32_t a, int32_t b) { return (a + b - 1) / b; }
+__host__ __device__ inline StreamSplit split_of_tiles(int32_t tiles, int32_t tpc, int32_t per,
+                                                      int32_t target, int32_t total_tiles,
+                                                      int32_t bal) {
   StreamSplit r;
-  int32_t k = sel_off.at(b + 1) - sel_off.at(b);
-  if (k < 0) k = 0;
-  r.tiles = k * tpc;
+  r.tiles = tiles;
   if (per > 0) {
     r.per = per;
-    r.wgs = ceil_div_i(r.tiles, per);
+    r.wgs = ceil_div_hd(r.tiles, per);
+  } else if (bal > 0) {
+    const int32_t cap = run_tile_cap(tpc);
+    const int32_t p = bal < cap ? bal : cap;
+    const int32_t w = ceil_div_hd(r.tiles, p);
+    r.per = w > 0 ? ceil_div_hd(r.tiles, w) : 1;  // even runs, none longer than p
+    r.wgs = w > 0 ? ceil_div_hd(r.tiles, r.per) : 0;
   } else {
     const int64_t num = 2 * static_cast<int64_t>(r.tiles) * target + total_tiles;
     int32_t w = total_tiles > 0 ? static_cast<int32_t>(num / (2 * static_cast<int64_t>(total_tiles))) : 0;
     if (w < 1) w = 1;
-    const int32_t w_min = ceil_div_i(r.tiles, run_tile_cap(tpc));
+    const int32_t w_min = ceil_div_hd(r.tiles, run_tile_cap(tpc));
     if (w < w_min) w = w_min;
     if (w > r.tiles) w = r.tiles;
-    r.per = w > 0 ? ceil_div_i(r.tiles, w) : 1;
+    r.per = w > 0 ? ceil_div_hd(r.tiles, w) : 1;
     // runs of `per` tiles may need fewer workgroups than w (e.g. 2620 tiles
     // over 256: runs of 11 fill 239), and a workgroup with no tiles would
     // still write a partial that the merge reads
-    r.wgs = w > 0 ? ceil_div_i(r.tiles, r.per) : 0;
+    r.wgs = w > 0 ? ceil_div_hd(r.tiles, r.per) : 0;
   }
   return r;
+}
+
+// Balanced run length of a uniform batch (B streams of t tiles each), the
+// closed form of balanced_run's search: p = ceil(t / floor(target / B)), or
+// t when there are more streams than `target`; 0 when the batch takes another
+// split.
+__host__ __device__ inline int32_t uniform_balanced_run(int32_t B, int32_t t, int32_t per,
+                                                        int32_t target) {
+  if (per > 0 || B > kWave || B < 1) return 0;
+  const int32_t m = target / B;
+  const int32_t p = m >= 1 ? ceil_div_hd(t, m) : t;
+  return p > 1 ? p : 1;
+}
+
+// Run length p of the balanced split (see the plan above), or 0 when the
+// batch takes the fixed or the proportional split.  Called by a full wave
+// (lane s holds stream s's tiles); every lane returns the same value.  A
+// uniform batch has the closed form p = ceil(T_b / floor(target / B)).
+__device__ __forceinline__ int32_t balanced_run(SelCsr sel_off, int32_t B, int32_t tpc,
+                                                int32_t per, int32_t target,
+                                                int32_t total_tiles) {
+  if (per > 0 || B > kWave || B < 1) return 0;
+  if (sel_off.uni > 0) return uniform_balanced_run(B, sel_off.uni * tpc, per, target);
+  const int lane = threadIdx.x & (kWave - 1);
+  int32_t t = 0;
+  if (lane < B) {
+    const int32_t k = sel_off.at(lane + 1) - sel_off.at(lane);
+    t = k > 0 ? k * tpc : 0;
+  }
+  // the longest stream (one workgroup each at p = its tiles)
+  uint32_t tmax = static_cast<uint32_t>(t);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1)
+    tmax = max(tmax, static_cast<uint32_t>(__shfl_xor(static_cast<int>(tmax), o)));
+  if (tmax == 0) return 1;
+  // smallest p in [ceil(T / target), tmax] with sum_b ceil(T_b / p) <= target
+  // (the sum does not grow with p; at p = tmax it is the number of streams)
+  int32_t lo = max(1, ceil_div_i(total_tiles, max(target, 1)));
+  int32_t hi = static_cast<int32_t>(tmax);
+  if (lo >= hi) return hi;
+  while (lo < hi) {
+    const int32_t mid = lo + (hi - lo) / 2;
+    const uint32_t w = t > 0 ? static_cast<uint32_t>(ceil_div_i(t, mid)) : 0u;
+    if (wave_sum_u32(w) <= static_cast<uint32_t>(target)) hi = mid;
+    else lo = mid + 1;
+  }
+  return lo;
+}
+
+__device__ __forceinline__ StreamSplit stream_split(SelCsr sel_off, int32_t b, int32_t tpc,
+                                                    int32_t per, int32_t target,
+                                                    int32_t total_tiles, int32_t bal) {
+  int32_t k = sel_off.at(b + 1) - sel_off.at(b);
+  if (k < 0) k = 0;
+  return split_of_tiles(k * tpc, tpc, per, target, total_tiles, bal);
 }
 
 // Run by one full wave: the stream owning workgroup `wg`, the workgroup's
@@ -219,9 +290,8 @@ __device__ __forceinline__ void find_stream_of_wg(SelCsr sel_off, int32_t B, int
                                                   StreamSplit* split_out,
                                                   int32_t* sel0_out = nullptr) {
   const int lane = threadIdx.x & (kWave - 1);
-  const int32_t total_tiles = (sel_off.at(B) - sel_off.at(0)) * tpc;
-  if (sel_off.uni > 0) {  // every stream has the same split
-    const StreamSplit sp = stream_split(sel_off, 0, tpc, per, target, total_tiles);
+  if (sel_off.uni > 0) {  // every stream has the same split, computed on the host
+    const StreamSplit sp = {sel_off.uni * tpc, sel_off.uwgs, sel_off.uper};
     if (sp.wgs > 0 && wg < B * sp.wgs) {
       *b_out = wg / sp.wgs;
       *local_out = wg - *b_out * sp.wgs;
@@ -235,13 +305,15 @@ __device__ __forceinline__ void find_stream_of_wg(SelCsr sel_off, int32_t B, int
     if (sel0_out) *sel0_out = 0;
     return;
   }
+  const int32_t total_tiles = (sel_off.at(B) - sel_off.at(0)) * tpc;
+  const int32_t bal = balanced_run(sel_off, B, tpc, per, target, total_tiles);
   int32_t base = 0;  // workgroups of streams before the current 64-stream window
   for (int32_t s0 = 0; s0 < B; s0 += kWave) {
     const int32_t s = s0 + lane;
     StreamSplit sp = {0, 0, 1};
     int32_t so = 0;
     if (s < B) {
-      sp = stream_split(sel_off, s, tpc, per, target, total_tiles);
+      sp = stream_split(sel_off, s, tpc, per, target, total_tiles, bal);
       so = sel_off.at(s);
     }
     const int32_t incl = static_cast<int32_t>(wave_inclusive_scan(static_cast<uint32_t>(sp.wgs)));
@@ -303,8 +375,8 @@ __device__ __forceinline__ AttnRun attn_prologue(const AttnArgs& a, int32_t* s_s
     const int32_t tpc = a.tiles_per_chunk;
     int32_t b, local, sel0;
     StreamSplit sp;
-    find_stream_of_wg(SelCsr{a.sel_off, a.uni_k}, a.B, tpc, a.per, a.target, blockIdx.x, &b,
-                      &local, &sp, &sel0);
+    find_stream_of_wg(SelCsr{a.sel_off, a.uni_k, a.uni_wgs, a.uni_per}, a.B, tpc, a.per,
+                      a.target, blockIdx.x, &b, &local, &sp, &sel0);
     AttnRun r = {b, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
     if (b >= 0) {
       r.local = local;
@@ -354,20 +426,22 @@ __device__ __forceinline__ void stream_wg_range(SelCsr sel_off, int32_t B, int32
                                                 int32_t tpc, int32_t per, int32_t target,
                                                 int32_t* first_out, int32_t* count_out) {
   const int lane = threadIdx.x & (kWave - 1);
-  const int32_t total_tiles = (sel_off.at(B) - sel_off.at(0)) * tpc;
-  if (sel_off.uni > 0) {  // every stream has the same split
-    const int32_t w = stream_split(sel_off, 0, tpc, per, target, total_tiles).wgs;
-    *first_out = b * w;
-    *count_out = w;
+  if (sel_off.uni > 0) {  // every stream has the same split, computed on the host
+    *first_out = b * sel_off.uwgs;
+    *count_out = sel_off.uwgs;
     return;
   }
+  const int32_t total_tiles = (sel_off.at(B) - sel_off.at(0)) * tpc;
+  const int32_t bal = balanced_run(sel_off, B, tpc, per, target, total_tiles);
   uint32_t acc = 0;
   for (int32_t s0 = 0; s0 < b; s0 += kWave) {
     const int32_t s = s0 + lane;
-    if (s < b) acc += static_cast<uint32_t>(stream_split(sel_off, s, tpc, per, target, total_tiles).wgs);
+    if (s < b)
+      acc += static_cast<uint32_t>(
+          stream_split(sel_off, s, tpc, per, target, total_tiles, bal).wgs);
   }
   *first_out = static_cast<int32_t>(wave_sum_u32(acc));
-  *count_out = stream_split(sel_off, b, tpc, per, target, total_tiles).wgs;
+  *count_out = stream_split(sel_off, b, tpc, per, target, total_tiles, bal).wgs;
 }
 
 // Device-scope (all XCDs' L2s) coherent stores of the split partials that a
