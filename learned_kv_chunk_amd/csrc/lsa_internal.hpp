@@ -238,31 +238,23 @@ __host__ __device__ inline int32_t uniform_balanced_run(int32_t B, int32_t t, in
   return p > 1 ? p : 1;
 }
 
-// Run length p of the balanced split (see the plan above), or 0 when the
-// batch takes the fixed or the proportional split.  Called by a full wave
-// (lane s holds stream s's tiles); every lane returns the same value.  A
-// uniform batch has the closed form p = ceil(T_b / floor(target / B)).
-__device__ __forceinline__ int32_t balanced_run(SelCsr sel_off, int32_t B, int32_t tpc,
-                                                int32_t per, int32_t target,
-                                                int32_t total_tiles) {
-  if (per > 0 || B > kWave || B < 1) return 0;
-  if (sel_off.uni > 0) return uniform_balanced_run(B, sel_off.uni * tpc, per, target);
-  const int lane = threadIdx.x & (kWave - 1);
-  int32_t t = 0;
-  if (lane < B) {
-    const int32_t k = sel_off.at(lane + 1) - sel_off.at(lane);
-    t = k > 0 ? k * tpc : 0;
-  }
+// Run length p of the balanced split of a ragged batch of B <= 64 streams
+// (see the plan above), from lane s's tiles t (stream s; 0 past B) and their
+// sum T.  Called by a full wave; every lane returns the same value.
+__device__ __forceinline__ int32_t balanced_run(int32_t t, int32_t total_tiles, int32_t B,
+                                                int32_t target) {
   // the longest stream (one workgroup each at p = its tiles)
   uint32_t tmax = static_cast<uint32_t>(t);
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1)
     tmax = max(tmax, static_cast<uint32_t>(__shfl_xor(static_cast<int>(tmax), o)));
   if (tmax == 0) return 1;
-  // smallest p in [ceil(T / target), tmax] with sum_b ceil(T_b / p) <= target
-  // (the sum does not grow with p; at p = tmax it is the number of streams)
+  // smallest p with sum_b ceil(T_b / p) <= target (the sum does not grow with
+  // p; at p = tmax it is the number of streams): at least ceil(T / target),
+  // and, since the sum is below T / p + B, at most ceil(T / (target - B))
   int32_t lo = max(1, ceil_div_i(total_tiles, max(target, 1)));
   int32_t hi = static_cast<int32_t>(tmax);
+  if (target > B) hi = min(hi, max(lo, ceil_div_i(total_tiles, target - B)));
   if (lo >= hi) return hi;
   while (lo < hi) {
     const int32_t mid = lo + (hi - lo) / 2;
@@ -271,6 +263,26 @@ __device__ __forceinline__ int32_t balanced_run(SelCsr sel_off, int32_t B, int32
     else lo = mid + 1;
   }
   return lo;
+}
+
+// A batch of at most 64 streams, one per lane (a full wave): lane s gets
+// stream s's split (zero tiles past B) and its first kept index.  The offsets
+// are read once, and the balanced run length comes from the same registers.
+__device__ __forceinline__ StreamSplit lane_stream_split(SelCsr sel_off, int32_t B, int32_t tpc,
+                                                         int32_t per, int32_t target,
+                                                         int32_t* so_out) {
+  const int lane = threadIdx.x & (kWave - 1);
+  int32_t so = 0, t = 0;
+  if (lane < B) {
+    so = sel_off.at(lane);
+    const int32_t k = sel_off.at(lane + 1) - so;
+    t = k > 0 ? k * tpc : 0;
+  }
+  *so_out = so;
+  const int32_t bal =
+      per > 0 ? 0 : balanced_run(t, static_cast<int32_t>(wave_sum_u32(static_cast<uint32_t>(t))),
+                                 B, target);
+  return split_of_tiles(t, tpc, per, target, 0, bal);
 }
 
 __device__ __forceinline__ StreamSplit stream_split(SelCsr sel_off, int32_t b, int32_t tpc,
@@ -305,15 +317,16 @@ __device__ __forceinline__ void find_stream_of_wg(SelCsr sel_off, int32_t B, int
     if (sel0_out) *sel0_out = 0;
     return;
   }
-  const int32_t total_tiles = (sel_off.at(B) - sel_off.at(0)) * tpc;
-  const int32_t bal = balanced_run(sel_off, B, tpc, per, target, total_tiles);
+  const int32_t total_tiles = B > kWave ? (sel_off.at(B) - sel_off.at(0)) * tpc : 0;
   int32_t base = 0;  // workgroups of streams before the current 64-stream window
   for (int32_t s0 = 0; s0 < B; s0 += kWave) {
     const int32_t s = s0 + lane;
     StreamSplit sp = {0, 0, 1};
     int32_t so = 0;
-    if (s < B) {
-      sp = stream_split(sel_off, s, tpc, per, target, total_tiles, bal);
+    if (B <= kWave) {  // one window: the balanced (or fixed) split of lane_stream_split
+      sp = lane_stream_split(sel_off, B, tpc, per, target, &so);
+    } else if (s < B) {  // more streams: the proportional (or fixed) split
+      sp = stream_split(sel_off, s, tpc, per, target, total_tiles, 0);
       so = sel_off.at(s);
     }
     const int32_t incl = static_cast<int32_t>(wave_inclusive_scan(static_cast<uint32_t>(sp.wgs)));
@@ -431,17 +444,23 @@ __device__ __forceinline__ void stream_wg_range(SelCsr sel_off, int32_t B, int32
     *count_out = sel_off.uwgs;
     return;
   }
+  if (B <= kWave) {  // one window: the balanced (or fixed) split of lane_stream_split
+    int32_t so;
+    const StreamSplit sp = lane_stream_split(sel_off, B, tpc, per, target, &so);
+    const uint32_t incl = wave_inclusive_scan(static_cast<uint32_t>(sp.wgs));
+    *first_out = static_cast<int32_t>(__builtin_amdgcn_readlane(incl - sp.wgs, b));
+    *count_out = __builtin_amdgcn_readlane(sp.wgs, b);
+    return;
+  }
   const int32_t total_tiles = (sel_off.at(B) - sel_off.at(0)) * tpc;
-  const int32_t bal = balanced_run(sel_off, B, tpc, per, target, total_tiles);
   uint32_t acc = 0;
   for (int32_t s0 = 0; s0 < b; s0 += kWave) {
     const int32_t s = s0 + lane;
     if (s < b)
-      acc += static_cast<uint32_t>(
-          stream_split(sel_off, s, tpc, per, target, total_tiles, bal).wgs);
+      acc += static_cast<uint32_t>(stream_split(sel_off, s, tpc, per, target, total_tiles, 0).wgs);
   }
   *first_out = static_cast<int32_t>(wave_sum_u32(acc));
-  *count_out = stream_split(sel_off, b, tpc, per, target, total_tiles, bal).wgs;
+  *count_out = stream_split(sel_off, b, tpc, per, target, total_tiles, 0).wgs;
 }
 
 // Device-scope (all XCDs' L2s) coherent stores of the split partials that a
