@@ -27,7 +27,10 @@ constexpr int kTileTokens = 32;        // tokens per attention tile
 //    each.  The longest run is what the launch waits for, and a stream whose
 //    share of the CUs is fractional would otherwise get one workgroup
 //    carrying up to 1.5 times the average (32 ragged streams: 102 tiles
-//    against 72.6, where this plan's longest run is 79);
+//    against 72.6, where this plan's longest run is 79).  A uniform batch
+//    (every stream keeps the same count) has the closed form
+//    p = ceil(T_b / floor(target / B)); the host computes that split and
+//    passes it in (SelCsr::uwgs, uper), so the kernels skip the search;
 //  * proportional split (per == 0, more than 64 streams): the `target`
 //    workgroups are shared out in proportion to the streams' tiles,
 //    w_b = max(1, round(T_b * target / T)), stream b's runs hold
@@ -48,8 +51,8 @@ __host__ __device__ __forceinline__ int32_t run_tile_cap(int32_t tpc) {
 
 struct AttnPlan {
   int32_t tiles_per_chunk;
-  int32_t per;      // tiles per workgroup, or 0 for the proportional split
-  int32_t target;   // workgroups the proportional split aims at
+  int32_t per;      // tiles per workgroup, or 0 for the balanced / proportional split
+  int32_t target;   // workgroups the balanced and proportional splits aim at
   int64_t grid;     // workgroups launched (upper bound of sum_b W_b)
   int64_t ws_rows;  // partial results the workspace holds (>= grid)
   int32_t split_heads;  // vector-ALU kernel: the waves share each tile, split its heads
@@ -244,10 +247,7 @@ __host__ __device__ inline int32_t uniform_balanced_run(int32_t B, int32_t t, in
 __device__ __forceinline__ int32_t balanced_run(int32_t t, int32_t total_tiles, int32_t B,
                                                 int32_t target) {
   // the longest stream (one workgroup each at p = its tiles)
-  uint32_t tmax = static_cast<uint32_t>(t);
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1)
-    tmax = max(tmax, static_cast<uint32_t>(__shfl_xor(static_cast<int>(tmax), o)));
+  const uint32_t tmax = wave_max_u32(static_cast<uint32_t>(t));
   if (tmax == 0) return 1;
   // smallest p with sum_b ceil(T_b / p) <= target (the sum does not grow with
   // p; at p = tmax it is the number of streams): at least ceil(T / target),

@@ -8,7 +8,8 @@
 // lanes owns one embedding row; lane i of the group reads the row's 16-byte
 // vectors i, i+G, ..., so each wave load instruction covers 64/G whole rows
 // with consecutive addresses.  The query's matching vectors stay in
-// registers, partial dots are reduced across the group with lane shuffles,
+// registers, partial dots are reduced across the group with DPP row
+// operations and a lane swap (group_sum: no trip through the LDS crossbar),
 // and the group's first lane writes the fp32 score.  Grid: (row blocks, B);
 // workgroups past the end of a stream exit at once.
 
@@ -81,8 +82,7 @@ __device__ __forceinline__ void score_rows(const T* __restrict__ q, const T* __r
 #pragma unroll
       for (int e = 0; e < E; ++e) acc = fmaf(qf[i][e], ef[e], acc);
     }
-#pragma unroll
-    for (int off = G / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, G);
+    acc = group_sum<G>(acc);
     const int32_t row = r_begin + p * kGroups + grp;
     if (gl == 0 && row < r_end) scores[row] = acc;
   }

@@ -32,6 +32,8 @@ constexpr int kDppQuadXor1 = 0xB1;  // quad_perm [1,0,3,2]
 constexpr int kDppQuadXor2 = 0x4E;  // quad_perm [2,3,0,1]
 constexpr int kDppRowRor4 = 0x124;
 constexpr int kDppRowRor8 = 0x128;
+constexpr int kDppRowMirror = 0x140;      // lane i of a row of 16 reads lane 15 - i
+constexpr int kDppRowHalfMirror = 0x141;  // lane i of a row of 8 reads lane 7 - i
 template <int N>
 constexpr int dpp_row_shr() { return 0x110 + N; }
 
@@ -87,6 +89,42 @@ __device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
   v += dpp_u32<kDppRowRor4>(v);
   v += dpp_u32<kDppRowRor8>(v);
   return xor32_sum_u32(xor16_sum_u32(v));
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, dpp_u32<kDppQuadXor1>(v));
+  v = max(v, dpp_u32<kDppQuadXor2>(v));
+  v = max(v, dpp_u32<kDppRowRor4>(v));
+  v = max(v, dpp_u32<kDppRowRor8>(v));
+  auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  v = max(r[0], r[1]);
+  r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return max(r[0], r[1]);
+}
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+  v = min(v, dpp_u32<kDppQuadXor1>(v));
+  v = min(v, dpp_u32<kDppQuadXor2>(v));
+  v = min(v, dpp_u32<kDppRowRor4>(v));
+  v = min(v, dpp_u32<kDppRowRor8>(v));
+  auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  v = min(r[0], r[1]);
+  r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return min(r[0], r[1]);
+}
+
+// Sum over each aligned group of G lanes (G = 4, 8, 16 or 32), returned in
+// every lane of the group: xor-1 and xor-2 steps inside quads, then the
+// mirrored half-row (the other quad of 8 lanes), the mirrored row (the other
+// 8 lanes of 16) and the xor-16 swap.
+template <int G>
+__device__ __forceinline__ float group_sum(float v) {
+  static_assert(G == 4 || G == 8 || G == 16 || G == 32, "group of 4, 8, 16 or 32 lanes");
+  v += dpp_f32<kDppQuadXor1>(v);
+  v += dpp_f32<kDppQuadXor2>(v);
+  if constexpr (G >= 8) v += dpp_f32<kDppRowHalfMirror>(v);
+  if constexpr (G >= 16) v += dpp_f32<kDppRowMirror>(v);
+  if constexpr (G >= 32) v = xor16_sum(v);
+  return v;
 }
 
 // Inclusive prefix sum over lanes 0..63 (lane i gets sum of lanes 0..i).
