@@ -456,9 +456,11 @@ __global__ __launch_bounds__(kMlaThreads, 1) void attn_mla_kernel(AttnArgs a) {
       a.ws_l[wg * H + head] = lt;
     }
   }
-  float* orow = a.ws_o + (wg * H + head) * kMlaDv + half * (kMlaDv / 2) + 4 * g;
 #pragma unroll
-  for (int c = 0; c < kMlaDv / 32; ++c) *reinterpret_cast<f32x4*>(orow + c * 16) = o[c];
+  for (int c = 0; c < kMlaDv / 32; ++c)  // 128 KiB per workgroup: written through
+    store_through_16(a.ws_o + wg * H * kMlaDv,
+                     static_cast<uint32_t>((head * kMlaDv + half * (kMlaDv / 2) + 4 * g + c * 16) * 4),
+                     __builtin_bit_cast(st_u32x4, o[c]));
 }
 
 }  // namespace

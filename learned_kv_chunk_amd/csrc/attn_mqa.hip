@@ -424,7 +424,14 @@ __global__ __launch_bounds__(mqa_waves<NHG>() * kWave, 1) void attn_mqa_kernel(
           *ol = lt;
         }
 #pragma unroll
-        for (int cg = 0; cg < D / 16; ++cg) *reinterpret_cast<f32x4*>(oo + cg * 16) = o[hg][cg];
+        for (int cg = 0; cg < D / 16; ++cg) {
+          if constexpr (NHG > 1)  // 16 KiB per workgroup: written through
+            store_through_16(a.ws_o + wg * H * D,
+                             static_cast<uint32_t>((head * D + 4 * g + cg * 16) * 4),
+                             __builtin_bit_cast(st_u32x4, o[hg][cg]));
+          else
+            *reinterpret_cast<f32x4*>(oo + cg * 16) = o[hg][cg];
+        }
       }
     }
   }

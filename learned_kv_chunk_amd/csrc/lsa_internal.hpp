@@ -471,6 +471,20 @@ __device__ __forceinline__ void store_coherent(float* p, float v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// 16 bytes stored at base + byte_off (base the same in every lane, byte_off
+// < 2^31; stores past that are dropped) with the sc1 cache policy: written through to the device's coherence point instead of being
+// left dirty in the XCD's L2 until the end of the kernel.  For large split
+// partials (the MLA kernel's 128 KiB per workgroup, the two-group MQA
+// kernel's 16 KiB) that made the partial kernel shorter (1 x 1M: 30.4 -> 28.5
+// us; 4 x 512K: 25.4 -> 24.3 us); for 8 KiB partials it was slower (16 x
+// 128K: 28.0 -> 28.5 us), interleaved on one box.
+typedef uint32_t st_u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void store_through_16(float* base, uint32_t byte_off, st_u32x4 v) {
+  const __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc(base, 0, 0x7fffffff, 0x00020000);
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, byte_off, 0, 16 /* sc1 */);
+}
+
 // Merge of one stream's split-KV partials by the NT threads of the stream's
 // last workgroup to finish (after arrive_last): rows first .. first + count -
 // 1 of the workspace are combined into out[b] and lse[b].  Thread i owns
