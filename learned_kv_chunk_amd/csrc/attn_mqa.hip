@@ -415,9 +415,10 @@ __global__ __launch_bounds__(mqa_waves<NHG>() * kWave, 1) void attn_mqa_kernel(
           store_coherent(ol, lt);
         }
 #pragma unroll
-        for (int cg = 0; cg < D / 16; ++cg)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) store_coherent(oo + cg * 16 + j, o[hg][cg][j]);
+        for (int cg = 0; cg < D / 16; ++cg)  // the same sc1 policy, 16 bytes at a time
+          store_through_16(a.ws_o + wg * H * D,
+                           static_cast<uint32_t>((head * D + 4 * g + cg * 16) * 4),
+                           __builtin_bit_cast(st_u32x4, o[hg][cg]));
       } else {
         if (g == 0) {
           *om = m[hg];

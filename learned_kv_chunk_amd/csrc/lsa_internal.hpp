@@ -549,7 +549,7 @@ __device__ __forceinline__ void merge_stream_block(const AttnArgs& a, int32_t b,
 }
 
 // Arrival of a workgroup whose partial for stream b has been written with
-// store_coherent: every wave waits until its own stores are acknowledged at
+// store_coherent or store_through_16: every wave waits until its own stores are acknowledged at
 // the device's coherence point, then one thread increments the stream's
 // counter (a device-scope atomic).  The workgroup that sees the count reach
 // wgs - 1 arrived last: every other partial is already at the coherence
