@@ -99,22 +99,46 @@ __device__ __forceinline__ void select_exclusive_scan2(uint32_t a, uint32_t b, u
 }
 
 // Loads scores[0..n) as order keys, KPT consecutive ones per thread (keys
-// past n are 0 and never counted).
+// past n are 0 and never counted).  With KPT a multiple of four every load is
+// a 16-byte load of an aligned block, whatever the alignment of the stream's
+// first score: a thread reads the KPT / 4 blocks that cover its scores, one
+// more when the stream starts r floats into a block, and picks its scores
+// from offset r (r is the same for the whole workgroup, so the pick is a
+// uniform branch).  A block holding none of the stream's scores is not read,
+// so no access leaves the aligned blocks of the stream's own scores.  (One
+// 4-byte load per score instead -- the form for a misaligned stream before --
+// took twice as long for 4096 scores: each instruction touched 64 lines.)
 template <int THREADS, int KPT>
 __device__ __forceinline__ void select_load_keys(const float* __restrict__ scores, int32_t n,
                                                  uint32_t (&key)[KPT]) {
   const int tid = threadIdx.x;
   float sv[KPT];
-  // all loads in flight; 16-byte loads where the stream's scores are aligned
-  if (KPT % 4 == 0 && (reinterpret_cast<uintptr_t>(scores) & 15u) == 0 && (tid + 1) * KPT <= n) {
-    const float4* v = reinterpret_cast<const float4*>(scores + tid * KPT);
+  if constexpr (KPT % 4 == 0) {
+    constexpr int NB = KPT / 4 + 1;
+    const int r = static_cast<int>((reinterpret_cast<uintptr_t>(scores) >> 2) & 3u);
+    const float4* blk = reinterpret_cast<const float4*>(scores - r) + tid * (KPT / 4);
+    float v[4 * NB];
 #pragma unroll
-    for (int i = 0; i < KPT / 4; ++i) {
-      const float4 f = v[i];
-      sv[4 * i] = f.x;
-      sv[4 * i + 1] = f.y;
-      sv[4 * i + 2] = f.z;
-      sv[4 * i + 3] = f.w;
+    for (int q = 0; q < NB; ++q) {
+      // the block's first float is score tid * KPT + 4q - r: read it only if
+      // the block holds a score of the stream
+      const bool need = (q < KPT / 4 || r != 0) && tid * KPT + 4 * q - r < n;
+      const float4 f = need ? blk[q] : make_float4(0.f, 0.f, 0.f, 0.f);
+      v[4 * q] = f.x;
+      v[4 * q + 1] = f.y;
+      v[4 * q + 2] = f.z;
+      v[4 * q + 3] = f.w;
+    }
+    switch (r) {
+#define LSA_PICK(R)                                     \
+  case R:                                               \
+    _Pragma("unroll") for (int i = 0; i < KPT; ++i) sv[i] = v[(R) + i]; \
+    break;
+      LSA_PICK(0)
+      LSA_PICK(1)
+      LSA_PICK(2)
+      LSA_PICK(3)
+#undef LSA_PICK
     }
   } else {
 #pragma unroll
