@@ -376,17 +376,19 @@ __device__ __forceinline__ void select_topk_keys(const uint32_t (&key)[KPT], int
   }
   uint32_t gt_before, eq_before;
   select_exclusive_scan2<THREADS>(n_gt, n_eq, &gt_before, &eq_before, lds.tot);
+  // a kept key's slot is the number of kept keys before it; one predicated
+  // store per key and no nested branches (a thread's keys are processed in
+  // order, so the counts before each follow by increments)
 #pragma unroll
   for (int i = 0; i < KPT; ++i) {
     const int32_t idx = tid * KPT + i;
-    if (idx >= n) continue;
-    if ((key[i] & mask) > prefix) {
-      out[gt_before + min(eq_before, remaining)] = idx;
-      ++gt_before;
-    } else if ((key[i] & mask) == prefix) {
-      if (eq_before < remaining) out[gt_before + eq_before] = idx;
-      ++eq_before;
-    }
+    const uint32_t km = key[i] & mask;
+    const bool gt = idx < n && km > prefix;
+    const bool eq = idx < n && km == prefix;
+    const uint32_t pos = gt_before + min(eq_before, remaining);
+    if (gt || (eq && eq_before < remaining)) out[pos] = idx;
+    gt_before += gt ? 1u : 0u;
+    eq_before += eq ? 1u : 0u;
   }
 }
 
