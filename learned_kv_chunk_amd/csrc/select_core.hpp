@@ -175,14 +175,14 @@ __device__ __forceinline__ void select_radix(const uint32_t (&key)[KPT], int32_t
       if (pm == 0) continue;
       if (pass == 0) {
         // the leading digit is shared by most lanes: the lanes holding the
-        // first participating lane's digit add as one, the others directly
+        // first participating lane's digit add as one (the lowest of them
+        // adds their count), the others directly -- one predicated atomic
         const uint32_t lead = __builtin_amdgcn_readlane(d, __ffsll(static_cast<long long>(pm)) - 1);
-        const uint64_t same = __ballot(part && d == lead);
-        if (part && d == lead) {
-          if ((same & below) == 0) atomicAdd(&hist[d], static_cast<uint32_t>(__popcll(same)));
-        } else if (part) {
-          atomicAdd(&hist[d], 1u);
-        }
+        const bool is_lead = part && d == lead;
+        const uint64_t same = __ballot(is_lead);
+        const uint32_t add = is_lead ? ((same & below) == 0 ? static_cast<uint32_t>(__popcll(same)) : 0u)
+                                     : (part ? 1u : 0u);
+        if (add != 0u) atomicAdd(&hist[d], add);
       } else if (part) {
         atomicAdd(&hist[d], 1u);
       }
