@@ -202,7 +202,7 @@ struct MqaLds {
   static constexpr int kTileBytes = kTileTokens * kRowBytes;              // per wave
   static constexpr int kStateO = NHG * (D / 16) * kWave * 16;            // lane-major o
   static constexpr int kStateBytes = kStateO + 2 * NHG * kWave * 4;      // + m, l
-  static constexpr int kBytes = cmax(kWaves * kTileBytes, (kWaves / 2) * kStateBytes);
+  static constexpr int kBytes = cmax(kWaves * kTileBytes, kWaves * kStateBytes);
 };
 
 template <int D, int NHG>
@@ -220,24 +220,44 @@ __device__ __forceinline__ void store_state(unsigned char* base, const float (&m
   }
 }
 
-template <int D, int NHG>
-__device__ __forceinline__ void merge_state(const unsigned char* base, float (&m)[NHG],
-                                            float (&l)[NHG], f32x4 (&o)[NHG][D / 16], int lane) {
+// Combines the WPG states a team stored (store_state, one slot per wave from
+// `team`) for column blocks cb0 .. cb0 + CPW - 1 of every head group: per
+// lane the maximum m, the rescaled sum l over the head's lanes (lt), and
+// the rescaled output blocks (os).
+template <int D, int NHG, int WPG, int CPW>
+__device__ __forceinline__ void team_states(const unsigned char* team, int cb0, float (&m)[NHG],
+                                            float (&lt)[NHG], f32x4 (&os)[NHG][CPW], int lane) {
   using L = MqaLds<D, NHG>;
 #pragma unroll
   for (int hg = 0; hg < NHG; ++hg) {
-    const float mo = reinterpret_cast<const float*>(base + L::kStateO)[hg * kWave + lane];
-    const float lo = reinterpret_cast<const float*>(base + L::kStateO)[(NHG + hg) * kWave + lane];
-    const float mx = fmaxf(m[hg], mo);
-    const float mu = (mx == -INFINITY) ? 0.f : mx;
-    const float fs = __builtin_amdgcn_exp2f(m[hg] - mu);
-    const float fo = __builtin_amdgcn_exp2f(mo - mu);
-    l[hg] = l[hg] * fs + lo * fo;
-    m[hg] = mx;
+    float mw[WPG], fw[WPG];
+    float mx = -INFINITY;
 #pragma unroll
-    for (int cg = 0; cg < D / 16; ++cg)
-      o[hg][cg] = o[hg][cg] * fs +
-                  reinterpret_cast<const f32x4*>(base)[(hg * (D / 16) + cg) * kWave + lane] * fo;
+    for (int w = 0; w < WPG; ++w) {
+      mw[w] = reinterpret_cast<const float*>(team + w * L::kStateBytes + L::kStateO)[hg * kWave +
+                                                                                    lane];
+      mx = fmaxf(mx, mw[w]);
+    }
+    const float mu = (mx == -INFINITY) ? 0.f : mx;
+    float ls = 0.f;
+#pragma unroll
+    for (int w = 0; w < WPG; ++w) {
+      fw[w] = __builtin_amdgcn_exp2f(mw[w] - mu);
+      ls = fmaf(reinterpret_cast<const float*>(team + w * L::kStateBytes +
+                                               L::kStateO)[(NHG + hg) * kWave + lane],
+                fw[w], ls);
+    }
+    m[hg] = mx;
+    lt[hg] = xor32_sum(xor16_sum(ls));
+#pragma unroll
+    for (int c = 0; c < CPW; ++c) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int w = 0; w < WPG; ++w)
+        acc += reinterpret_cast<const f32x4*>(team + w * L::kStateBytes)
+                   [(hg * (D / 16) + cb0 + c) * kWave + lane] * fw[w];
+      os[hg][c] = acc;
+    }
   }
 }
 
@@ -368,72 +388,66 @@ __global__ __launch_bounds__(mqa_waves<NHG>() * kWave, 1) void attn_mqa_kernel(
     }
   }
 
-  // tree-merge the states of each head group's waves into its first wave
-  // (halving the live waves per round; a group's slots follow its index)
-#pragma unroll
-  for (int stride = WPG / 2; stride >= 1; stride /= 2) {
-    __syncthreads();
-    if (wl >= stride && wl < 2 * stride)
-      store_state<D, NHG>(smem + (grp * (WPG / 2) + wl - stride) * L::kStateBytes, m, l, o, lane);
-    __syncthreads();
-    if (wl < stride)
-      merge_state<D, NHG>(smem + (grp * (WPG / 2) + wl) * L::kStateBytes, m, l, o, lane);
-  }
+  // Every wave stores its state; then wave wl of a team combines the team's
+  // WPG states for its own slice of the output columns, CPW 16-column blocks
+  // of every head, and writes that slice: one barrier, and the partial's
+  // stores spread over the waves (a tree merge into the first wave took two
+  // rounds of two barriers, and that wave stored the whole partial)
+  constexpr int CB = D / 16;
+  constexpr int CPW = CB / WPG;
+  static_assert(CPW * WPG == CB, "the column blocks split evenly over a team's waves");
+  __syncthreads();  // every wave is done with its tile buffers
+  store_state<D, NHG>(smem + wave * L::kStateBytes, m, l, o, lane);
+  __syncthreads();
+  float lt[NHG];
+  f32x4 os[NHG][CPW];
+  team_states<D, NHG, WPG, CPW>(smem + grp * WPG * L::kStateBytes, wl * CPW, m, lt, os, lane);
+
   const int64_t wg = blockIdx.x;
   if (a.fuse_merge && run.wgs == 1) {
     // the stream's only workgroup holds its whole softmax state: normalise
     // and write the output directly, no partial and no merge
-    if (wl == 0) {
-#pragma unroll
-      for (int hg = 0; hg < NHG; ++hg) {
-        const int head = head0 + hg * 16;
-        if (head >= H) continue;
-        const float lt = xor32_sum(xor16_sum(l[hg]));
-        const float inv = lt > 0.f ? 1.f / lt : 0.f;
-        const int64_t orow = static_cast<int64_t>(b) * H + head;
-        if (g == 0 && a.lse != nullptr)
-          a.lse[orow] = lt > 0.f ? (m[hg] + log2f(lt)) * 0.69314718055994530942f : -INFINITY;
-#pragma unroll
-        for (int cg = 0; cg < D / 16; ++cg)
-          *reinterpret_cast<f32x4*>(a.out + orow * D + cg * 16 + 4 * g) = o[hg][cg] * inv;
-      }
-    }
-    return;
-  }
-  if (wl == 0) {
 #pragma unroll
     for (int hg = 0; hg < NHG; ++hg) {
       const int head = head0 + hg * 16;
       if (head >= H) continue;
-      const float lt = xor32_sum(xor16_sum(l[hg]));
-      float* om = a.ws_m + wg * H + head;
-      float* ol = a.ws_l + wg * H + head;
-      float* oo = a.ws_o + (wg * H + head) * D + 4 * g;
+      const float inv = lt[hg] > 0.f ? 1.f / lt[hg] : 0.f;
+      const int64_t orow = static_cast<int64_t>(b) * H + head;
+      if (wl == 0 && g == 0 && a.lse != nullptr)
+        a.lse[orow] =
+            lt[hg] > 0.f ? (m[hg] + log2f(lt[hg])) * 0.69314718055994530942f : -INFINITY;
+#pragma unroll
+      for (int c = 0; c < CPW; ++c)
+        *reinterpret_cast<f32x4*>(a.out + orow * D + (wl * CPW + c) * 16 + 4 * g) =
+            os[hg][c] * inv;
+    }
+    return;
+  }
+#pragma unroll
+  for (int hg = 0; hg < NHG; ++hg) {
+    const int head = head0 + hg * 16;
+    if (head >= H) continue;
+    float* om = a.ws_m + wg * H + head;
+    float* ol = a.ws_l + wg * H + head;
+    if (wl == 0 && g == 0) {
       if (a.fuse_merge) {  // the stream's last workgroup reads these at device scope
-        if (g == 0) {
-          store_coherent(om, m[hg]);
-          store_coherent(ol, lt);
-        }
-#pragma unroll
-        for (int cg = 0; cg < D / 16; ++cg)  // the same sc1 policy, 16 bytes at a time
-          store_through_16(a.ws_o + wg * H * D,
-                           static_cast<uint32_t>((head * D + 4 * g + cg * 16) * 4),
-                           __builtin_bit_cast(st_u32x4, o[hg][cg]));
+        store_coherent(om, m[hg]);
+        store_coherent(ol, lt[hg]);
       } else {
-        if (g == 0) {
-          *om = m[hg];
-          *ol = lt;
-        }
-#pragma unroll
-        for (int cg = 0; cg < D / 16; ++cg) {
-          if constexpr (NHG > 1)  // 16 KiB per workgroup: written through
-            store_through_16(a.ws_o + wg * H * D,
-                             static_cast<uint32_t>((head * D + 4 * g + cg * 16) * 4),
-                             __builtin_bit_cast(st_u32x4, o[hg][cg]));
-          else
-            *reinterpret_cast<f32x4*>(oo + cg * 16) = o[hg][cg];
-        }
+        *om = m[hg];
+        *ol = lt[hg];
       }
+    }
+#pragma unroll
+    for (int c = 0; c < CPW; ++c) {
+      const int col = (wl * CPW + c) * 16 + 4 * g;
+      // sc1 (written through) for the in-kernel merge, which reads them at
+      // device scope, and for the two-group kernel's 16 KiB per workgroup
+      if (a.fuse_merge || NHG > 1)
+        store_through_16(a.ws_o + wg * H * D, static_cast<uint32_t>((head * D + col) * 4),
+                         __builtin_bit_cast(st_u32x4, os[hg][c]));
+      else
+        *reinterpret_cast<f32x4*>(a.ws_o + (wg * H + head) * D + col) = os[hg][c];
     }
   }
   if (!a.fuse_merge) return;
