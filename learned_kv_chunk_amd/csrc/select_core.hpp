@@ -183,8 +183,10 @@ __device__ __forceinline__ void select_radix(const uint32_t (&key)[KPT], int32_t
         const uint32_t add = is_lead ? ((same & below) == 0 ? static_cast<uint32_t>(__popcll(same)) : 0u)
                                      : (part ? 1u : 0u);
         if (add != 0u) atomicAdd(&hist[d], add);
-      } else if (part) {
-        atomicAdd(&hist[d], 1u);
+      } else {
+        // few keys still take part: the others add zero, which keeps the
+        // atomic unconditional (no exec-mask branches around it)
+        atomicAdd(&hist[d], part ? 1u : 0u);
       }
     }
     select_sync<THREADS>();
@@ -197,18 +199,19 @@ __device__ __forceinline__ void select_radix(const uint32_t (&key)[KPT], int32_t
     const uint32_t total = __builtin_amdgcn_readlane(incl, 63);
     uint32_t ge = total - incl;  // keys whose digit is above this lane's four
     const uint32_t cnt[4] = {c.x, c.y, c.z, c.w};
+    // the ranges (gt, gt + cnt] of the digits are disjoint and cover
+    // (0, total], so exactly one digit holds `remaining`: selects, no branches
     uint32_t pick = 0, gt_pick = 0, n_pick = 0;
     bool found = false;
 #pragma unroll
     for (int j = 3; j >= 0; --j) {
       const uint32_t gt = ge;
       ge += cnt[j];
-      if (!found && gt < remaining && remaining <= ge) {
-        found = true;
-        pick = 4u * lane + j;
-        gt_pick = gt;
-        n_pick = cnt[j];
-      }
+      const bool here = gt < remaining && remaining <= ge;
+      pick = here ? 4u * lane + j : pick;
+      gt_pick = here ? gt : gt_pick;
+      n_pick = here ? cnt[j] : n_pick;
+      found = found || here;
     }
     const uint64_t hit = __ballot(found);
     const int src = __ffsll(static_cast<long long>(hit)) - 1;
@@ -298,14 +301,13 @@ __device__ __forceinline__ bool select_buckets(const uint32_t (&key)[KPT], int32
   uint32_t pick = 0, gt_pick = 0;
   bool found = false;
 #pragma unroll
-  for (int j = 15; j >= 0; --j) {
+  for (int j = 15; j >= 0; --j) {  // exactly one bin holds the k-th key (as in the radix pass)
     const uint32_t gt = ge;
     ge += cnt[j];
-    if (!found && gt < static_cast<uint32_t>(k) && static_cast<uint32_t>(k) <= ge) {
-      found = true;
-      pick = 16u * lane + j;
-      gt_pick = gt;
-    }
+    const bool here = gt < static_cast<uint32_t>(k) && static_cast<uint32_t>(k) <= ge;
+    pick = here ? 16u * lane + j : pick;
+    gt_pick = here ? gt : gt_pick;
+    found = found || here;
   }
   const uint64_t hit = __ballot(found);
   const int src = __ffsll(static_cast<long long>(hit)) - 1;
