@@ -108,9 +108,13 @@ __device__ __forceinline__ void select_exclusive_scan2(uint32_t a, uint32_t b, u
 // so no access leaves the aligned blocks of the stream's own scores.  (One
 // 4-byte load per score instead -- the form for a misaligned stream before --
 // took twice as long for 4096 scores: each instruction touched 64 lines.)
-template <int THREADS, int KPT>
+// `meanwhile` runs once the loads are issued, before their data is used.
+struct NoWork {
+  __device__ void operator()() const {}
+};
+template <int THREADS, int KPT, typename F = NoWork>
 __device__ __forceinline__ void select_load_keys(const float* __restrict__ scores, int32_t n,
-                                                 uint32_t (&key)[KPT]) {
+                                                 uint32_t (&key)[KPT], F meanwhile = F()) {
   const int tid = threadIdx.x;
   float sv[KPT];
   if constexpr (KPT % 4 == 0) {
@@ -129,6 +133,7 @@ __device__ __forceinline__ void select_load_keys(const float* __restrict__ score
       v[4 * q + 2] = f.z;
       v[4 * q + 3] = f.w;
     }
+    meanwhile();
     switch (r) {
 #define LSA_PICK(R)                                     \
   case R:                                               \
@@ -143,23 +148,35 @@ __device__ __forceinline__ void select_load_keys(const float* __restrict__ score
   } else {
 #pragma unroll
     for (int i = 0; i < KPT; ++i) sv[i] = scores[min(tid * KPT + i, n - 1)];
+    meanwhile();
   }
 #pragma unroll
   for (int i = 0; i < KPT; ++i) key[i] = (tid * KPT + i < n) ? order_key(sv[i]) : 0u;
+}
+
+// Zeroes the radix histograms (every one of the THREADS threads; a barrier
+// must follow before the passes).
+template <int THREADS>
+__device__ __forceinline__ void select_clear_hist(SelectLds<THREADS>& lds) {
+  for (int i = threadIdx.x; i < 4 * 256; i += THREADS) (&lds.hist[0][0])[i] = 0u;
 }
 
 // Radix passes: the key T of the k-th largest key (`prefix`) and how many
 // keys equal to T are kept (`remaining`), T compared on the bits of `mask`.
 // The passes stop as soon as every key of the chosen digit is kept: then the
 // digits resolved so far already separate the kept keys (T is a prefix, and
-// all keys sharing it are kept).
+// all keys sharing it are kept).  cleared: the histograms are already zero
+// (select_clear_hist and a barrier).
 template <int THREADS, int KPT>
 __device__ __forceinline__ void select_radix(const uint32_t (&key)[KPT], int32_t n, int32_t k,
                                              SelectLds<THREADS>& lds, uint32_t* prefix_out,
-                                             uint32_t* remaining_out, uint32_t* mask_out) {
+                                             uint32_t* remaining_out, uint32_t* mask_out,
+                                             bool cleared = false) {
   const int tid = threadIdx.x;
-  for (int i = tid; i < 4 * 256; i += THREADS) (&lds.hist[0][0])[i] = 0u;
-  select_sync<THREADS>();
+  if (!cleared) {
+    select_clear_hist<THREADS>(lds);
+    select_sync<THREADS>();
+  }
 
   const uint64_t below = lanemask_lt();
   uint32_t prefix = 0, mask = 0, remaining = static_cast<uint32_t>(k);
@@ -359,13 +376,15 @@ __device__ __forceinline__ bool select_buckets(const uint32_t (&key)[KPT], int32
 template <int THREADS, int KPT, bool BUCKETS = (KPT >= 8)>
 __device__ __forceinline__ void select_topk_keys(const uint32_t (&key)[KPT], int32_t n,
                                                  int32_t k, int32_t* __restrict__ out,
-                                                 SelectLds<THREADS>& lds) {
+                                                 SelectLds<THREADS>& lds, bool cleared = false) {
   const int tid = threadIdx.x;
   uint32_t prefix, remaining, mask = 0xffffffffu;
   // the bucket pass pays off from eight keys per thread (streams of several
-  // thousand chunks); below that the radix passes are as fast
+  // thousand chunks); below that the radix passes are as fast.  cleared: the
+  // radix histograms are zero already (not after a bucket pass, which uses
+  // their words)
   if (!BUCKETS || !select_buckets<THREADS, KPT>(key, n, k, lds, &prefix, &remaining))
-    select_radix<THREADS, KPT>(key, n, k, lds, &prefix, &remaining, &mask);
+    select_radix<THREADS, KPT>(key, n, k, lds, &prefix, &remaining, &mask, cleared && !BUCKETS);
 
   // keys above T (on the bits of mask) are kept, and the first `remaining`
   // keys equal to T in index order
@@ -400,8 +419,17 @@ __device__ __forceinline__ void select_topk_block(const float* __restrict__ scor
                                                   int32_t k, int32_t* __restrict__ out,
                                                   SelectLds<THREADS>& lds) {
   uint32_t key[KPT];
-  select_load_keys<THREADS, KPT>(scores, n, key);
-  select_topk_keys<THREADS, KPT, BUCKETS>(key, n, k, out, lds);
+  if constexpr (BUCKETS) {
+    select_load_keys<THREADS, KPT>(scores, n, key);
+    select_topk_keys<THREADS, KPT, BUCKETS>(key, n, k, out, lds);
+  } else {
+    // the histograms are cleared while the scores are in flight
+    select_load_keys<THREADS, KPT>(scores, n, key, [&]() {
+      select_clear_hist<THREADS>(lds);
+      select_sync<THREADS>();
+    });
+    select_topk_keys<THREADS, KPT, BUCKETS>(key, n, k, out, lds, true);
+  }
 }
 
 // The kept set of an attention workgroup's stream, ranked in its prologue by
