@@ -89,26 +89,60 @@ AttnPlan make_attn_plan(const lsa_shape& s, int32_t target) {
   return p;
 }
 
+// The absorbed-MLA partials hold 64 heads x 512 columns each (128 KiB in
+// fp32, a third of the KV bytes of a 1M-token step over 239 workgroups);
+// rounding the unnormalised rows to bf16 halves what the partial kernel
+// writes and the merge reads.  The rounding (at most 2^-9 relative per
+// element, round to nearest even) is of the order of the one the kernel
+// already applies to the attention weights before the P.V product; the
+// maxima, the sums and every accumulation stay fp32.
+bool partial_o_bf16(const lsa_shape& s) { return mla_attn_supported(s); }
+
 PartialLayout partial_layout(const lsa_shape& s, const AttnPlan& p) {
   PartialLayout L;
+  const size_t oes = partial_o_bf16(s) ? 2 : sizeof(float);
   const size_t rows = static_cast<size_t>(p.ws_rows) * static_cast<size_t>(s.num_q_heads);
   L.cnt_off = 0;  // same place for every shape (see kCounterStreams)
   L.m_off = static_cast<size_t>(kCounterStreams) * sizeof(int32_t);
   L.l_off = L.m_off + align256(rows * sizeof(float));
   L.o_off = L.l_off + align256(rows * sizeof(float));
-  L.total = L.o_off + align256(rows * static_cast<size_t>(s.head_dim_v) * sizeof(float));
+  L.total = L.o_off + align256(rows * static_cast<size_t>(s.head_dim_v) * oes);
   return L;
 }
 
 namespace {
 
 constexpr int kMergeBatch = 16;   // partials whose loads are in flight together
-constexpr int kMergeGroups = 64;  // most groups of partials a stream is cut into
+// most groups of partials a stream is cut into (fewer for the bf16 partials,
+// whose group states take EPL words per lane in LDS)
+template <int EPL>
+constexpr int merge_groups() { return EPL == 1 ? 64 : 16; }
 
-// (max, sum, output) state of a set of partials, log2 domain.
+// (max, sum, output) state of a set of partials, log2 domain; EPL output
+// elements per lane.
+template <int EPL>
 struct MergeState {
-  float m, l, acc;
+  float m, l, acc[EPL];
 };
+
+// Output elements ec .. ec + EPL - 1 of partial row `row`: one fp32 element,
+// or (EPL = 2, bf16 partials) an aligned pair of bf16 in one 4-byte load.
+template <int EPL>
+__device__ __forceinline__ void load_partial(const AttnArgs& a, int64_t row, int32_t elems,
+                                             int32_t ec, float (&v)[EPL]) {
+  if constexpr (EPL == 1) {
+    v[0] = a.ws_o[row * elems + ec];
+  } else {
+    typedef uint32_t w_t __attribute__((ext_vector_type(EPL / 2)));
+    const w_t w = *reinterpret_cast<const w_t*>(
+        reinterpret_cast<const uint16_t*>(a.ws_o) + (row * elems + ec));
+#pragma unroll
+    for (int i = 0; i < EPL / 2; ++i) {
+      v[2 * i] = __uint_as_float(w[i] << 16);
+      v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  }
+}
 
 // Folds partials [p_lo, p_hi) of the stream (rows first + p) into one state,
 // kMergeBatch loads in flight and one rescale per batch.  HU: every lane of
@@ -117,17 +151,21 @@ struct MergeState {
 // its l) and lane reads hand them to the whole wave, instead of 32 loads of
 // one value per wave (measured: 1 % more steps/s at 1 x 1M, 0.3-0.4 % on
 // the MQA workloads).
-template <bool HU>
-__device__ __forceinline__ MergeState fold_partials(const AttnArgs& a, int64_t first,
-                                                    int32_t p_lo, int32_t p_hi, int32_t h,
-                                                    int32_t ec) {
+template <bool HU, int EPL>
+__device__ __forceinline__ MergeState<EPL> fold_partials(const AttnArgs& a, int64_t first,
+                                                         int32_t p_lo, int32_t p_hi, int32_t h,
+                                                         int32_t ec) {
   const int32_t H = a.H, elems = a.H * a.dv;
-  MergeState st = {-INFINITY, 0.f, 0.f};
+  MergeState<EPL> st;
+  st.m = -INFINITY;
+  st.l = 0.f;
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) st.acc[i] = 0.f;
   for (int32_t p0 = p_lo; p0 < p_hi; p0 += kMergeBatch) {
-    float mv[kMergeBatch], lv[kMergeBatch], ov[kMergeBatch];
+    float mv[kMergeBatch], lv[kMergeBatch], ov[kMergeBatch][EPL];
 #pragma unroll
     for (int u = 0; u < kMergeBatch; ++u)
-      ov[u] = a.ws_o[(first + min(p0 + u, p_hi - 1)) * elems + ec];
+      load_partial<EPL>(a, first + min(p0 + u, p_hi - 1), elems, ec, ov[u]);
     if (HU) {
       const int lane = threadIdx.x & (kWave - 1);
       const int j = lane & (kMergeBatch - 1);
@@ -153,13 +191,15 @@ __device__ __forceinline__ MergeState fold_partials(const AttnArgs& a, int64_t f
       if (p0 + u < p_hi) mb = fmaxf(mb, mv[u]);
     const float mu = (mb == -INFINITY) ? 0.f : mb;
     const float f = __builtin_amdgcn_exp2f(st.m - mu);
-    st.acc *= f;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) st.acc[i] *= f;
     st.l *= f;
 #pragma unroll
     for (int u = 0; u < kMergeBatch; ++u) {
       if (p0 + u < p_hi) {
         const float w = __builtin_amdgcn_exp2f(mv[u] - mu);
-        st.acc = fmaf(ov[u], w, st.acc);
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) st.acc[i] = fmaf(ov[u][i], w, st.acc[i]);
         st.l = fmaf(lv[u], w, st.l);
       }
     }
@@ -169,65 +209,83 @@ __device__ __forceinline__ MergeState fold_partials(const AttnArgs& a, int64_t f
 }
 
 // total <- total (+) g
-__device__ __forceinline__ void combine_state(MergeState& t, const MergeState& g) {
+template <int EPL>
+__device__ __forceinline__ void combine_state(MergeState<EPL>& t, const MergeState<EPL>& g) {
   const float mx = fmaxf(t.m, g.m);
   const float mu = (mx == -INFINITY) ? 0.f : mx;
   const float ft = __builtin_amdgcn_exp2f(t.m - mu);
   const float fg = __builtin_amdgcn_exp2f(g.m - mu);
   t.l = fmaf(g.l, fg, t.l * ft);
-  t.acc = fmaf(g.acc, fg, t.acc * ft);
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) t.acc[i] = fmaf(g.acc[i], fg, t.acc[i] * ft);
   t.m = mx;
 }
 
-// One workgroup of MW waves per (stream, 64 consecutive output elements of the
-// flattened [H][dv] row); lane i owns element i of the block.  A stream's
-// partials are cut into groups (16, or more per group when a stream has over
-// 1024 partials, so that there are at most 64 groups); each group is folded
-// into one state, kMergeBatch partials per round trip with one rescale per
-// batch, and the group states are combined in group order.  With MW waves,
-// wave w folds groups w, w + MW, ... and the states meet in LDS; with one
-// wave the combine runs as the groups are folded.  The arithmetic is the same
-// for every MW and depends only on the plan, so reruns are bit-identical and
-// a stream's result does not depend on the launch shape the batch selects.
-template <int MW, bool HU>
+// One workgroup of MW waves per (stream, 64 * EPL consecutive output elements
+// of the flattened [H][dv] row); lane i owns elements EPL i .. EPL i + EPL - 1
+// of the block (EPL = 2 for bf16 partials, one 4-byte load per partial).  A
+// stream's partials are cut into groups (16, or more per group when a stream
+// has over 1024 partials, so that there are at most 64 groups); each group is
+// folded into one state, kMergeBatch partials per round trip with one rescale
+// per batch, and the group states are combined in group order.  With MW
+// waves, wave w folds groups w, w + MW, ... and the states meet in LDS; with
+// one wave the combine runs as the groups are folded.  The arithmetic is the
+// same for every MW and depends only on the plan, so reruns are bit-identical
+// and a stream's result does not depend on the launch shape the batch selects.
+template <int MW, bool HU, int EPL>
 __global__ __launch_bounds__(MW * kWave) void merge_kernel(AttnArgs a, int32_t nblk) {
-  __shared__ float s_state[MW > 1 ? 3 : 1][MW > 1 ? kMergeGroups : 1][kWave];
+  constexpr int kGroups = merge_groups<EPL>();
+  __shared__ float s_state[MW > 1 ? 2 + EPL : 1][MW > 1 ? kGroups : 1][kWave];
   const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
   const int32_t b = static_cast<int32_t>(blockIdx.x) / nblk;
   const int32_t blk = static_cast<int32_t>(blockIdx.x) - b * nblk;
   const int32_t H = a.H, dv = a.dv;
   const int32_t elems = H * dv;
-  const int32_t e = blk * kWave + lane;
-  const int32_t ec = min(e, elems - 1);
+  const int32_t e = (blk * kWave + lane) * EPL;
+  const int32_t ec = min(e, elems - EPL);
   const int32_t h = ec / dv;
 
   int32_t first, count;
   stream_wg_range(SelCsr{a.sel_off, a.uni_k, a.uni_wgs, a.uni_per}, a.B, b, a.tiles_per_chunk,
                   a.per, a.target, &first, &count);
-  const int32_t gs = max(kMergeBatch, ceil_div_i(count, kMergeGroups));
+  const int32_t gs = max(kMergeBatch, ceil_div_i(count, kGroups));
   const int32_t ngroups = ceil_div_i(count, gs);
 
-  MergeState total = {-INFINITY, 0.f, 0.f};
+  MergeState<EPL> total;
+  total.m = -INFINITY;
+  total.l = 0.f;
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) total.acc[i] = 0.f;
   if (MW == 1) {
     for (int32_t g = 0; g < ngroups; ++g)
-      combine_state(total, fold_partials<HU>(a, first, g * gs, min(count, (g + 1) * gs), h, ec));
+      combine_state(total,
+                    fold_partials<HU, EPL>(a, first, g * gs, min(count, (g + 1) * gs), h, ec));
   } else {
     for (int32_t g = wave; g < ngroups; g += MW) {
-      const MergeState st = fold_partials<HU>(a, first, g * gs, min(count, (g + 1) * gs), h, ec);
+      const MergeState<EPL> st =
+          fold_partials<HU, EPL>(a, first, g * gs, min(count, (g + 1) * gs), h, ec);
       s_state[0][g][lane] = st.m;
       s_state[1][g][lane] = st.l;
-      s_state[2][g][lane] = st.acc;
+#pragma unroll
+      for (int i = 0; i < EPL; ++i) s_state[2 + i][g][lane] = st.acc[i];
     }
     __syncthreads();
     if (wave != 0) return;
-    for (int32_t g = 0; g < ngroups; ++g)
-      combine_state(total, MergeState{s_state[0][g][lane], s_state[1][g][lane],
-                                      s_state[2][g][lane]});
+    for (int32_t g = 0; g < ngroups; ++g) {
+      MergeState<EPL> st;
+      st.m = s_state[0][g][lane];
+      st.l = s_state[1][g][lane];
+#pragma unroll
+      for (int i = 0; i < EPL; ++i) st.acc[i] = s_state[2 + i][g][lane];
+      combine_state(total, st);
+    }
   }
   if (e >= elems) return;
   const int64_t orow = static_cast<int64_t>(b) * H + h;
   const int32_t c = e - h * dv;
-  a.out[orow * dv + c] = (total.l > 0.f) ? total.acc / total.l : 0.f;
+#pragma unroll
+  for (int i = 0; i < EPL; ++i)
+    a.out[orow * dv + c + i] = (total.l > 0.f) ? total.acc[i] / total.l : 0.f;
   if (c == 0 && a.lse != nullptr)
     a.lse[orow] = (total.l > 0.f) ? (total.m + log2f(total.l)) * 0.69314718055994530942f
                                   : -INFINITY;
@@ -248,22 +306,37 @@ hipError_t launch_clear_counters(void* ws, hipStream_t st) {
 
 hipError_t launch_attn_merge(const lsa_shape& s, const AttnArgs& a, const AttnPlan& plan,
                              hipStream_t st) {
-  const int32_t nblk = (s.num_q_heads * s.head_dim_v + kWave - 1) / kWave;
-  const int64_t grid = static_cast<int64_t>(nblk) * s.batch;
   // one wave per workgroup while a stream has a couple of groups of partials
   // on average, eight when streams have many (a long single stream)
   const bool one = plan.grid <= static_cast<int64_t>(2 * kMergeBatch) * s.batch;
   // a block of 64 output elements lies inside one head when dv is a multiple of 64
   const bool hu = s.head_dim_v % kWave == 0;
-  const dim3 g(static_cast<uint32_t>(grid));
+  if (a.o_bf16) {
+    // bf16 partials: two elements per lane (one 4-byte load per partial), a
+    // block of 128 inside one head; sixteen waves, so that each folds one
+    // group of a long stream.  Measured at 1 x 1M (239 partials, attention
+    // phase, interleaved on one box): 34.0 us with eight waves, 33.5 with
+    // sixteen, the same with four elements per lane, 35.5 with eight.
+    constexpr int EPL = 2;
+    if (s.head_dim_v % (EPL * kWave) != 0) return hipErrorNotSupported;
+    const int32_t nblk = s.num_q_heads * s.head_dim_v / (EPL * kWave);
+    const dim3 g(static_cast<uint32_t>(static_cast<int64_t>(nblk) * s.batch));
+    if (one)
+      hipLaunchKernelGGL((merge_kernel<1, true, EPL>), g, dim3(kWave), 0, st, a, nblk);
+    else
+      hipLaunchKernelGGL((merge_kernel<16, true, EPL>), g, dim3(16 * kWave), 0, st, a, nblk);
+    return hipGetLastError();
+  }
+  const int32_t nblk = (s.num_q_heads * s.head_dim_v + kWave - 1) / kWave;
+  const dim3 g(static_cast<uint32_t>(static_cast<int64_t>(nblk) * s.batch));
   if (one && hu)
-    hipLaunchKernelGGL((merge_kernel<1, true>), g, dim3(kWave), 0, st, a, nblk);
+    hipLaunchKernelGGL((merge_kernel<1, true, 1>), g, dim3(kWave), 0, st, a, nblk);
   else if (one)
-    hipLaunchKernelGGL((merge_kernel<1, false>), g, dim3(kWave), 0, st, a, nblk);
+    hipLaunchKernelGGL((merge_kernel<1, false, 1>), g, dim3(kWave), 0, st, a, nblk);
   else if (hu)
-    hipLaunchKernelGGL((merge_kernel<8, true>), g, dim3(8 * kWave), 0, st, a, nblk);
+    hipLaunchKernelGGL((merge_kernel<8, true, 1>), g, dim3(8 * kWave), 0, st, a, nblk);
   else
-    hipLaunchKernelGGL((merge_kernel<8, false>), g, dim3(8 * kWave), 0, st, a, nblk);
+    hipLaunchKernelGGL((merge_kernel<8, false, 1>), g, dim3(8 * kWave), 0, st, a, nblk);
   return hipGetLastError();
 }
 

@@ -22,7 +22,8 @@
 // so the matrix work is split evenly with nothing computed twice, and a wave
 // holds 64 accumulator registers.  The transposed products keep the softmax
 // state of a head in one lane (no cross-lane traffic to rescale), as in the
-// MQA kernel.  Each pair writes the partial result of its own heads.
+// MQA kernel.  Each pair writes the partial result of its own heads: the
+// maximum and sum in fp32, the unnormalised output row rounded to bf16.
 #include <math.h>
 
 #include "lsa_internal.hpp"
@@ -32,6 +33,7 @@ namespace lsa {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -456,11 +458,23 @@ __global__ __launch_bounds__(kMlaThreads, 1) void attn_mla_kernel(AttnArgs a) {
       a.ws_l[wg * H + head] = lt;
     }
   }
+  // The output rows as bf16 (64 KiB per workgroup at 64 heads), written
+  // through in 16-byte pieces.  Lane (r16, g) holds columns 4g .. 4g+3 of
+  // each 16-column block; for a pair of blocks (c, c+1) one permlane16_swap
+  // per 32-bit word hands an even-row lane (g = 0, 2) columns 4g .. 4g+7 of
+  // block c and an odd-row lane columns 4(g-1) .. 4g+3 of block c+1.
+  unsigned char* ob = reinterpret_cast<unsigned char*>(a.ws_o) + wg * H * kMlaDv * 2;
+  const int odd = g & 1;
 #pragma unroll
-  for (int c = 0; c < kMlaDv / 32; ++c)  // 128 KiB per workgroup: written through
-    store_through_16(a.ws_o + wg * H * kMlaDv,
-                     static_cast<uint32_t>((head * kMlaDv + half * (kMlaDv / 2) + 4 * g + c * 16) * 4),
-                     __builtin_bit_cast(st_u32x4, o[c]));
+  for (int c = 0; c < kMlaDv / 32; c += 2) {
+    const st_u32x2 pa = __builtin_bit_cast(st_u32x2, __builtin_convertvector(o[c], bf16x4));
+    const st_u32x2 pb = __builtin_bit_cast(st_u32x2, __builtin_convertvector(o[c + 1], bf16x4));
+    const auto x = __builtin_amdgcn_permlane16_swap(pa.x, pb.x, false, false);
+    const auto y = __builtin_amdgcn_permlane16_swap(pa.y, pb.y, false, false);
+    const int col = half * (kMlaDv / 2) + 16 * (c + odd) + 8 * (g >> 1);
+    store_through_16(reinterpret_cast<float*>(ob), static_cast<uint32_t>((head * kMlaDv + col) * 2),
+                     st_u32x4{x[0], y[0], x[1], y[1]});
+  }
 }
 
 }  // namespace

@@ -155,6 +155,7 @@ lsa_status enqueue_attention(const lsa_shape& s, const AttnSetup& setup, int32_t
   a.ws_m = reinterpret_cast<float*>(static_cast<char*>(ws) + pl.m_off);
   a.ws_l = reinterpret_cast<float*>(static_cast<char*>(ws) + pl.l_off);
   a.ws_o = reinterpret_cast<float*>(static_cast<char*>(ws) + pl.o_off);
+  a.o_bf16 = partial_o_bf16(s) ? 1 : 0;
   a.counters = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + pl.cnt_off);
   // in-kernel merge, or the merge launch after the partial kernel
   const bool fused = !partial_only && fuse_merge_in_kernel(s, plan);

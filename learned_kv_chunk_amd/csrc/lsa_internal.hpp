@@ -68,14 +68,18 @@ int32_t device_cu_count();
 // 0 for every shape (so that no shape's partials ever overlap another shape's
 // counters in a shared workspace; they are zero between calls, every launch
 // leaves them as it found them); then the split-KV partials m[rows][H],
-// l[rows][H] (fp32, log2 domain max and sum) and o[rows][H][dv] (fp32,
-// unnormalised), rows = ws_rows.  Batches of more than kCounterStreams
-// streams merge in a separate launch.
+// l[rows][H] (fp32, log2 domain max and sum) and o[rows][H][dv]
+// (unnormalised; fp32, or bf16 where partial_o_bf16 holds), rows = ws_rows.
+// Batches of more than kCounterStreams streams merge in a separate launch.
 constexpr int32_t kCounterStreams = 16384;
 struct PartialLayout {
   size_t m_off, l_off, o_off, cnt_off, total;
 };
 PartialLayout partial_layout(const lsa_shape& s, const AttnPlan& p);
+// Whether the partial output rows o are stored as bf16 (the absorbed-MLA
+// kernel: 64 heads x 512 latent columns per partial, so the partials are a
+// large fraction of a step's bytes; the maxima and sums stay fp32).
+bool partial_o_bf16(const lsa_shape& s);
 
 struct AttnArgs {
   const void* q;          // [B][H][dqk]
@@ -89,7 +93,8 @@ struct AttnArgs {
   float* lse;
   float* ws_m;
   float* ws_l;
-  float* ws_o;
+  float* ws_o;             // fp32 partial rows, or (o_bf16) the same region as bf16 bits
+  int32_t o_bf16;          // 1: partial rows are bf16 (partial_o_bf16)
   int32_t* counters;      // per-stream arrival counters (zero between calls)
   int32_t fuse_merge;     // 1: the partial kernel merges each stream itself
   // In-kernel top-k (sel_scores non-null): every workgroup ranks its
@@ -479,10 +484,17 @@ __device__ __forceinline__ void store_coherent(float* p, float v) {
 // us; 4 x 512K: 25.4 -> 24.3 us); for 8 KiB partials it was slower (16 x
 // 128K: 28.0 -> 28.5 us), interleaved on one box.
 typedef uint32_t st_u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t st_u32x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ void store_through_16(float* base, uint32_t byte_off, st_u32x4 v) {
   const __amdgpu_buffer_rsrc_t r =
       __builtin_amdgcn_make_buffer_rsrc(base, 0, 0x7fffffff, 0x00020000);
   __builtin_amdgcn_raw_buffer_store_b128(v, r, byte_off, 0, 16 /* sc1 */);
+}
+// The same for 8 bytes.
+__device__ __forceinline__ void store_through_8(void* base, uint32_t byte_off, st_u32x2 v) {
+  const __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc(base, 0, 0x7fffffff, 0x00020000);
+  __builtin_amdgcn_raw_buffer_store_b64(v, r, byte_off, 0, 16 /* sc1 */);
 }
 
 // Merge of one stream's split-KV partials by the NT threads of the stream's
