@@ -273,6 +273,27 @@ def test_workspace_holds_every_partial():
             assert lsa.workspace_bytes(s) >= need, (per, B, k, H, dv)
 
 
+def test_workspace_holds_every_mla_partial():
+    # absorbed MLA: the output rows of its partials are bf16 (2 bytes per
+    # latent column), the maxima and sums fp32
+    for per in [4, 8, 64, 256]:
+        for H, k in [(64, 655), (16, 40), (1, 8)]:
+            s = shape(batch=1, max_k=k, total_k=k, num_q_heads=H, head_dim_qk=576,
+                      head_dim_v=512, v_aliases_k=1, chunk_size=128,
+                      softmax_scale=576 ** -0.5, attn_tiles_per_block=per,
+                      max_chunks=8192, total_chunks=8192, index_dim=256)
+            tiles = k * 4
+            wgs = -(-tiles // per) + 1
+            need = wgs * H * (512 * 2 + 2 * 4)
+            assert lsa.workspace_bytes(s) >= need, (per, H, k)
+    # the 1M-token shape's default plan (about 256 workgroups): half of what
+    # fp32 rows would take
+    s = shape(batch=1, max_k=655, total_k=655, num_q_heads=64, head_dim_qk=576,
+              head_dim_v=512, v_aliases_k=1, chunk_size=128, softmax_scale=576 ** -0.5,
+              max_chunks=8192, total_chunks=8192, index_dim=256)
+    assert lsa.workspace_bytes(s) < 256 * 64 * 512 * 4
+
+
 def _mh(s, heads=128, dim=128, q=DUMMY, w=DUMMY, rec=DUMMY, co=DUMMY, out=DUMMY):
     return lsa.library().lsa_score_fp8_multihead(ctypes.byref(s.c()), heads, dim, q, w, rec, co,
                                                  out, None)
