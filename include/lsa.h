@@ -377,7 +377,9 @@ lsa_status lsa_pool_delta_update(const lsa_shape* shape, const void* k_host, con
  * computed split-KV: workgroups own runs of 32-token tiles, keep an fp32
  * online softmax, and their partial (max, sum, output) results are combined
  * by log-sum-exp (by the last workgroup of each stream to finish, or by a
- * merge pass).
+ * merge pass).  For absorbed latent attention the partial output rows are
+ * stored rounded to bf16 (at most 2^-9 relative per element); the maxima,
+ * the sums and the combination stay fp32.
  * q_dev: [B][H][head_dim_qk].  kv_mode LSA_KV_STORE: k_base/v_base are the
  * stores ([sum L][d]) and chunk sel_idx[s] of stream b is read in place.
  * kv_mode LSA_KV_POOL: k_base/v_base are pools written by lsa_gather_chunks
