@@ -130,17 +130,14 @@ struct MergeState {
 template <int EPL>
 __device__ __forceinline__ void load_partial(const AttnArgs& a, int64_t row, int32_t elems,
                                              int32_t ec, float (&v)[EPL]) {
+  static_assert(EPL == 1 || EPL == 2, "one fp32 element or two bf16 elements per lane");
   if constexpr (EPL == 1) {
     v[0] = a.ws_o[row * elems + ec];
-  } else {
-    typedef uint32_t w_t __attribute__((ext_vector_type(EPL / 2)));
-    const w_t w = *reinterpret_cast<const w_t*>(
+  } else {  // ec is even: the pair is one aligned 32-bit word
+    const uint32_t w = *reinterpret_cast<const uint32_t*>(
         reinterpret_cast<const uint16_t*>(a.ws_o) + (row * elems + ec));
-#pragma unroll
-    for (int i = 0; i < EPL / 2; ++i) {
-      v[2 * i] = __uint_as_float(w[i] << 16);
-      v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
-    }
+    v[0] = __uint_as_float(w << 16);
+    v[1] = __uint_as_float(w & 0xffff0000u);
   }
 }
 
